@@ -1,0 +1,444 @@
+"""Plain fp64 reference of the TurboQuant key path.  TEST INFRASTRUCTURE ONLY.
+
+Sources (cited by page title and section; see oracle/__init__.py):
+
+* [Qiita explainer]   "TurboQuant" explainer on qiita.com (kai_kou): sections
+  "Stage 1: PolarQuant", "Stage 2: QJL" (estimator equation), the community
+  compression table ("圧縮率（8Kコンテキスト、FP16ベースライン289MB）").
+* [ai.spot.hk]        "Google TurboQuant：LLM KV Cache 壓縮 6 倍…": sections
+  "隨機旋轉與Beta分佈" (per-coordinate quantisation after a random rotation) and
+  "無偏內積估計" (TURBOQUANT_prod: (b-1)-bit MSE stage + 1-bit QJL, total b
+  bits, unbiased inner products).
+* [ICLR 2026 digest]  "ICLR 2026論文解説: TurboQuant — Shannon限界に迫る…":
+  "Step 1: PolarQuant" (normalise, rotate, R = H_d D / sqrt(d), Sylvester
+  recursion, coordinates ~ N(0, 1/d)), "理論的保証" (Theorem 2),
+  "実装の擬似コード" (zero-vector rule, sign convention 0 = positive),
+  "実装のポイント" (norm stored on the side, 8 sign bits per byte).
+
+Readings where the pages are silent or disagree (each also listed in
+the design doc):
+
+* b counts all bits: (b-1) Lloyd-Max bits + 1 QJL bit per coordinate.
+* the codebook is Lloyd-Max for N(0, 1/d); the middle threshold is exactly 0.
+* code_i = number of thresholds t_j with y_i >= t_j (a tie goes up).
+* QJL sign bit = [ (S r)_j < 0 ]  (0 = positive, -0.0 counts as positive).
+* S has i.i.d. N(0, 1) entries, m rows; r is formed in the original domain.
+* both norms are stored as IEEE half (round to nearest even) and the
+  estimator uses the stored values.
+* delta and S come from a counter-based SplitMix64 stream (below), not from
+  numpy's RandomState: only their distribution matters to the method.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "splitmix64_draw", "rademacher_signs", "gaussian_sketch",
+    "sylvester_hadamard", "rotation_matrix", "lloyd_max_std_normal",
+    "Codebook", "make_codebook", "EncodeResult", "encode", "pack", "unpack",
+    "packed_nbytes", "decode_mse", "score", "estimate_inner_product",
+    "exact_logits", "top_k", "fp16_midpoint_flag", "ZERO_NORM",
+    "FLAG_BAND", "kv_bytes_per_vector",
+]
+
+ZERO_NORM = 1e-10      # zero-vector rule [ICLR 2026 digest, 実装の擬似コード]
+FLAG_BAND = 1e-6       # decision-boundary band used to flag parity cases
+
+_U64 = np.uint64
+_GAMMA = 0x9E3779B97F4A7C15          # SplitMix64 increment (Steele, Lea & Flood 2014)
+_M1 = 0xBF58476D1CE4E5B9
+_M2 = 0x94D049BB133111EB
+_MASK = (1 << 64) - 1
+
+
+# --------------------------------------------------------------------------
+# Seeded randomness: counter-based SplitMix64 (published generator).
+# --------------------------------------------------------------------------
+
+def _mix64_int(z: int) -> int:
+    """SplitMix64 output finaliser on one Python integer (mod 2**64)."""
+    z &= _MASK
+    z = ((z ^ (z >> 30)) * _M1) & _MASK
+    z = ((z ^ (z >> 27)) * _M2) & _MASK
+    return z ^ (z >> 31)
+
+
+def _mix64_arr(z: np.ndarray) -> np.ndarray:
+    z = z.astype(_U64, copy=True)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> _U64(30))) * _U64(_M1)
+        z = (z ^ (z >> _U64(27))) * _U64(_M2)
+    return z ^ (z >> _U64(31))
+
+
+def splitmix64_draw(seed: int, stream: int, index) -> np.ndarray:
+    """Draw number ``index`` of stream ``stream`` for ``seed`` (uint64).
+
+    base  = mix64(seed + stream * GAMMA)
+    draw  = mix64(base + (index + 1) * GAMMA)       (all mod 2**64)
+
+    i.e. the index-th output of a SplitMix64 sequence whose seed is itself
+    the stream-th SplitMix64 output of ``seed``.  Parity unpinned beyond the
+    two independent implementations of this definition agreeing bit for bit.
+    """
+    base = _mix64_int(seed + stream * _GAMMA)
+    idx = np.asarray(index, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        state = _U64(base) + (idx + _U64(1)) * _U64(_GAMMA)
+    return _mix64_arr(state)
+
+
+def rademacher_signs(seed: int, d: int) -> np.ndarray:
+    """delta_i in {+1, -1}: +1 when bit 63 of draw (stream 1, index i) is 0.
+
+    The Rademacher diagonal D of the rotation [ICLR 2026 digest, Step 1:
+    D has independent +-1 entries with equal probability].
+    """
+    x = splitmix64_draw(seed, 1, np.arange(d, dtype=np.uint64))
+    return np.where((x >> _U64(63)) == 0, 1, -1).astype(np.int8)
+
+
+def gaussian_sketch(seed: int, m: int, d: int) -> np.ndarray:
+    """S[j, i] ~ N(0, 1) by Box-Muller from stream-2 draws 2(jd+i), 2(jd+i)+1.
+
+    u1 = ((x >> 11) + 1) * 2**-53 in (0, 1], u2 = (y >> 11) * 2**-53 in [0, 1),
+    z = sqrt(-2 ln u1) cos(2 pi u2), rounded to float32 (nearest even).  The
+    QJL projection is a Gaussian random matrix [Qiita explainer, Stage 2].
+    libm's log/cos (math module) are used so that the host library, which
+    also calls libm, draws the same fp64 values.
+    """
+    n = m * d
+    draws = splitmix64_draw(seed, 2, np.arange(2 * n, dtype=np.uint64))
+    xs = (draws[0::2] >> _U64(11)).tolist()
+    ys = (draws[1::2] >> _U64(11)).tolist()
+    two53 = 2.0 ** -53
+    out = np.empty(n, dtype=np.float64)
+    log, cos, sqrt, tau = math.log, math.cos, math.sqrt, 2.0 * math.pi
+    for t in range(n):
+        u1 = (xs[t] + 1) * two53
+        u2 = ys[t] * two53
+        out[t] = sqrt(-2.0 * log(u1)) * cos(tau * u2)
+    return out.astype(np.float32).reshape(m, d)
+
+
+# --------------------------------------------------------------------------
+# Rotation: R = H_d D / sqrt(d)  [ICLR 2026 digest, Step 1, eq. for R].
+# --------------------------------------------------------------------------
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """H_1 = [1];  H_2n = [[H_n, H_n], [H_n, -H_n]]  (integer matrix)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def rotation_matrix(delta: np.ndarray) -> np.ndarray:
+    """Dense R = H_d diag(delta) / sqrt(d) in float64."""
+    d = delta.shape[0]
+    return sylvester_hadamard(d).astype(np.float64) * delta.astype(np.float64)[None, :] / math.sqrt(d)
+
+
+# --------------------------------------------------------------------------
+# Lloyd-Max quantizer for N(0, 1), then scaled to N(0, 1/d).
+# --------------------------------------------------------------------------
+
+def _phi(x: float) -> float:
+    return 0.0 if math.isinf(x) else math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _upper_tail(x: float) -> float:
+    """P(X >= x) for X ~ N(0,1), via erfc to keep tail accuracy."""
+    return 0.0 if math.isinf(x) else 0.5 * math.erfc(x / math.sqrt(2.0))
+
+
+def lloyd_max_std_normal(B: int, tol: float = 1e-15, max_iter: int = 100000):
+    """(levels[2**B], thresholds[2**B - 1]) of the MSE-optimal quantizer of N(0,1).
+
+    Lloyd's two conditions, iterated to a fixed point: every threshold is the
+    midpoint of its two neighbouring levels, every level is the conditional
+    mean of its cell, E[X | a <= X < b] = (phi(a) - phi(b)) / (Phi(b) - Phi(a)).
+    The law is symmetric and L is even, so the iteration runs on the positive
+    half with the middle threshold fixed at exactly 0 and the negative half
+    mirrored.  Shared by all coordinates, "zero memory overhead"
+    [Qiita explainer, Stage 1 step 3; ICLR 2026 digest, Step 1].
+    """
+    if B < 1:
+        raise ValueError("B >= 1")
+    K = (1 << B) // 2                      # levels on the positive half
+    c = [0.5 + 2.0 * (k + 0.5) / K for k in range(K)]   # any increasing start
+    for _ in range(max_iter):
+        t = [0.0] + [(c[k - 1] + c[k]) / 2.0 for k in range(1, K)] + [math.inf]
+        new = []
+        for k in range(K):
+            a, b = t[k], t[k + 1]
+            mass = _upper_tail(a) - _upper_tail(b)
+            new.append((_phi(a) - _phi(b)) / mass)
+        delta = max(abs(x - y) for x, y in zip(new, c))
+        c = new
+        if delta < tol:
+            break
+    pos_levels = np.array(c, dtype=np.float64)
+    pos_thr = np.array([(c[k - 1] + c[k]) / 2.0 for k in range(1, K)], dtype=np.float64)
+    levels = np.concatenate([-pos_levels[::-1], pos_levels])
+    thresholds = np.concatenate([-pos_thr[::-1], [0.0], pos_thr])
+    return levels, thresholds
+
+
+# --------------------------------------------------------------------------
+# Codebook = every piece of quantizer state derived from (d, b, m, seed).
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Codebook:
+    d: int
+    bits: int            # total bits per coordinate: (bits-1) Lloyd-Max + 1 QJL
+    m: int               # QJL sketch rows
+    seed: int
+    levels: np.ndarray   # [L] ascending, for N(0, 1/d)
+    thresholds: np.ndarray  # [L-1] ascending
+    delta: np.ndarray    # [d] int8 Rademacher signs
+    S: np.ndarray        # [m, d] float64 holding float32-rounded N(0,1) draws
+    R: np.ndarray        # [d, d] float64 dense rotation
+
+    @property
+    def B(self) -> int:
+        return self.bits - 1
+
+    @property
+    def L(self) -> int:
+        return 1 << (self.bits - 1)
+
+
+def make_codebook(d: int, bits: int, m: int, seed: int) -> Codebook:
+    """Quantizer state: Lloyd-Max for N(0,1/d) with L = 2**(bits-1) levels
+    (scale equivariance: N(0,1) levels times 1/sqrt(d)), delta and S from the
+    seed, and the dense rotation.  [ai.spot.hk, 無偏內積估計: (b-1)-bit MSE
+    stage; ICLR 2026 digest, Step 1: coordinates ~ N(0, 1/d)]."""
+    if bits < 2:
+        raise ValueError("bits >= 2 (one bit is the QJL sign)")
+    lv, th = lloyd_max_std_normal(bits - 1)
+    sigma = 1.0 / math.sqrt(d)
+    delta = rademacher_signs(seed, d)
+    S = gaussian_sketch(seed, m, d).astype(np.float64)
+    return Codebook(d=d, bits=bits, m=m, seed=seed, levels=lv * sigma,
+                    thresholds=th * sigma, delta=delta, S=S,
+                    R=rotation_matrix(delta))
+
+
+# --------------------------------------------------------------------------
+# Encode  [ICLR 2026 digest, Step 1 + 実装の擬似コード; Qiita explainer,
+# Stage 2; ai.spot.hk, 無偏內積估計].
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class EncodeResult:
+    codes: np.ndarray      # [n, d] uint8 level index
+    signs: np.ndarray      # [n, m] uint8, 1 = (S r)_j < 0
+    nu: np.ndarray         # [n] fp64 ||k||
+    rho: np.ndarray        # [n] fp64 ||k - k_mse||
+    nu16: np.ndarray       # [n] float16 stored norm
+    rho16: np.ndarray      # [n] float16 stored residual norm
+    y: np.ndarray          # [n, d] rotated unit key
+    p: np.ndarray          # [n, m] S r
+    zero: np.ndarray       # [n] bool: zero-vector rule applied
+    code_flag: np.ndarray  # [n, d] y within FLAG_BAND of a threshold
+    sign_flag: np.ndarray  # [n, m] |p|/nu within FLAG_BAND of 0
+    nu16_flag: np.ndarray  # [n] nu within FLAG_BAND (relative) of an fp16 midpoint
+    rho16_flag: np.ndarray
+    zero_flag: np.ndarray  # [n] nu within FLAG_BAND (relative) of ZERO_NORM
+
+
+def fp16_midpoint_flag(v: np.ndarray, band: float = FLAG_BAND) -> np.ndarray:
+    """True where v lies within ``band`` (relative) of a point halfway
+    between two adjacent float16 values, i.e. where float32 and float64
+    rounding to half may legitimately disagree by one ulp."""
+    v = np.asarray(v, dtype=np.float64)
+    lo = v.astype(np.float16)
+    lo = np.where(lo.astype(np.float64) > v, np.nextafter(lo, np.float16(-np.inf)), lo)
+    hi = np.nextafter(lo, np.float16(np.inf))
+    mid = (lo.astype(np.float64) + hi.astype(np.float64)) / 2.0
+    return np.abs(v - mid) <= band * np.abs(v)
+
+
+def quantize_rotated(cb: Codebook, y: np.ndarray) -> np.ndarray:
+    """code = #{j : y >= t_j}  (levels ascending, ties go up)."""
+    return np.searchsorted(cb.thresholds, y, side="right").astype(np.uint8)
+
+
+def encode(cb: Codebook, keys: np.ndarray, S: Optional[np.ndarray] = None) -> EncodeResult:
+    """Encode rows of ``keys`` ([n, d], any float dtype, used as exact fp64).
+
+    Per key k: nu = ||k||; if nu < 1e-10 the record is all zero.  Otherwise
+    x = k / nu, y = R x, code_i = #{t_j <= y_i}, k_mse = nu R^T c[code],
+    r = k - k_mse, rho = ||r||, p = S r, sign bit_j = [p_j < 0];
+    nu and rho are stored as float16.  ``S`` overrides the codebook's sketch
+    (Monte-Carlo tests).
+    """
+    S = cb.S if S is None else np.asarray(S, dtype=np.float64)
+    k = np.asarray(keys, dtype=np.float64)
+    n, d = k.shape
+    assert d == cb.d
+    nu = np.sqrt(np.sum(k * k, axis=1))
+    zero = nu < ZERO_NORM
+    safe = np.where(zero, 1.0, nu)
+    x = k / safe[:, None]
+    y = x @ cb.R.T                                   # y = R x
+    codes = quantize_rotated(cb, y)
+    yhat = cb.levels[codes]
+    k_mse = safe[:, None] * (yhat @ cb.R)            # nu R^T yhat
+    r = k - k_mse
+    rho = np.sqrt(np.sum(r * r, axis=1))
+    p = r @ S.T                                      # S r
+    signs = (p < 0).astype(np.uint8)
+    codes[zero] = 0
+    signs[zero] = 0
+    rho = np.where(zero, 0.0, rho)
+    nu_st = np.where(zero, 0.0, nu)
+    dist = np.min(np.abs(y[:, :, None] - cb.thresholds[None, None, :]), axis=2)
+    code_flag = (dist <= FLAG_BAND) & ~zero[:, None]
+    sign_flag = (np.abs(p) / safe[:, None] <= FLAG_BAND) & ~zero[:, None]
+    return EncodeResult(
+        codes=codes, signs=signs, nu=nu_st, rho=rho,
+        nu16=nu_st.astype(np.float16), rho16=rho.astype(np.float16),
+        y=y, p=p, zero=zero, code_flag=code_flag, sign_flag=sign_flag,
+        nu16_flag=fp16_midpoint_flag(nu_st) & ~zero,
+        rho16_flag=fp16_midpoint_flag(rho) & ~zero,
+        zero_flag=np.abs(nu - ZERO_NORM) <= FLAG_BAND * ZERO_NORM)
+
+
+# --------------------------------------------------------------------------
+# Packed layout (the library's record format, implemented here on its own).
+#   planes: uint32 [G][P][N][d/32], P = bits; planes 0..bits-2 hold code bit
+#           p (LSB first), plane bits-1 holds the QJL sign bits (m = d);
+#           bit j of word w is coordinate (or sketch row) 32 w + j;
+#   then norms: uint32 [G][N] = half(nu) | half(rho) << 16.
+# Eight sign bits per byte [ICLR 2026 digest, 実装のポイント].
+# --------------------------------------------------------------------------
+
+def packed_nbytes(cb: Codebook, G: int, N: int) -> int:
+    return G * N * (cb.B * cb.d // 8 + cb.m // 8 + 4)
+
+
+def _bits_to_words(bits: np.ndarray) -> np.ndarray:
+    """[..., 32 W] of 0/1 -> [..., W] uint32 with bit j of word w = element 32w+j."""
+    sh = bits.shape
+    b = bits.reshape(sh[:-1] + (sh[-1] // 32, 32)).astype(np.uint64)
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    return (b * weights).sum(axis=-1).astype(np.uint32)
+
+
+def _words_to_bits(words: np.ndarray) -> np.ndarray:
+    w = words.astype(np.uint64)[..., None]
+    bits = (w >> np.arange(32, dtype=np.uint64)) & np.uint64(1)
+    return bits.reshape(words.shape[:-1] + (words.shape[-1] * 32,)).astype(np.uint8)
+
+
+def pack(cb: Codebook, codes, signs, nu16, rho16) -> np.ndarray:
+    """codes [G,N,d], signs [G,N,m], nu16/rho16 [G,N] -> uint8 buffer."""
+    assert cb.m == cb.d, "the packed layout stores m = d sign bits"
+    codes = np.asarray(codes, dtype=np.uint8)
+    G, N, d = codes.shape
+    planes = np.empty((G, cb.bits, N, d // 32), dtype=np.uint32)
+    for p in range(cb.B):
+        planes[:, p] = _bits_to_words((codes >> p) & 1)
+    planes[:, cb.B] = _bits_to_words(np.asarray(signs, dtype=np.uint8))
+    nb = np.asarray(nu16, dtype=np.float16).view(np.uint16).astype(np.uint32)
+    rb = np.asarray(rho16, dtype=np.float16).view(np.uint16).astype(np.uint32)
+    norms = (nb | (rb << np.uint32(16))).astype(np.uint32)
+    out = np.concatenate([planes.reshape(-1).view(np.uint8), norms.reshape(-1).view(np.uint8)])
+    assert out.size == packed_nbytes(cb, G, N)
+    return out
+
+
+def unpack(cb: Codebook, buf: np.ndarray, G: int, N: int):
+    """Inverse of :func:`pack`: (codes [G,N,d], signs [G,N,m], nu16, rho16)."""
+    buf = np.ascontiguousarray(np.asarray(buf).reshape(-1).view(np.uint8))
+    assert buf.size == packed_nbytes(cb, G, N)
+    d = cb.d
+    nplane = G * cb.bits * N * (d // 32)
+    planes = buf[: nplane * 4].view(np.uint32).reshape(G, cb.bits, N, d // 32)
+    norms = buf[nplane * 4:].view(np.uint32).reshape(G, N)
+    codes = np.zeros((G, N, d), dtype=np.uint8)
+    for p in range(cb.B):
+        codes |= (_words_to_bits(planes[:, p]) << p).astype(np.uint8)
+    signs = _words_to_bits(planes[:, cb.B])
+    nu16 = (norms & np.uint32(0xFFFF)).astype(np.uint16).view(np.float16)
+    rho16 = (norms >> np.uint32(16)).astype(np.uint16).view(np.float16)
+    return codes, signs, nu16, rho16
+
+
+# --------------------------------------------------------------------------
+# Decode and score.
+# --------------------------------------------------------------------------
+
+def decode_mse(cb: Codebook, buf: np.ndarray, G: int, N: int) -> np.ndarray:
+    """k_mse = nu~ R^T c[code] for every record: [G, N, d] fp64.  The MSE-only
+    reconstruction (what the community API calls the MSE compressor
+    [Qiita explainer, API table])."""
+    codes, _, nu16, _ = unpack(cb, buf, G, N)
+    return nu16.astype(np.float64)[..., None] * (cb.levels[codes] @ cb.R)
+
+
+def estimate_inner_product(q, k_mse, rho, S, sign_bits) -> np.ndarray:
+    """<q, k_mse> + rho * sqrt(pi/2) / m * <S q, sign(S r)>
+    [Qiita explainer, Stage 2: QJL, estimator equation].
+
+    q [..., d]; k_mse [..., d]; rho [...]; S [m, d]; sign_bits [..., m] with
+    1 meaning a negative projection.  Broadcasting over leading axes."""
+    m = S.shape[0]
+    q = np.asarray(q, dtype=np.float64)
+    sgn = 1.0 - 2.0 * np.asarray(sign_bits, dtype=np.float64)
+    return (np.sum(q * k_mse, axis=-1)
+            + np.asarray(rho, dtype=np.float64) * math.sqrt(math.pi / 2.0) / m
+            * np.sum((q @ S.T) * sgn, axis=-1))
+
+
+def score(cb: Codebook, buf: np.ndarray, G: int, N: int, q: np.ndarray) -> np.ndarray:
+    """Logits [G, Qg, N] of queries q [G, Qg, d] against the packed keys of
+    their group, from the stored record only (so it can score any producer's
+    buffer).  Queries stay full precision; keys are never dequantised by the
+    estimator's definition beyond k_mse."""
+    q = np.asarray(q, dtype=np.float64)
+    codes, signs, nu16, rho16 = unpack(cb, buf, G, N)
+    k_mse = nu16.astype(np.float64)[..., None] * (cb.levels[codes] @ cb.R)   # [G,N,d]
+    sgn = 1.0 - 2.0 * signs.astype(np.float64)                                # [G,N,m]
+    sq = q @ cb.S.T                                                           # [G,Qg,m]
+    mse = np.einsum("gqd,gnd->gqn", q, k_mse)
+    qjl = np.einsum("gqm,gnm->gqn", sq, sgn)
+    return mse + rho16.astype(np.float64)[:, None, :] * math.sqrt(math.pi / 2.0) / cb.m * qjl
+
+
+def exact_logits(keys: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Unquantised q . k in fp64: keys [G, N, d], q [G, Qg, d] -> [G, Qg, N]."""
+    return np.einsum("gqd,gnd->gqn", np.asarray(q, np.float64), np.asarray(keys, np.float64))
+
+
+def top_k(scores: np.ndarray, k: int):
+    """Per row: the k largest scores, ordered by score descending and then by
+    index ascending.  Returns (indices int64, values)."""
+    s = np.asarray(scores)
+    n = s.shape[-1]
+    idx = np.lexsort((np.broadcast_to(np.arange(n), s.shape), -s), axis=-1)[..., :k]
+    return idx, np.take_along_axis(s, idx, axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Byte accounting of the packed cache (keys) and an MSE-only value cache.
+# --------------------------------------------------------------------------
+
+def kv_bytes_per_vector(d: int, bits: int):
+    """(key bytes, value bytes) per cached vector: keys hold (bits-1)-bit codes,
+    d sign bits and two half norms; values hold bits-bit MSE codes and one
+    half norm.  Reproduces the community compression table on the Qiita
+    explainer only with half-precision norms."""
+    key = (bits - 1) * d // 8 + d // 8 + 4
+    val = bits * d // 8 + 2
+    return key, val
