@@ -273,14 +273,17 @@ def quantize_rotated(cb: Codebook, y: np.ndarray) -> np.ndarray:
     return np.searchsorted(cb.thresholds, y, side="right").astype(np.uint8)
 
 
-def encode(cb: Codebook, keys: np.ndarray, S: Optional[np.ndarray] = None) -> EncodeResult:
+def encode(cb: Codebook, keys: np.ndarray, S: Optional[np.ndarray] = None,
+           codes: Optional[np.ndarray] = None) -> EncodeResult:
     """Encode rows of ``keys`` ([n, d], any float dtype, used as exact fp64).
 
     Per key k: nu = ||k||; if nu < 1e-10 the record is all zero.  Otherwise
     x = k / nu, y = R x, code_i = #{t_j <= y_i}, k_mse = nu R^T c[code],
     r = k - k_mse, rho = ||r||, p = S r, sign bit_j = [p_j < 0];
     nu and rho are stored as float16.  ``S`` overrides the codebook's sketch
-    (Monte-Carlo tests).
+    (Monte-Carlo tests); ``codes`` ([n, d]) replaces the threshold decision
+    so that the residual stage can be recomputed for codes another encoder
+    chose at a flagged boundary coordinate.
     """
     S = cb.S if S is None else np.asarray(S, dtype=np.float64)
     k = np.asarray(keys, dtype=np.float64)
@@ -289,9 +292,13 @@ def encode(cb: Codebook, keys: np.ndarray, S: Optional[np.ndarray] = None) -> En
     nu = np.sqrt(np.sum(k * k, axis=1))
     zero = nu < ZERO_NORM
     safe = np.where(zero, 1.0, nu)
-    x = k / safe[:, None]
-    y = x @ cb.R.T                                   # y = R x
-    codes = quantize_rotated(cb, y)
+    # y = R x = H_d (D k) / (nu sqrt(d)): the integer matrix H_d is applied to
+    # D k first, so a coordinate that is exactly zero stays exactly zero (fp64
+    # sums of float32/bf16 inputs are exact) and the tie rule sees it as such.
+    H = sylvester_hadamard(d).astype(np.float64)
+    u = (k * cb.delta.astype(np.float64)[None, :]) @ H.T
+    y = u / (safe[:, None] * math.sqrt(d))
+    codes = quantize_rotated(cb, y) if codes is None else np.array(codes, dtype=np.uint8)
     yhat = cb.levels[codes]
     k_mse = safe[:, None] * (yhat @ cb.R)            # nu R^T yhat
     r = k - k_mse

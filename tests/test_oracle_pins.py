@@ -425,3 +425,21 @@ def test_fp16_midpoint_flag():
     mid = (float(a) + float(b)) / 2
     f = O.fp16_midpoint_flag(np.array([mid, mid * (1 + 2e-6), float(a), 1.0003]))
     assert f.tolist() == [True, False, False, False]
+
+
+def test_exact_zero_coordinates_take_the_upper_middle_level():
+    """k = e_0 + e_1 rotates to coordinates (+-delta_0 +- delta_1)/(sqrt(2d)),
+    exactly zero on half of them (Sylvester rows i and the sign pattern of
+    delta); a value on the middle threshold 0 goes up, to level L/2."""
+    d = 128
+    for bits in (2, 3, 4):
+        cb = O.make_codebook(d, bits, d, 42)
+        k = np.zeros((1, d))
+        k[0, :2] = 1.0
+        e = O.encode(cb, k)
+        H = O.sylvester_hadamard(d)
+        zero = (cb.delta[0] * H[:, 0] + cb.delta[1] * H[:, 1]) == 0
+        assert zero.sum() == d // 2
+        assert np.all(e.y[0][zero] == 0.0)
+        assert np.all(e.codes[0][zero] == cb.L // 2)
+        assert np.allclose(np.abs(e.y[0][~zero]), 1.0 / math.sqrt(d // 2), rtol=1e-15)
