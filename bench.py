@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant key path on one MI355X.
+
+One step = the whole hot path over one batch: encode a full key cache
+(1,048,576 bf16 keys of the Llama-3.1-8B-shaped decode workload: batch 16,
+8 KV heads x 8192 positions, d = 128, b = 3) and score one decode step of
+queries (32 heads, GQA 4) against a packed cache.  Inputs are resident in
+HBM before timing starts; buffers rotate over more than the 256 MB
+Infinity Cache so that every launch streams from HBM.
+
+Prints one JSON line (driver contract) with the end-to-end keys/s, per
+kernel throughput, the roofline of the dominant kernel (HIP events on the
+launch stream), and the oracle timed on the host cores on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed keys scored/s + HBM GB/s (d=128, b=3); keys encoded/s"
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload (1 = the headline decode config)")
+    ap.add_argument("--bits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in ("kv_cache_vector_rotate_amd/csrc/tq_kernels.hip", "kv_cache_vector_rotate_amd/csrc/tq_host.cpp"):
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole groups, encode + score, until ~budget_s of work."""
+    import oracle as O
+    from kv_cache_vector_rotate_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    cbo = O.make_codebook(wl.d, wl.bits, wl.m, 42)
+    keys_done, t_work, groups = 0, 0.0, 0
+    for g in range(wl.G):
+        k = W.group_keys(wl, g)
+        q = W.group_queries(wl, g)
+        t0 = time.perf_counter()
+        e = O.encode(cbo, k)
+        buf = O.pack(cbo, e.codes[None], e.signs[None], e.nu16[None], e.rho16[None])
+        O.score(cbo, buf, 1, wl.N, q[None])
+        t_work += time.perf_counter() - t0
+        keys_done += wl.N
+        groups += 1
+        if t_work >= budget_s:
+            break
+    return {"value": keys_done / t_work, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{groups} of {wl.G} groups ({keys_done} keys): fp64 encode + pack + score of "
+                      f"{wl.Qg} queries per group, {t_work:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_vector_rotate_amd as K
+    from kv_cache_vector_rotate_amd import workloads as W
+
+    wl = W.workload(args.config, bits=args.bits)
+    G, N, Qg, d, bits = wl.G, wl.N, wl.Qg, wl.d, wl.bits
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    keys_np = W.all_keys(wl)
+    q_np = W.all_queries(wl)
+    if wl.key_dtype == "bf16":
+        keys0 = torch.from_numpy(keys_np.view(np.int16)).to(dev).view(torch.bfloat16)
+        q = torch.from_numpy(q_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        keys0 = torch.from_numpy(keys_np).to(dev)
+        q = torch.from_numpy(q_np).to(dev)
+    del keys_np
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    cb = K.Codebook(d, bits, d, 42)
+    key_bytes = keys0.numel() * keys0.element_size()
+    pbytes = K.packed_nbytes(cb, G, N)
+    logit_bytes = G * Qg * N * 4
+    mall = 256 << 20
+    nk = max(2, -(-3 * mall // key_bytes))          # key copies
+    npk = max(4, -(-3 * mall // pbytes))            # packed copies
+    nl = max(2, -(-mall // logit_bytes))
+    keys = [keys0] + [keys0.clone() for _ in range(nk - 1)]
+    packed = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(npk)]
+    logits = [torch.empty((G, Qg, N), dtype=torch.float32, device=dev) for _ in range(nl)]
+    ws = torch.empty(max(16, K.score_workspace_nbytes(cb, G, Qg)), dtype=torch.uint8, device=dev)
+    for i in range(npk):
+        K.encode_keys(cb, keys[i % nk], out=packed[i])
+    torch.cuda.synchronize()
+
+    def step(i, evs=None):
+        if evs is not None:
+            evs[0].record()
+        K.encode_keys(cb, keys[i % nk], out=packed[i % npk])
+        if evs is not None:
+            evs[1].record()
+        # score a cache encoded earlier (not the one just written, which may still
+        # sit in the Infinity Cache)
+        K.score_logits(cb, q, packed[(i + npk // 2) % npk], N, out=logits[i % nl], ws=ws)
+        if evs is not None:
+            evs[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    sc_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    keys_per_step = G * N
+    ms_per_step = wall * 1e3 / args.steps
+    enc_alg = key_bytes + pbytes                               # read keys, write records
+    q_bytes = q.numel() * q.element_size()
+    sc_alg = pbytes + logit_bytes + q_bytes                    # read records + queries, write logits
+    enc_avg_s = enc_ms.mean() * 1e-3
+    sc_avg_s = sc_ms.mean() * 1e-3
+    enc_gbps = enc_alg / enc_avg_s / 1e9
+    sc_gbps = sc_alg / sc_avg_s / 1e9
+    dominant = "encode" if enc_avg_s >= sc_avg_s else "score"
+    traffic = read_traffic(f"encode128_b{bits}_traffic.txt" if dominant == "encode"
+                           else f"score128_b{bits}_traffic.txt")
+    roof = {"bound": "hbm", "kernel": "encode128_kernel" if dominant == "encode" else "score (prep + score128_kernel)",
+            "achieved": round(enc_gbps if dominant == "encode" else sc_gbps, 1),
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round((enc_gbps if dominant == "encode" else sc_gbps) / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(enc_alg if dominant == "encode" else sc_alg)}
+    out = {
+        "metric": METRIC,
+        "value": round(keys_per_step / (ms_per_step * 1e-3), 1),
+        "unit": "keys/s (encode full cache + score one decode step, per step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "groups": G, "keys_per_group": N, "queries_per_group": Qg,
+                   "d": d, "bits": bits, "m": wl.m, "key_dtype": wl.key_dtype},
+        "score": {"keys_per_s": round(keys_per_step / sc_avg_s, 1),
+                  "logits_per_s": round(G * Qg * N / sc_avg_s, 1),
+                  "hbm_GBps": round(sc_gbps, 1), "frac_of_peak": round(sc_gbps / PEAK_HBM_GBPS, 4),
+                  "packed_kv_GBps": round(pbytes / sc_avg_s / 1e9, 1),
+                  "us_median": round(float(np.median(sc_ms)) * 1e3, 2),
+                  "us_p10": round(float(np.percentile(sc_ms, 10)) * 1e3, 2),
+                  "us_p90": round(float(np.percentile(sc_ms, 90)) * 1e3, 2),
+                  "algorithmic_bytes": int(sc_alg)},
+        "encode": {"keys_per_s": round(keys_per_step / enc_avg_s, 1),
+                   "hbm_GBps": round(enc_gbps, 1), "frac_of_peak": round(enc_gbps / PEAK_HBM_GBPS, 4),
+                   "packed_kv_GBps": round(pbytes / enc_avg_s / 1e9, 1),
+                   "us_median": round(float(np.median(enc_ms)) * 1e3, 2),
+                   "us_p10": round(float(np.percentile(enc_ms, 10)) * 1e3, 2),
+                   "us_p90": round(float(np.percentile(enc_ms, 90)) * 1e3, 2),
+                   "algorithmic_bytes": int(enc_alg)},
+        "roofline": roof,
+        "rotation": {"key_copies": nk, "packed_copies": npk, "logit_copies": nl},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * tq.h — C ABI of the TurboQuant key-path library for AMD Instinct MI355X
+ * (gfx950).  Plain pointers and sizes only; device pointers are HIP device
+ * allocations (for example torch tensors' data_ptr()), streams are
+ * hipStream_t passed as void* (NULL = the default stream).
+ *
+ * The operation it implements, from the pages:
+ *  - keys are normalised, rotated with R = H_d D / sqrt(d) (Sylvester
+ *    Hadamard H_d, Rademacher diagonal D), and each rotated coordinate,
+ *    approximately N(0, 1/d), is coded by a shared Lloyd-Max scalar quantizer
+ *    [ICLR 2026 paper digest (0h-n0.github.io), "Step 1: PolarQuant", eq. for R
+ *    and Theorem 1; Qiita explainer (kai_kou), "Stage 1" step 3];
+ *  - with b total bits, b-1 bits go to that MSE stage and 1 bit to a QJL sign
+ *    sketch of the residual [ai.spot.hk TurboQuant article, "無偏內積估計"];
+ *  - a full-precision query is scored against the packed key with
+ *      <q,k> ~ <q,k_mse> + ||r|| sqrt(pi/2)/m <S q, sign(S r)>
+ *    [Qiita explainer, "Stage 2: QJL", estimator equation];
+ *  - the norm is kept on the side and zero vectors (||k|| < 1e-10) give an
+ *    all-zero record [ICLR 2026 paper digest, "実装の擬似コード",
+ *    "実装のポイント"].
+ *
+ * Packed key record layout (one buffer for G groups x N keys, m = d):
+ *   planes: uint32 [G][bits][N][d/32].  Planes 0..bits-2 hold bit p of the
+ *           level index (LSB first; levels ascending, code 0 = most negative
+ *           level); plane bits-1 holds the QJL sign bits, 1 = negative.
+ *           Bit j of word w is coordinate (or sketch row) 32*w + j.
+ *   norms:  uint32 [G][N] = half(||k||) | half(||r||) << 16  (IEEE half, RNE).
+ *   Total:  G*N*((bits-1)*d/8 + d/8 + 4) bytes.
+ *
+ * Status: every entry point returns TQ_OK (0) or a negative TQ_ERR_* code.
+ * No C++ exception crosses this boundary.  Launches are asynchronous on the
+ * given stream; device faults surface at the caller's next synchronisation.
+ * Inputs are not checked for NaN/Inf (outputs are then unspecified); key
+ * norms >= 65520 overflow the half-precision norm and are unsupported.
+ * All pointer arguments of the GPU calls must be 16-byte aligned.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = -1,          /* null/misaligned pointer, negative size, bad dtype */
+  TQ_ERR_UNSUPPORTED = -2,  /* parameter outside what the kernels implement */
+  TQ_ERR_ALLOC = -3,        /* host or device allocation failed */
+  TQ_ERR_HIP = -4,          /* a HIP runtime call or launch failed; see tq_last_hip_error */
+  TQ_ERR_WORKSPACE = -5     /* workspace pointer null or smaller than required */
+};
+
+/* Element types of keys, queries and decoded outputs. */
+enum { TQ_F32 = 0, TQ_BF16 = 1 };
+
+typedef struct tq_codebook tq_codebook;
+
+/*
+ * Host-only: the quantizer tables derived from (d, bits, m, seed), written to
+ * caller-owned host arrays (any may be NULL):
+ *   levels[L], thresholds[L-1]  Lloyd-Max levels/boundaries for N(0, 1/d),
+ *                               L = 2^(bits-1), ascending, float64;
+ *   delta[d]                    Rademacher signs (+1/-1) of D;
+ *   S[m*d]                      QJL sketch, row-major, N(0,1) draws as float32;
+ *   S_rot[m*d]                  S R^T in float64 (the sketch seen from the
+ *                               rotated domain: S r = (S R^T)(R r)).
+ * delta and S come from a counter-based SplitMix64 stream: draw(seed, s, i) =
+ * mix64(mix64(seed + s*G) + (i+1)*G), G = 0x9E3779B97F4A7C15; delta_i = +1 iff
+ * bit 63 of draw(seed,1,i) is 0; S[j][i] = fp32(sqrt(-2 ln u1) cos(2 pi u2)),
+ * u1 = ((x>>11)+1) 2^-53, u2 = (y>>11) 2^-53, x,y = draw(seed,2,2(jd+i)+{0,1}).
+ * Touches no GPU.  Errors: TQ_ERR_UNSUPPORTED (d not a power of two in
+ * [32, 1024], bits not in {2,3,4}, m != d), TQ_ERR_ALLOC.
+ */
+int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed,
+                       double* levels, double* thresholds, int8_t* delta,
+                       float* S, double* S_rot);
+
+/*
+ * Build the quantizer state for (d, bits, m, seed) on the current HIP device:
+ * the tables above plus the kernels' constant blocks (thresholds and levels in
+ * float32, the sketch split into float16 hi/lo parts laid out for the matrix
+ * cores, Walsh coefficients of the levels for the scorer).  The handle owns
+ * its device memory (hipMalloc) and is immutable afterwards, so it may be
+ * shared by streams and threads; it is valid on the device that was current
+ * here.  Supported: d in {128, 1024}, bits in {2, 3, 4}, m == d.
+ * Errors: TQ_ERR_ARG (out NULL), TQ_ERR_UNSUPPORTED, TQ_ERR_ALLOC, TQ_ERR_HIP.
+ */
+int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out);
+
+/* Release a codebook (NULL is a no-op).  The caller must ensure no launch
+ * that uses it is still in flight. */
+void tq_free_codebook(tq_codebook* cb);
+
+/* Host copies of a codebook's tables (same meaning as tq_codebook_tables;
+ * any pointer may be NULL).  Errors: TQ_ERR_ARG (cb NULL). */
+int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds,
+                       int8_t* delta, float* S, double* S_rot);
+
+/* (d, bits, m, seed) of a codebook; any pointer may be NULL. */
+int tq_codebook_info(const tq_codebook* cb, int32_t* d, int32_t* bits, int32_t* m,
+                     uint64_t* seed);
+
+/* Bytes of a packed buffer for G groups of N keys; 0 on bad arguments. */
+size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
+
+/*
+ * Encode G*N keys (rows of d elements, [G][N][d] contiguous, TQ_F32 or
+ * TQ_BF16) into the packed layout above.  Per key k: nu = ||k||; zero record if
+ * nu < 1e-10; else y = R k / nu, code_i = #{thresholds <= y_i},
+ * residual r = k - nu R^T c[code], rho = ||r||, sign bit_j = [(S r)_j < 0]
+ * (S r is evaluated as (S R^T)(R r) on the matrix cores, float32 accumulation
+ * of a three-term float16 split), norms stored as half.
+ * keys and packed are device pointers owned by the caller; G*N == 0 is a
+ * no-op.  Errors: TQ_ERR_ARG, TQ_ERR_HIP.
+ */
+int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype,
+                   int64_t G, int64_t N, void* packed, void* stream);
+
+/* Workspace bytes tq_score_logits needs for G groups of Qg queries. */
+size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
+
+/*
+ * Estimated logits of full-precision queries against packed keys:
+ *   logits[g][h][n] = nu~ <R q, c[code]> + rho~ sqrt(pi/2)/m <S q, 1 - 2 sbit>
+ * for query h of group g, q[g][h][0..d) (TQ_F32 or TQ_BF16), against key n of
+ * group g (GQA: query head j*Qg + h uses KV head j).  logits is float32
+ * [G][Qg][N].  Two launches on the stream: per-query preparation (R q via a
+ * Hadamard butterfly, S q, their sums) into ws, then a streaming pass over the
+ * packed keys.  All buffers are caller-owned device memory; ws must hold
+ * tq_score_workspace_bytes(cb, G, Qg) bytes.  G*N*Qg == 0 is a no-op.
+ * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256), TQ_ERR_HIP.
+ */
+int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
+                    int32_t Qg, const void* packed, int64_t N, float* logits, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * MSE-only reconstruction of every packed key: out[g][n] = nu~ R^T c[code]
+ * (the community API's MSE compressor) as TQ_F32 or TQ_BF16 [G][N][d].
+ * Errors: TQ_ERR_ARG, TQ_ERR_HIP.
+ */
+int tq_decode_mse(const tq_codebook* cb, const void* packed, int64_t G, int64_t N,
+                  void* out, int32_t out_dtype, void* stream);
+
+/*
+ * Measurement helper, not part of the method: unquantised logits
+ * logits[g][h][n] = q[g][h] . k[g][n] for bf16 q [G][Qg][d] and bf16 keys
+ * [G][N][d], float32 accumulation.  The comparator for scoring packed keys.
+ * Supported: d == 128, 1 <= Qg <= 8.  Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED,
+ * TQ_ERR_HIP.
+ */
+int tq_dense_logits_bf16(const void* q, const void* keys, int64_t G, int32_t Qg,
+                         int64_t N, int32_t d, float* logits, void* stream);
+
+/* Static description of a status code. */
+const char* tq_status_string(int status);
+
+/* hipError_t of the last failing HIP call on this thread (0 if none). */
+int tq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,14 @@
+"""TurboQuant key path on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/tq.h`` (libtq.so, built
+in-tree by ``kv_cache_vector_rotate_amd.build``).  Every step of the path runs
+in the library's HIP kernels; this module only checks tensors and passes
+pointers, sizes and the current stream.  If the library is missing the calls
+raise instead of falling back to anything else.
+"""
+
+from ._binding import (  # noqa: F401
+    TQ_F32, TQ_BF16, TQError, Codebook, codebook_tables, encode_keys, score_logits,
+    decode_mse, dense_logits_bf16, packed_nbytes, score_workspace_nbytes, library,
+    library_path, EXPORTED_SYMBOLS,
+)

@@ -1,0 +1,223 @@
+"""ctypes binding of libtq.so: argument checks and marshalling only.
+
+torch is used for device memory and the current HIP stream; no computation
+of the method happens here.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+TQ_F32, TQ_BF16 = 0, 1
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libtq.so")
+
+# Every entry point declared in include/tq.h.
+EXPORTED_SYMBOLS = (
+    "tq_codebook_tables", "tq_make_codebook", "tq_free_codebook", "tq_codebook_export",
+    "tq_codebook_info", "tq_packed_bytes", "tq_encode_keys", "tq_score_workspace_bytes",
+    "tq_score_logits", "tq_decode_mse", "tq_dense_logits_bf16", "tq_status_string",
+    "tq_last_hip_error",
+)
+
+_c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
+_SIGS = {
+    "tq_codebook_tables": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, _vp, _vp, _vp, _vp, _vp]),
+    "tq_make_codebook": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, ctypes.POINTER(_vp)]),
+    "tq_free_codebook": (None, [_vp]),
+    "tq_codebook_export": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "tq_codebook_info": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
+    "tq_packed_bytes": (_c_sz, [_vp, _c_i64, _c_i64]),
+    "tq_encode_keys": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _vp]),
+    "tq_score_workspace_bytes": (_c_sz, [_vp, _c_i64, _c_i32]),
+    "tq_score_logits": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp,
+                                       _c_sz, _vp]),
+    "tq_decode_mse": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i32, _vp]),
+    "tq_dense_logits_bf16": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i32, _c_i64, _c_i32, _vp, _vp]),
+    "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tq_last_hip_error": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = what
+        if _lib is not None and status != 0:
+            msg = f"{what}: {_lib.tq_status_string(status).decode()} (status {status}"
+            if status == -4:
+                msg += f", hipError {_lib.tq_last_hip_error()}"
+            msg += ")"
+        super().__init__(msg)
+
+
+def library():
+    """Load libtq.so (built in-tree).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise TQError(-1, f"{library_path} is missing; build it with "
+                              "`python -m kv_cache_vector_rotate_amd.build`")
+        lib = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise TQError(rc, what)
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data if isinstance(a, np.ndarray) else a.data_ptr())
+
+
+def codebook_tables(d: int, bits: int, m: int | None = None, seed: int = 42):
+    """Host-only quantizer tables (no GPU): levels, thresholds, delta, S, S R^T."""
+    m = d if m is None else m
+    L = 1 << (bits - 1)
+    out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
+               delta=np.empty(d, np.int8), S=np.empty((m, d), np.float32),
+               S_rot=np.empty((m, d), np.float64))
+    _check(library().tq_codebook_tables(d, bits, m, seed, *(_ptr(out[k]) for k in
+                                        ("levels", "thresholds", "delta", "S", "S_rot"))),
+           "tq_codebook_tables")
+    return out
+
+
+class Codebook:
+    """Device-resident quantizer state for (d, bits, m, seed)."""
+
+    def __init__(self, d: int = 128, bits: int = 3, m: int | None = None, seed: int = 42):
+        lib = library()
+        self.d, self.bits, self.m, self.seed = d, bits, d if m is None else m, seed
+        h = ctypes.c_void_p()
+        _check(lib.tq_make_codebook(d, bits, self.m, seed, ctypes.byref(h)), "tq_make_codebook")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            library().tq_free_codebook(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):  # pragma: no cover - best effort
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def export(self):
+        L = 1 << (self.bits - 1)
+        out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
+                   delta=np.empty(self.d, np.int8), S=np.empty((self.m, self.d), np.float32),
+                   S_rot=np.empty((self.m, self.d), np.float64))
+        _check(library().tq_codebook_export(self._h, *(_ptr(out[k]) for k in
+                                            ("levels", "thresholds", "delta", "S", "S_rot"))),
+               "tq_codebook_export")
+        return out
+
+
+def packed_nbytes(cb: Codebook, G: int, N: int) -> int:
+    return int(library().tq_packed_bytes(cb.handle, G, N))
+
+
+def score_workspace_nbytes(cb: Codebook, G: int, Qg: int) -> int:
+    return int(library().tq_score_workspace_bytes(cb.handle, G, Qg))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    if t.dtype == torch.float32:
+        return TQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need_cuda(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def encode_keys(cb: Codebook, keys, out=None):
+    """keys [G, N, d] (float32/bfloat16, device) -> packed uint8 [packed_nbytes]."""
+    torch = _torch()
+    _need_cuda(keys, "keys")
+    G, N, d = keys.shape
+    if d != cb.d:
+        raise ValueError("key dimension does not match the codebook")
+    nb = packed_nbytes(cb, G, N)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=keys.device)
+    elif out.numel() * out.element_size() < nb:
+        raise ValueError("packed buffer too small")
+    _check(library().tq_encode_keys(cb.handle, _ptr(keys), _dtype_code(keys), G, N, _ptr(out),
+                                    _stream()), "tq_encode_keys")
+    return out
+
+
+def score_logits(cb: Codebook, q, packed, N: int, out=None, ws=None):
+    """q [G, Qg, d] against packed keys of N per group -> float32 [G, Qg, N]."""
+    torch = _torch()
+    _need_cuda(q, "q")
+    _need_cuda(packed, "packed")
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    if out is None:
+        out = torch.empty((G, Qg, N), dtype=torch.float32, device=q.device)
+    wsb = score_workspace_nbytes(cb, G, Qg)
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check(library().tq_score_logits(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(packed), N,
+                                     _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _stream()), "tq_score_logits")
+    return out
+
+
+def decode_mse(cb: Codebook, packed, G: int, N: int, dtype=None, out=None):
+    """packed keys -> nu~ R^T c[code], [G, N, d] float32 (default) or bfloat16."""
+    torch = _torch()
+    _need_cuda(packed, "packed")
+    dtype = torch.float32 if dtype is None else dtype
+    if out is None:
+        out = torch.empty((G, N, cb.d), dtype=dtype, device=packed.device)
+    _check(library().tq_decode_mse(cb.handle, _ptr(packed), G, N, _ptr(out), _dtype_code(out),
+                                   _stream()), "tq_decode_mse")
+    return out
+
+
+def dense_logits_bf16(q, keys, out=None):
+    """Unquantised comparator: bf16 q [G, Qg, d] . bf16 keys [G, N, d] -> float32 [G, Qg, N]."""
+    torch = _torch()
+    _need_cuda(q, "q")
+    _need_cuda(keys, "keys")
+    G, Qg, d = q.shape
+    N = keys.shape[1]
+    if out is None:
+        out = torch.empty((G, Qg, N), dtype=torch.float32, device=q.device)
+    _check(library().tq_dense_logits_bf16(_ptr(q), _ptr(keys), G, Qg, N, d, _ptr(out), _stream()),
+           "tq_dense_logits_bf16")
+    return out

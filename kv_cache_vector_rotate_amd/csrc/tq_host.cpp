@@ -1,0 +1,430 @@
+// Host core of the TurboQuant key-path library: quantizer tables, the C ABI,
+// argument validation and device set-up.  The kernels live in tq_kernels.hip.
+//
+// Method sources (by page title and section):
+//  * rotation R = H_d D / sqrt(d), Sylvester H_d, Rademacher D:
+//    ICLR 2026 paper digest (0h-n0.github.io), "Step 1: PolarQuant";
+//  * shared Lloyd-Max scalar quantizer for the N(0, 1/d) coordinate law:
+//    Qiita explainer (kai_kou), "Stage 1" step 3; ICLR 2026 digest, Theorem 1;
+//  * (b-1)-bit MSE stage + 1-bit QJL of the residual, total b bits:
+//    ai.spot.hk TurboQuant article, "無偏內積估計";
+//  * Gaussian projection S and the sqrt(pi/2)/m estimator constant:
+//    Qiita explainer, "Stage 2: QJL", estimator equation.
+
+#include "tq_internal.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <new>
+
+#include "../../include/tq.h"
+
+struct tq_codebook : public tq::Codebook {};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return TQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- SplitMix64
+// Counter-based use of the SplitMix64 generator (Steele, Lea & Flood 2014):
+//   draw(seed, stream, i) = mix(mix(seed + stream*G) + (i + 1)*G),  G = golden gamma.
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+inline uint64_t splitmix_finalize(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct Stream {
+  uint64_t base;
+  Stream(uint64_t seed, uint64_t stream) : base(splitmix_finalize(seed + stream * kGamma)) {}
+  uint64_t operator()(uint64_t i) const { return splitmix_finalize(base + (i + 1) * kGamma); }
+};
+
+void make_delta(uint64_t seed, int d, int8_t* out) {
+  Stream s(seed, 1);
+  for (int i = 0; i < d; ++i) out[i] = (s(static_cast<uint64_t>(i)) >> 63) ? int8_t(-1) : int8_t(1);
+}
+
+void make_sketch(uint64_t seed, int m, int d, float* out) {
+  Stream s(seed, 2);
+  const double two_pi = 2.0 * M_PI;
+  const double ulp53 = std::ldexp(1.0, -53);
+  for (int64_t t = 0, n = int64_t(m) * d; t < n; ++t) {
+    const uint64_t x = s(2 * uint64_t(t)), y = s(2 * uint64_t(t) + 1);
+    const double u1 = double((x >> 11) + 1) * ulp53;   // (0, 1]
+    const double u2 = double(y >> 11) * ulp53;         // [0, 1)
+    const double z = std::sqrt(-2.0 * std::log(u1)) * std::cos(two_pi * u2);  // Box-Muller
+    out[t] = static_cast<float>(z);
+  }
+}
+
+// ------------------------------------------------------------------ Lloyd-Max
+// MSE-optimal L-level quantizer of the standard normal law.  The law is
+// symmetric and L even, so only the positive half is iterated, with the
+// centre boundary pinned at 0: alternate "boundary = midpoint of its two
+// levels" and "level = centroid of its cell" until the levels stop moving.
+void lloyd_max_normal(int L, double* levels, double* thresholds) {
+  const int K = L / 2;
+  std::vector<double> c(K), b(K + 1);
+  for (int k = 0; k < K; ++k) c[k] = (k + 0.5) * 3.0 / K;
+  const double inv_sqrt2 = 1.0 / std::sqrt(2.0), inv_sqrt2pi = 1.0 / std::sqrt(2.0 * M_PI);
+  auto pdf = [&](double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * inv_sqrt2pi; };
+  auto tail = [&](double x) { return std::isinf(x) ? 0.0 : 0.5 * std::erfc(x * inv_sqrt2); };
+  for (int it = 0; it < 200000; ++it) {
+    b[0] = 0.0;
+    b[K] = INFINITY;
+    for (int k = 1; k < K; ++k) b[k] = 0.5 * (c[k - 1] + c[k]);
+    double moved = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double nc = (pdf(b[k]) - pdf(b[k + 1])) / (tail(b[k]) - tail(b[k + 1]));
+      moved = std::fmax(moved, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (moved < 1e-15) break;
+  }
+  for (int k = 0; k < K; ++k) {
+    levels[K + k] = c[k];
+    levels[K - 1 - k] = -c[k];
+  }
+  thresholds[K - 1] = 0.0;
+  for (int k = 1; k < K; ++k) {
+    const double t = 0.5 * (c[k - 1] + c[k]);
+    thresholds[K - 1 + k] = t;
+    thresholds[K - 1 - k] = -t;
+  }
+}
+
+// S R^T = S D H / sqrt(d) (H symmetric): a Hadamard transform of each row of
+// S * delta, in float64.
+void sketch_rotated(const float* S, const int8_t* delta, int m, int d, double* out) {
+  const double scale = 1.0 / std::sqrt(double(d));
+  for (int j = 0; j < m; ++j) {
+    double* row = out + int64_t(j) * d;
+    for (int i = 0; i < d; ++i) row[i] = double(S[int64_t(j) * d + i]) * delta[i];
+    for (int h = 1; h < d; h <<= 1)
+      for (int i0 = 0; i0 < d; i0 += 2 * h)
+        for (int i = i0; i < i0 + h; ++i) {
+          const double a = row[i], c = row[i + h];
+          row[i] = a + c;
+          row[i + h] = a - c;
+        }
+    for (int i = 0; i < d; ++i) row[i] *= scale;
+  }
+}
+
+bool valid_params(int d, int bits, int m) {
+  if (d < 32 || d > 1024 || (d & (d - 1))) return false;
+  if (bits < 2 || bits > 4) return false;
+  return m == d;
+}
+
+bool device_params(int d) { return d == 128 || d == 1024; }
+
+uint16_t half_bits(double v) {
+  const _Float16 h = static_cast<_Float16>(v);   // round to nearest even
+  uint16_t u;
+  std::memcpy(&u, &h, 2);
+  return u;
+}
+
+// Lane layout of the d = 128 encoder (two lanes per key): after its butterfly,
+// register r of the lane in wave half h holds rotated coordinate
+//   coord(h, r) = (r % 32) + 32 * (h + 2 * (r / 32)).
+// The matrix-core B operand takes K-slice [8h, 8h+8) of each 16-wide chunk kc
+// from registers r = 8*kc + t, so the A operand (S R^T rows) must present the
+// same coordinates: fragment (kc, jb, lane L) holds row 32*jb + L%32 at
+// coordinates coord(L/32, 8*kc + t), t = 0..7.
+void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>& frag) {
+  const int d = 128;
+  frag.assign(2 * 8 * 4 * 64 * 8, 0);
+  const size_t lo_off = size_t(8) * 4 * 64 * 8;
+  for (int kc = 0; kc < 8; ++kc)
+    for (int jb = 0; jb < 4; ++jb)
+      for (int L = 0; L < 64; ++L) {
+        const int j = 32 * jb + (L & 31), h = L >> 5;
+        for (int t = 0; t < 8; ++t) {
+          const int r = 8 * kc + t;
+          const int coord = (r & 31) + 32 * (h + 2 * (r >> 5));
+          const double v = S_rot[size_t(j) * d + coord];
+          const _Float16 hi = static_cast<_Float16>(v);
+          const _Float16 lo = static_cast<_Float16>(v - static_cast<double>(hi));
+          const size_t at = ((size_t(kc) * 4 + jb) * 64 + L) * 8 + t;
+          std::memcpy(&frag[at], &hi, 2);
+          std::memcpy(&frag[lo_off + at], &lo, 2);
+        }
+      }
+}
+
+void fill_consts(tq::Codebook& cb) {
+  tq::DevConsts& k = cb.consts;
+  std::memset(&k, 0, sizeof(k));
+  const int L = 1 << (cb.bits - 1), K = L / 2;
+  for (int i = 0; i < K - 1; ++i) k.tpos[i] = float(cb.thresholds[K + i]);
+  for (int i = 0; i < K; ++i) k.cpos_s[i] = float(cb.levels[K + i] * double(tq::kResidualScale));
+  for (int i = 0; i < L; ++i) k.levels[i] = float(cb.levels[i]);
+  // Walsh expansion of the level table over s_p = 2*bit_p - 1:
+  //   c(code) = sum_S alpha_S prod_{p in S} s_p ; only odd |S| survive (odd symmetry).
+  const int B = cb.bits - 1;
+  const int subsets[4] = {1, 2, 4, 7};
+  double asum = 0.0;
+  for (int a = 0; a < 4; ++a) {
+    const int S = subsets[a];
+    if (S >= (1 << B)) { k.alpha[a] = 0.f; continue; }
+    double acc = 0.0;
+    for (int code = 0; code < L; ++code) {
+      double prod = 1.0;
+      for (int p = 0; p < B; ++p)
+        if (S >> p & 1) prod *= ((code >> p) & 1) ? 1.0 : -1.0;
+      acc += cb.levels[code] * prod;
+    }
+    k.alpha[a] = float(acc / L);
+    asum += acc / L;
+  }
+  k.alpha_sum = float(asum);
+  k.sqrt_d = float(std::sqrt(double(cb.d)));
+  k.inv_sqrt_d = float(1.0 / std::sqrt(double(cb.d)));
+  k.qjl_scale = float(std::sqrt(M_PI / 2.0) / cb.m);
+  for (int i = 0; i < cb.d; ++i)
+    if (cb.delta[i] < 0) k.dneg[i >> 5] |= 1u << (i & 31);
+}
+
+int build_tables(tq::Codebook& cb) {
+  const int d = cb.d, m = cb.m, L = 1 << (cb.bits - 1);
+  try {
+    cb.levels.resize(L);
+    cb.thresholds.resize(L - 1);
+    cb.delta.resize(d);
+    cb.S.resize(size_t(m) * d);
+    cb.S_rot.resize(size_t(m) * d);
+  } catch (const std::bad_alloc&) {
+    return TQ_ERR_ALLOC;
+  }
+  lloyd_max_normal(L, cb.levels.data(), cb.thresholds.data());
+  const double sigma = 1.0 / std::sqrt(double(d));   // N(0,1) -> N(0, 1/d)
+  for (double& v : cb.levels) v *= sigma;
+  for (double& v : cb.thresholds) v *= sigma;
+  make_delta(cb.seed, d, cb.delta.data());
+  make_sketch(cb.seed, m, d, cb.S.data());
+  sketch_rotated(cb.S.data(), cb.delta.data(), m, d, cb.S_rot.data());
+  fill_consts(cb);
+  return TQ_OK;
+}
+
+void release_device(tq::Codebook& cb) {
+  if (cb.d_consts) (void)hipFree(cb.d_consts);
+  if (cb.d_frag) (void)hipFree(cb.d_frag);
+  if (cb.d_S) (void)hipFree(cb.d_S);
+  if (cb.d_flip_bf16) (void)hipFree(cb.d_flip_bf16);
+  if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
+  cb.d_consts = nullptr;
+  cb.d_frag = nullptr;
+  cb.d_S = nullptr;
+  cb.d_flip_bf16 = nullptr;
+  cb.d_flip_f32 = nullptr;
+}
+
+template <typename T>
+hipError_t upload(T** dst, const void* src, size_t bytes) {
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
+  if (e != hipSuccess) { *dst = nullptr; return e; }
+  return hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
+}
+
+int upload_device(tq::Codebook& cb) {
+  hipError_t e = hipGetDevice(&cb.device);
+  if (e != hipSuccess) return hip_fail(e);
+  e = upload(&cb.d_consts, &cb.consts, sizeof(tq::DevConsts));
+  if (e == hipSuccess) e = upload(&cb.d_S, cb.S.data(), cb.S.size() * sizeof(float));
+  if (e == hipSuccess && cb.d == 128) {
+    std::vector<uint16_t> frag;
+    build_fragments_128(cb.S_rot, frag);
+    e = upload(&cb.d_frag, frag.data(), frag.size() * sizeof(uint16_t));
+    // Sign-flip words applying D to the raw inputs of the lane that loads
+    // coordinates [64h, 64h + 64): bf16 pairs (two per word) and float32.
+    std::vector<uint32_t> fb(64, 0), ff(128, 0);
+    for (int h = 0; h < 2; ++h)
+      for (int e2 = 0; e2 < 64; ++e2)
+        if (cb.delta[64 * h + e2] < 0) {
+          fb[h * 32 + e2 / 2] |= (e2 & 1) ? 0x80000000u : 0x00008000u;
+          ff[h * 64 + e2] = 0x80000000u;
+        }
+    if (e == hipSuccess) e = upload(&cb.d_flip_bf16, fb.data(), fb.size() * 4);
+    if (e == hipSuccess) e = upload(&cb.d_flip_f32, ff.data(), ff.size() * 4);
+  }
+  if (e != hipSuccess) {
+    release_device(cb);
+    return hip_fail(e);
+  }
+  return TQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_device(const tq::Codebook& cb) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  return dev == cb.device ? TQ_OK : TQ_ERR_ARG;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed, double* levels,
+                       double* thresholds, int8_t* delta, float* S, double* S_rot) {
+  if (!valid_params(d, bits, m)) return TQ_ERR_UNSUPPORTED;
+  tq::Codebook cb;
+  cb.d = d;
+  cb.bits = bits;
+  cb.m = m;
+  cb.seed = seed;
+  const int rc = build_tables(cb);
+  if (rc != TQ_OK) return rc;
+  const int L = 1 << (bits - 1);
+  if (levels) std::memcpy(levels, cb.levels.data(), L * sizeof(double));
+  if (thresholds) std::memcpy(thresholds, cb.thresholds.data(), (L - 1) * sizeof(double));
+  if (delta) std::memcpy(delta, cb.delta.data(), d);
+  if (S) std::memcpy(S, cb.S.data(), cb.S.size() * sizeof(float));
+  if (S_rot) std::memcpy(S_rot, cb.S_rot.data(), cb.S_rot.size() * sizeof(double));
+  return TQ_OK;
+}
+
+int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out) {
+  if (!out) return TQ_ERR_ARG;
+  *out = nullptr;
+  if (!valid_params(d, bits, m) || !device_params(d)) return TQ_ERR_UNSUPPORTED;
+  std::unique_ptr<tq_codebook> cb(new (std::nothrow) tq_codebook());
+  if (!cb) return TQ_ERR_ALLOC;
+  cb->d = d;
+  cb->bits = bits;
+  cb->m = m;
+  cb->seed = seed;
+  int rc = build_tables(*cb);
+  if (rc != TQ_OK) return rc;
+  rc = upload_device(*cb);
+  if (rc != TQ_OK) return rc;
+  *out = cb.release();
+  return TQ_OK;
+}
+
+void tq_free_codebook(tq_codebook* cb) {
+  if (!cb) return;
+  release_device(*cb);
+  delete cb;
+}
+
+int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds, int8_t* delta,
+                       float* S, double* S_rot) {
+  if (!cb) return TQ_ERR_ARG;
+  const int L = 1 << (cb->bits - 1);
+  if (levels) std::memcpy(levels, cb->levels.data(), L * sizeof(double));
+  if (thresholds) std::memcpy(thresholds, cb->thresholds.data(), (L - 1) * sizeof(double));
+  if (delta) std::memcpy(delta, cb->delta.data(), cb->d);
+  if (S) std::memcpy(S, cb->S.data(), cb->S.size() * sizeof(float));
+  if (S_rot) std::memcpy(S_rot, cb->S_rot.data(), cb->S_rot.size() * sizeof(double));
+  return TQ_OK;
+}
+
+int tq_codebook_info(const tq_codebook* cb, int32_t* d, int32_t* bits, int32_t* m,
+                     uint64_t* seed) {
+  if (!cb) return TQ_ERR_ARG;
+  if (d) *d = cb->d;
+  if (bits) *bits = cb->bits;
+  if (m) *m = cb->m;
+  if (seed) *seed = cb->seed;
+  return TQ_OK;
+}
+
+size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N) {
+  if (!cb || G < 0 || N < 0) return 0;
+  const int64_t per = int64_t(cb->bits - 1) * cb->d / 8 + cb->m / 8 + 4;
+  return size_t(G) * size_t(N) * size_t(per);
+}
+
+int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, int64_t G,
+                   int64_t N, void* packed, void* stream) {
+  if (!cb || G < 0 || N < 0 || (key_dtype != TQ_F32 && key_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (G == 0 || N == 0) return TQ_OK;
+  if (!keys || !packed || !aligned16(keys) || !aligned16(packed)) return TQ_ERR_ARG;
+  if (!tq::encode_supported(*cb)) return TQ_ERR_UNSUPPORTED;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, N, packed,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg) {
+  if (!cb || G < 0 || Qg < 0) return 0;
+  return tq::score_workspace_bytes(*cb, G, Qg);
+}
+
+int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                    const void* packed, int64_t N, float* logits, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16))
+    return TQ_ERR_ARG;
+  if (Qg > 256) return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || N == 0 || Qg == 0) return TQ_OK;
+  if (!q || !packed || !logits || !aligned16(q) || !aligned16(packed) || !aligned16(logits))
+    return TQ_ERR_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < tq::score_workspace_bytes(*cb, G, Qg))
+    return TQ_ERR_WORKSPACE;
+  if (!tq::score_supported(*cb)) return TQ_ERR_UNSUPPORTED;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_score(*cb, q, q_dtype, G, Qg, packed, N, logits, ws,
+                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_decode_mse(const tq_codebook* cb, const void* packed, int64_t G, int64_t N, void* out,
+                  int32_t out_dtype, void* stream) {
+  if (!cb || G < 0 || N < 0 || (out_dtype != TQ_F32 && out_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (G == 0 || N == 0) return TQ_OK;
+  if (!packed || !out || !aligned16(packed) || !aligned16(out)) return TQ_ERR_ARG;
+  if (cb->d != 128) return TQ_ERR_UNSUPPORTED;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_decode(*cb, packed, G, N, out, out_dtype,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_dense_logits_bf16(const void* q, const void* keys, int64_t G, int32_t Qg, int64_t N,
+                         int32_t d, float* logits, void* stream) {
+  if (G < 0 || N < 0 || Qg < 0) return TQ_ERR_ARG;
+  if (d != 128 || Qg > 8) return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || N == 0 || Qg == 0) return TQ_OK;
+  if (!q || !keys || !logits || !aligned16(q) || !aligned16(keys) || !aligned16(logits))
+    return TQ_ERR_ARG;
+  hipError_t e = tq::launch_dense_bf16(q, keys, G, Qg, N, d, logits,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+const char* tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_ARG: return "invalid argument (null or misaligned pointer, negative size, bad dtype, wrong device)";
+    case TQ_ERR_UNSUPPORTED: return "unsupported parameter";
+    case TQ_ERR_ALLOC: return "allocation failed";
+    case TQ_ERR_HIP: return "HIP runtime error";
+    case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int tq_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

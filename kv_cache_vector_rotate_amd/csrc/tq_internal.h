@@ -1,0 +1,59 @@
+// Internal declarations shared by the host core (tq_host.cpp) and the HIP
+// kernels (tq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+namespace tq {
+
+// Constant block the kernels read (one per codebook, device resident).
+// Scales: "t" and "c" values are for N(0, 1/d) (unit-vector coordinates).
+struct DevConsts {
+  float tpos[8];      // positive thresholds t_{L/2}..t_{L-2} (L/2-1 of them), ascending
+  float cpos_s[8];    // positive levels c_{L/2}..c_{L-1}, times 2^12 (encoder residual scale)
+  float levels[16];   // all L levels, ascending (decoder)
+  float alpha[4];     // Walsh coefficients of the levels: s0, s1, s2, s0*s1*s2 terms
+  float sqrt_d;       // sqrt(d)
+  float inv_sqrt_d;   // 1/sqrt(d)
+  float qjl_scale;    // sqrt(pi/2) / m
+  float alpha_sum;    // alpha[0] + ... + alpha[3]
+  uint32_t dneg[32];  // bit (i % 32) of word i/32 set where delta_i = -1 (d <= 1024)
+  uint32_t pad[4];
+};
+
+constexpr float kResidualScale = 4096.0f;  // 2^12: keeps residual hi/lo halves normal
+
+struct Codebook {
+  int d = 0, bits = 0, m = 0;
+  uint64_t seed = 0;
+  int device = 0;
+  // host tables
+  std::vector<double> levels, thresholds, S_rot;
+  std::vector<int8_t> delta;
+  std::vector<float> S;
+  DevConsts consts{};
+  // device copies
+  DevConsts* d_consts = nullptr;
+  uint4* d_frag = nullptr;       // S R^T as float16 hi/lo, matrix-core A-operand order
+  float* d_S = nullptr;          // S, float32 [m][d]
+  uint32_t* d_flip_bf16 = nullptr;  // [2][d/4] sign-flip words for bf16 pairs (d = 128)
+  uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
+};
+
+// Launchers (tq_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
+                         void* packed, hipStream_t s);
+hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                        const void* packed, int64_t N, float* logits, void* ws, hipStream_t s);
+hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
+                         int odtype, hipStream_t s);
+hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg, int64_t N, int d,
+                             float* logits, hipStream_t s);
+size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg);
+bool encode_supported(const Codebook& cb);
+bool score_supported(const Codebook& cb);
+
+}  // namespace tq

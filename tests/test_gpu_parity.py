@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Sizes span several 32-key tiles with ragged tails; the full-size decode
+workload is checked on sampled groups in the launch configuration the
+benchmark times.  Rules are in tests/parity.py.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from kv_cache_vector_rotate_amd import workloads as W
+from parity import check_encode, check_logits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+K = pytest.importorskip("kv_cache_vector_rotate_amd")
+
+
+def _dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    return t.to(dtype) if dtype != torch.float32 else t
+
+
+def _keys(rng, G, N, d=128, outliers=True):
+    scale = np.exp(rng.normal(0, math.sqrt(0.5), d))
+    if outliers:
+        scale[rng.choice(d, 4, replace=False)] *= 20
+    return (rng.standard_normal((G, N, d)) * scale).astype(np.float32)
+
+
+def _round_bf16(a):
+    return W.bf16_bits_to_f32(W.f32_to_bf16_bits(a))
+
+
+def _encode_and_check(bits, keys, dtype, seed=42):
+    G, N, d = keys.shape
+    cbo = O.make_codebook(d, bits, d, seed)
+    cb = K.Codebook(d, bits, d, seed)
+    print(f"[case] encode G={G} N={N} bits={bits} dtype={dtype}", flush=True)
+    packed = K.encode_keys(cb, _dev(keys, dtype))
+    torch.cuda.synchronize()
+    buf = packed.cpu().numpy()
+    codes, signs, nu16, rho16 = O.unpack(cbo, buf, G, N)
+    stats = check_encode(cbo, keys.reshape(-1, d), codes.reshape(-1, d), signs.reshape(-1, d),
+                         nu16.reshape(-1), rho16.reshape(-1))
+    return cb, cbo, packed, buf, stats
+
+
+def _score_and_check(cb, cbo, packed, buf, q, keys, dtype):
+    G, Qg, d = q.shape
+    N = keys.shape[1]
+    print(f"[case] score G={G} Qg={Qg} N={N} bits={cb.bits}", flush=True)
+    lg = K.score_logits(cb, _dev(q, dtype), packed, N)
+    torch.cuda.synchronize()
+    ref = O.score(cbo, buf, G, N, q)
+    return check_logits(lg.cpu().numpy(), ref, q, np.linalg.norm(keys.astype(np.float64), axis=-1))
+
+
+def test_config0_full():
+    """Single head, N = 4096 fp32 keys, 4 queries, b = 3: the whole workload."""
+    wl = W.workload(0)
+    keys = W.group_keys(wl, 0)[None]
+    q = W.group_queries(wl, 0)[None]
+    cb, cbo, packed, buf, st = _encode_and_check(3, keys, torch.float32)
+    print(st)
+    _score_and_check(cb, cbo, packed, buf, q, keys, torch.float32)
+    dec = K.decode_mse(cb, packed, 1, wl.N).cpu().numpy().astype(np.float64)
+    ref = O.decode_mse(cbo, buf, 1, wl.N)
+    nu = np.linalg.norm(keys.astype(np.float64), axis=-1)
+    assert np.all(np.abs(dec - ref) <= 1e-6 * nu[..., None])
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("N", [1, 31, 33, 1000])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ragged_groups(bits, N, dt):
+    rng = np.random.default_rng(1000 * bits + N + (7 if dt == "bf16" else 0))
+    G, Qg = 3, 5
+    keys = _keys(rng, G, N)
+    q = rng.standard_normal((G, Qg, 128)).astype(np.float32)
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    if dt == "bf16":
+        keys, q = _round_bf16(keys), _round_bf16(q)
+    cb, cbo, packed, buf, _ = _encode_and_check(bits, keys, dtype, seed=bits)
+    _score_and_check(cb, cbo, packed, buf, q, keys, dtype)
+
+
+def test_special_keys():
+    """Zero keys, keys below the zero-norm rule, one-hot and repeated-value keys."""
+    rng = np.random.default_rng(5)
+    keys = _keys(rng, 1, 70)
+    keys[0, 0] = 0.0
+    keys[0, 1] = 0.0
+    keys[0, 1, 3] = 1e-12            # below 1e-10: zero record
+    keys[0, 2] = 0.0
+    keys[0, 2, 17] = 3.0             # one-hot
+    keys[0, 3] = 0.5                 # constant
+    keys[0, 4] = 0.0
+    keys[0, 4, :2] = 1.0             # exact zeros after the rotation
+    keys[0, 5] *= 1e-6               # tiny but encodable
+    keys[0, 6] *= 1e3                # large norm (still < 65504)
+    cb, cbo, packed, buf, _ = _encode_and_check(3, keys, torch.float32)
+    codes, signs, nu16, rho16 = O.unpack(cbo, buf, 1, 70)
+    assert not codes[0, :2].any() and not signs[0, :2].any()
+    assert float(nu16[0, 0]) == 0.0 and float(nu16[0, 1]) == 0.0
+    q = rng.standard_normal((1, 4, 128)).astype(np.float32)
+    _score_and_check(cb, cbo, packed, buf, q, keys, torch.float32)
+    lg = K.score_logits(cb, _dev(q, torch.float32), packed, 70).cpu().numpy()
+    assert np.all(lg[0, :, :2] == 0.0)
+
+
+def test_encode_is_deterministic():
+    rng = np.random.default_rng(9)
+    keys = _dev(_keys(rng, 4, 777), torch.bfloat16)
+    cb = K.Codebook(128, 3)
+    a = K.encode_keys(cb, keys).clone()
+    b = K.encode_keys(cb, keys)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_score_mse_term_equals_decode():
+    """With the stored residual norms cleared, the score is <q, decode_mse(k)>
+    (the two boundary calls cross-check each other)."""
+    rng = np.random.default_rng(11)
+    G, N, Qg = 2, 500, 4
+    keys = _keys(rng, G, N)
+    for bits in (2, 3, 4):
+        cb = K.Codebook(128, bits)
+        packed = K.encode_keys(cb, _dev(keys, torch.float32))
+        nb = packed.numel()
+        norms = packed[nb - 4 * G * N:].view(torch.int32)
+        norms &= 0xFFFF
+        q = _dev(rng.standard_normal((G, Qg, 128)), torch.float32)
+        lg = K.score_logits(cb, q, packed, N).double()
+        dec = K.decode_mse(cb, packed, G, N).double()
+        ref = torch.einsum("gqd,gnd->gqn", q.double(), dec)
+        tol = 1e-5 * q.double().norm(dim=-1)[:, :, None] * dec.norm(dim=-1)[:, None, :] + 1e-6
+        assert torch.all((lg - ref).abs() <= tol)
+
+
+def test_config1_full_size_sampled_groups():
+    """Llama-3.1-8B-shaped decode (G = 128, N = 8192, bf16, b = 3) encoded and
+    scored in full; the oracle checks sampled groups in full."""
+    wl = W.workload(1)
+    keys_bits = W.all_keys(wl)                        # uint16 bf16 patterns
+    q_bits = W.all_queries(wl)
+    keys = torch.from_numpy(keys_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    q = torch.from_numpy(q_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    cb = K.Codebook(128, 3)
+    cbo = O.make_codebook(128, 3, 128, 42)
+    print("[case] config1 full encode", flush=True)
+    packed = K.encode_keys(cb, keys)
+    print("[case] config1 full score", flush=True)
+    lg = K.score_logits(cb, q, packed, wl.N)
+    torch.cuda.synchronize()
+    buf = packed.cpu().numpy()
+    lgh = lg.cpu().numpy()
+    codes, signs, nu16, rho16 = O.unpack(cbo, buf, wl.G, wl.N)
+    for g in (0, 77, 127):
+        kg = W.bf16_bits_to_f32(keys_bits[g])
+        check_encode(cbo, kg, codes[g], signs[g], nu16[g], rho16[g])
+        one = O.pack(cbo, codes[g:g + 1], signs[g:g + 1], nu16[g:g + 1], rho16[g:g + 1])
+        qg = W.bf16_bits_to_f32(q_bits[g])[None]
+        ref = O.score(cbo, one, 1, wl.N, qg)
+        check_logits(lgh[g:g + 1], ref, qg, np.linalg.norm(kg.astype(np.float64), axis=-1)[None])
+
+
+def test_dense_logits_comparator():
+    rng = np.random.default_rng(2)
+    G, N, Qg = 3, 1001, 4
+    keys = _round_bf16(_keys(rng, G, N))
+    q = _round_bf16(rng.standard_normal((G, Qg, 128)).astype(np.float32))
+    out = K.dense_logits_bf16(_dev(q, torch.bfloat16), _dev(keys, torch.bfloat16)).cpu().numpy()
+    ref = O.exact_logits(keys, q)
+    tol = 1e-5 * np.linalg.norm(q, axis=-1)[:, :, None] * np.linalg.norm(keys, axis=-1)[:, None, :]
+    assert np.all(np.abs(out - ref) <= tol)
+
+
+def test_gpu_argument_errors():
+    cb = K.Codebook(128, 3)
+    keys = torch.zeros((1, 8, 128), device="cuda")
+    packed = K.encode_keys(cb, keys)
+    lib = K.library()
+    import ctypes
+    mis = ctypes.c_void_p(keys.data_ptr() + 4)
+    assert lib.tq_encode_keys(cb.handle, mis, 0, 1, 7, ctypes.c_void_p(packed.data_ptr()), None) == -1
+    assert lib.tq_encode_keys(cb.handle, ctypes.c_void_p(keys.data_ptr()), 7, 1, 8,
+                              ctypes.c_void_p(packed.data_ptr()), None) == -1
+    q = torch.zeros((1, 4, 128), device="cuda")
+    out = torch.empty((1, 4, 8), device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    rc = lib.tq_score_logits(cb.handle, ctypes.c_void_p(q.data_ptr()), 0, 1, 4,
+                             ctypes.c_void_p(packed.data_ptr()), 8, ctypes.c_void_p(out.data_ptr()),
+                             ctypes.c_void_p(ws.data_ptr()), 16, None)
+    assert rc == -5
+    # empty inputs are no-ops
+    assert lib.tq_encode_keys(cb.handle, None, 0, 0, 8, None, None) == 0
+    with pytest.raises(K.TQError):
+        K.Codebook(128, 7)
