@@ -119,7 +119,9 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
 int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype,
                    int64_t G, int64_t N, void* packed, void* stream);
 
-/* Workspace bytes tq_score_logits needs for G groups of Qg queries. */
+/* Workspace bytes tq_score_logits needs for G groups of Qg queries (the
+ * current kernels prepare queries on chip and need none: 0; ws may then be
+ * NULL). */
 size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
 
 /*
@@ -127,10 +129,11 @@ size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
  *   logits[g][h][n] = nu~ <R q, c[code]> + rho~ sqrt(pi/2)/m <S q, 1 - 2 sbit>
  * for query h of group g, q[g][h][0..d) (TQ_F32 or TQ_BF16), against key n of
  * group g (GQA: query head j*Qg + h uses KV head j).  logits is float32
- * [G][Qg][N].  Two launches on the stream: per-query preparation (R q via a
- * Hadamard butterfly, S q, their sums) into ws, then a streaming pass over the
- * packed keys.  All buffers are caller-owned device memory; ws must hold
- * tq_score_workspace_bytes(cb, G, Qg) bytes.  G*N*Qg == 0 is a no-op.
+ * [G][Qg][N].  One launch on the stream: each workgroup prepares its queries
+ * (R q via a Hadamard butterfly, S q, their sums) and then streams the packed
+ * keys of its range.  All buffers are caller-owned device memory; ws must hold
+ * tq_score_workspace_bytes(cb, G, Qg) bytes (may be NULL when that is 0).
+ * G*N*Qg == 0 is a no-op.
  * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256), TQ_ERR_HIP.
  */
 int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,

@@ -142,7 +142,7 @@ uint16_t half_bits(double v) {
 // The matrix-core B operand takes K-slice [8h, 8h+8) of each 16-wide chunk kc
 // from registers r = 8*kc + t, so the A operand (S R^T rows) must present the
 // same coordinates: fragment (kc, jb, lane L) holds row 32*jb + L%32 at
-// coordinates coord(L/32, 8*kc + t), t = 0..7.
+// coordinates coord(L/32, 8*kc + t), t = 0..7.  Stored negated (see the encoder).
 void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>& frag) {
   const int d = 128;
   frag.assign(2 * 8 * 4 * 64 * 8, 0);
@@ -154,7 +154,8 @@ void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>
         for (int t = 0; t < 8; ++t) {
           const int r = 8 * kc + t;
           const int coord = (r & 31) + 32 * (h + 2 * (r >> 5));
-          const double v = S_rot[size_t(j) * d + coord];
+          // negated: the encoder forms the negated residual c[code] - y
+          const double v = -S_rot[size_t(j) * d + coord];
           const _Float16 hi = static_cast<_Float16>(v);
           const _Float16 lo = static_cast<_Float16>(v - static_cast<double>(hi));
           const size_t at = ((size_t(kc) * 4 + jb) * 64 + L) * 8 + t;
@@ -223,12 +224,12 @@ void release_device(tq::Codebook& cb) {
   if (cb.d_consts) (void)hipFree(cb.d_consts);
   if (cb.d_frag) (void)hipFree(cb.d_frag);
   if (cb.d_S) (void)hipFree(cb.d_S);
-  if (cb.d_flip_bf16) (void)hipFree(cb.d_flip_bf16);
+  if (cb.d_dpair) (void)hipFree(cb.d_dpair);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
   cb.d_consts = nullptr;
   cb.d_frag = nullptr;
   cb.d_S = nullptr;
-  cb.d_flip_bf16 = nullptr;
+  cb.d_dpair = nullptr;
   cb.d_flip_f32 = nullptr;
 }
 
@@ -248,16 +249,23 @@ int upload_device(tq::Codebook& cb) {
     std::vector<uint16_t> frag;
     build_fragments_128(cb.S_rot, frag);
     e = upload(&cb.d_frag, frag.data(), frag.size() * sizeof(uint16_t));
-    // Sign-flip words applying D to the raw inputs of the lane that loads
-    // coordinates [64h, 64h + 64): bf16 pairs (two per word) and float32.
-    std::vector<uint32_t> fb(64, 0), ff(128, 0);
+    // D for the lane that loads coordinates [64h, 64h + 64): for bf16 keys the
+    // pairs (d_2p, +d_2p+1) and (d_2p, -d_2p+1) that turn one dot2 per output
+    // into the first butterfly stage; for float32 keys sign-flip words.
+    std::vector<uint32_t> dp(128, 0), ff(128, 0);
+    const uint32_t one = 0x3F80u, neg = 0xBF80u;   // bf16 +1, -1
     for (int h = 0; h < 2; ++h)
-      for (int e2 = 0; e2 < 64; ++e2)
-        if (cb.delta[64 * h + e2] < 0) {
-          fb[h * 32 + e2 / 2] |= (e2 & 1) ? 0x80000000u : 0x00008000u;
-          ff[h * 64 + e2] = 0x80000000u;
-        }
-    if (e == hipSuccess) e = upload(&cb.d_flip_bf16, fb.data(), fb.size() * 4);
+      for (int p = 0; p < 32; ++p) {
+        const int i0 = 64 * h + 2 * p, i1 = i0 + 1;
+        const uint32_t a = cb.delta[i0] < 0 ? neg : one;
+        const uint32_t b = cb.delta[i1] < 0 ? neg : one;
+        const uint32_t nb = b ^ 0x8000u;
+        dp[(h * 2 + 0) * 32 + p] = a | (b << 16);
+        dp[(h * 2 + 1) * 32 + p] = a | (nb << 16);
+      }
+    for (int i = 0; i < 128; ++i)
+      if (cb.delta[i] < 0) ff[(i >> 6) * 64 + (i & 63)] = 0x80000000u;
+    if (e == hipSuccess) e = upload(&cb.d_dpair, dp.data(), dp.size() * 4);
     if (e == hipSuccess) e = upload(&cb.d_flip_f32, ff.data(), ff.size() * 4);
   }
   if (e != hipSuccess) {
@@ -357,6 +365,7 @@ int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
   if (G == 0 || N == 0) return TQ_OK;
   if (!keys || !packed || !aligned16(keys) || !aligned16(packed)) return TQ_ERR_ARG;
   if (!tq::encode_supported(*cb)) return TQ_ERR_UNSUPPORTED;
+  if (G * ((N + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;   // 32-key tiles < 2^31
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
   hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, N, packed,
@@ -378,8 +387,8 @@ int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64
   if (G == 0 || N == 0 || Qg == 0) return TQ_OK;
   if (!q || !packed || !logits || !aligned16(q) || !aligned16(packed) || !aligned16(logits))
     return TQ_ERR_ARG;
-  if (!ws || !aligned16(ws) || ws_bytes < tq::score_workspace_bytes(*cb, G, Qg))
-    return TQ_ERR_WORKSPACE;
+  const size_t need = tq::score_workspace_bytes(*cb, G, Qg);
+  if (need > 0 && (!ws || !aligned16(ws) || ws_bytes < need)) return TQ_ERR_WORKSPACE;
   if (!tq::score_supported(*cb)) return TQ_ERR_UNSUPPORTED;
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;

@@ -39,7 +39,7 @@ struct Codebook {
   DevConsts* d_consts = nullptr;
   uint4* d_frag = nullptr;       // S R^T as float16 hi/lo, matrix-core A-operand order
   float* d_S = nullptr;          // S, float32 [m][d]
-  uint32_t* d_flip_bf16 = nullptr;  // [2][d/4] sign-flip words for bf16 pairs (d = 128)
+  uint32_t* d_dpair = nullptr;      // [2 halves][+/-][32] bf16 pairs (d_a, +-d_b) (d = 128)
   uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
 };
 

@@ -49,6 +49,21 @@ __device__ __forceinline__ float h2f_bits(uint32_t b) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// x = hi + lo for two values: hi = RTZ_f16(x) packed by one convert, and
+// lo = RN_f16(x - hi) (x - hi is exact in float32).  Builtins only: the
+// registers feed the matrix cores, and the compiler's hazard checks do not
+// see through inline assembly.
+__device__ __forceinline__ void split_f16_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+  const half2v l = {static_cast<_Float16>(x0 - static_cast<float>(h[0])),
+                    static_cast<_Float16>(x1 - static_cast<float>(h[1]))};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 int num_cus() {
   static int cus = 0;
   static std::once_flag once;
@@ -65,7 +80,7 @@ int num_cus() {
 // ============================================================== encode, d = 128
 //
 // Lane layout: a wave encodes 32 keys at a time, two lanes per key.  Lane
-// L = 32h + kl loads coordinates [64h, 64h + 64) of key kl into x[0..63].
+// L = 32h + kl holds coordinates [64h, 64h + 64) of key kl in x[0..63].
 // Six butterfly stages run inside the register file; the stage across the
 // two halves uses v_permlane32_swap on register pairs (r, r + 32), which
 // leaves register r of half h holding coordinate
@@ -74,319 +89,475 @@ int num_cus() {
 // The residual registers feed the matrix-core B operand directly (K order
 // = register order); the host lays S R^T out in the matching A order.
 
-constexpr int kEncThreads = 256;
-constexpr int kEncWaves = kEncThreads / 64;
+struct EncConsts {
+  float tpos[3], cpos[4], sqrt_d;
+};
 
-template <int B, bool BF16>
-__global__ __launch_bounds__(kEncThreads, 2) void encode128_kernel(
-    const void* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
-    uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
-    const uint4* __restrict__ frag, const uint32_t* __restrict__ flip) {
-  constexpr int K = 1 << (B - 1);      // levels on the positive half
-  constexpr int P = B + 1;             // planes per key
-  constexpr int NFLIP = BF16 ? 64 : 128;
-  __shared__ uint4 s_frag[4096];       // [hi | lo][kc 8][jb 4][lane 64]
-  __shared__ uint32_t s_flip[NFLIP];
+__device__ __forceinline__ void load_enc_consts(const DevConsts* __restrict__ cst, EncConsts& c) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) c.tpos[k] = cst->tpos[k];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c.cpos[k] = cst->cpos_s[k];
+  c.sqrt_d = cst->sqrt_d;
+}
 
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 4096; i += kEncThreads) s_frag[i] = frag[i];
-  for (int i = tid; i < NFLIP; i += kEncThreads) s_flip[i] = flip[i];
-  float tpos[K > 1 ? K - 1 : 1], cpos[K];
+// Butterfly stages of strides first_stride..32 inside the lane, then the
+// stride-64 stage across the wave halves.
+__device__ __forceinline__ void butterfly_rest(float (&x)[64], int first_stride) {
 #pragma unroll
-  for (int k = 0; k < K - 1; ++k) tpos[k] = cst->tpos[k];
-#pragma unroll
-  for (int k = 0; k < K; ++k) cpos[k] = cst->cpos_s[k];
-  const float sqrt_d = cst->sqrt_d;
-  __syncthreads();
-
-  const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, kl = lane & 31;
-  const int64_t tpg = (N + 31) / 32;
-  const int64_t ntiles = G * tpg;
-
-  for (int64_t tile = int64_t(blockIdx.x) * kEncWaves + wave; tile < ntiles;
-       tile += int64_t(gridDim.x) * kEncWaves) {
-    const int64_t g = tile / tpg;
-    const int64_t n = (tile - g * tpg) * 32 + kl;
-    const bool valid = n < N;
-    // Lanes past the end of a ragged group load the group's last key; their
-    // results are never stored and each key occupies its own matrix column.
-    const int64_t nl = valid ? n : N - 1;
-    float x[64];
-    float nu2 = 0.f;
-
-    // ---- load, apply D (sign flips), accumulate ||k||^2
-    if constexpr (BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          static_cast<const uint16_t*>(keys) + ((g * N + nl) * 128 + 64 * h));
-      const uint4* fl = reinterpret_cast<const uint4*>(s_flip) + h * 8;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint4 v = src[c];
-        const uint4 f = fl[c];
-        const uint32_t w[4] = {v.x ^ f.x, v.y ^ f.y, v.z ^ f.z, v.w ^ f.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          x[8 * c + 2 * t] = __uint_as_float(w[t] << 16);
-          x[8 * c + 2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
-        }
-      }
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(
-          static_cast<const float*>(keys) + ((g * N + nl) * 128 + 64 * h));
-      const uint4* fl = reinterpret_cast<const uint4*>(s_flip) + h * 16;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const uint4 v = src[c];
-        const uint4 f = fl[c];
-        x[4 * c + 0] = __uint_as_float(v.x ^ f.x);
-        x[4 * c + 1] = __uint_as_float(v.y ^ f.y);
-        x[4 * c + 2] = __uint_as_float(v.z ^ f.z);
-        x[4 * c + 3] = __uint_as_float(v.w ^ f.w);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 64; ++r) nu2 = fmaf(x[r], x[r], nu2);
-
-    // ---- Hadamard butterfly: strides 1..32 in registers, stride 64 across halves
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-#pragma unroll
-      for (int r = 0; r < 64; ++r) {
-        if (r & s) continue;
-        const float a = x[r], b = x[r + s];
-        x[r] = a + b;
-        x[r + s] = a - b;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[r]), __float_as_uint(x[r + 32]),
-                                                 false, false);
-      const float a = __uint_as_float(pr[0]), b = __uint_as_float(pr[1]);
-      x[r] = a + b;
-      x[r + 32] = a - b;
-    }
-
-    nu2 = xor32_sum(nu2);
-    const float nu = sqrtf(nu2);
-    const bool zero = !(nu >= 1e-10f);
-    const float nsd = nu * sqrt_d;                       // u = y * nu * sqrt(d)
-    const float gsc = zero ? 0.f : kResidualScale / nsd;  // u -> 2^12 y
-    float tu[K > 1 ? K - 1 : 1];
-#pragma unroll
-    for (int k = 0; k < K - 1; ++k) tu[k] = tpos[k] * nsd;
-
-    // ---- Lloyd-Max codes (sign bit + magnitude thresholds), residual, hi/lo split
-    uint32_t wu[2] = {0u, 0u};
-    uint32_t wd[K > 1 ? K - 1 : 1][2];
-#pragma unroll
-    for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k][0] = wd[k][1] = 0u;
-    half8 bhi[8], blo[8];
-    float rho2 = 0.f;
+  for (int st = 1; st < 64; st <<= 1) {
+    if (st < first_stride) continue;
 #pragma unroll
     for (int r = 0; r < 64; ++r) {
-      const int ws = r >> 5;
-      // sign-flipped zero inputs can leave -0 after the butterfly; + 0 makes an
-      // exact zero count as non-negative (a value on the middle threshold goes up)
-      const float u = x[r] + 0.0f;
-      const float a = fabsf(u);
-      wu[ws] = push_sign(wu[ws], u);
-      float mag = cpos[0];
-#pragma unroll
-      for (int k = 0; k < K - 1; ++k) {
-        const float dk = a - tu[k];
-        wd[k][ws] = push_sign(wd[k][ws], dk);
-        mag = (dk >= 0.f) ? cpos[k + 1] : mag;
-      }
-      const float yh = copysignf(mag, u);
-      const float ep = fmaf(u, gsc, -yh);
-      rho2 = fmaf(ep, ep, rho2);
-      const _Float16 hi = static_cast<_Float16>(ep);
-      bhi[r >> 3][r & 7] = hi;
-      blo[r >> 3][r & 7] = static_cast<_Float16>(ep - static_cast<float>(hi));
+      if (r & st) continue;
+      const float a = x[r], b = x[r + st];
+      x[r] = a + b;
+      x[r + st] = a - b;
     }
-    rho2 = xor32_sum(rho2);
-    const float rho = zero ? 0.f : sqrtf(rho2) * (nu * (1.0f / kResidualScale));
-
-    // words were filled oldest-bit-first: bit (r % 32) sits at 31 - r % 32
-    uint32_t pw[P - 1][2];
+  }
 #pragma unroll
-    for (int ws = 0; ws < 2; ++ws) {
-      const uint32_t u_ = __builtin_bitreverse32(wu[ws]);
-      if constexpr (B == 1) {
-        pw[0][ws] = ~u_;
-      } else if constexpr (B == 2) {
-        pw[1][ws] = ~u_;
-        pw[0][ws] = ~(u_ ^ __builtin_bitreverse32(wd[0][ws]));
-      } else {
-        const uint32_t d0 = __builtin_bitreverse32(wd[0][ws]);
-        const uint32_t d1 = __builtin_bitreverse32(wd[1][ws]);
-        const uint32_t d2 = __builtin_bitreverse32(wd[2][ws]);
-        pw[2][ws] = ~u_;
-        pw[1][ws] = ~(u_ ^ d1);
-        pw[0][ws] = ~(u_ ^ d0 ^ d1 ^ d2);
-      }
-    }
-    const bool keep = valid && !zero;
-    uint32_t* pl = planes + (g * P) * N * 4;
-#pragma unroll
-    for (int p = 0; p < P - 1; ++p) {
-      // (word h, word 2+h) of each lane -> (words 2h, 2h+1): swap across halves
-      auto pr = __builtin_amdgcn_permlane32_swap(pw[p][0], pw[p][1], false, false);
-      if (valid)
-        *reinterpret_cast<uint2*>(pl + (p * N + n) * 4 + 2 * h) =
-            make_uint2(keep ? uint32_t(pr[0]) : 0u, keep ? uint32_t(pr[1]) : 0u);
-    }
-
-    // ---- QJL projection p = (S R^T) r_rot on the matrix cores (fp32 accumulate,
-    //      three-term fp16 split: hi*hi + hi*lo + lo*hi), then sign words.
-    // The fragment table never changes inside the tile loop; an opaque lane
-    // offset keeps the compiler from hoisting all 64 reads (256 VGPRs) out of it.
-    int fl_off = lane;
-    asm volatile("" : "+v"(fl_off));
-    const half8* fh = reinterpret_cast<const half8*>(s_frag) + fl_off;
-    const half8* fo = reinterpret_cast<const half8*>(s_frag + 2048) + fl_off;
-    uint32_t sw[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const half8 ahi = fh[(kc * 4 + jb) * 64];
-        const half8 alo = fo[(kc * 4 + jb) * 64];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhi[kc], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blo[kc], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhi[kc], acc, 0, 0, 0);
-      }
-      // lane (kl, h) holds rows j = 32 jb + 8 (v / 4) + 4 h + (v % 4) of key kl
-      uint32_t b16 = 0u;
-#pragma unroll
-      for (int v = 15; v >= 0; --v) b16 = push_sign(b16, acc[v]);
-      uint32_t t = (b16 | (b16 << 8)) & 0x00FF00FFu;
-      t = (t | (t << 4)) & 0x0F0F0F0Fu;
-      sw[jb] = xor32_or(t << (4 * h));
-    }
-
-    if (valid) {
-      const bool keep_s = keep && rho2 > 0.f;
-      uint2 so = make_uint2(keep_s ? (h ? sw[2] : sw[0]) : 0u, keep_s ? (h ? sw[3] : sw[1]) : 0u);
-      *reinterpret_cast<uint2*>(pl + ((P - 1) * N + n) * 4 + 2 * h) = so;
-      if (h == 0) {
-        const uint32_t nb = keep ? f2h_bits(nu) : 0u;
-        const uint32_t rb = keep ? f2h_bits(rho) : 0u;
-        norms[g * N + n] = nb | (rb << 16);
-      }
-    }
+  for (int r = 0; r < 32; ++r) {
+    auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[r]), __float_as_uint(x[r + 32]),
+                                               false, false);
+    const float a = __uint_as_float(pr[0]), b = __uint_as_float(pr[1]);
+    x[r] = a + b;
+    x[r + 32] = a - b;
   }
 }
 
-// ============================================================== query prep
-// One wave per query: Rq = R q (butterfly; lane L holds coordinates L, L+64),
-// Sq = S q (lane L computes rows L and L + 64), and the sums of both.
-// Workspace: float [G*Qg][2][128] then float [G*Qg][4] (sum Rq, sum Sq, 0, 0).
+// Everything after the rotation for the 32 keys of one wave tile: codes and
+// code planes, residual and its norm, the matrix-core QJL projection, sign
+// words, stores.  x holds u = H D k (unnormalised); nu2 is this lane's half
+// of ||k||^2.  Rotated values must carry no -0 (an exact zero counts as
+// non-negative).
+// Results of one lane for one tile: words (2h, 2h+1) of every plane of key
+// (g, n) and, for h = 0, the packed half norms.
+struct TileOut {
+  uint2 w[4];        // planes 0..B (code planes, then the sign plane at index B)
+  uint32_t norm;
+  int64_t g, n;
+  bool valid;
+};
 
-constexpr int kPrepThreads = 256;
+template <int B>
+__device__ __forceinline__ void store_tile(const TileOut& o, int lane, int64_t N,
+                                           uint32_t* __restrict__ planes,
+                                           uint32_t* __restrict__ norms) {
+  constexpr int P = B + 1;
+  if (!o.valid) return;
+  const int h = lane >> 5;
+  uint32_t* pl = planes + (o.g * P) * N * 4;
+#pragma unroll
+  for (int p = 0; p < P; ++p) *reinterpret_cast<uint2*>(pl + (p * N + o.n) * 4 + 2 * h) = o.w[p];
+  if (h == 0) norms[o.g * N + o.n] = o.norm;
+}
 
-template <bool BF16>
-__global__ __launch_bounds__(kPrepThreads) void prep128_kernel(
-    const void* __restrict__ q, int64_t nq, const DevConsts* __restrict__ cst,
-    const float* __restrict__ S, float* __restrict__ ws) {
-  __shared__ float s_q[kPrepThreads / 64][128];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t qv_ = int64_t(blockIdx.x) * (kPrepThreads / 64) + wave;
-  const bool valid = qv_ < nq;           // every wave reaches the barrier below
-  const int64_t qi = valid ? qv_ : nq - 1;
-  float v0, v1;
-  if constexpr (BF16) {
-    const uint16_t* qb = static_cast<const uint16_t*>(q) + qi * 128;
-    v0 = __uint_as_float(uint32_t(qb[lane]) << 16);
-    v1 = __uint_as_float(uint32_t(qb[lane + 64]) << 16);
-  } else {
-    const float* qf = static_cast<const float*>(q) + qi * 128;
-    v0 = qf[lane];
-    v1 = qf[lane + 64];
-  }
-  s_q[wave][lane] = v0;
-  s_q[wave][lane + 64] = v1;
-  const uint32_t n0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
-  const uint32_t n1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
-  float a = n0 ? -v0 : v0, b = n1 ? -v1 : v1;
-  float y0 = a + b, y1 = a - b;       // stride 64 in registers
+template <int B>
+__device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, const EncConsts& ec,
+                                            const uint4* __restrict__ s_frag, int lane, int64_t g,
+                                            int64_t n, bool valid, TileOut& out) {
+  constexpr int K = 1 << (B - 1);      // levels on the positive half
+  constexpr int P = B + 1;             // planes per key
+  const int h = lane >> 5;
+  nu2 = xor32_sum(nu2);
+  const float nu = sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * ec.sqrt_d;                       // u = y * nu * sqrt(d)
+  const float gsc = zero ? 0.f : kResidualScale / nsd;    // u -> 2^12 y
+  float tu[K > 1 ? K - 1 : 1];
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const float p0 = __shfl_xor(y0, s), p1 = __shfl_xor(y1, s);
-    const bool up = lane & s;
-    y0 = up ? p0 - y0 : y0 + p0;
-    y1 = up ? p1 - y1 : y1 + p1;
-  }
-  y0 *= cst->inv_sqrt_d;
-  y1 *= cst->inv_sqrt_d;
-  __syncthreads();   // s_q rows written by other lanes of the wave
-  float s0 = 0.f, s1 = 0.f;
-  const float4* r0 = reinterpret_cast<const float4*>(S + int64_t(lane) * 128);
-  const float4* r1 = reinterpret_cast<const float4*>(S + int64_t(lane + 64) * 128);
-  const float4* qv = reinterpret_cast<const float4*>(s_q[wave]);
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) {
-    const float4 qq = qv[i], a0 = r0[i], a1 = r1[i];
-    s0 = fmaf(a0.x, qq.x, fmaf(a0.y, qq.y, fmaf(a0.z, qq.z, fmaf(a0.w, qq.w, s0))));
-    s1 = fmaf(a1.x, qq.x, fmaf(a1.y, qq.y, fmaf(a1.z, qq.z, fmaf(a1.w, qq.w, s1))));
-  }
-  float* out = ws + qi * 256;
-  if (valid) {
-    out[lane] = y0;
-    out[lane + 64] = y1;
-    out[128 + lane] = s0;
-    out[128 + lane + 64] = s1;
-  }
-  float sr = y0 + y1, ss = s0 + s1;
+  for (int k = 0; k < K - 1; ++k) tu[k] = ec.tpos[k] * nsd;
+
+  // ---- Lloyd-Max codes (sign bit + magnitude thresholds), residual, hi/lo
+  //      split, and the QJL projection p = (S R^T) r_rot on the matrix cores,
+  //      interleaved: as soon as the 16 coordinates of chunk kc are split into
+  //      fp16 hi/lo, its 12 MFMAs (4 row blocks x hi*hi + hi*lo + lo*hi, fp32
+  //      accumulation) are issued, so the matrix core runs while the vector
+  //      ALU quantises the next chunk.
+  // The fragment table never changes inside the tile loop; an opaque lane
+  // offset keeps the compiler from hoisting its 64 reads out of the loop.
+  int fl_off = lane;
+  asm volatile("" : "+v"(fl_off));
+  const half8* fh = reinterpret_cast<const half8*>(s_frag) + fl_off;
+  const half8* fo = reinterpret_cast<const half8*>(s_frag + 2048) + fl_off;
+  uint32_t wu[2] = {0u, 0u};
+  uint32_t wd[K > 1 ? K - 1 : 1][2];
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    sr += __shfl_xor(sr, s);
-    ss += __shfl_xor(ss, s);
+  for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k][0] = wd[k][1] = 0u;
+  f32x16 acc[4] = {};
+  float rho2 = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    uint32_t bh[4], bl[4];   // residual as packed f16 pairs (hi, lo) of registers 8kc..8kc+7
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      float ep[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rr = 8 * kc + 2 * pr + t, ws = rr >> 5;
+        const float u = x[rr];
+        const float a = fabsf(u);
+        wu[ws] = push_sign(wu[ws], u);
+        float mag = ec.cpos[0];
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) {
+          const float dk = a - tu[k];
+          wd[k][ws] = push_sign(wd[k][ws], dk);
+          mag = (dk >= 0.f) ? ec.cpos[k + 1] : mag;
+        }
+        const float yh = copysignf(mag, u);
+        // the negated residual yh - u g = 2^12 (c[code] - y): one fma with a
+        // negated source; the fragment table holds -S R^T, so the products
+        // below still come out as +S r
+        ep[t] = fmaf(-u, gsc, yh);
+        rho2 = fmaf(ep[t], ep[t], rho2);
+      }
+      split_f16_pair(ep[0], ep[1], bh[pr], bl[pr]);
+    }
+    const half8 bhi = __builtin_bit_cast(half8, u32x4{bh[0], bh[1], bh[2], bh[3]});
+    const half8 blo = __builtin_bit_cast(half8, u32x4{bl[0], bl[1], bl[2], bl[3]});
+    // per-chunk opaque offset (no instruction): keeps this chunk's 8 fragment
+    // reads next to its MFMAs instead of all 64 being hoisted to the top
+    int ko = kc * 4 * 64;
+    asm volatile("" : "+v"(ko));
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const half8 ahi = fh[ko + jb * 64];
+      const half8 alo = fo[ko + jb * 64];
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhi, acc[jb], 0, 0, 0);
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blo, acc[jb], 0, 0, 0);
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhi, acc[jb], 0, 0, 0);
+    }
+    // bound the scheduler's window to one chunk (limits register pressure)
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (valid && lane == 0) {
-    float* sums = ws + nq * 256 + qi * 4;
-    sums[0] = sr;
-    sums[1] = ss;
-    sums[2] = 0.f;
-    sums[3] = 0.f;
+  rho2 = xor32_sum(rho2);
+  const float rho = zero ? 0.f : sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+
+  // words were filled oldest-bit-first: bit (r % 32) sits at 31 - r % 32
+  uint32_t pw[P - 1][2];
+#pragma unroll
+  for (int ws = 0; ws < 2; ++ws) {
+    const uint32_t u_ = __builtin_bitreverse32(wu[ws]);
+    if constexpr (B == 1) {
+      pw[0][ws] = ~u_;
+    } else if constexpr (B == 2) {
+      pw[1][ws] = ~u_;
+      pw[0][ws] = ~(u_ ^ __builtin_bitreverse32(wd[0][ws]));
+    } else {
+      const uint32_t d0 = __builtin_bitreverse32(wd[0][ws]);
+      const uint32_t d1 = __builtin_bitreverse32(wd[1][ws]);
+      const uint32_t d2 = __builtin_bitreverse32(wd[2][ws]);
+      pw[2][ws] = ~u_;
+      pw[1][ws] = ~(u_ ^ d1);
+      pw[0][ws] = ~(u_ ^ d0 ^ d1 ^ d2);
+    }
+  }
+  const bool keep = valid && !zero;
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p) {
+    // (word h, word 2+h) of each lane -> (words 2h, 2h+1): swap across halves
+    auto pr = __builtin_amdgcn_permlane32_swap(pw[p][0], pw[p][1], false, false);
+    out.w[p] = make_uint2(keep ? uint32_t(pr[0]) : 0u, keep ? uint32_t(pr[1]) : 0u);
+  }
+
+  // ---- sign words: lane (kl, h) holds rows j = 32 jb + 8 (v / 4) + 4 h + (v % 4) of key kl
+  uint32_t sw[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    uint32_t b16 = 0u;
+#pragma unroll
+    for (int v = 15; v >= 0; --v) b16 = push_sign(b16, acc[jb][v]);
+    uint32_t t = (b16 | (b16 << 8)) & 0x00FF00FFu;
+    t = (t | (t << 4)) & 0x0F0F0F0Fu;
+    sw[jb] = xor32_or(t << (4 * h));
+  }
+
+  const bool keep_s = keep && rho2 > 0.f;
+  out.w[P - 1] = make_uint2(keep_s ? (h ? sw[2] : sw[0]) : 0u, keep_s ? (h ? sw[3] : sw[1]) : 0u);
+  out.norm = keep ? (uint32_t(f2h_bits(nu)) | (uint32_t(f2h_bits(rho)) << 16)) : 0u;
+  out.g = g;
+  out.n = n;
+  out.valid = valid;
+}
+
+// ---- bf16 keys.  Eight waves per workgroup, one workgroup per CU.  Each
+// wave owns an 8 KB LDS buffer that the next tile's keys stream into
+// (global_load_lds, 16 B per lane, no registers held) while the current tile
+// is encoded.  The first butterfly stage, the bf16 -> f32 conversion and the
+// sign flips D run as one v_dot2_f32_bf16 per output against (d_a, +-d_b)
+// pairs; its +0 addend also turns a sum of signed zeros into +0.
+constexpr int kEncBfThreads = 512;
+constexpr int kEncBfWaves = kEncBfThreads / 64;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void issue_tile_dma(const uint16_t* __restrict__ keys, uint32_t tile,
+                                               uint32_t tpg, int64_t N, int lane, uint4* buf) {
+  const int h = lane >> 5, kl = lane & 31;
+  const uint32_t gt = tile / tpg;
+  const int64_t g = gt;
+  const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
+  const int64_t nl = n < N ? n : N - 1;
+  const uint4* src = reinterpret_cast<const uint4*>(keys + ((g * N + nl) * 128 + 64 * h));
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + c),
+                                     (lds_void*)(buf + c * 64), 16, 0, 0);
+}
+
+template <int B>
+__global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
+    const uint16_t* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
+    uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
+    const uint4* __restrict__ frag, const uint32_t* __restrict__ dpair) {
+  __shared__ uint4 s_frag[4096];                   // 64 KB: [hi | lo][kc 8][jb 4][lane 64]
+  __shared__ uint4 s_raw[kEncBfWaves][8 * 64];     // 64 KB: per-wave key tile
+  __shared__ uint4 s_dp[2][2][8];                  // [h][+/-][pairs 4 per entry]
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, kl = lane & 31;
+  // wave-uniform tile bookkeeping lives in scalar registers (tiles < 2^31)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t tpg = uint32_t((N + 31) / 32);
+  const uint32_t ntiles = uint32_t(G) * tpg;
+  const uint32_t stride = gridDim.x * kEncBfWaves;
+  uint32_t tile = blockIdx.x * kEncBfWaves + wave;
+  uint4* buf = s_raw[wave];
+  if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, lane, buf);
+  for (int i = tid; i < 4096; i += kEncBfThreads) s_frag[i] = frag[i];
+  if (tid < 32) reinterpret_cast<uint4*>(s_dp)[tid] = reinterpret_cast<const uint4*>(dpair)[tid];
+  EncConsts ec;
+  load_enc_consts(cst, ec);
+  __syncthreads();
+
+  // Each iteration: wait for this tile's keys (the DMA issued one iteration
+  // earlier, and the previous iteration's stores, are the only vector memory
+  // operations in flight), copy them to registers, start the next tile's DMA,
+  // write the previous tile's results, then encode this tile.  The compiler
+  // does not track the loop-carried DMA, hence the explicit wait.
+  TileOut prev;
+  prev.valid = false;
+  for (; tile < ntiles; tile += stride) {
+    const uint32_t gt = tile / tpg;
+    const int64_t g = gt;
+    const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
+    const bool valid = n < N;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint4 raw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) raw[c] = buf[c * 64 + lane];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
+    if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, lane, buf);
+    store_tile<B>(prev, lane, N, planes, norms);
+
+    float x[64];
+    float nu2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 dp = s_dp[h][0][c], dm = s_dp[h][1][c];
+      const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+      const uint32_t wp[4] = {dp.x, dp.y, dp.z, dp.w};
+      const uint32_t wm[4] = {dm.x, dm.y, dm.z, dm.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x2 kv = __builtin_bit_cast(bf16x2, w[t]);
+        x[8 * c + 2 * t] =
+            __builtin_amdgcn_fdot2_f32_bf16(kv, __builtin_bit_cast(bf16x2, wp[t]), 0.0f, false);
+        x[8 * c + 2 * t + 1] =
+            __builtin_amdgcn_fdot2_f32_bf16(kv, __builtin_bit_cast(bf16x2, wm[t]), 0.0f, false);
+        nu2 = __builtin_amdgcn_fdot2_f32_bf16(kv, kv, nu2, false);
+      }
+    }
+    butterfly_rest(x, 2);
+    encode_tail<B>(x, nu2, ec, s_frag, lane, g, n, valid, prev);
+  }
+  store_tile<B>(prev, lane, N, planes, norms);
+}
+
+// ---- float32 keys (register loads, four waves per workgroup).
+constexpr int kEncThreads = 256;
+constexpr int kEncWaves = kEncThreads / 64;
+
+template <int B>
+__global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
+    const float* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
+    uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
+    const uint4* __restrict__ frag, const uint32_t* __restrict__ flip) {
+  __shared__ uint4 s_frag[4096];       // [hi | lo][kc 8][jb 4][lane 64]
+  __shared__ uint32_t s_flip[128];
+
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 4096; i += kEncThreads) s_frag[i] = frag[i];
+  for (int i = tid; i < 128; i += kEncThreads) s_flip[i] = flip[i];
+  EncConsts ec;
+  load_enc_consts(cst, ec);
+  __syncthreads();
+
+  const int lane = tid & 63, h = lane >> 5, kl = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t tpg = uint32_t((N + 31) / 32);
+  const uint32_t ntiles = uint32_t(G) * tpg;
+  for (uint32_t tile = blockIdx.x * kEncWaves + wave; tile < ntiles; tile += gridDim.x * kEncWaves) {
+    const uint32_t gt = tile / tpg;
+    const int64_t g = gt;
+    const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
+    const bool valid = n < N;
+    // lanes past the end of a ragged group load the group's last key; their
+    // results are never stored and each key has its own matrix column
+    const int64_t nl = valid ? n : N - 1;
+    const uint4* src = reinterpret_cast<const uint4*>(keys + ((g * N + nl) * 128 + 64 * h));
+    const uint4* fl = reinterpret_cast<const uint4*>(s_flip) + h * 16;
+    float x[64];
+    float nu2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint4 v = src[c];
+      const uint4 f = fl[c];
+      x[4 * c + 0] = __uint_as_float(v.x ^ f.x);
+      x[4 * c + 1] = __uint_as_float(v.y ^ f.y);
+      x[4 * c + 2] = __uint_as_float(v.z ^ f.z);
+      x[4 * c + 3] = __uint_as_float(v.w ^ f.w);
+    }
+#pragma unroll
+    for (int r = 0; r < 64; ++r) nu2 = fmaf(x[r], x[r], nu2);
+    // the first stage adds +0 to its outputs: sign-flipped zero inputs would
+    // otherwise leave -0 behind, and an exact zero must count as non-negative
+#pragma unroll
+    for (int r = 0; r < 64; r += 2) {
+      const float a = x[r], b = x[r + 1];
+      x[r] = (a + b) + 0.0f;
+      x[r + 1] = (a - b) + 0.0f;
+    }
+    butterfly_rest(x, 2);
+    TileOut out;
+    encode_tail<B>(x, nu2, ec, s_frag, lane, g, n, valid, out);
+    store_tile<B>(out, lane, N, planes, norms);
   }
 }
 
 // ============================================================== score, d = 128
-// One workgroup per (group, 4-query chunk, key range).  LDS holds, for the
-// chunk's 4 queries, T[tab][pos][byte] = sum over set bits t of byte of
-// 2 * X[8 pos + t] with X = R q (tab 0, indexed by code-plane bytes) or S q
-// (tab 1, indexed by sign-plane bytes).  Each lane then scores one key per
-// step with 16 table reads per plane.
+// One workgroup (1024 threads) per (group g, chunk of 4 query heads, key
+// range).  It prepares its queries itself -- R q by a butterfly (one query
+// per wave, lane L holding coordinates L and L + 64), S q as 128 dot products
+// per query -- and builds, in LDS, byte subset-sum tables
+//   T[tab][pos][byte] = sum over set bits t of byte of 2 X[8 pos + t]
+// (four queries per 16-byte entry) with X = R q (tab 0, read with code-plane
+// bytes) and X = S q (tab 1, read with sign-plane bytes).  Each lane then
+// scores one key per step, (B + 1) planes x 16 table reads with 4 adds each;
+// sixteen waves per CU keep enough records in flight.
 
-constexpr int kScoreThreads = 512;
+constexpr int kScoreThreads = 1024;
 
-template <int B>
+template <int B, bool QBF16>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
-    const uint4* __restrict__ planes, const uint32_t* __restrict__ norms, int64_t G, int64_t N,
-    int Qg, int nqc, int splits, const float* __restrict__ ws, float* __restrict__ logits,
-    const DevConsts* __restrict__ cst) {
+    const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
+    int64_t G, int64_t N, int Qg, int nqc, int splits, float* __restrict__ logits,
+    const DevConsts* __restrict__ cst, const float* __restrict__ S) {
   constexpr int P = B + 1;
   __shared__ f32x4 s_lut[2][16][256];      // 128 KB
   __shared__ f32x4 s_nib[2][16][2][16];    // 16 KB
-  __shared__ f32x4 s_x[2][128];            // 4 KB
+  __shared__ f32x4 s_x[2][128];            // 4 KB: 2 R q | 2 S q, 4 queries per entry
+  __shared__ float s_q[4][128];            // 2 KB: the chunk's raw queries
+  __shared__ float s_red4[kScoreThreads / 64][4];   // per-wave partial sums of S q
+  __shared__ float s_sum[2][4];            // sum R q, sum S q per query
 
-  const int tid = threadIdx.x;
-  int64_t b = blockIdx.x;
-  const int split = int(b % splits);
-  b /= splits;
-  const int qc = int(b % nqc);
-  const int64_t g = b / nqc;
-  const int64_t nq = G * Qg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int64_t blk = blockIdx.x;
+  const int split = int(blk % splits);
+  blk /= splits;
+  const int qc = int(blk % nqc);
+  const int64_t g = blk / nqc;
+  const int64_t chunk = ((N + splits - 1) / splits + 63) / 64 * 64;
+  const int64_t n0 = int64_t(split) * chunk;
+  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
+  const uint4* pg = planes + g * P * N;
+  const uint32_t* ng = norms + g * N;
 
-  for (int i = tid; i < 2 * 128 * 4; i += kScoreThreads) {
-    const int qq = i & 3, c = (i >> 2) & 127, tab = i >> 9;
+  int64_t n = n0 + tid;
+  // S rows for this thread's share of S q: row j = tid / 8, columns
+  // [16 c8, 16 c8 + 16) -- S (64 KB) is read once per workgroup, all loads in flight
+  const int jrow = tid >> 3, c8 = tid & 7;
+  float4 srow[4];
+  {
+    const float4* row = reinterpret_cast<const float4*>(S + int64_t(jrow) * 128 + 16 * c8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) srow[i] = row[i];
+  }
+  if (tid < 512) {  // queries of the chunk (heads past Qg are zero)
+    const int qq = tid >> 7, c = tid & 127;
     const int qh = qc * 4 + qq;
-    s_x[tab][c][qq] = (qh < Qg) ? 2.0f * ws[(g * Qg + qh) * 256 + tab * 128 + c] : 0.0f;  // element write
+    float v = 0.f;
+    if (qh < Qg) {
+      const int64_t at = (g * Qg + qh) * 128 + c;
+      if constexpr (QBF16)
+        v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
+      else
+        v = static_cast<const float*>(q)[at];
+    }
+    s_q[qq][c] = v;
   }
   __syncthreads();
+  if (wave < 4) {  // R q = H D q / sqrt(d)
+    const float v0 = s_q[wave][lane], v1 = s_q[wave][lane + 64];
+    const uint32_t f0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
+    const uint32_t f1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
+    const float a = f0 ? -v0 : v0, bq = f1 ? -v1 : v1;
+    float y0 = a + bq, y1 = a - bq;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+      const float p0 = __shfl_xor(y0, st), p1 = __shfl_xor(y1, st);
+      const bool up = lane & st;
+      y0 = up ? p0 - y0 : y0 + p0;
+      y1 = up ? p1 - y1 : y1 + p1;
+    }
+    y0 *= cst->inv_sqrt_d;
+    y1 *= cst->inv_sqrt_d;
+    s_x[0][lane][wave] = 2.0f * y0;
+    s_x[0][lane + 64][wave] = 2.0f * y1;
+    float sr = y0 + y1;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) sr += __shfl_xor(sr, st);
+    if (lane == 0) s_sum[0][wave] = sr;
+  }
+  {  // S q: partial dots of row jrow over 16 columns for the 4 queries
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * c8 + 4 * i;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(&s_q[qq][c]);
+        acc[qq] = fmaf(srow[i].x, xv[0], fmaf(srow[i].y, xv[1], fmaf(srow[i].z, xv[2], fmaf(srow[i].w, xv[3], acc[qq]))));
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      acc[qq] += __shfl_xor(acc[qq], 1);
+      acc[qq] += __shfl_xor(acc[qq], 2);
+      acc[qq] += __shfl_xor(acc[qq], 4);
+    }
+    if (c8 == 0) s_x[1][jrow] = f32x4{2.0f * acc[0], 2.0f * acc[1], 2.0f * acc[2], 2.0f * acc[3]};
+    // sum over rows of S q: lanes with c8 == 0 hold the 8 rows of this wave
+    float sv[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      sv[qq] = c8 == 0 ? acc[qq] : 0.f;
+#pragma unroll
+      for (int st = 8; st < 64; st <<= 1) sv[qq] += __shfl_xor(sv[qq], st);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) s_red4[wave][qq] = sv[qq];
+    }
+  }
+  __syncthreads();
+  if (tid < 4) {
+    float t = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < kScoreThreads / 64; ++wv) t += s_red4[wv][tid];
+    s_sum[1][tid] = t;
+  }
   for (int i = tid; i < 2 * 16 * 2 * 16; i += kScoreThreads) {
     const int nib = i & 15, hf = (i >> 4) & 1, pos = (i >> 5) & 15, tab = i >> 9;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -400,45 +571,45 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const int byte = i & 255, pos = (i >> 8) & 15, tab = i >> 12;
     s_lut[tab][pos][byte] = s_nib[tab][pos][0][byte & 15] + s_nib[tab][pos][1][byte >> 4];
   }
+  __syncthreads();
+  // per-query sums are the same for every lane: keep them in scalar registers
   float sr[4], ss[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
-    const int qh = qc * 4 + qq;
-    const float* sums = ws + nq * 256 + (g * Qg + (qh < Qg ? qh : 0)) * 4;
-    sr[qq] = sums[0];
-    ss[qq] = sums[1];
+    sr[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_sum[0][qq])));
+    ss[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_sum[1][qq])));
   }
   const float a0 = cst->alpha[0], a1 = cst->alpha[1], a2 = cst->alpha[2], a3 = cst->alpha[3];
   const float asum = cst->alpha_sum, qs = cst->qjl_scale;
-  __syncthreads();
 
-  const int64_t chunk = ((N + splits - 1) / splits + 63) / 64 * 64;
-  const int64_t n0 = int64_t(split) * chunk;
-  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
-  const uint4* pg = planes + g * P * N;
+  // four table reads (one plane word) at a time keep the live registers low
+  // enough for four waves per SIMD; sixteen waves keep the LDS busy
+  auto add_plane = [&](const uint4 wv, int tab, float* acc) {
+    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 tv = s_lut[tab][wi * 4 + k][(ww[wi] >> (8 * k)) & 255u];
+        acc[0] += tv[0]; acc[1] += tv[1]; acc[2] += tv[2]; acc[3] += tv[3];
+      }
+      // an empty fence (no instruction) that takes the accumulators: this
+      // word's adds complete before the next word's table reads are issued
+      asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]) : : "memory");
+    }
+  };
 
-  for (int64_t n = n0 + tid; n < n1; n += kScoreThreads) {
+  for (; n < n1; n += kScoreThreads) {
     uint4 w[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) w[p] = pg[p * N + n];
-    const uint32_t nrm = norms[g * N + n];
-    float acc[4][4];     // [term][query]: planes 0..B-1 (and parity), sign plane last
+    const uint32_t nrm = ng[n];
+    float acc[4][4];   // [term][query]: code planes 0..B-1, sign plane in [3]
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) acc[t][qq] = 0.f;
-
-    auto add_plane = [&](const uint4 wv, int tab, float* a) {
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4 tv = s_lut[tab][wi * 4 + k][(ww[wi] >> (8 * k)) & 255u];
-          a[0] += tv[0]; a[1] += tv[1]; a[2] += tv[2]; a[3] += tv[3];
-        }
-    };
-    float mse[4], qjl[4];
+    float mse[4];
     if constexpr (B == 1) {
       add_plane(w[0], 0, acc[0]);
       add_plane(w[1], 1, acc[3]);
@@ -452,27 +623,24 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
       for (int qq = 0; qq < 4; ++qq)
         mse[qq] = fmaf(a0, acc[0][qq], a1 * acc[1][qq]) - asum * sr[qq];
     } else {
+      // three code planes and their parity plane (the s0*s1*s2 Walsh term)
       add_plane(w[0], 0, acc[0]);
       add_plane(w[1], 0, acc[1]);
       add_plane(w[2], 0, acc[2]);
-      const uint4 px = make_uint4(w[0].x ^ w[1].x ^ w[2].x, w[0].y ^ w[1].y ^ w[2].y,
-                                  w[0].z ^ w[1].z ^ w[2].z, w[0].w ^ w[1].w ^ w[2].w);
       float accx[4] = {0.f, 0.f, 0.f, 0.f};
-      add_plane(px, 0, accx);
+      add_plane(make_uint4(w[0].x ^ w[1].x ^ w[2].x, w[0].y ^ w[1].y ^ w[2].y,
+                           w[0].z ^ w[1].z ^ w[2].z, w[0].w ^ w[1].w ^ w[2].w), 0, accx);
       add_plane(w[3], 1, acc[3]);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
         mse[qq] = fmaf(a0, acc[0][qq], fmaf(a1, acc[1][qq], fmaf(a2, acc[2][qq], a3 * accx[qq]))) -
                   asum * sr[qq];
     }
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) qjl[qq] = ss[qq] - acc[3][qq];
-    const float nu = h2f_bits(nrm & 0xffffu), rho = h2f_bits(nrm >> 16);
-    const float rs = rho * qs;
+    const float nu = h2f_bits(nrm & 0xffffu), rs = h2f_bits(nrm >> 16) * qs;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int qh = qc * 4 + qq;
-      if (qh < Qg) logits[(g * Qg + qh) * N + n] = fmaf(nu, mse[qq], rs * qjl[qq]);
+      if (qh < Qg) logits[(g * Qg + qh) * N + n] = fmaf(nu, mse[qq], rs * (ss[qq] - acc[3][qq]));
     }
   }
 }
@@ -582,44 +750,52 @@ __global__ __launch_bounds__(256) void dense128_kernel(const uint16_t* __restric
 bool encode_supported(const Codebook& cb) { return cb.d == 128; }
 bool score_supported(const Codebook& cb) { return cb.d == 128; }
 
+// The scorer prepares its queries inside each workgroup and needs no workspace.
 size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg) {
-  return size_t(G) * size_t(Qg) * (size_t(cb.d) + size_t(cb.m) + 4) * sizeof(float);
+  (void)cb;
+  (void)G;
+  (void)Qg;
+  return 0;
 }
 
 hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                          void* packed, hipStream_t s) {
   const int64_t ntiles = G * ((N + 31) / 32);
-  const int64_t want = (ntiles + kEncWaves - 1) / kEncWaves;
-  const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 2));
   uint32_t* planes = static_cast<uint32_t*>(packed);
   uint32_t* norms = planes + G * N * int64_t(cb.bits) * (cb.d / 32);
-  const bool bf = dtype == 1;
-  const uint32_t* flip = bf ? cb.d_flip_bf16 : cb.d_flip_f32;
-#define TQ_ENC(BB, BF)                                                                     \
-  hipLaunchKernelGGL((encode128_kernel<BB, BF>), dim3(grid), dim3(kEncThreads), 0, s, keys, G, N, \
-                     planes, norms, cb.d_consts, cb.d_frag, flip)
-  switch (cb.bits - 1) {
-    case 1: if (bf) TQ_ENC(1, true); else TQ_ENC(1, false); break;
-    case 2: if (bf) TQ_ENC(2, true); else TQ_ENC(2, false); break;
-    default: if (bf) TQ_ENC(3, true); else TQ_ENC(3, false); break;
+  if (dtype == 1) {
+    const int64_t want = (ntiles + kEncBfWaves - 1) / kEncBfWaves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus())));
+    const uint16_t* kb = static_cast<const uint16_t*>(keys);
+#define TQ_ENCB(BB)                                                                              \
+  hipLaunchKernelGGL((encode128_bf16_kernel<BB>), dim3(grid), dim3(kEncBfThreads), 0, s, kb, G, N, \
+                     planes, norms, cb.d_consts, cb.d_frag, cb.d_dpair)
+    switch (cb.bits - 1) {
+      case 1: TQ_ENCB(1); break;
+      case 2: TQ_ENCB(2); break;
+      default: TQ_ENCB(3); break;
+    }
+#undef TQ_ENCB
+  } else {
+    const int64_t want = (ntiles + kEncWaves - 1) / kEncWaves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 2));
+    const float* kf = static_cast<const float*>(keys);
+#define TQ_ENCF(BB)                                                                             \
+  hipLaunchKernelGGL((encode128_f32_kernel<BB>), dim3(grid), dim3(kEncThreads), 0, s, kf, G, N, \
+                     planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32)
+    switch (cb.bits - 1) {
+      case 1: TQ_ENCF(1); break;
+      case 2: TQ_ENCF(2); break;
+      default: TQ_ENCF(3); break;
+    }
+#undef TQ_ENCF
   }
-#undef TQ_ENC
   return hipGetLastError();
 }
 
 hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                         const void* packed, int64_t N, float* logits, void* ws, hipStream_t s) {
-  const int64_t nq = G * Qg;
-  float* wsf = static_cast<float*>(ws);
-  const int pgrid = int((nq + kPrepThreads / 64 - 1) / (kPrepThreads / 64));
-  if (qdtype == 1)
-    hipLaunchKernelGGL((prep128_kernel<true>), dim3(pgrid), dim3(kPrepThreads), 0, s, q, nq,
-                       cb.d_consts, cb.d_S, wsf);
-  else
-    hipLaunchKernelGGL((prep128_kernel<false>), dim3(pgrid), dim3(kPrepThreads), 0, s, q, nq,
-                       cb.d_consts, cb.d_S, wsf);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  (void)ws;
   const int nqc = (Qg + 3) / 4;
   const int64_t units = G * nqc;
   const int64_t cus = num_cus();
@@ -629,13 +805,14 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const uint4* planes = static_cast<const uint4*>(packed);
   const uint32_t* norms =
       static_cast<const uint32_t*>(packed) + G * N * int64_t(cb.bits) * (cb.d / 32);
-#define TQ_SC(BB)                                                                        \
-  hipLaunchKernelGGL((score128_kernel<BB>), dim3(grid), dim3(kScoreThreads), 0, s, planes, norms, \
-                     G, N, Qg, nqc, splits, wsf, logits, cb.d_consts)
+  const bool bf = qdtype == 1;
+#define TQ_SC(BB, QB)                                                                           \
+  hipLaunchKernelGGL((score128_kernel<BB, QB>), dim3(grid), dim3(kScoreThreads), 0, s, q, planes, \
+                     norms, G, N, Qg, nqc, splits, logits, cb.d_consts, cb.d_S)
   switch (cb.bits - 1) {
-    case 1: TQ_SC(1); break;
-    case 2: TQ_SC(2); break;
-    default: TQ_SC(3); break;
+    case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
+    case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
+    default: if (bf) TQ_SC(3, true); else TQ_SC(3, false); break;
   }
 #undef TQ_SC
   return hipGetLastError();

@@ -193,11 +193,17 @@ def test_gpu_argument_errors():
                               ctypes.c_void_p(packed.data_ptr()), None) == -1
     q = torch.zeros((1, 4, 128), device="cuda")
     out = torch.empty((1, 4, 8), device="cuda")
-    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    assert lib.tq_score_workspace_bytes(cb.handle, 1, 4) == 0     # queries are prepared on chip
     rc = lib.tq_score_logits(cb.handle, ctypes.c_void_p(q.data_ptr()), 0, 1, 4,
                              ctypes.c_void_p(packed.data_ptr()), 8, ctypes.c_void_p(out.data_ptr()),
-                             ctypes.c_void_p(ws.data_ptr()), 16, None)
-    assert rc == -5
+                             None, 0, None)
+    assert rc == 0
+    assert lib.tq_score_logits(cb.handle, ctypes.c_void_p(q.data_ptr() + 4), 0, 1, 4,
+                               ctypes.c_void_p(packed.data_ptr()), 8, ctypes.c_void_p(out.data_ptr()),
+                               None, 0, None) == -1
+    assert lib.tq_score_logits(cb.handle, ctypes.c_void_p(q.data_ptr()), 0, 1, 300,
+                               ctypes.c_void_p(packed.data_ptr()), 8, ctypes.c_void_p(out.data_ptr()),
+                               None, 0, None) == -2
     # empty inputs are no-ops
     assert lib.tq_encode_keys(cb.handle, None, 0, 0, 8, None, None) == 0
     with pytest.raises(K.TQError):
