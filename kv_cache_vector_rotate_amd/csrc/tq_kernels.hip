@@ -437,17 +437,43 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
 }
 
 // ============================================================== score, d = 128
-// One workgroup (1024 threads) per (group g, chunk of 4 query heads, key
-// range).  It prepares its queries itself -- R q by a butterfly (one query
-// per wave, lane L holding coordinates L and L + 64), S q as 128 dot products
-// per query -- and builds, in LDS, byte subset-sum tables
-//   T[tab][pos][byte] = sum over set bits t of byte of 2 X[8 pos + t]
-// (four queries per 16-byte entry) with X = R q (tab 0, read with code-plane
-// bytes) and X = S q (tab 1, read with sign-plane bytes).  Each lane then
-// scores one key per step, (B + 1) planes x 16 table reads with 4 adds each;
-// sixteen waves per CU keep enough records in flight.
+// One workgroup (1024 threads, 16 waves) per (group g, chunk of 4 query heads,
+// key range).  Set-up:
+//  - R q by a butterfly (waves 0-3, one query each; lane L holds coordinates
+//    L and L + 64);
+//  - S q: wave w multiplies rows 64 (w & 1) + L of S by columns
+//    16 (w >> 1) .. 16 (w >> 1) + 15 of the four queries, which are the same
+//    for the whole wave and sit in scalar registers; eight partial sums per row;
+//  - byte subset-sum tables  T[ty][idx][pos] = sum over set bits t of idx of
+//    2 X_ty[8 pos + t], four queries per 16-byte entry, X_0 = R q (read with
+//    code-plane bytes), X_1 = S q (read with sign-plane bytes).
+// Entry (ty, idx, pos) lives at byte ty * 64K + idx * 256 + pos * 16, so byte
+// position pos is always in LDS bank group pos.  Lane L visits the sixteen
+// byte positions of a plane in the order k ^ (L & 15): the sixteen lanes the
+// LDS serves together then hit sixteen different bank groups whatever the
+// key bytes are, and the random gathers run at the conflict-free rate.
+// Each lane scores one key per step: (B + 1) planes (B = 3: plus the parity
+// plane) x 16 table reads with 4 adds each; the next step's records are
+// loaded before the current ones are scored.
 
 constexpr int kScoreThreads = 1024;
+
+struct ScoreLds {
+  f32x4 tab[2 * 256 * 16];   // 128 KB, first: its byte offsets are the table addresses
+  f32x4 x[2][8][16];         // [ty][t][pos] = 2 X_ty[8 pos + t]
+  f32x4 part[8][128];        // S q partial sums, [column segment][row]
+  f32x4 sum[2];              // sum over all coordinates of 2 X_ty
+};
+
+// o[i] = w[i ^ (2 s2 + s1)]: the lane's word order for its position order
+__device__ __forceinline__ void permute_words(const uint4 w, bool s2, bool s1, uint32_t (&o)[4]) {
+  const uint32_t t0 = s2 ? w.z : w.x, t1 = s2 ? w.w : w.y;
+  const uint32_t t2 = s2 ? w.x : w.z, t3 = s2 ? w.y : w.w;
+  o[0] = s1 ? t1 : t0;
+  o[1] = s1 ? t0 : t1;
+  o[2] = s1 ? t3 : t2;
+  o[3] = s1 ? t2 : t3;
+}
 
 template <int B, bool QBF16>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
@@ -455,14 +481,11 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     int64_t G, int64_t N, int Qg, int nqc, int splits, float* __restrict__ logits,
     const DevConsts* __restrict__ cst, const float* __restrict__ S) {
   constexpr int P = B + 1;
-  __shared__ f32x4 s_lut[2][16][256];      // 128 KB
-  __shared__ f32x4 s_nib[2][16][2][16];    // 16 KB
-  __shared__ f32x4 s_x[2][128];            // 4 KB: 2 R q | 2 S q, 4 queries per entry
-  __shared__ float s_q[4][128];            // 2 KB: the chunk's raw queries
-  __shared__ float s_red4[kScoreThreads / 64][4];   // per-wave partial sums of S q
-  __shared__ float s_sum[2][4];            // sum R q, sum S q per query
+  constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
+  __shared__ ScoreLds sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t blk = blockIdx.x;
   const int split = int(blk % splits);
   blk /= splits;
@@ -474,32 +497,76 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const uint4* pg = planes + g * P * N;
   const uint32_t* ng = norms + g * N;
 
-  int64_t n = n0 + tid;
-  // S rows for this thread's share of S q: row j = tid / 8, columns
-  // [16 c8, 16 c8 + 16) -- S (64 KB) is read once per workgroup, all loads in flight
-  const int jrow = tid >> 3, c8 = tid & 7;
+  // ---- loads: S rows, this wave's query (waves 0-3), then the first key tile
+  const int seg = wave >> 1;
+  const int jrow = 64 * (wave & 1) + lane;
   float4 srow[4];
   {
-    const float4* row = reinterpret_cast<const float4*>(S + int64_t(jrow) * 128 + 16 * c8);
+    const float4* row = reinterpret_cast<const float4*>(S + int64_t(jrow) * 128 + 16 * seg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) srow[i] = row[i];
   }
-  if (tid < 512) {  // queries of the chunk (heads past Qg are zero)
-    const int qq = tid >> 7, c = tid & 127;
-    const int qh = qc * 4 + qq;
-    float v = 0.f;
-    if (qh < Qg) {
-      const int64_t at = (g * Qg + qh) * 128 + c;
-      if constexpr (QBF16)
-        v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
-      else
-        v = static_cast<const float*>(q)[at];
+  float v0 = 0.f, v1 = 0.f;
+  if (wave < 4 && qc * 4 + wave < Qg) {
+    const int64_t at = (g * Qg + qc * 4 + wave) * 128 + lane;
+    if constexpr (QBF16) {
+      v0 = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
+      v1 = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at + 64]) << 16);
+    } else {
+      v0 = static_cast<const float*>(q)[at];
+      v1 = static_cast<const float*>(q)[at + 64];
     }
-    s_q[qq][c] = v;
   }
-  __syncthreads();
-  if (wave < 4) {  // R q = H D q / sqrt(d)
-    const float v0 = s_q[wave][lane], v1 = s_q[wave][lane + 64];
+  auto load_tile = [&](int64_t b, uint4 (&wv)[P], uint32_t& nv) {
+    const int64_t n = std::min<int64_t>(b + lane, n1 - 1);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pg + p * N + n));
+      wv[p] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    nv = __builtin_nontemporal_load(&ng[n]);
+  };
+  int64_t base = n0 + int64_t(wave) * 64;
+  uint4 w[P];
+  uint32_t nrm = 0;
+  if (base < n1) load_tile(base, w, nrm);
+
+  // ---- S q partial sums over this wave's sixteen columns
+  {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int qh = qc * 4 + qq;
+      if (qh < Qg) {
+        const int64_t at = (g * Qg + qh) * 128 + 16 * seg;
+        float qv[16];
+        if constexpr (QBF16) {
+          const uint32_t* qp = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + at);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t pr = qp[m];
+            qv[2 * m] = __uint_as_float(pr << 16);
+            qv[2 * m + 1] = __uint_as_float(pr & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 16; ++m) qv[m] = static_cast<const float*>(q)[at + m];
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a = fmaf(srow[i].x, qv[4 * i], a);
+          a = fmaf(srow[i].y, qv[4 * i + 1], a);
+          a = fmaf(srow[i].z, qv[4 * i + 2], a);
+          a = fmaf(srow[i].w, qv[4 * i + 3], a);
+        }
+        acc[qq] = a;
+      }
+    }
+    sm.part[seg][jrow] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  }
+  // ---- R q = H D q / sqrt(d)
+  if (wave < 4) {
     const uint32_t f0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
     const uint32_t f1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
     const float a = f0 ? -v0 : v0, bq = f1 ? -v1 : v1;
@@ -511,86 +578,105 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
       y0 = up ? p0 - y0 : y0 + p0;
       y1 = up ? p1 - y1 : y1 + p1;
     }
-    y0 *= cst->inv_sqrt_d;
-    y1 *= cst->inv_sqrt_d;
-    s_x[0][lane][wave] = 2.0f * y0;
-    s_x[0][lane + 64][wave] = 2.0f * y1;
-    float sr = y0 + y1;
-#pragma unroll
-    for (int st = 1; st < 64; st <<= 1) sr += __shfl_xor(sr, st);
-    if (lane == 0) s_sum[0][wave] = sr;
+    float* xf = reinterpret_cast<float*>(&sm.x[0][0][0]);
+    xf[((lane & 7) * 16 + (lane >> 3)) * 4 + wave] = 2.0f * (y0 * cst->inv_sqrt_d);
+    xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = 2.0f * (y1 * cst->inv_sqrt_d);
   }
-  {  // S q: partial dots of row jrow over 16 columns for the 4 queries
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  if (tid < 128) {
+    f32x4 t = sm.part[0][tid];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * c8 + 4 * i;
+    for (int k = 1; k < 8; ++k) t += sm.part[k][tid];
+    sm.x[1][tid & 7][tid >> 3] = 2.0f * t;
+  }
+  __syncthreads();
+  // ---- tables: thread (pos, ty, hi) writes entries idx = 8 hi + j, j = 0..7
+  {
+    const int pos = tid & 15, ty = (tid >> 4) & 1, hi = tid >> 5;
+    f32x4 xv[8];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(&s_q[qq][c]);
-        acc[qq] = fmaf(srow[i].x, xv[0], fmaf(srow[i].y, xv[1], fmaf(srow[i].z, xv[2], fmaf(srow[i].w, xv[3], acc[qq]))));
+    for (int t = 0; t < 8; ++t) xv[t] = sm.x[ty][t][pos];
+    f32x4 bs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 3; t < 8; ++t) {
+      const float on = float((hi >> (t - 3)) & 1);
+      bs[0] = fmaf(on, xv[t][0], bs[0]);
+      bs[1] = fmaf(on, xv[t][1], bs[1]);
+      bs[2] = fmaf(on, xv[t][2], bs[2]);
+      bs[3] = fmaf(on, xv[t][3], bs[3]);
+    }
+    f32x4 e[8];
+    e[0] = bs;
+    e[1] = bs + xv[0];
+    e[2] = bs + xv[1];
+    e[3] = e[2] + xv[0];
+    e[4] = bs + xv[2];
+    e[5] = e[4] + xv[0];
+    e[6] = e[4] + xv[1];
+    e[7] = e[6] + xv[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm.tab[(ty * 256 + hi * 8 + j) * 16 + pos] = e[j];
+    if (wave == 15) {   // lanes 32..63 hold the full-byte sums (idx 255) of every position
+      f32x4 t = e[7];
+#pragma unroll
+      for (int st = 1; st < 16; st <<= 1) {
+        t[0] += __shfl_xor(t[0], st);
+        t[1] += __shfl_xor(t[1], st);
+        t[2] += __shfl_xor(t[2], st);
+        t[3] += __shfl_xor(t[3], st);
       }
-    }
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      acc[qq] += __shfl_xor(acc[qq], 1);
-      acc[qq] += __shfl_xor(acc[qq], 2);
-      acc[qq] += __shfl_xor(acc[qq], 4);
-    }
-    if (c8 == 0) s_x[1][jrow] = f32x4{2.0f * acc[0], 2.0f * acc[1], 2.0f * acc[2], 2.0f * acc[3]};
-    // sum over rows of S q: lanes with c8 == 0 hold the 8 rows of this wave
-    float sv[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      sv[qq] = c8 == 0 ? acc[qq] : 0.f;
-#pragma unroll
-      for (int st = 8; st < 64; st <<= 1) sv[qq] += __shfl_xor(sv[qq], st);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) s_red4[wave][qq] = sv[qq];
+      if (lane == 32) sm.sum[0] = t;
+      if (lane == 48) sm.sum[1] = t;
     }
   }
   __syncthreads();
-  if (tid < 4) {
-    float t = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < kScoreThreads / 64; ++wv) t += s_red4[wv][tid];
-    s_sum[1][tid] = t;
-  }
-  for (int i = tid; i < 2 * 16 * 2 * 16; i += kScoreThreads) {
-    const int nib = i & 15, hf = (i >> 4) & 1, pos = (i >> 5) & 15, tab = i >> 9;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (nib >> t & 1) acc += s_x[tab][8 * pos + 4 * hf + t];
-    s_nib[tab][pos][hf][nib] = acc;
-  }
-  __syncthreads();
-  for (int i = tid; i < 2 * 16 * 256; i += kScoreThreads) {
-    const int byte = i & 255, pos = (i >> 8) & 15, tab = i >> 12;
-    s_lut[tab][pos][byte] = s_nib[tab][pos][0][byte & 15] + s_nib[tab][pos][1][byte >> 4];
-  }
-  __syncthreads();
-  // per-query sums are the same for every lane: keep them in scalar registers
+
+  // per-query sums (sum R q, sum S q) are the same for every lane
+  // (the components are copied to scalars first: a bit cast of a vector
+  // element lvalue reads the vector's first component)
   float sr[4], ss[4];
+  {
+    const f32x4 s0 = sm.sum[0], s1 = sm.sum[1];
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    sr[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_sum[0][qq])));
-    ss[qq] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_sum[1][qq])));
+    for (int qq = 0; qq < 4; ++qq) {
+      const float a = s0[qq], b = s1[qq];
+      sr[qq] = 0.5f * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a)));
+      ss[qq] = 0.5f * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b)));
+    }
   }
   const float a0 = cst->alpha[0], a1 = cst->alpha[1], a2 = cst->alpha[2], a3 = cst->alpha[3];
   const float asum = cst->alpha_sum, qs = cst->qjl_scale;
 
-  // four table reads (one plane word) at a time keep the live registers low
-  // enough for four waves per SIMD; sixteen waves keep the LDS busy
-  auto add_plane = [&](const uint4 wv, int tab, float* acc) {
-    const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  // Per-lane address pieces.  Lookup (a, c) of a plane reads position
+  // (4 a + c) ^ r, which is byte c ^ (r & 3) of permuted word a; one byte
+  // permute assembles  ty * 64K + byte * 256 + slot * 16  from the word, a
+  // pair of slot bytes (plus a 0x01 byte for ty = 1) and a selector.
+  const uint32_t r = lane & 15, rb = r & 3;
+  uint32_t bp[4][2], sel[2][4];
 #pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 tv = s_lut[tab][wi * 4 + k][(ww[wi] >> (8 * k)) & 255u];
+    for (int h = 0; h < 2; ++h) {
+      bp[a][h] = (((4u * a + 2 * h) ^ r) << 4) | (((4u * a + 2 * h + 1) ^ r) << 12) | (1u << 16);
+      asm volatile("" : "+v"(bp[a][h]));
+    }
+#pragma unroll
+  for (int ty = 0; ty < 2; ++ty)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sel[ty][c] = uint32_t(c & 1) | ((4u + (c ^ rb)) << 8) | ((ty ? 2u : 12u) << 16) | (12u << 24);
+      asm volatile("" : "+v"(sel[ty][c]));
+    }
+  const bool s2 = lane & 8, s1 = lane & 4;
+  const char* tabp = reinterpret_cast<const char*>(sm.tab);
+
+  auto add_plane = [&](const uint32_t (&rw)[4], int ty, float* acc) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t ad = __builtin_amdgcn_perm(rw[a], bp[a][c >> 1], sel[ty][c]);
+        const f32x4 tv = *reinterpret_cast<const f32x4*>(tabp + ad);
         acc[0] += tv[0]; acc[1] += tv[1]; acc[2] += tv[2]; acc[3] += tv[3];
       }
       // an empty fence (no instruction) that takes the accumulators: this
@@ -599,49 +685,48 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     }
   };
 
-  for (; n < n1; n += kScoreThreads) {
-    uint4 w[P];
+  for (; base < n1; base += kScoreThreads) {
+    uint4 wn[P];
+    uint32_t nn = 0;
+    if (base + kScoreThreads < n1) load_tile(base + kScoreThreads, wn, nn);
+    uint32_t rw[NW][4];
 #pragma unroll
-    for (int p = 0; p < P; ++p) w[p] = pg[p * N + n];
-    const uint32_t nrm = ng[n];
-    float acc[4][4];   // [term][query]: code planes 0..B-1, sign plane in [3]
+    for (int p = 0; p < P; ++p) permute_words(w[p], s2, s1, rw[p]);
+    if constexpr (B == 3) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < 4; ++i) rw[P][i] = rw[0][i] ^ rw[1][i] ^ rw[2][i];
+    }
+    float acc[NW][4];
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) acc[t][qq] = 0.f;
-    float mse[4];
-    if constexpr (B == 1) {
-      add_plane(w[0], 0, acc[0]);
-      add_plane(w[1], 1, acc[3]);
+    // code planes (and parity) against R q, the sign plane (index B) against S q
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) mse[qq] = a0 * acc[0][qq] - asum * sr[qq];
-    } else if constexpr (B == 2) {
-      add_plane(w[0], 0, acc[0]);
-      add_plane(w[1], 0, acc[1]);
-      add_plane(w[2], 1, acc[3]);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        mse[qq] = fmaf(a0, acc[0][qq], a1 * acc[1][qq]) - asum * sr[qq];
-    } else {
-      // three code planes and their parity plane (the s0*s1*s2 Walsh term)
-      add_plane(w[0], 0, acc[0]);
-      add_plane(w[1], 0, acc[1]);
-      add_plane(w[2], 0, acc[2]);
-      float accx[4] = {0.f, 0.f, 0.f, 0.f};
-      add_plane(make_uint4(w[0].x ^ w[1].x ^ w[2].x, w[0].y ^ w[1].y ^ w[2].y,
-                           w[0].z ^ w[1].z ^ w[2].z, w[0].w ^ w[1].w ^ w[2].w), 0, accx);
-      add_plane(w[3], 1, acc[3]);
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        mse[qq] = fmaf(a0, acc[0][qq], fmaf(a1, acc[1][qq], fmaf(a2, acc[2][qq], a3 * accx[qq]))) -
-                  asum * sr[qq];
-    }
+    for (int t = 0; t < B; ++t) add_plane(rw[t], 0, acc[t]);
+    if constexpr (B == 3) add_plane(rw[P], 0, acc[P]);
+    add_plane(rw[B], 1, acc[B]);
+
     const float nu = h2f_bits(nrm & 0xffffu), rs = h2f_bits(nrm >> 16) * qs;
+    const int64_t n = base + lane;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
+      float mse;
+      if constexpr (B == 1) {
+        mse = a0 * acc[0][qq] - asum * sr[qq];
+      } else if constexpr (B == 2) {
+        mse = fmaf(a0, acc[0][qq], a1 * acc[1][qq]) - asum * sr[qq];
+      } else {
+        mse = fmaf(a0, acc[0][qq], fmaf(a1, acc[1][qq], fmaf(a2, acc[2][qq], a3 * acc[P][qq]))) -
+              asum * sr[qq];
+      }
       const int qh = qc * 4 + qq;
-      if (qh < Qg) logits[(g * Qg + qh) * N + n] = fmaf(nu, mse[qq], rs * (ss[qq] - acc[3][qq]));
+      if (n < n1 && qh < Qg)   // streamed output: no reuse, written past the caches
+        __builtin_nontemporal_store(fmaf(nu, mse, rs * (ss[qq] - acc[B][qq])), &logits[(g * Qg + qh) * N + n]);
     }
+#pragma unroll
+    for (int p = 0; p < P; ++p) w[p] = wn[p];
+    nrm = nn;
   }
 }
 
