@@ -134,7 +134,8 @@ size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
  * keys of its range.  All buffers are caller-owned device memory; ws must hold
  * tq_score_workspace_bytes(cb, G, Qg) bytes (may be NULL when that is 0).
  * G*N*Qg == 0 is a no-op.
- * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256), TQ_ERR_HIP.
+ * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256 or G > 2^31 - 1),
+ * TQ_ERR_HIP.
  */
 int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
                     int32_t Qg, const void* packed, int64_t N, float* logits, void* ws,

@@ -223,12 +223,12 @@ int build_tables(tq::Codebook& cb) {
 void release_device(tq::Codebook& cb) {
   if (cb.d_consts) (void)hipFree(cb.d_consts);
   if (cb.d_frag) (void)hipFree(cb.d_frag);
-  if (cb.d_S) (void)hipFree(cb.d_S);
+  if (cb.d_St) (void)hipFree(cb.d_St);
   if (cb.d_dpair) (void)hipFree(cb.d_dpair);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
   cb.d_consts = nullptr;
   cb.d_frag = nullptr;
-  cb.d_S = nullptr;
+  cb.d_St = nullptr;
   cb.d_dpair = nullptr;
   cb.d_flip_f32 = nullptr;
 }
@@ -244,7 +244,12 @@ int upload_device(tq::Codebook& cb) {
   hipError_t e = hipGetDevice(&cb.device);
   if (e != hipSuccess) return hip_fail(e);
   e = upload(&cb.d_consts, &cb.consts, sizeof(tq::DevConsts));
-  if (e == hipSuccess) e = upload(&cb.d_S, cb.S.data(), cb.S.size() * sizeof(float));
+  if (e == hipSuccess) {   // the scorer reads S column by column: store its transpose
+    std::vector<float> st(cb.S.size());
+    for (int j = 0; j < cb.m; ++j)
+      for (int c = 0; c < cb.d; ++c) st[size_t(c) * cb.m + j] = cb.S[size_t(j) * cb.d + c];
+    e = upload(&cb.d_St, st.data(), st.size() * sizeof(float));
+  }
   if (e == hipSuccess && cb.d == 128) {
     std::vector<uint16_t> frag;
     build_fragments_128(cb.S_rot, frag);
@@ -383,7 +388,7 @@ int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64
                     void* stream) {
   if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16))
     return TQ_ERR_ARG;
-  if (Qg > 256) return TQ_ERR_UNSUPPORTED;
+  if (Qg > 256 || G > INT32_MAX) return TQ_ERR_UNSUPPORTED;   // one grid row per group
   if (G == 0 || N == 0 || Qg == 0) return TQ_OK;
   if (!q || !packed || !logits || !aligned16(q) || !aligned16(packed) || !aligned16(logits))
     return TQ_ERR_ARG;

@@ -38,7 +38,7 @@ struct Codebook {
   // device copies
   DevConsts* d_consts = nullptr;
   uint4* d_frag = nullptr;       // S R^T as float16 hi/lo, matrix-core A-operand order
-  float* d_S = nullptr;          // S, float32 [m][d]
+  float* d_St = nullptr;         // S transposed, float32 [d][m]
   uint32_t* d_dpair = nullptr;      // [2 halves][+/-][32] bf16 pairs (d_a, +-d_b) (d = 128)
   uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
 };

@@ -437,10 +437,10 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
 }
 
 // ============================================================== score, d = 128
-// One workgroup (1024 threads, 16 waves) per (group g, chunk of 4 query heads,
-// key range).  Set-up:
+// Grid (g, chunk of 4 query heads, key range); 1024 threads, 16 waves.
+// Set-up:
 //  - R q by a butterfly (waves 0-3, one query each; lane L holds coordinates
-//    L and L + 64);
+//    L and L + 64), exchanges through DPP, swizzles and half-wave swaps;
 //  - S q: wave w multiplies rows 64 (w & 1) + L of S by columns
 //    16 (w >> 1) .. 16 (w >> 1) + 15 of the four queries, which are the same
 //    for the whole wave and sit in scalar registers; eight partial sums per row;
@@ -453,8 +453,10 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
 // LDS serves together then hit sixteen different bank groups whatever the
 // key bytes are, and the random gathers run at the conflict-free rate.
 // Each lane scores one key per step: (B + 1) planes (B = 3: plus the parity
-// plane) x 16 table reads with 4 adds each; the next step's records are
-// loaded before the current ones are scored.
+// plane) x 16 table reads with 4 adds each.  Every wave keeps D key tiles in
+// flight in registers; the first D are requested before the set-up, so the
+// key stream starts at once.  All loads are unconditional (clamped to the
+// range) so that each wait covers exactly the data it needs.
 
 constexpr int kScoreThreads = 1024;
 
@@ -475,48 +477,69 @@ __device__ __forceinline__ void permute_words(const uint4 w, bool s2, bool s1, u
   o[3] = s1 ? t2 : t3;
 }
 
+// value of lane L ^ S
+template <int S>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (S == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+  if constexpr (S == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+  if constexpr (S == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x101F));
+  if constexpr (S == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));
+  if constexpr (S == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+}
+
+// one butterfly stage of stride S: (a, b) -> (a + b, a - b) over lanes L, L ^ S
+template <int S>
+__device__ __forceinline__ float butterfly_lane(float y, bool up) {
+  const float p = lane_xor<S>(y);
+  return up ? p - y : y + p;
+}
+
+__device__ __forceinline__ float butterfly_lane32(float y, bool up) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  const float r0 = __uint_as_float(r[0]), r1 = __uint_as_float(r[1]);
+  return up ? r0 - r1 : r0 + r1;   // lanes < 32: (own, partner); lanes >= 32: (partner, own)
+}
+
 template <int B, bool QBF16>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
-    int64_t G, int64_t N, int Qg, int nqc, int splits, float* __restrict__ logits,
-    const DevConsts* __restrict__ cst, const float* __restrict__ S) {
+    int64_t N, int Qg, int64_t chunk, float* __restrict__ logits, const DevConsts* __restrict__ cst,
+    const float* __restrict__ St) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
+  constexpr int D = B == 3 ? 2 : 3;        // key tiles in flight per wave
+  constexpr int64_t kStride = kScoreThreads;   // keys between a wave's consecutive tiles
   __shared__ ScoreLds sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int64_t blk = blockIdx.x;
-  const int split = int(blk % splits);
-  blk /= splits;
-  const int qc = int(blk % nqc);
-  const int64_t g = blk / nqc;
-  const int64_t chunk = ((N + splits - 1) / splits + 63) / 64 * 64;
-  const int64_t n0 = int64_t(split) * chunk;
-  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
+  const int64_t g = blockIdx.x;
+  const int qc = blockIdx.y;
+  const int64_t n0 = int64_t(blockIdx.z) * chunk;
+  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);   // n0 < n1: the host sizes the grid so
   const uint4* pg = planes + g * P * N;
   const uint32_t* ng = norms + g * N;
 
-  // ---- loads: S rows, this wave's query (waves 0-3), then the first key tile
+  // ---- loads: S columns, the R q input, the first D key tiles
   const int seg = wave >> 1;
   const int jrow = 64 * (wave & 1) + lane;
-  float4 srow[4];
-  {
-    const float4* row = reinterpret_cast<const float4*>(S + int64_t(jrow) * 128 + 16 * seg);
+  float sv[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) srow[i] = row[i];
-  }
-  float v0 = 0.f, v1 = 0.f;
-  if (wave < 4 && qc * 4 + wave < Qg) {
-    const int64_t at = (g * Qg + qc * 4 + wave) * 128 + lane;
+  for (int m = 0; m < 16; ++m) sv[m] = St[(16 * seg + m) * 128 + jrow];
+  uint32_t u0, u1;   // raw bits of the R q input (converted after the pin below)
+  {
+    const int qr = std::min(qc * 4 + (wave & 3), Qg - 1);
+    const int64_t at = (g * Qg + qr) * 128 + lane;
     if constexpr (QBF16) {
-      v0 = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at]) << 16);
-      v1 = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[at + 64]) << 16);
+      u0 = static_cast<const uint16_t*>(q)[at];
+      u1 = static_cast<const uint16_t*>(q)[at + 64];
     } else {
-      v0 = static_cast<const float*>(q)[at];
-      v1 = static_cast<const float*>(q)[at + 64];
+      u0 = static_cast<const uint32_t*>(q)[at];
+      u1 = static_cast<const uint32_t*>(q)[at + 64];
     }
   }
+  uint32_t dn0 = cst->dneg[lane >> 5], dn1 = cst->dneg[2 + (lane >> 5)];
   auto load_tile = [&](int64_t b, uint4 (&wv)[P], uint32_t& nv) {
     const int64_t n = std::min<int64_t>(b + lane, n1 - 1);
 #pragma unroll
@@ -526,58 +549,56 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     }
     nv = __builtin_nontemporal_load(&ng[n]);
   };
-  int64_t base = n0 + int64_t(wave) * 64;
-  uint4 w[P];
-  uint32_t nrm = 0;
-  if (base < n1) load_tile(base, w, nrm);
+  const int64_t first = n0 + int64_t(wave) * 64;
+  uint4 w[D][P];
+  uint32_t nr[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) load_tile(first + k * kStride, w[k], nr[k]);
+  // (an empty use outside the branch below keeps these loads ahead of the key
+  // tiles: issued later, waiting for them would also wait for the tiles)
+  asm volatile("" : "+v"(u0), "+v"(u1), "+v"(dn0), "+v"(dn1));
+  const float v0 = __uint_as_float(QBF16 ? u0 << 16 : u0), v1 = __uint_as_float(QBF16 ? u1 << 16 : u1);
 
   // ---- S q partial sums over this wave's sixteen columns
   {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int qh = qc * 4 + qq;
-      if (qh < Qg) {
-        const int64_t at = (g * Qg + qh) * 128 + 16 * seg;
-        float qv[16];
-        if constexpr (QBF16) {
-          const uint32_t* qp = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + at);
+      const int64_t at = (g * Qg + std::min(qh, Qg - 1)) * 128 + 16 * seg;
+      float qv[16];
+      if constexpr (QBF16) {
+        const uint32_t* qp = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + at);
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t pr = qp[m];
-            qv[2 * m] = __uint_as_float(pr << 16);
-            qv[2 * m + 1] = __uint_as_float(pr & 0xffff0000u);
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < 16; ++m) qv[m] = static_cast<const float*>(q)[at + m];
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t pr = qp[m];
+          qv[2 * m] = __uint_as_float(pr << 16);
+          qv[2 * m + 1] = __uint_as_float(pr & 0xffff0000u);
         }
-        float a = 0.f;
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a = fmaf(srow[i].x, qv[4 * i], a);
-          a = fmaf(srow[i].y, qv[4 * i + 1], a);
-          a = fmaf(srow[i].z, qv[4 * i + 2], a);
-          a = fmaf(srow[i].w, qv[4 * i + 3], a);
-        }
-        acc[qq] = a;
+        for (int m = 0; m < 16; ++m) qv[m] = static_cast<const float*>(q)[at + m];
       }
+      float a = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) a = fmaf(sv[m], qv[m], a);
+      acc[qq] = qh < Qg ? a : 0.f;
     }
     sm.part[seg][jrow] = f32x4{acc[0], acc[1], acc[2], acc[3]};
   }
   // ---- R q = H D q / sqrt(d)
   if (wave < 4) {
-    const uint32_t f0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
-    const uint32_t f1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
-    const float a = f0 ? -v0 : v0, bq = f1 ? -v1 : v1;
+    const bool live = qc * 4 + wave < Qg;
+    const uint32_t f0 = (dn0 >> (lane & 31)) & 1u;
+    const uint32_t f1 = (dn1 >> (lane & 31)) & 1u;
+    const float a = live ? (f0 ? -v0 : v0) : 0.f, bq = live ? (f1 ? -v1 : v1) : 0.f;
     float y0 = a + bq, y1 = a - bq;
-#pragma unroll
-    for (int st = 1; st < 64; st <<= 1) {
-      const float p0 = __shfl_xor(y0, st), p1 = __shfl_xor(y1, st);
-      const bool up = lane & st;
-      y0 = up ? p0 - y0 : y0 + p0;
-      y1 = up ? p1 - y1 : y1 + p1;
-    }
+    y0 = butterfly_lane<1>(y0, lane & 1);   y1 = butterfly_lane<1>(y1, lane & 1);
+    y0 = butterfly_lane<2>(y0, lane & 2);   y1 = butterfly_lane<2>(y1, lane & 2);
+    y0 = butterfly_lane<4>(y0, lane & 4);   y1 = butterfly_lane<4>(y1, lane & 4);
+    y0 = butterfly_lane<8>(y0, lane & 8);   y1 = butterfly_lane<8>(y1, lane & 8);
+    y0 = butterfly_lane<16>(y0, lane & 16); y1 = butterfly_lane<16>(y1, lane & 16);
+    y0 = butterfly_lane32(y0, lane & 32);   y1 = butterfly_lane32(y1, lane & 32);
     float* xf = reinterpret_cast<float*>(&sm.x[0][0][0]);
     xf[((lane & 7) * 16 + (lane >> 3)) * 4 + wave] = 2.0f * (y0 * cst->inv_sqrt_d);
     xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = 2.0f * (y1 * cst->inv_sqrt_d);
@@ -619,11 +640,11 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     if (wave == 15) {   // lanes 32..63 hold the full-byte sums (idx 255) of every position
       f32x4 t = e[7];
 #pragma unroll
-      for (int st = 1; st < 16; st <<= 1) {
-        t[0] += __shfl_xor(t[0], st);
-        t[1] += __shfl_xor(t[1], st);
-        t[2] += __shfl_xor(t[2], st);
-        t[3] += __shfl_xor(t[3], st);
+      for (int c = 0; c < 4; ++c) {
+        t[c] += lane_xor<1>(t[c]);
+        t[c] += lane_xor<2>(t[c]);
+        t[c] += lane_xor<4>(t[c]);
+        t[c] += lane_xor<8>(t[c]);
       }
       if (lane == 32) sm.sum[0] = t;
       if (lane == 48) sm.sum[1] = t;
@@ -685,13 +706,10 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     }
   };
 
-  for (; base < n1; base += kScoreThreads) {
-    uint4 wn[P];
-    uint32_t nn = 0;
-    if (base + kScoreThreads < n1) load_tile(base + kScoreThreads, wn, nn);
+  auto score_tile = [&](const uint4 (&wt)[P], uint32_t nrm, int64_t b) {
     uint32_t rw[NW][4];
 #pragma unroll
-    for (int p = 0; p < P; ++p) permute_words(w[p], s2, s1, rw[p]);
+    for (int p = 0; p < P; ++p) permute_words(wt[p], s2, s1, rw[p]);
     if constexpr (B == 3) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) rw[P][i] = rw[0][i] ^ rw[1][i] ^ rw[2][i];
@@ -708,7 +726,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     add_plane(rw[B], 1, acc[B]);
 
     const float nu = h2f_bits(nrm & 0xffffu), rs = h2f_bits(nrm >> 16) * qs;
-    const int64_t n = base + lane;
+    const int64_t n = b + lane;
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       float mse;
@@ -722,12 +740,23 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
       }
       const int qh = qc * 4 + qq;
       if (n < n1 && qh < Qg)   // streamed output: no reuse, written past the caches
-        __builtin_nontemporal_store(fmaf(nu, mse, rs * (ss[qq] - acc[B][qq])), &logits[(g * Qg + qh) * N + n]);
+        __builtin_nontemporal_store(fmaf(nu, mse, rs * (ss[qq] - acc[B][qq])),
+                                    &logits[(g * Qg + qh) * N + n]);
     }
+  };
+
+  // tiles t = 0, 1, ... of this wave start at first + t * kStride; tile t
+  // sits in slot t % D and its slot is refilled with tile t + D right after
+  const int64_t ntiles = first < n1 ? (n1 - first + kStride - 1) / kStride : 0;
+  for (int64_t t0 = 0; t0 < ntiles; t0 += D) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) w[p] = wn[p];
-    nrm = nn;
+    for (int k = 0; k < D; ++k) {
+      if (t0 + k < ntiles) score_tile(w[k], nr[k], first + (t0 + k) * kStride);
+      load_tile(first + (t0 + k + D) * kStride, w[k], nr[k]);
+    }
   }
+  // the refills past the range are never used: let them land before the wave ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ============================================================== decode, d = 128
@@ -881,19 +910,23 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
 hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                         const void* packed, int64_t N, float* logits, void* ws, hipStream_t s) {
   (void)ws;
+  // enough workgroups for every CU: split each (group, query chunk) unit's
+  // keys into ranges of at least 512 keys, a multiple of 64 each
   const int nqc = (Qg + 3) / 4;
   const int64_t units = G * nqc;
   const int64_t cus = num_cus();
-  int splits = int(std::max<int64_t>(1, (cus + units - 1) / units));
-  splits = int(std::min<int64_t>(splits, std::max<int64_t>(1, (N + 511) / 512)));
-  const int64_t grid = units * splits;
+  int64_t want = std::max<int64_t>(1, (cus + units - 1) / units);
+  want = std::min<int64_t>(want, std::max<int64_t>(1, (N + 511) / 512));
+  const int64_t chunk = ((N + want - 1) / want + 63) / 64 * 64;
+  const int64_t splits = (N + chunk - 1) / chunk;
+  const dim3 grid{unsigned(G), unsigned(nqc), unsigned(splits)};
   const uint4* planes = static_cast<const uint4*>(packed);
   const uint32_t* norms =
       static_cast<const uint32_t*>(packed) + G * N * int64_t(cb.bits) * (cb.d / 32);
   const bool bf = qdtype == 1;
-#define TQ_SC(BB, QB)                                                                           \
-  hipLaunchKernelGGL((score128_kernel<BB, QB>), dim3(grid), dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, G, N, Qg, nqc, splits, logits, cb.d_consts, cb.d_S)
+#define TQ_SC(BB, QB)                                                                   \
+  hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
+                     norms, N, Qg, chunk, logits, cb.d_consts, cb.d_St)
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
