@@ -214,6 +214,15 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
       }
       split_f16_pair(ep[0], ep[1], bh[pr], bl[pr]);
     }
+    // an empty use of the code words (no instruction): their bits are
+    // accumulated chunk by chunk instead of being recombined after all the
+    // products, which would keep every comparison result live meanwhile
+    if constexpr (K > 2) {
+      asm volatile("" : "+v"(wu[0]), "+v"(wu[1]), "+v"(wd[0][0]), "+v"(wd[0][1]), "+v"(wd[1][0]),
+                   "+v"(wd[1][1]), "+v"(wd[2][0]), "+v"(wd[2][1]));
+    } else {
+      asm volatile("" : "+v"(wu[0]), "+v"(wu[1]), "+v"(wd[0][0]), "+v"(wd[0][1]));
+    }
     const half8 bhi = __builtin_bit_cast(half8, u32x4{bh[0], bh[1], bh[2], bh[3]});
     const half8 blo = __builtin_bit_cast(half8, u32x4{bl[0], bl[1], bl[2], bl[3]});
     // per-chunk opaque offset (no instruction): keeps this chunk's 8 fragment
@@ -222,8 +231,12 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
     asm volatile("" : "+v"(ko));
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      const half8 ahi = fh[ko + jb * 64];
-      const half8 alo = fo[ko + jb * 64];
+      // B = 3 keeps more code words live: read each row block's fragments
+      // next to its own products so that only two are held at a time
+      int kj = ko + jb * 64;
+      if constexpr (B == 3) asm volatile("" : "+v"(kj));
+      const half8 ahi = fh[kj];
+      const half8 alo = fo[kj];
       acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhi, acc[jb], 0, 0, 0);
       acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blo, acc[jb], 0, 0, 0);
       acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhi, acc[jb], 0, 0, 0);
