@@ -175,9 +175,11 @@ def main():
     enc_gbps = enc_alg / enc_avg_s / 1e9
     sc_gbps = sc_alg / sc_avg_s / 1e9
     dominant = "encode" if enc_avg_s >= sc_avg_s else "score"
-    traffic = read_traffic(f"encode128_b{bits}_traffic.txt" if dominant == "encode"
-                           else f"score128_b{bits}_traffic.txt")
-    roof = {"bound": "hbm", "kernel": "encode128_kernel" if dominant == "encode" else "score (prep + score128_kernel)",
+    traffic = read_traffic(f"encode128_{wl.key_dtype}_b{bits}_workload{args.config}.txt" if dominant == "encode"
+                           else f"score128_b{bits}_workload{args.config}.txt")
+    enc_kernel = f"encode128_{wl.key_dtype}_kernel<{bits - 1}>"
+    sc_kernel = f"score128_kernel<{bits - 1}, {'true' if wl.key_dtype == 'bf16' else 'false'}>"
+    roof = {"bound": "hbm", "kernel": enc_kernel if dominant == "encode" else sc_kernel,
             "achieved": round(enc_gbps if dominant == "encode" else sc_gbps, 1),
             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round((enc_gbps if dominant == "encode" else sc_gbps) / PEAK_HBM_GBPS, 4),
