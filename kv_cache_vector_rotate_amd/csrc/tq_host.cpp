@@ -165,6 +165,28 @@ void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>
       }
 }
 
+// d = 1024: fragment (rb, ks, hl, lane L) holds row 32 rb + L % 32 of S R^T
+// at coordinates 16 ks + 8 (L / 32) + t, t = 0..7 (matrix-core A order for
+// 32x32x16), hl = 0 the float16 value, hl = 1 the float16 remainder.
+void build_fragments_wide(const std::vector<double>& S_rot, int d, std::vector<uint16_t>& frag) {
+  const int nrb = d / 32, nks = d / 16;
+  frag.assign(size_t(nrb) * nks * 2 * 64 * 8, 0);
+  for (int rb = 0; rb < nrb; ++rb)
+    for (int ks = 0; ks < nks; ++ks)
+      for (int L = 0; L < 64; ++L) {
+        const int j = 32 * rb + (L & 31);
+        for (int t = 0; t < 8; ++t) {
+          const int k = 16 * ks + 8 * (L >> 5) + t;
+          const double v = S_rot[size_t(j) * d + k];
+          const _Float16 hi = static_cast<_Float16>(v);
+          const _Float16 lo = static_cast<_Float16>(v - static_cast<double>(hi));
+          const size_t base = ((size_t(rb) * nks + ks) * 2) * 64 * 8;
+          std::memcpy(&frag[base + size_t(L) * 8 + t], &hi, 2);
+          std::memcpy(&frag[base + 64 * 8 + size_t(L) * 8 + t], &lo, 2);
+        }
+      }
+}
+
 void fill_consts(tq::Codebook& cb) {
   tq::DevConsts& k = cb.consts;
   std::memset(&k, 0, sizeof(k));
@@ -226,6 +248,8 @@ void release_device(tq::Codebook& cb) {
   if (cb.d_St) (void)hipFree(cb.d_St);
   if (cb.d_dpair) (void)hipFree(cb.d_dpair);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
+  if (cb.d_fragW) (void)hipFree(cb.d_fragW);
+  cb.d_fragW = nullptr;
   cb.d_consts = nullptr;
   cb.d_frag = nullptr;
   cb.d_St = nullptr;
@@ -243,7 +267,15 @@ hipError_t upload(T** dst, const void* src, size_t bytes) {
 int upload_device(tq::Codebook& cb) {
   hipError_t e = hipGetDevice(&cb.device);
   if (e != hipSuccess) return hip_fail(e);
+  if (hipDeviceGetAttribute(&cb.num_cus, hipDeviceAttributeMultiprocessorCount, cb.device) != hipSuccess ||
+      cb.num_cus <= 0)
+    cb.num_cus = 256;
   e = upload(&cb.d_consts, &cb.consts, sizeof(tq::DevConsts));
+  if (e == hipSuccess && cb.d == 1024) {
+    std::vector<uint16_t> frag;
+    build_fragments_wide(cb.S_rot, cb.d, frag);
+    e = upload(&cb.d_fragW, frag.data(), frag.size() * sizeof(uint16_t));
+  }
   if (e == hipSuccess) {   // the scorer reads S column by column: store its transpose
     std::vector<float> st(cb.S.size());
     for (int j = 0; j < cb.m; ++j)

@@ -41,6 +41,8 @@ struct Codebook {
   float* d_St = nullptr;         // S transposed, float32 [d][m]
   uint32_t* d_dpair = nullptr;      // [2 halves][+/-][32] bf16 pairs (d_a, +-d_b) (d = 128)
   uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
+  uint4* d_fragW = nullptr;         // S R^T hi/lo for d = 1024: [row block 32][k-step 64][hi/lo][lane 64]
+  int num_cus = 0;                  // compute units of the device
 };
 
 // Launchers (tq_kernels.hip).  Return hipSuccess or the launch error.
@@ -53,6 +55,9 @@ hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int6
 hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg, int64_t N, int d,
                              float* logits, hipStream_t s);
 size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg);
+// d = 1024 (tq_wide.hip)
+hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
+                              void* packed, hipStream_t s);
 bool encode_supported(const Codebook& cb);
 bool score_supported(const Codebook& cb);
 

@@ -874,7 +874,7 @@ __global__ __launch_bounds__(256) void dense128_kernel(const uint16_t* __restric
 
 }  // namespace
 
-bool encode_supported(const Codebook& cb) { return cb.d == 128; }
+bool encode_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
 bool score_supported(const Codebook& cb) { return cb.d == 128; }
 
 // The scorer prepares its queries inside each workgroup and needs no workspace.
@@ -887,6 +887,7 @@ size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg) {
 
 hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                          void* packed, hipStream_t s) {
+  if (cb.d == 1024) return launch_encode_wide(cb, keys, dtype, G, N, packed, s);
   const int64_t ntiles = G * ((N + 31) / 32);
   uint32_t* planes = static_cast<uint32_t*>(packed);
   uint32_t* norms = planes + G * N * int64_t(cb.bits) * (cb.d / 32);

@@ -1,0 +1,394 @@
+// TurboQuant key path for d = m = 1024 (the vector-search shape) on gfx950.
+//
+// Encode runs as two kernels over a chunk of keys:
+//   rotate1024_kernel  one key per wave: y = H D k / (nu sqrt(d)) (1024-point
+//                      butterfly: four stages inside the lane, six across
+//                      lanes), Lloyd-Max codes -> code planes, nu and rho, and
+//                      the scaled residual 2^12 (y - c[code]) to a workspace;
+//   qjl1024_kernel     the QJL projection p = (S R^T) r_rot for 64 keys per
+//                      workgroup on the matrix cores (three-term fp16 split,
+//                      fp32 accumulation), then sign words [p < 0].
+// [ICLR 2026 paper digest, "Step 1: PolarQuant" (R = H_d D / sqrt(d)) and the
+//  implementation pseudocode (zero vectors, sign convention); Qiita
+//  explainer, "Stage 2: QJL" (sign sketch of the residual).]
+
+#include "tq_internal.h"
+
+#include <algorithm>
+#include <cstdint>
+
+namespace tq {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 1024;
+
+__device__ __forceinline__ uint32_t push_sign(uint32_t acc, float v) {
+  return __builtin_amdgcn_alignbit(acc, __float_as_uint(v), 31);   // (acc << 1) | signbit(v)
+}
+
+__device__ __forceinline__ uint16_t f2h_bits(float v) {
+  const _Float16 h = static_cast<_Float16>(v);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// value of lane L ^ S (S < 32)
+template <int S>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int x = __float_as_int(v);
+  if constexpr (S == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+  if constexpr (S == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+  if constexpr (S == 4) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x101F));
+  if constexpr (S == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));
+  if constexpr (S == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(x, 0x401F));
+}
+
+__device__ __forceinline__ uint32_t lane_xor1_u(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// butterfly stage across lanes L, L ^ S on every register: (a, b) -> (a + b, a - b)
+template <int S>
+__device__ __forceinline__ void stage_lanes(float (&x)[16], int lane) {
+  const float sg = (lane & S) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) x[t] = fmaf(sg, x[t], lane_xor<S>(x[t]));
+}
+
+__device__ __forceinline__ void stage_lanes32(float (&x)[16], int lane) {
+  const bool up = lane & 32;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[t]), __float_as_uint(x[t]), false, false);
+    const float r0 = __uint_as_float(r[0]), r1 = __uint_as_float(r[1]);
+    x[t] = up ? r0 - r1 : r0 + r1;   // lanes < 32: (own, partner); lanes >= 32: (partner, own)
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += lane_xor<1>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<16>(v);
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------- rotate
+// Lane L holds coordinates 16 L + t, t = 0..15: strides 1..8 inside the lane,
+// 16..512 across lanes.  Each lane fills 16 bits of a plane word (word L / 2,
+// bits 16 (L & 1) + t); even lanes then hold whole words after one DPP swap.
+// The residual is written as 2^12 (y - c[code]) (unit-vector units), zero for
+// zero keys, in natural coordinate order: ws[key][1024] float32.
+template <int B, bool BF16>
+__global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict__ keys, int64_t k0,
+                                                         int64_t nk, int64_t N,
+                                                         uint32_t* __restrict__ planes,
+                                                         uint32_t* __restrict__ norms,
+                                                         float* __restrict__ ws,
+                                                         const DevConsts* __restrict__ cst) {
+  constexpr int K = 1 << (B - 1);   // levels on the positive half
+  constexpr int P = B + 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t wstride = int64_t(gridDim.x) * 4;
+  float tpos[K > 1 ? K - 1 : 1], cpos[K];
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) tpos[k] = cst->tpos[k];
+#pragma unroll
+  for (int k = 0; k < K; ++k) cpos[k] = cst->cpos_s[k];
+  const float sqrt_d = cst->sqrt_d;
+  const uint32_t dn = (cst->dneg[lane >> 1] >> (16 * (lane & 1))) & 0xffffu;
+
+  for (int64_t w = wave0; w < nk; w += wstride) {
+    const int64_t kk = k0 + w;   // key index over [G][N]
+    float x[16];
+    if constexpr (BF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + kk * kD + 16 * lane);
+      const uint4 a = src[0], b = src[1];
+      const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[2 * i] = __uint_as_float(u[i] << 16);
+        x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + kk * kD + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = src[i];
+        x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+      }
+    }
+    float nu2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) nu2 = fmaf(x[t], x[t], nu2);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = __uint_as_float(__float_as_uint(x[t]) ^ (((dn >> t) & 1u) << 31));
+    // first stage adds +0: sign-flipped zeros would otherwise leave -0, and an
+    // exact zero must count as non-negative
+#pragma unroll
+    for (int t = 0; t < 16; t += 2) {
+      const float a = x[t], b = x[t + 1];
+      x[t] = (a + b) + 0.0f;
+      x[t + 1] = (a - b) + 0.0f;
+    }
+#pragma unroll
+    for (int st = 2; st < 16; st <<= 1)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (t & st) continue;
+        const float a = x[t], b = x[t + st];
+        x[t] = a + b;
+        x[t + st] = a - b;
+      }
+    stage_lanes<1>(x, lane);
+    stage_lanes<2>(x, lane);
+    stage_lanes<4>(x, lane);
+    stage_lanes<8>(x, lane);
+    stage_lanes<16>(x, lane);
+    stage_lanes32(x, lane);
+
+    nu2 = wave_sum(nu2);
+    const float nu = sqrtf(nu2);
+    const bool zero = !(nu >= 1e-10f);
+    const float nsd = nu * sqrt_d;                          // u = y nu sqrt(d)
+    const float gsc = zero ? 0.f : kResidualScale / nsd;    // u -> 2^12 y
+    float tu[K > 1 ? K - 1 : 1];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) tu[k] = tpos[k] * nsd;
+
+    uint32_t wu = 0u, wd[K > 1 ? K - 1 : 1];
+#pragma unroll
+    for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k] = 0u;
+    float rho2 = 0.f;
+    float ep[16];
+#pragma unroll
+    for (int t = 15; t >= 0; --t) {   // pushed last = bit 0: bit t holds coordinate 16 L + t
+      const float u = x[t], a = fabsf(u);
+      wu = push_sign(wu, u);
+      float mag = cpos[0];
+#pragma unroll
+      for (int k = 0; k < K - 1; ++k) {
+        const float dk = a - tu[k];
+        wd[k] = push_sign(wd[k], dk);
+        mag = (dk >= 0.f) ? cpos[k + 1] : mag;
+      }
+      const float e = fmaf(u, gsc, -copysignf(mag, u));     // 2^12 (y - c[code])
+      ep[t] = zero ? 0.f : e;
+      rho2 = fmaf(ep[t], ep[t], rho2);
+    }
+    rho2 = wave_sum(rho2);
+    const float rho = zero ? 0.f : sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+
+    // the low halves (even lanes) take the odd lane's 16 bits as their high half
+    const uint32_t fu = (wu & 0xffffu) | (lane_xor1_u(wu) << 16);
+    uint32_t fd[K > 1 ? K - 1 : 1];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) fd[k] = (wd[k] & 0xffffu) | (lane_xor1_u(wd[k]) << 16);
+    uint32_t pw[P - 1];
+    if constexpr (B == 1) {
+      pw[0] = ~fu;
+    } else if constexpr (B == 2) {
+      pw[1] = ~fu;
+      pw[0] = ~(fu ^ fd[0]);
+    } else {
+      pw[2] = ~fu;
+      pw[1] = ~(fu ^ fd[1]);
+      pw[0] = ~(fu ^ fd[0] ^ fd[1] ^ fd[2]);
+    }
+    const int64_t g = kk / N, n = kk - g * N;
+    if (!(lane & 1)) {
+#pragma unroll
+      for (int p = 0; p < P - 1; ++p)
+        planes[((g * P + p) * N + n) * 32 + (lane >> 1)] = zero ? 0u : pw[p];
+    }
+    if (lane == 0) norms[g * N + n] = zero ? 0u : (uint32_t(f2h_bits(nu)) | (uint32_t(f2h_bits(rho)) << 16));
+    float4* dst = reinterpret_cast<float4*>(ws + w * kD + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_float4(ep[4 * i], ep[4 * i + 1], ep[4 * i + 2], ep[4 * i + 3]);
+  }
+}
+
+// ---------------------------------------------------------------- QJL projection
+// Workgroup tile: all 1024 sketch rows x 64 keys; wave w owns rows
+// [128 w, 128 w + 128) (four 32-row blocks) and both 32-key blocks.  The
+// residuals stream through LDS in 64-coordinate chunks (converted to fp16
+// hi/lo fragments on the way in, double-buffered); the (S R^T) fragments come
+// straight from global memory (L2-resident, 4 MB) in matrix-core A order.
+// Sixteen waves would cap registers at 128; eight waves with 128 accumulators
+// each keep the fragment reads one k-step ahead.
+constexpr int kQjlThreads = 512;
+constexpr int kQjlKeys = 64;
+
+struct QjlLds {
+  uint4 b[2][4][2][2][64];   // [buf][k-step][key block][hi/lo][lane]: 32 KB
+};
+
+__device__ __forceinline__ void split_f16x8(const float (&v)[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v hv = {static_cast<_Float16>(v[2 * i]), static_cast<_Float16>(v[2 * i + 1])};
+    const half2v lv = {static_cast<_Float16>(v[2 * i] - static_cast<float>(hv[0])),
+                       static_cast<_Float16>(v[2 * i + 1] - static_cast<float>(hv[1]))};
+    h[i] = __builtin_bit_cast(uint32_t, hv);
+    l[i] = __builtin_bit_cast(uint32_t, lv);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__global__ __launch_bounds__(kQjlThreads, 1) void qjl1024_kernel(const float* __restrict__ ws, int64_t k0,
+                                                                 int64_t nk, int64_t N, int P,
+                                                                 uint32_t* __restrict__ planes,
+                                                                 const uint4* __restrict__ fragA) {
+  __shared__ QjlLds sm;
+  __shared__ uint32_t s_sign[kQjlKeys][33];   // [key][word], padded
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int64_t ntiles = (nk + kQjlKeys - 1) / kQjlKeys;
+  // staging: thread -> (key, 8 coordinates) of a 64-coordinate chunk
+  const int skey = tid >> 3, spart = tid & 7;
+
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t kb = tile * kQjlKeys;
+    const int64_t src_key = std::min<int64_t>(kb + skey, nk - 1);
+    const float* srow = ws + src_key * kD + 8 * spart;
+    auto load_chunk = [&](int c, float (&v)[8]) {
+      const float4* p = reinterpret_cast<const float4*>(srow + 64 * c);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    };
+    auto store_chunk = [&](int buf, const float (&v)[8]) {
+      uint4 hi, lo;
+      split_f16x8(v, hi, lo);
+      // coordinates 8 spart..8 spart+7 of the chunk: k-step spart / 2, k half spart & 1
+      const int ks = spart >> 1, slot = (skey & 31) + 32 * (spart & 1), cb = skey >> 5;
+      sm.b[buf][ks][cb][0][slot] = hi;
+      sm.b[buf][ks][cb][1][slot] = lo;
+    };
+    float v[8];
+    load_chunk(0, v);
+    store_chunk(0, v);
+    __syncthreads();
+
+    f32x16 acc[4][2] = {};
+    // A fragments (row block rb of this wave, global k-step ks): read three
+    // (row block, k-step) steps ahead into a ring of four register pairs
+    const uint4* fa = fragA + (size_t(4 * wave) * 64 * 2) * 64 + lane;
+    auto load_a = [&](int step, half8& ah, half8& al) {   // step = 4 ks + rb
+      const int ks = step >> 2, rb = step & 3;
+      const uint4* f = fa + ((size_t(rb) * 64 + ks) * 2) * 64;
+      ah = __builtin_bit_cast(half8, f[0]);
+      al = __builtin_bit_cast(half8, f[64]);
+    };
+    half8 ah[4], al[4];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) load_a(i, ah[i], al[i]);
+#pragma unroll 1
+    for (int c = 0; c < 16; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < 16) load_chunk(c + 1, v);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        half8 bh[2], bl[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          bh[cb] = __builtin_bit_cast(half8, sm.b[buf][ks][cb][0][lane]);
+          bl[cb] = __builtin_bit_cast(half8, sm.b[buf][ks][cb][1][lane]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int step = 16 * c + 4 * ks + rb;           // ring slot = step % 4 = rb
+          if (step + 3 < 256) load_a(step + 3, ah[(rb + 3) & 3], al[(rb + 3) & 3]);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[rb], bh[cb], acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[rb], bl[cb], acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[rb], bh[cb], acc[rb][cb], 0, 0, 0);
+          }
+        }
+      }
+      if (c + 1 < 16) store_chunk(buf ^ 1, v);
+      __syncthreads();
+    }
+
+    // sign words: lane (key kl, half h) holds rows 8 (v / 4) + 4 h + (v % 4) of
+    // each 32-row block; spread the 16 bits into nibbles and OR the halves
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        uint32_t b16 = 0u;
+#pragma unroll
+        for (int vv = 15; vv >= 0; --vv) b16 = push_sign(b16, acc[rb][cb][vv]);
+        uint32_t t = (b16 | (b16 << 8)) & 0x00FF00FFu;
+        t = (t | (t << 4)) & 0x0F0F0F0Fu;
+        t <<= 4 * h;
+        auto pr = __builtin_amdgcn_permlane32_swap(t, t, false, false);
+        const uint32_t word = pr[0] | pr[1];
+        if (h == 0) s_sign[32 * cb + (lane & 31)][4 * wave + rb] = word;
+      }
+    __syncthreads();
+    // 64 keys x 32 words: thread -> (key, 4 words)
+    {
+      const int key = tid >> 3, q4 = tid & 7;
+      const int64_t kk = kb + key;
+      if (kk < nk) {
+        const int64_t gk = k0 + kk;
+        const int64_t g = gk / N, n = gk - g * N;
+        uint4* dst = reinterpret_cast<uint4*>(planes + ((g * P + (P - 1)) * N + n) * 32) + q4;
+        *dst = make_uint4(s_sign[key][4 * q4], s_sign[key][4 * q4 + 1], s_sign[key][4 * q4 + 2],
+                          s_sign[key][4 * q4 + 3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+size_t encode_wide_chunk_keys() { return size_t(1) << 16; }   // 64K keys: 256 MiB of residuals
+
+hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
+                              void* packed, hipStream_t s) {
+  const int64_t total = G * N;
+  const int P = cb.bits;
+  uint32_t* planes = static_cast<uint32_t*>(packed);
+  uint32_t* norms = planes + total * int64_t(P) * (kD / 32);
+  const int64_t chunk = std::min<int64_t>(total, int64_t(encode_wide_chunk_keys()));
+  float* ws = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), size_t(chunk) * kD * sizeof(float), s);
+  if (e != hipSuccess) return e;
+  const int cus = std::max(1, cb.num_cus);
+  for (int64_t k0 = 0; k0 < total && e == hipSuccess; k0 += chunk) {
+    const int64_t nk = std::min<int64_t>(chunk, total - k0);
+    const int rgrid = int(std::min<int64_t>((nk + 3) / 4, int64_t(cus) * 8));
+#define TQ_ROT(BB, BF)                                                                          \
+    hipLaunchKernelGGL((rotate1024_kernel<BB, BF>), dim3(rgrid), dim3(256), 0, s, keys, k0, nk, N, \
+                       planes, norms, ws, cb.d_consts)
+    const bool bf = dtype == 1;
+    switch (cb.bits - 1) {
+      case 1: if (bf) TQ_ROT(1, true); else TQ_ROT(1, false); break;
+      case 2: if (bf) TQ_ROT(2, true); else TQ_ROT(2, false); break;
+      default: if (bf) TQ_ROT(3, true); else TQ_ROT(3, false); break;
+    }
+#undef TQ_ROT
+    const int qgrid = int(std::min<int64_t>((nk + kQjlKeys - 1) / kQjlKeys, int64_t(cus)));
+    hipLaunchKernelGGL(qjl1024_kernel, dim3(qgrid), dim3(kQjlThreads), 0, s, ws, k0, nk, N, P, planes,
+                       cb.d_fragW);
+    e = hipGetLastError();
+  }
+  const hipError_t ef = hipFreeAsync(ws, s);
+  return e != hipSuccess ? e : ef;
+}
+
+}  // namespace tq
