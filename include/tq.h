@@ -114,14 +114,19 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
  * (S r is evaluated as (S R^T)(R r) on the matrix cores, float32 accumulation
  * of a three-term float16 split), norms stored as half.
  * keys and packed are device pointers owned by the caller; G*N == 0 is a
- * no-op.  Errors: TQ_ERR_ARG, TQ_ERR_HIP.
+ * no-op.  d = 1024 runs in chunks of 65,536 keys through a temporary of
+ * 256 MiB taken from the device's stream-ordered pool (hipMallocAsync /
+ * hipFreeAsync on the given stream); d = 128 allocates nothing.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP (also when that
+ * temporary cannot be allocated).
  */
 int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype,
                    int64_t G, int64_t N, void* packed, void* stream);
 
-/* Workspace bytes tq_score_logits needs for G groups of Qg queries (the
- * current kernels prepare queries on chip and need none: 0; ws may then be
- * NULL). */
+/* Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
+ * d = 128 (each workgroup prepares its queries on chip; ws may be NULL);
+ * G*Qg*(2*1024 + 4)*4 for d = 1024 (the prepared queries 2 R q, 2 S q and
+ * their sums). */
 size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
 
 /*
@@ -133,13 +138,34 @@ size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
  * (R q via a Hadamard butterfly, S q, their sums) and then streams the packed
  * keys of its range.  All buffers are caller-owned device memory; ws must hold
  * tq_score_workspace_bytes(cb, G, Qg) bytes (may be NULL when that is 0).
- * G*N*Qg == 0 is a no-op.
+ * G*N*Qg == 0 is a no-op.  d = 1024 runs a query-preparation kernel into ws
+ * first, then scores with nibble subset-sum tables (same estimator).
  * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256 or G > 2^31 - 1),
  * TQ_ERR_HIP.
  */
 int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
                     int32_t Qg, const void* packed, int64_t N, float* logits, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * Vector-search top-k by the same estimated inner product as tq_score_logits
+ * (nearest-neighbour search over an index of packed vectors [ICLR 2026 paper
+ * digest, vector-search results]): for every query h of group g, the k keys
+ * of that group with the largest estimate, best first, ties broken by the
+ * smaller key index; the logit matrix is never formed.
+ *   idx[g][h][k]     int32 key index in [0, N), -1 where N < k (device, caller-owned)
+ *   scores[g][h][k]  float32 estimate, -inf where N < k (device, caller-owned)
+ * ws must hold tq_score_topk_workspace_bytes(cb, G, Qg, N, k) bytes of device
+ * memory (prepared queries plus per-key-range candidate lists).
+ * Supported: d == 1024, 1 <= k <= 16, Qg <= 256, N <= 2^31 - 1.
+ * Errors: TQ_ERR_ARG (null/misaligned pointer, N == 0), TQ_ERR_UNSUPPORTED,
+ * TQ_ERR_WORKSPACE, TQ_ERR_HIP.
+ */
+size_t tq_score_topk_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N,
+                                     int32_t k);
+int tq_score_topk(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                  const void* packed, int64_t N, int32_t k, int32_t* idx, float* scores, void* ws,
+                  size_t ws_bytes, void* stream);
 
 /*
  * MSE-only reconstruction of every packed key: out[g][n] = nu~ R^T c[code]

@@ -19,8 +19,8 @@ library_path = os.path.join(_HERE, "libtq.so")
 EXPORTED_SYMBOLS = (
     "tq_codebook_tables", "tq_make_codebook", "tq_free_codebook", "tq_codebook_export",
     "tq_codebook_info", "tq_packed_bytes", "tq_encode_keys", "tq_score_workspace_bytes",
-    "tq_score_logits", "tq_decode_mse", "tq_dense_logits_bf16", "tq_status_string",
-    "tq_last_hip_error",
+    "tq_score_logits", "tq_score_topk_workspace_bytes", "tq_score_topk", "tq_decode_mse",
+    "tq_dense_logits_bf16", "tq_status_string", "tq_last_hip_error",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -35,6 +35,9 @@ _SIGS = {
     "tq_score_workspace_bytes": (_c_sz, [_vp, _c_i64, _c_i32]),
     "tq_score_logits": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp,
                                        _c_sz, _vp]),
+    "tq_score_topk_workspace_bytes": (_c_sz, [_vp, _c_i64, _c_i32, _c_i64, _c_i32]),
+    "tq_score_topk": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _c_i32, _vp, _vp,
+                                     _vp, _c_sz, _vp]),
     "tq_decode_mse": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i32, _vp]),
     "tq_dense_logits_bf16": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i32, _c_i64, _c_i32, _vp, _vp]),
     "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -195,6 +198,31 @@ def score_logits(cb: Codebook, q, packed, N: int, out=None, ws=None):
                                      _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream()), "tq_score_logits")
     return out
+
+
+def score_topk_workspace_nbytes(cb: Codebook, G: int, Qg: int, N: int, k: int) -> int:
+    return int(library().tq_score_topk_workspace_bytes(cb.handle, G, Qg, N, k))
+
+
+def score_topk(cb: Codebook, q, packed, N: int, k: int = 10, ws=None):
+    """Best k keys per query by the estimated inner product: q [G, Qg, d]
+    against packed keys of N per group -> (int32 idx [G, Qg, k], float32
+    scores [G, Qg, k]), best first, ties to the smaller index."""
+    torch = _torch()
+    _need_cuda(q, "q")
+    _need_cuda(packed, "packed")
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    idx = torch.empty((G, Qg, k), dtype=torch.int32, device=q.device)
+    scores = torch.empty((G, Qg, k), dtype=torch.float32, device=q.device)
+    if ws is None:
+        wsb = score_topk_workspace_nbytes(cb, G, Qg, N, k)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check(library().tq_score_topk(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(packed), N, k,
+                                   _ptr(idx), _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream()), "tq_score_topk")
+    return idx, scores
 
 
 def decode_mse(cb: Codebook, packed, G: int, N: int, dtype=None, out=None):

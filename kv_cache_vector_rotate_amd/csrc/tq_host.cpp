@@ -434,6 +434,30 @@ int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 
+size_t tq_score_topk_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N,
+                                     int32_t k) {
+  if (!cb || G <= 0 || Qg <= 0 || N <= 0 || k < 1 || k > tq::kMaxTopKAbi || cb->d != 1024) return 0;
+  return tq::topk_wide_bytes(*cb, G, Qg, N, k);
+}
+
+int tq_score_topk(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                  const void* packed, int64_t N, int32_t k, int32_t* idx, float* scores, void* ws,
+                  size_t ws_bytes, void* stream) {
+  if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (k < 1 || k > tq::kMaxTopKAbi) return TQ_ERR_UNSUPPORTED;
+  if (cb->d != 1024 || Qg > 256 || G > INT32_MAX || N > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || Qg == 0) return TQ_OK;
+  if (N == 0) return TQ_ERR_ARG;
+  if (!q || !packed || !idx || !scores || !aligned16(q) || !aligned16(packed)) return TQ_ERR_ARG;
+  const size_t need = tq::topk_wide_bytes(*cb, G, Qg, N, k);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_topk_wide(*cb, q, q_dtype, G, Qg, packed, N, k, idx, scores, ws,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
 int tq_decode_mse(const tq_codebook* cb, const void* packed, int64_t G, int64_t N, void* out,
                   int32_t out_dtype, void* stream) {
   if (!cb || G < 0 || N < 0 || (out_dtype != TQ_F32 && out_dtype != TQ_BF16)) return TQ_ERR_ARG;

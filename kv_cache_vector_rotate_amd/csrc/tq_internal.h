@@ -58,6 +58,14 @@ size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg);
 // d = 1024 (tq_wide.hip)
 hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                               void* packed, hipStream_t s);
+size_t score_wide_prep_bytes(int64_t G, int Qg);
+size_t topk_wide_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N, int K);
+hipError_t launch_score_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                             const void* packed, int64_t N, float* logits, void* ws, hipStream_t s);
+hipError_t launch_topk_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                            const void* packed, int64_t N, int K, int32_t* idx, float* scores,
+                            void* ws, hipStream_t s);
+constexpr int kMaxTopKAbi = 16;
 bool encode_supported(const Codebook& cb);
 bool score_supported(const Codebook& cb);
 

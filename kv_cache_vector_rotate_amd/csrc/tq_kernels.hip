@@ -875,14 +875,12 @@ __global__ __launch_bounds__(256) void dense128_kernel(const uint16_t* __restric
 }  // namespace
 
 bool encode_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
-bool score_supported(const Codebook& cb) { return cb.d == 128; }
+bool score_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
 
-// The scorer prepares its queries inside each workgroup and needs no workspace.
+// d = 128: each workgroup prepares its queries itself, no workspace; d = 1024:
+// the prepared queries (2 R q, 2 S q and their sums) for all groups.
 size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg) {
-  (void)cb;
-  (void)G;
-  (void)Qg;
-  return 0;
+  return cb.d == 1024 ? score_wide_prep_bytes(G, Qg) : 0;
 }
 
 hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
@@ -923,7 +921,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
 
 hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                         const void* packed, int64_t N, float* logits, void* ws, hipStream_t s) {
-  (void)ws;
+  if (cb.d == 1024) return launch_score_wide(cb, q, qdtype, G, Qg, packed, N, logits, ws, s);
   // enough workgroups for every CU: split each (group, query chunk) unit's
   // keys into ranges of at least 512 keys, a multiple of 64 each
   const int nqc = (Qg + 3) / 4;

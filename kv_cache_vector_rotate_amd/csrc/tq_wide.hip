@@ -354,6 +354,315 @@ __global__ __launch_bounds__(kQjlThreads, 1) void qjl1024_kernel(const float* __
   }
 }
 
+// ---------------------------------------------------------------- query preparation
+// One workgroup per query: X_0 = 2 R q (butterfly in wave 0), X_1 = 2 S q
+// (thread j forms row j from S^T columns, the query in LDS), and their sums.
+// ws layout: float X[G*Qg][2][1024], then float sums[G*Qg][4] (sum R q, sum S q).
+template <bool QBF16>
+__global__ __launch_bounds__(1024) void qprep1024_kernel(const void* __restrict__ q, int64_t nq,
+                                                        float* __restrict__ X, float* __restrict__ sums,
+                                                        const DevConsts* __restrict__ cst,
+                                                        const float* __restrict__ St) {
+  __shared__ float s_q[kD];
+  __shared__ float s_part[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t gq = blockIdx.x;
+  if constexpr (QBF16)
+    s_q[tid] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[gq * kD + tid]) << 16);
+  else
+    s_q[tid] = static_cast<const float*>(q)[gq * kD + tid];
+  __syncthreads();
+  float* xr = X + gq * 2 * kD;
+  if (wave == 0) {
+    const uint32_t dn = (cst->dneg[lane >> 1] >> (16 * (lane & 1))) & 0xffffu;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = __uint_as_float(__float_as_uint(s_q[16 * lane + t]) ^ (((dn >> t) & 1u) << 31));
+#pragma unroll
+    for (int st = 1; st < 16; st <<= 1)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (t & st) continue;
+        const float a = x[t], b = x[t + st];
+        x[t] = a + b;
+        x[t + st] = a - b;
+      }
+    stage_lanes<1>(x, lane);
+    stage_lanes<2>(x, lane);
+    stage_lanes<4>(x, lane);
+    stage_lanes<8>(x, lane);
+    stage_lanes<16>(x, lane);
+    stage_lanes32(x, lane);
+    float sr = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      x[t] *= cst->inv_sqrt_d;
+      sr += x[t];
+    }
+    float4* dst = reinterpret_cast<float4*>(xr + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dst[i] = make_float4(2.f * x[4 * i], 2.f * x[4 * i + 1], 2.f * x[4 * i + 2], 2.f * x[4 * i + 3]);
+    sr = wave_sum(sr);
+    if (lane == 0) sums[gq * 4 + 0] = sr;
+  }
+  // S q, row j = tid: sum over c of S^T[c][j] q[c]
+  float acc = 0.f;
+#pragma unroll 16
+  for (int c = 0; c < kD; ++c) acc = fmaf(St[int64_t(c) * kD + tid], s_q[c], acc);
+  xr[kD + tid] = 2.f * acc;
+  const float ws_ = wave_sum(acc);
+  if (lane == 0) s_part[wave] = ws_;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += s_part[w];
+    sums[gq * 4 + 1] = t;
+  }
+}
+
+// ---------------------------------------------------------------- score
+// Grid (g, chunk of 4 query heads, key range); 1024 threads.  Nibble
+// subset-sum tables cover all 1024 coordinates at once (no table rebuilds,
+// each packed record is read once):
+//   T[ty][pos][nib] = sum over set bits t of nib of X_ty[4 pos + t]
+// (four queries per 16-byte entry), entry (ty, pos = 16 blk + pl, nib) at
+// byte ty * 64K + blk * 4K + nib * 256 + pl * 16: position pl of a 16-position
+// block always lies in LDS bank group pl, and lane L visits the positions of
+// a block in the order k ^ (L & 15), so the sixteen lanes served together
+// never share a bank group.  Per key and plane: 256 lookups, 4 adds each.
+// TOPK: instead of storing logits, each wave keeps the best K (score desc,
+// index asc) per query in lanes 0..K-1; the workgroup merges its waves' lists
+// into ws_topk[g][qh][range][K].
+constexpr int kWideThreads = 1024;
+constexpr int kMaxTopK = 16;
+
+struct WideLds {
+  f32x4 tab[2 * 16 * 16 * 16];            // 128 KB
+  float lst_s[16][4][kMaxTopK];           // per-wave lists for the merge
+  int32_t lst_i[16][4][kMaxTopK];
+};
+
+__device__ __forceinline__ bool better(float s, int32_t i, float t_s, int32_t t_i) {
+  return s > t_s || (s == t_s && i < t_i);
+}
+
+// insert (cs, ci) into the list held in lanes 0..K-1 (ls, li), if it belongs there
+__device__ __forceinline__ void list_insert(float& ls, int32_t& li, float cs, int32_t ci, int lane, int K) {
+  const bool ahead = lane < K && better(ls, li, cs, ci);
+  const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(ahead));
+  if (pos >= K) return;
+  const float ps = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ls), 0x111, 0xF, 0xF, false));   // row_shr:1
+  const int32_t pi = __builtin_amdgcn_mov_dpp(li, 0x111, 0xF, 0xF, false);
+  if (lane < K) {
+    if (lane == pos) { ls = cs; li = ci; }
+    else if (lane > pos) { ls = ps; li = pi; }
+  }
+}
+
+template <int B, bool TOPK>
+__global__ __launch_bounds__(kWideThreads, 1) void score1024_kernel(
+    const uint4* __restrict__ planes, const uint32_t* __restrict__ norms, int64_t N, int Qg,
+    int64_t chunk, const float* __restrict__ X, const float* __restrict__ sums,
+    float* __restrict__ logits, int K, float* __restrict__ tk_s, int32_t* __restrict__ tk_i,
+    const DevConsts* __restrict__ cst) {
+  constexpr int P = B + 1;
+  constexpr int NW = B == 3 ? P + 1 : P;
+  __shared__ WideLds sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t g = blockIdx.x;
+  const int qc = blockIdx.y;
+  const int64_t n0 = int64_t(blockIdx.z) * chunk;
+  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
+
+  // ---- tables: thread (pl, half, blk, ty) writes nibbles 8 half .. 8 half + 7
+  {
+    const int pl = tid & 15, hf = (tid >> 4) & 1, blk = (tid >> 5) & 15, ty = tid >> 9;
+    const int pos = 16 * blk + pl;
+    f32x4 xv[4];   // coordinate 4 pos + t, four queries
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int qh = qc * 4 + qq;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (qh < Qg) v = *reinterpret_cast<const float4*>(X + ((g * Qg + qh) * 2 + ty) * kD + 4 * pos);
+      xv[0][qq] = v.x; xv[1][qq] = v.y; xv[2][qq] = v.z; xv[3][qq] = v.w;
+    }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 b = hf ? xv[3] : z;
+    f32x4 e[8];
+    e[0] = b;
+    e[1] = b + xv[0];
+    e[2] = b + xv[1];
+    e[3] = e[2] + xv[0];
+    e[4] = b + xv[2];
+    e[5] = e[4] + xv[0];
+    e[6] = e[4] + xv[1];
+    e[7] = e[6] + xv[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm.tab[((ty * 16 + blk) * 16 + 8 * hf + j) * 16 + pl] = e[j];
+  }
+  __syncthreads();
+
+  float sr[4], ss[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int qh = std::min(qc * 4 + qq, Qg - 1);
+    sr[qq] = sums[(g * Qg + qh) * 4 + 0];
+    ss[qq] = sums[(g * Qg + qh) * 4 + 1];
+  }
+  const float a0 = cst->alpha[0], a1 = cst->alpha[1], a2 = cst->alpha[2], a3 = cst->alpha[3];
+  const float asum = cst->alpha_sum, qs = cst->qjl_scale;
+
+  // per-lane pieces of the lookup order: lookup k of a block reads position
+  // pl = k ^ r: word (k >> 3) of the block after swapping the pair when
+  // r >= 8, nibble (k & 7) ^ (r & 7)
+  const uint32_t r = lane & 15;
+  uint32_t pk[16], nb[8];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    pk[k] = (uint32_t(k) ^ r) << 4;
+    asm volatile("" : "+v"(pk[k]));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    nb[k] = 4u * (uint32_t(k) ^ (r & 7));
+    asm volatile("" : "+v"(nb[k]));
+  }
+  const bool swp = r & 8;
+  const char* tabp = reinterpret_cast<const char*>(sm.tab);
+  const uint4* pg = planes + g * P * N * 8;   // 128-byte plane records: 8 x 16 B
+  const uint32_t* ng = norms + g * N;
+
+  float ls[4], tsc[4];
+  int32_t li[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) { ls[qq] = -__builtin_huge_valf(); li[qq] = 0x7fffffff; tsc[qq] = 0.f; }
+
+  // one block of 64 coordinates (two words) of one plane against table ty
+  auto add_block = [&](uint32_t w0, uint32_t w1, int ty, int blk, float* acc) {
+    const uint32_t u0 = swp ? w1 : w0, u1 = swp ? w0 : w1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t nib = __builtin_amdgcn_ubfe(k < 8 ? u0 : u1, nb[k & 7], 4);
+      uint32_t ad = (nib << 8) | pk[k];
+      if (ty) ad |= 0x10000u;
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(tabp + ad + blk * 4096);
+      acc[0] += tv[0]; acc[1] += tv[1]; acc[2] += tv[2]; acc[3] += tv[3];
+      if ((k & 3) == 3)
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]) : : "memory");
+    }
+  };
+
+  for (int64_t base = n0 + int64_t(wave) * 64; base < n1; base += kWideThreads) {
+    const int64_t n = std::min<int64_t>(base + lane, n1 - 1);
+    float acc[NW][4];
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) acc[t][qq] = 0.f;
+#pragma unroll 1
+    for (int step = 0; step < 8; ++step) {   // 128 coordinates (four words) per step
+      uint4 w[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) w[p] = pg[(p * N + n) * 8 + step];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int blk = 2 * step + hb;
+        uint32_t wa[P], wb[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          wa[p] = hb ? w[p].z : w[p].x;
+          wb[p] = hb ? w[p].w : w[p].y;
+        }
+#pragma unroll
+        for (int t = 0; t < B; ++t) add_block(wa[t], wb[t], 0, blk, acc[t]);
+        if constexpr (B == 3) add_block(wa[0] ^ wa[1] ^ wa[2], wb[0] ^ wb[1] ^ wb[2], 0, blk, acc[P]);
+        add_block(wa[B], wb[B], 1, blk, acc[B]);
+      }
+    }
+    const uint32_t nrm = ng[n];
+    const float nu = __builtin_bit_cast(_Float16, uint16_t(nrm & 0xffffu));
+    const float rs = float(__builtin_bit_cast(_Float16, uint16_t(nrm >> 16))) * qs;
+    const bool valid = base + lane < n1;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      float mse;
+      if constexpr (B == 1) {
+        mse = a0 * acc[0][qq] - asum * sr[qq];
+      } else if constexpr (B == 2) {
+        mse = fmaf(a0, acc[0][qq], a1 * acc[1][qq]) - asum * sr[qq];
+      } else {
+        mse = fmaf(a0, acc[0][qq], fmaf(a1, acc[1][qq], fmaf(a2, acc[2][qq], a3 * acc[P][qq]))) -
+              asum * sr[qq];
+      }
+      const float v = fmaf(nu, mse, rs * (ss[qq] - acc[B][qq]));
+      const int qh = qc * 4 + qq;
+      if constexpr (!TOPK) {
+        if (valid && qh < Qg) __builtin_nontemporal_store(v, &logits[(g * Qg + qh) * N + n]);
+      } else {
+        // candidates against the list's current last entry, inserted one by one
+        const float t_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[qq]), K - 1));
+        const int32_t t_i = __builtin_amdgcn_readlane(li[qq], K - 1);
+        uint64_t m = __builtin_amdgcn_ballot_w64(valid && better(v, int32_t(n), t_s, t_i));
+        while (m) {
+          const int b = __builtin_ctzll(m);
+          m &= m - 1;
+          const float cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), b));
+          const int32_t ci = __builtin_amdgcn_readlane(int32_t(n), b);
+          list_insert(ls[qq], li[qq], cs, ci, lane, K);
+        }
+      }
+    }
+  }
+  if constexpr (TOPK) {
+    if (lane < K) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) { sm.lst_s[wave][qq][lane] = ls[qq]; sm.lst_i[wave][qq][lane] = li[qq]; }
+    }
+    __syncthreads();
+    if (wave < 4) {   // wave qq merges query qq's sixteen lists
+      const int qq = wave;
+      float ms = lane < K ? sm.lst_s[0][qq][lane] : -__builtin_huge_valf();
+      int32_t mi = lane < K ? sm.lst_i[0][qq][lane] : 0x7fffffff;
+      for (int w = 1; w < 16; ++w)
+        for (int j = 0; j < K; ++j) {
+          const float cs = sm.lst_s[w][qq][j];
+          const int32_t ci = sm.lst_i[w][qq][j];
+          list_insert(ms, mi, cs, ci, lane, K);
+        }
+      const int qh = qc * 4 + qq;
+      if (qh < Qg && lane < K) {
+        const int64_t at = ((g * Qg + qh) * int64_t(gridDim.z) + blockIdx.z) * K + lane;
+        tk_s[at] = ms;
+        tk_i[at] = mi;
+      }
+    }
+  }
+}
+
+// merge the per-range lists of one query: one wave per (g, qh)
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ tk_s,
+                                                        const int32_t* __restrict__ tk_i, int ranges,
+                                                        int K, int32_t* __restrict__ out_i,
+                                                        float* __restrict__ out_s) {
+  const int lane = threadIdx.x;
+  const int64_t gq = blockIdx.x;
+  float ms = -__builtin_huge_valf();
+  int32_t mi = 0x7fffffff;
+  for (int r = 0; r < ranges; ++r)
+    for (int j = 0; j < K; ++j) {
+      const int64_t at = (gq * ranges + r) * K + j;
+      list_insert(ms, mi, tk_s[at], tk_i[at], lane, K);
+    }
+  if (lane < K) {
+    const bool some = mi != 0x7fffffff;
+    out_i[gq * K + lane] = some ? mi : -1;
+    out_s[gq * K + lane] = ms;
+  }
+}
+
 }  // namespace
 
 size_t encode_wide_chunk_keys() { return size_t(1) << 16; }   // 64K keys: 256 MiB of residuals
@@ -389,6 +698,85 @@ hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, i
   }
   const hipError_t ef = hipFreeAsync(ws, s);
   return e != hipSuccess ? e : ef;
+}
+
+size_t score_wide_prep_bytes(int64_t G, int Qg) {
+  return size_t(G) * Qg * (2 * kD + 4) * sizeof(float);
+}
+
+int64_t score_wide_ranges(const Codebook& cb, int64_t G, int Qg, int64_t N, int64_t* chunk_out) {
+  const int nqc = (Qg + 3) / 4;
+  const int64_t units = G * nqc;
+  const int64_t cus = std::max(1, cb.num_cus);
+  int64_t want = std::max<int64_t>(1, (cus + units - 1) / units);
+  want = std::min<int64_t>(want, std::max<int64_t>(1, (N + 1023) / 1024));
+  const int64_t chunk = ((N + want - 1) / want + 63) / 64 * 64;
+  if (chunk_out) *chunk_out = chunk;
+  return (N + chunk - 1) / chunk;
+}
+
+size_t topk_wide_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N, int K) {
+  const int64_t ranges = score_wide_ranges(cb, G, Qg, N, nullptr);
+  return score_wide_prep_bytes(G, Qg) + size_t(G) * Qg * ranges * K * 8;
+}
+
+static hipError_t prep_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg, float* X,
+                            float* sums, hipStream_t s) {
+  const int64_t nq = G * Qg;
+  if (qdtype == 1)
+    hipLaunchKernelGGL(qprep1024_kernel<true>, dim3(unsigned(nq)), dim3(1024), 0, s, q, nq, X, sums,
+                       cb.d_consts, cb.d_St);
+  else
+    hipLaunchKernelGGL(qprep1024_kernel<false>, dim3(unsigned(nq)), dim3(1024), 0, s, q, nq, X, sums,
+                       cb.d_consts, cb.d_St);
+  return hipGetLastError();
+}
+
+template <bool TOPK>
+static hipError_t score_wide(const Codebook& cb, const void* packed, int64_t G, int Qg, int64_t N,
+                             const float* X, const float* sums, float* logits, int K, float* tk_s,
+                             int32_t* tk_i, hipStream_t s) {
+  int64_t chunk = 0;
+  const int64_t ranges = score_wide_ranges(cb, G, Qg, N, &chunk);
+  const dim3 grid{unsigned(G), unsigned((Qg + 3) / 4), unsigned(ranges)};
+  const uint4* planes = static_cast<const uint4*>(packed);
+  const uint32_t* norms = static_cast<const uint32_t*>(packed) + G * N * int64_t(cb.bits) * (kD / 32);
+#define TQ_SW(BB)                                                                                  \
+  hipLaunchKernelGGL((score1024_kernel<BB, TOPK>), grid, dim3(kWideThreads), 0, s, planes, norms, N, Qg, \
+                     chunk, X, sums, logits, K, tk_s, tk_i, cb.d_consts)
+  switch (cb.bits - 1) {
+    case 1: TQ_SW(1); break;
+    case 2: TQ_SW(2); break;
+    default: TQ_SW(3); break;
+  }
+#undef TQ_SW
+  return hipGetLastError();
+}
+
+hipError_t launch_score_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                             const void* packed, int64_t N, float* logits, void* ws, hipStream_t s) {
+  float* X = static_cast<float*>(ws);
+  float* sums = X + G * Qg * 2 * kD;
+  hipError_t e = prep_wide(cb, q, qdtype, G, Qg, X, sums, s);
+  if (e != hipSuccess) return e;
+  return score_wide<false>(cb, packed, G, Qg, N, X, sums, logits, 0, nullptr, nullptr, s);
+}
+
+hipError_t launch_topk_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                            const void* packed, int64_t N, int K, int32_t* idx, float* scores,
+                            void* ws, hipStream_t s) {
+  float* X = static_cast<float*>(ws);
+  float* sums = X + G * Qg * 2 * kD;
+  const int64_t ranges = score_wide_ranges(cb, G, Qg, N, nullptr);
+  float* tk_s = reinterpret_cast<float*>(static_cast<char*>(ws) + score_wide_prep_bytes(G, Qg));
+  int32_t* tk_i = reinterpret_cast<int32_t*>(tk_s + G * Qg * ranges * K);
+  hipError_t e = prep_wide(cb, q, qdtype, G, Qg, X, sums, s);
+  if (e != hipSuccess) return e;
+  e = score_wide<true>(cb, packed, G, Qg, N, X, sums, nullptr, K, tk_s, tk_i, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, tk_s, tk_i,
+                     int(ranges), K, idx, scores);
+  return hipGetLastError();
 }
 
 }  // namespace tq
