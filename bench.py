@@ -97,12 +97,8 @@ def cpu_baseline(wl, budget_s):
                       f"{wl.Qg} queries per group, {t_work:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode.",
-              file=sys.stderr)
-        sys.exit(2)
+def run_decode(args):
+    """Workloads 0, 1, 3 (and 2 through run_long_context): one step = encode + score."""
     import torch
     import kv_cache_vector_rotate_amd as K
     from kv_cache_vector_rotate_amd import workloads as W
@@ -216,6 +212,163 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _event_times(fn, reps, warm=2):
+    import torch
+    for _ in range(warm):
+        fn(-1)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])   # ms
+
+
+def _stats(ms, alg_bytes=None, units=None, unit_name="keys"):
+    out = {"us_median": round(float(np.median(ms)) * 1e3, 2),
+           "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+           "us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+    mean_s = float(ms.mean()) * 1e-3
+    if units is not None:
+        out[f"{unit_name}_per_s"] = round(units / mean_s, 1)
+    if alg_bytes is not None:
+        gbps = alg_bytes / mean_s / 1e9
+        out.update({"algorithmic_bytes": int(alg_bytes), "hbm_GBps": round(gbps, 1),
+                    "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)})
+    return out
+
+
+def run_long_context(args):
+    """Workload 2 (G=32 x N=131072, b=4): score against the packed cache and the
+    in-library bf16 q.K GEMV on the same shapes, both against the HBM roofline."""
+    import torch
+    import kv_cache_vector_rotate_amd as K
+    from kv_cache_vector_rotate_amd import workloads as W
+    wl = W.workload(2, bits=args.bits)
+    G, N, Qg, d, bits = wl.G, wl.N, wl.Qg, wl.d, wl.bits
+    dev = torch.device("cuda:0")
+    keys0 = torch.from_numpy(W.all_keys(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(W.all_queries(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    cb = K.Codebook(d, bits, d, 42)
+    key_bytes = keys0.numel() * 2
+    pbytes = K.packed_nbytes(cb, G, N)
+    mall = 256 << 20
+    keys = [keys0, keys0.clone()]
+    npk = max(3, -(-3 * mall // pbytes))
+    packed = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(npk)]
+    for p_ in packed:
+        K.encode_keys(cb, keys0, out=p_)
+    logits = torch.empty((G, Qg, N), dtype=torch.float32, device=dev)
+    enc = _event_times(lambda i: K.encode_keys(cb, keys[i % 2], out=packed[i % npk]), max(3, args.steps // 10))
+    sc = _event_times(lambda i: K.score_logits(cb, q, packed[i % npk], N, out=logits), args.steps)
+    dn = _event_times(lambda i: K.dense_logits_bf16(q, keys[i % 2], out=logits), args.steps)
+    logit_bytes = G * Qg * N * 4
+    q_bytes = q.numel() * 2
+    out = {"metric": "packed keys scored/s + HBM GB/s; bf16 q.K GEMV on the same shapes",
+           "config": {"workload": wl.name, "groups": G, "keys_per_group": N, "queries_per_group": Qg,
+                      "d": d, "bits": bits},
+           "encode": _stats(enc, key_bytes + pbytes, G * N),
+           "score": _stats(sc, pbytes + logit_bytes + q_bytes, G * N),
+           "dense_bf16_gemv": _stats(dn, key_bytes + logit_bytes + q_bytes, G * N),
+           "score_speedup_vs_dense": round(float(dn.mean() / sc.mean()), 3),
+           "bytes_ratio_dense_over_score": round((key_bytes + logit_bytes) / (pbytes + logit_bytes), 3)}
+    print(json.dumps(out), flush=True)
+
+
+def run_cache_sweep(args):
+    """Workload 3 (Qwen2.5-3B-shaped cache, 72 groups x 8192 keys, Qg=8) at
+    b = 2, 3, 4: encode/score throughput, packed bytes against the fp16 K+V
+    cache, and the cosine between estimated and exact logits per query head."""
+    import torch
+    import kv_cache_vector_rotate_amd as K
+    from kv_cache_vector_rotate_amd import workloads as W
+    wl = W.workload(3)
+    G, N, Qg, d = wl.G, wl.N, wl.Qg, wl.d
+    dev = torch.device("cuda:0")
+    keys = torch.from_numpy(W.all_keys(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = torch.from_numpy(W.all_queries(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    exact = torch.matmul(q.float(), keys.float().transpose(1, 2).contiguous())   # [G, Qg, N]
+    fp16_kv = G * N * d * 2 * 2
+    rows = []
+    for bits in (2, 3, 4):
+        cb = K.Codebook(d, bits, d, 42)
+        pbytes = K.packed_nbytes(cb, G, N)
+        packed = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+        enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed[i % 2]), max(5, args.steps // 4))
+        lg = torch.empty((G, Qg, N), dtype=torch.float32, device=dev)
+        sc = _event_times(lambda i: K.score_logits(cb, q, packed[i % 2], N, out=lg), args.steps)
+        est = K.score_logits(cb, q, packed[0], N).double()
+        ex = exact.double()
+        cos = (est * ex).sum(-1) / (est.norm(dim=-1) * ex.norm(dim=-1))
+        v_bytes = G * N * (bits * d // 8 + 2)          # values: bits-bit MSE codes + one half norm
+        rows.append({"bits": bits, "packed_key_bytes": int(pbytes), "value_bytes_mse": int(v_bytes),
+                     "kv_bytes": int(pbytes + v_bytes), "fp16_kv_bytes": int(fp16_kv),
+                     "compression_vs_fp16": round(fp16_kv / (pbytes + v_bytes), 3),
+                     "logit_cosine_mean": round(float(cos.mean()), 6),
+                     "logit_cosine_min": round(float(cos.min()), 6),
+                     "query_heads": int(cos.numel()),
+                     "encode": _stats(enc, keys.numel() * 2 + pbytes, G * N),
+                     "score": _stats(sc, pbytes + G * Qg * N * 4 + q.numel() * 2, G * N)})
+    print(json.dumps({"metric": "bytes vs fp16 K+V, logit cosine, keys/s per bit width",
+                      "config": {"workload": wl.name, "groups": G, "keys_per_group": N,
+                                 "queries_per_group": Qg, "d": d}, "sweep": rows}), flush=True)
+
+
+def run_search(args):
+    """Workload 4 (1,048,576 unit vectors, d = m = 1024, b = 4, 256 queries):
+    encode all vectors, then the top-10 per query by the estimated inner
+    product.  The encoder's projection is matrix-core bound; the top-10 is
+    bound by vector ALU and LDS (the masked sums run as table lookups)."""
+    import torch
+    import kv_cache_vector_rotate_amd as K
+    from kv_cache_vector_rotate_amd import workloads as W
+    wl = W.workload(4)
+    N, d, bits, Qn = wl.N, wl.d, wl.bits, wl.Qg
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    keys = torch.empty((1, N, d), dtype=torch.float32, device=dev)
+    step = 1 << 16
+    for s0 in range(0, N, step):
+        keys[0, s0:s0 + step] = torch.from_numpy(W.group_keys(wl, 0, s0, min(step, N - s0))).to(dev)
+        if (s0 // step) % 4 == 3:
+            print(f"[bench] {s0 + step} vectors generated", file=sys.stderr, flush=True)
+    q = torch.from_numpy(W.group_queries(wl, 0)).to(dev)[None]
+    print(f"[bench] search inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    cb = K.Codebook(d, bits, d, 42)
+    pbytes = K.packed_nbytes(cb, 1, N)
+    packed = torch.empty(pbytes, dtype=torch.uint8, device=dev)
+    enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed), max(2, args.steps // 50), warm=1)
+    ws = torch.empty(K.score_topk_workspace_nbytes(cb, 1, Qn, N, 10), dtype=torch.uint8, device=dev)
+    tk = _event_times(lambda i: K.score_topk(cb, q, packed, N, 10, ws=ws), 1, warm=1)
+    enc_flops = 2.0 * d * d * N * 3        # three fp16 products per output of S R^T r
+    enc_s = float(enc.mean()) * 1e-3
+    out = {"metric": "vectors encoded/s; (vector, query) pairs scored/s with top-10",
+           "config": {"workload": wl.name, "vectors": N, "d": d, "bits": bits, "queries": Qn, "k": 10},
+           "encode": dict(_stats(enc, keys.numel() * 4 + pbytes, N, "vectors"),
+                          mfma_TFLOPs=round(enc_flops / enc_s / 1e12, 1),
+                          mfma_frac_of_fp16_dense_peak=round(enc_flops / enc_s / 2.5e15, 4)),
+           "topk": _stats(tk, None, N * Qn, "pairs")}
+    print(json.dumps(out), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.config == 2:
+        run_long_context(args)
+    elif args.config == 3 and args.bits is None:
+        run_cache_sweep(args)
+    elif args.config == 4:
+        run_search(args)
+    else:
+        run_decode(args)
 
 
 if __name__ == "__main__":
