@@ -56,10 +56,14 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // lo = RN_f16(x - hi) (x - hi is exact in float32).  Builtins only: the
 // registers feed the matrix cores, and the compiler's hazard checks do not
 // see through inline assembly.
-__device__ __forceinline__ void split_f16_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+// mone must hold -1.0f in a register the compiler cannot see through: then
+// x - hi is one mixed-precision fma per value (v_fma_mix_f32 reads the half
+// straight from the packed register) instead of a convert and a subtract.
+__device__ __forceinline__ void split_f16_pair(float x0, float x1, float mone, uint32_t& hi,
+                                               uint32_t& lo) {
   const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-  const half2v l = {static_cast<_Float16>(x0 - static_cast<float>(h[0])),
-                    static_cast<_Float16>(x1 - static_cast<float>(h[1]))};
+  const half2v l = {static_cast<_Float16>(__builtin_fmaf(static_cast<float>(h[0]), mone, x0)),
+                    static_cast<_Float16>(__builtin_fmaf(static_cast<float>(h[1]), mone, x1))};
   hi = __builtin_bit_cast(uint32_t, h);
   lo = __builtin_bit_cast(uint32_t, l);
 }
@@ -186,9 +190,10 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
   for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k][0] = wd[k][1] = 0u;
   f32x16 acc[4] = {};
   float rho2 = 0.f;
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    uint32_t bh[4], bl[4];   // residual as packed f16 pairs (hi, lo) of registers 8kc..8kc+7
+  float mone = -1.0f;
+  asm volatile("" : "+v"(mone));
+  // codes, residual and fp16 hi/lo split of the 8 registers of chunk kc
+  auto quant_chunk = [&](int kc, uint32_t (&bh)[4], uint32_t (&bl)[4]) {
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
       float ep[2];
@@ -212,36 +217,66 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
         ep[t] = fmaf(-u, gsc, yh);
         rho2 = fmaf(ep[t], ep[t], rho2);
       }
-      split_f16_pair(ep[0], ep[1], bh[pr], bl[pr]);
+      split_f16_pair(ep[0], ep[1], mone, bh[pr], bl[pr]);
     }
-    // an empty use of the code words (no instruction): their bits are
-    // accumulated chunk by chunk instead of being recombined after all the
-    // products, which would keep every comparison result live meanwhile
+  };
+  // an empty use of the code words (no instruction): their bits are
+  // accumulated chunk by chunk instead of being recombined after all the
+  // products, which would keep every comparison result live meanwhile
+  auto pin_words = [&]() {
     if constexpr (K > 2) {
       asm volatile("" : "+v"(wu[0]), "+v"(wu[1]), "+v"(wd[0][0]), "+v"(wd[0][1]), "+v"(wd[1][0]),
                    "+v"(wd[1][1]), "+v"(wd[2][0]), "+v"(wd[2][1]));
     } else {
       asm volatile("" : "+v"(wu[0]), "+v"(wu[1]), "+v"(wd[0][0]), "+v"(wd[0][1]));
     }
-    const half8 bhi = __builtin_bit_cast(half8, u32x4{bh[0], bh[1], bh[2], bh[3]});
-    const half8 blo = __builtin_bit_cast(half8, u32x4{bl[0], bl[1], bl[2], bl[3]});
-    // per-chunk opaque offset (no instruction): keeps this chunk's 8 fragment
-    // reads next to its MFMAs instead of all 64 being hoisted to the top
+  };
+  // Software pipeline over the 8 chunks: the 12 matrix products of chunk kc
+  // share one scheduling region with the vector work of chunk kc + 1 and are
+  // interleaved with it (one product per eight vector instructions), so the
+  // matrix core runs while this wave quantises instead of stalling its issue.
+  uint32_t bh[2][4], bl[2][4];
+  half8 ahi[2][4], alo[2][4];
+  // fragments of chunk kc are read one region ahead, behind a per-chunk
+  // opaque offset (no instruction) that keeps them from being hoisted out of
+  // the tile loop
+  auto read_frag = [&](int kc, half8 (&fhv)[4], half8 (&flv)[4]) {
     int ko = kc * 4 * 64;
     asm volatile("" : "+v"(ko));
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      // B = 3 keeps more code words live: read each row block's fragments
-      // next to its own products so that only two are held at a time
-      int kj = ko + jb * 64;
-      if constexpr (B == 3) asm volatile("" : "+v"(kj));
-      const half8 ahi = fh[kj];
-      const half8 alo = fo[kj];
-      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, bhi, acc[jb], 0, 0, 0);
-      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, blo, acc[jb], 0, 0, 0);
-      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, bhi, acc[jb], 0, 0, 0);
+      fhv[jb] = fh[ko + jb * 64];
+      flv[jb] = fo[ko + jb * 64];
     }
-    // bound the scheduler's window to one chunk (limits register pressure)
+  };
+  read_frag(0, ahi[0], alo[0]);
+  quant_chunk(0, bh[0], bl[0]);
+  pin_words();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    const int cur = kc & 1;
+    if (kc < 7) {
+      read_frag(kc + 1, ahi[cur ^ 1], alo[cur ^ 1]);
+      quant_chunk(kc + 1, bh[cur ^ 1], bl[cur ^ 1]);
+    }
+    const half8 bhi = __builtin_bit_cast(half8, u32x4{bh[cur][0], bh[cur][1], bh[cur][2], bh[cur][3]});
+    const half8 blo = __builtin_bit_cast(half8, u32x4{bl[cur][0], bl[cur][1], bl[cur][2], bl[cur][3]});
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[cur][jb], bhi, acc[jb], 0, 0, 0);
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[cur][jb], blo, acc[jb], 0, 0, 0);
+      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[cur][jb], bhi, acc[jb], 0, 0, 0);
+    }
+    if (kc < 7) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // next chunk's fragment reads first
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+      }
+    }
+    pin_words();
     __builtin_amdgcn_sched_barrier(0);
   }
   rho2 = xor32_sum(rho2);
