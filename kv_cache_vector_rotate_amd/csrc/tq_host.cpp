@@ -286,20 +286,17 @@ int upload_device(tq::Codebook& cb) {
     std::vector<uint16_t> frag;
     build_fragments_128(cb.S_rot, frag);
     e = upload(&cb.d_frag, frag.data(), frag.size() * sizeof(uint16_t));
-    // D for the lane that loads coordinates [64h, 64h + 64): for bf16 keys the
-    // pairs (d_2p, +d_2p+1) and (d_2p, -d_2p+1) that turn one dot2 per output
-    // into the first butterfly stage; for float32 keys sign-flip words.
-    std::vector<uint32_t> dp(128, 0), ff(128, 0);
-    const uint32_t one = 0x3F80u, neg = 0xBF80u;   // bf16 +1, -1
-    for (int h = 0; h < 2; ++h)
-      for (int p = 0; p < 32; ++p) {
-        const int i0 = 64 * h + 2 * p, i1 = i0 + 1;
-        const uint32_t a = cb.delta[i0] < 0 ? neg : one;
-        const uint32_t b = cb.delta[i1] < 0 ? neg : one;
-        const uint32_t nb = b ^ 0x8000u;
-        dp[(h * 2 + 0) * 32 + p] = a | (b << 16);
-        dp[(h * 2 + 1) * 32 + p] = a | (nb << 16);
-      }
+    // D as bf16 sign bits in the order the rotation product reads the keys:
+    // [k-half e][k-step ks][word j] covers coordinates 16 ks + 8 e + 2 j, +1;
+    // for float32 keys sign-flip words for the lane holding [64h, 64h + 64).
+    std::vector<uint32_t> dp(64, 0), ff(128, 0);
+    for (int e = 0; e < 2; ++e)
+      for (int ks = 0; ks < 8; ++ks)
+        for (int j = 0; j < 4; ++j) {
+          const int i0 = 16 * ks + 8 * e + 2 * j;
+          dp[(e * 8 + ks) * 4 + j] = (cb.delta[i0] < 0 ? 0x8000u : 0u) |
+                                     (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
+        }
     for (int i = 0; i < 128; ++i)
       if (cb.delta[i] < 0) ff[(i >> 6) * 64 + (i & 63)] = 0x80000000u;
     if (e == hipSuccess) e = upload(&cb.d_dpair, dp.data(), dp.size() * 4);

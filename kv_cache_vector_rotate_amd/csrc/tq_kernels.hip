@@ -332,13 +332,30 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
 // ---- bf16 keys.  Eight waves per workgroup, one workgroup per CU.  Each
 // wave owns an 8 KB LDS buffer that the next tile's keys stream into
 // (global_load_lds, 16 B per lane, no registers held) while the current tile
-// is encoded.  The first butterfly stage, the bf16 -> f32 conversion and the
-// sign flips D run as one v_dot2_f32_bf16 per output against (d_a, +-d_b)
-// pairs; its +0 addend also turns a sum of signed zeros into +0.
+// is encoded.  The rotation u = H D k runs on the matrix cores: bf16 keys
+// times +-1 are exact products, so one bf16 product per 32 x 32 x 16 block
+// gives u with fp32 accumulation (32 products per 32-key tile), where the
+// butterfly would cost about 550 vector instructions per tile.
+//
+// Product layout.  B operand (keys, K = input coordinate): lane (kl, e) of
+// k-step ks holds coordinates 16 ks + 8 e + t (t = 0..7) of key kl, which is
+// exactly the 16-byte chunk 2 ks + e of the key: the DMA places chunk
+// 2 c + h of key kl at slot c * 64 + lane, so each k-step is one
+// conflict-free 16-byte LDS read, and D is one XOR of the bf16 sign bits.
+// A operand (Hadamard rows, M = output coordinate): output row
+// 32 mb + 8 g + 4 h + e' of block mb lands in accumulator 4 g + e' of lane
+// half h; it is assigned the coordinate that the butterfly would leave in
+// register r = 16 mb + 4 g + e' of that half, (r % 32) + 32 (h + 2 (r / 32)),
+// so everything after the rotation is shared with the float32 kernel.
+// For Sylvester's H the entry sign is the parity of (row & column); with the
+// bit fields above it splits into a per-lane pattern over t, a per-lane flip
+// tied to bit 1 of ks, and a flip that depends on (mb, ks) only, so four
+// register fragments (G0, G1 and their negations) serve all 32 products.
 constexpr int kEncBfThreads = 512;
 constexpr int kEncBfWaves = kEncBfThreads / 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ void issue_tile_dma(const uint16_t* __restrict__ keys, uint32_t tile,
@@ -348,21 +365,46 @@ __device__ __forceinline__ void issue_tile_dma(const uint16_t* __restrict__ keys
   const int64_t g = gt;
   const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
   const int64_t nl = n < N ? n : N - 1;
-  const uint4* src = reinterpret_cast<const uint4*>(keys + ((g * N + nl) * 128 + 64 * h));
+  const uint4* src = reinterpret_cast<const uint4*>(keys + (g * N + nl) * 128) + h;
 #pragma unroll
   for (int c = 0; c < 8; ++c)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + c),
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * c),
                                      (lds_void*)(buf + c * 64), 16, 0, 0);
+}
+
+// Hadamard A fragments of this lane (row rho = lane % 32, k-half e = lane / 32):
+// g[0] = G0, g[1] = G1, g[2] = -G0, g[3] = -G1 (bf16 +-1, eight per fragment).
+__device__ __forceinline__ void hadamard_frags(int lane, u32x4 (&g)[4]) {
+  const int rho = lane & 31, e = lane >> 5;
+  const int e0 = rho & 1, e1 = (rho >> 1) & 1, hq = (rho >> 2) & 1;
+  const int g0 = (rho >> 3) & 1, g1 = (rho >> 4) & 1;
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = 2 * j + u;
+      const int sgn = (e0 & t) ^ (e1 & (t >> 1)) ^ (g0 & (t >> 2)) ^ (g1 & e);
+      v |= (sgn ? 0xBF80u : 0x3F80u) << (16 * u);
+    }
+    w[j] = v;
+  }
+  const uint32_t f1 = hq ? 0x80008000u : 0u;
+  g[0] = u32x4{w[0], w[1], w[2], w[3]};
+  g[1] = u32x4{w[0] ^ f1, w[1] ^ f1, w[2] ^ f1, w[3] ^ f1};
+  g[2] = g[0] ^ 0x80008000u;
+  g[3] = g[1] ^ 0x80008000u;
 }
 
 template <int B>
 __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     const uint16_t* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
     uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
-    const uint4* __restrict__ frag, const uint32_t* __restrict__ dpair) {
+    const uint4* __restrict__ frag, const uint32_t* __restrict__ dmask) {
   __shared__ uint4 s_frag[4096];                   // 64 KB: [hi | lo][kc 8][jb 4][lane 64]
   __shared__ uint4 s_raw[kEncBfWaves][8 * 64];     // 64 KB: per-wave key tile
-  __shared__ uint4 s_dp[2][2][8];                  // [h][+/-][pairs 4 per entry]
+  __shared__ uint4 s_dm[2][8];                     // D as bf16 sign bits, [k-half][k-step]
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, kl = lane & 31;
   // wave-uniform tile bookkeeping lives in scalar registers (tiles < 2^31)
@@ -374,9 +416,11 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
   uint4* buf = s_raw[wave];
   if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, lane, buf);
   for (int i = tid; i < 4096; i += kEncBfThreads) s_frag[i] = frag[i];
-  if (tid < 32) reinterpret_cast<uint4*>(s_dp)[tid] = reinterpret_cast<const uint4*>(dpair)[tid];
+  if (tid < 16) reinterpret_cast<uint4*>(s_dm)[tid] = reinterpret_cast<const uint4*>(dmask)[tid];
   EncConsts ec;
   load_enc_consts(cst, ec);
+  u32x4 hf[4];
+  hadamard_frags(lane, hf);
   __syncthreads();
 
   // Each iteration: wait for this tile's keys (the DMA issued one iteration
@@ -392,32 +436,40 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
     const bool valid = n < N;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    uint4 raw[8];
+    u32x4 raw[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) raw[c] = buf[c * 64 + lane];
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = buf[c * 64 + lane];
+      raw[c] = u32x4{v.x, v.y, v.z, v.w};
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
     if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, lane, buf);
     store_tile<B>(prev, lane, N, planes, norms);
 
-    float x[64];
     float nu2 = 0.f;
+    f32x16 y[4] = {};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 dp = s_dp[h][0][c], dm = s_dp[h][1][c];
-      const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
-      const uint32_t wp[4] = {dp.x, dp.y, dp.z, dp.w};
-      const uint32_t wm[4] = {dm.x, dm.y, dm.z, dm.w};
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 dm = s_dm[h][ks];
+      const u32x4 kv = raw[ks] ^ u32x4{dm.x, dm.y, dm.z, dm.w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16x2 kv = __builtin_bit_cast(bf16x2, w[t]);
-        x[8 * c + 2 * t] =
-            __builtin_amdgcn_fdot2_f32_bf16(kv, __builtin_bit_cast(bf16x2, wp[t]), 0.0f, false);
-        x[8 * c + 2 * t + 1] =
-            __builtin_amdgcn_fdot2_f32_bf16(kv, __builtin_bit_cast(bf16x2, wm[t]), 0.0f, false);
-        nu2 = __builtin_amdgcn_fdot2_f32_bf16(kv, kv, nu2, false);
+        const bf16x2 p = __builtin_bit_cast(bf16x2, uint32_t(raw[ks][t]));
+        nu2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, nu2, false);
+      }
+      const bf16x8 bk = __builtin_bit_cast(bf16x8, kv);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int neg = ((mb & 1) & (ks & 1)) ^ ((mb >> 1) & (ks >> 2));
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, hf[((ks >> 1) & 1) + 2 * neg]);
+        y[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bk, y[mb], 0, 0, 0);
       }
     }
-    butterfly_rest(x, 2);
+    float x[64];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) x[16 * mb + a] = y[mb][a];
     encode_tail<B>(x, nu2, ec, s_frag, lane, g, n, valid, prev);
   }
   store_tile<B>(prev, lane, N, planes, norms);
@@ -588,14 +640,19 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     }
   }
   uint32_t dn0 = cst->dneg[lane >> 5], dn1 = cst->dneg[2 + (lane >> 5)];
+  // wave-uniform plane bases + 32-bit lane offsets (key index < 2^28): the
+  // loads take the scalar-base form and need no 64-bit address arithmetic
   auto load_tile = [&](int64_t b, uint4 (&wv)[P], uint32_t& nv) {
-    const int64_t n = std::min<int64_t>(b + lane, n1 - 1);
+    const uint32_t n = uint32_t(std::min<int64_t>(b + lane, n1 - 1));
+    const uint32_t off16 = n * 16u, off4 = n * 4u;   // byte offsets, < 2^32
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(pg + p * N + n));
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pg + p * N) + off16));
       wv[p] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    nv = __builtin_nontemporal_load(&ng[n]);
+    nv = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ng) + off4));
   };
   const int64_t first = n0 + int64_t(wave) * 64;
   uint4 w[D][P];
@@ -715,6 +772,9 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   }
   const float a0 = cst->alpha[0], a1 = cst->alpha[1], a2 = cst->alpha[2], a3 = cst->alpha[3];
   const float asum = cst->alpha_sum, qs = cst->qjl_scale;
+  float* lrow[4];   // logit rows of the chunk's queries (wave-uniform)
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
 
   // Per-lane address pieces.  Lookup (a, c) of a plane reads position
   // (4 a + c) ^ r, which is byte c ^ (r & 3) of permuted word a; one byte
@@ -774,7 +834,9 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     add_plane(rw[B], 1, acc[B]);
 
     const float nu = h2f_bits(nrm & 0xffffu), rs = h2f_bits(nrm >> 16) * qs;
-    const int64_t n = b + lane;
+    const bool in_range = b + lane < n1;
+    uint32_t off4 = (uint32_t(b) + uint32_t(lane)) * 4u;
+    asm volatile("" : "+v"(off4));   // keep the offset 32-bit (scalar-base stores)
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       float mse;
@@ -787,9 +849,9 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
               asum * sr[qq];
       }
       const int qh = qc * 4 + qq;
-      if (n < n1 && qh < Qg)   // streamed output: no reuse, written past the caches
+      if (in_range && qh < Qg)   // streamed output: no reuse, written past the caches
         __builtin_nontemporal_store(fmaf(nu, mse, rs * (ss[qq] - acc[B][qq])),
-                                    &logits[(g * Qg + qh) * N + n]);
+                                    reinterpret_cast<float*>(reinterpret_cast<char*>(lrow[qq]) + off4));
     }
   };
 

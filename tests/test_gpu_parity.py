@@ -113,6 +113,28 @@ def test_special_keys():
     assert np.all(lg[0, :, :2] == 0.0)
 
 
+def test_special_keys_bf16():
+    """bf16 keys (rotation on the matrix cores): zero, one-hot, constant and
+    two-hot keys.  Rotated coordinates that are exactly zero take the
+    non-negative code, so those keys must match the oracle's codes exactly,
+    flagged coordinates included."""
+    rng = np.random.default_rng(6)
+    keys = _round_bf16(_keys(rng, 1, 40))
+    keys[0, 0] = 0.0
+    keys[0, 1] = 0.0
+    keys[0, 1, 100] = 3.0            # one-hot
+    keys[0, 2] = 0.5                 # constant: many exact cancellations
+    keys[0, 3] = 0.0
+    keys[0, 3, 5:7] = 1.0            # half of the rotated coordinates exactly zero
+    keys[0, 4] = 0.0
+    keys[0, 4, [9, 70]] = [2.0, -2.0]
+    cb, cbo, packed, buf, _ = _encode_and_check(3, keys, torch.bfloat16)
+    codes, signs, nu16, rho16 = O.unpack(cbo, buf, 1, 40)
+    assert not codes[0, 0].any() and not signs[0, 0].any() and float(nu16[0, 0]) == 0.0
+    ref = O.encode(cbo, keys[0, :5].astype(np.float64))
+    assert np.array_equal(codes[0, 1:5].astype(np.int64), ref.codes[1:5].astype(np.int64))
+
+
 def test_encode_is_deterministic():
     rng = np.random.default_rng(9)
     keys = _dev(_keys(rng, 4, 777), torch.bfloat16)
