@@ -64,24 +64,28 @@ typedef struct tq_codebook tq_codebook;
  *   levels[L], thresholds[L-1]  Lloyd-Max levels/boundaries for N(0, 1/d),
  *                               L = 2^(bits-1), ascending, float64;
  *   delta[d]                    Rademacher signs (+1/-1) of D;
- *   S[m*d]                      QJL sketch, row-major, N(0,1) draws as float32;
- *   S_rot[m*d]                  S R^T in float64 (the sketch seen from the
- *                               rotated domain: S r = (S R^T)(R r)).
- * delta and S come from a counter-based SplitMix64 stream: draw(seed, s, i) =
- * mix64(mix64(seed + s*G) + (i+1)*G), G = 0x9E3779B97F4A7C15; delta_i = +1 iff
- * bit 63 of draw(seed,1,i) is 0; S[j][i] = fp32(sqrt(-2 ln u1) cos(2 pi u2)),
- * u1 = ((x>>11)+1) 2^-53, u2 = (y>>11) 2^-53, x,y = draw(seed,2,2(jd+i)+{0,1}).
+ *   S[m*d]                      QJL sketch, row-major, float64: S = S_rot R;
+ *   S_rot[m*d]                  S R^T (the sketch seen from the rotated
+ *                               domain, S r = S_rot (R r)): N(0,1) draws
+ *                               rounded to float16, held in float64.
+ * R is orthogonal, so S has the i.i.d. N(0,1) law of the QJL projection
+ * [Qiita explainer, "Stage 2: QJL"] up to the float16 rounding of the draws.
+ * delta and S_rot come from a counter-based SplitMix64 stream: draw(seed, s, i)
+ * = mix64(mix64(seed + s*G) + (i+1)*G), G = 0x9E3779B97F4A7C15; delta_i = +1
+ * iff bit 63 of draw(seed,1,i) is 0; S_rot[j][i] = fp16(sqrt(-2 ln u1)
+ * cos(2 pi u2)), u1 = ((x>>11)+1) 2^-53, u2 = (y>>11) 2^-53,
+ * x,y = draw(seed,2,2(jd+i)+{0,1}).
  * Touches no GPU.  Errors: TQ_ERR_UNSUPPORTED (d not a power of two in
  * [32, 1024], bits not in {2,3,4}, m != d), TQ_ERR_ALLOC.
  */
 int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed,
                        double* levels, double* thresholds, int8_t* delta,
-                       float* S, double* S_rot);
+                       double* S, double* S_rot);
 
 /*
  * Build the quantizer state for (d, bits, m, seed) on the current HIP device:
  * the tables above plus the kernels' constant blocks (thresholds and levels in
- * float32, the sketch split into float16 hi/lo parts laid out for the matrix
+ * float32, S_rot as float16 laid out for the matrix
  * cores, Walsh coefficients of the levels for the scorer).  The handle owns
  * its device memory (hipMalloc) and is immutable afterwards, so it may be
  * shared by streams and threads; it is valid on the device that was current
@@ -97,7 +101,7 @@ void tq_free_codebook(tq_codebook* cb);
 /* Host copies of a codebook's tables (same meaning as tq_codebook_tables;
  * any pointer may be NULL).  Errors: TQ_ERR_ARG (cb NULL). */
 int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds,
-                       int8_t* delta, float* S, double* S_rot);
+                       int8_t* delta, double* S, double* S_rot);
 
 /* (d, bits, m, seed) of a codebook; any pointer may be NULL. */
 int tq_codebook_info(const tq_codebook* cb, int32_t* d, int32_t* bits, int32_t* m,
@@ -111,8 +115,9 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
  * TQ_BF16) into the packed layout above.  Per key k: nu = ||k||; zero record if
  * nu < 1e-10; else y = R k / nu, code_i = #{thresholds <= y_i},
  * residual r = k - nu R^T c[code], rho = ||r||, sign bit_j = [(S r)_j < 0]
- * (S r is evaluated as (S R^T)(R r) on the matrix cores, float32 accumulation
- * of a three-term float16 split), norms stored as half.
+ * (S r is evaluated as S_rot (R r) on the matrix cores: S_rot is exact in
+ * float16, R r is split into float16 hi + lo, float32 accumulation), norms
+ * stored as half.
  * keys and packed are device pointers owned by the caller; G*N == 0 is a
  * no-op.  d = 1024 runs in chunks of 65,536 keys through a temporary of
  * 256 MiB taken from the device's stream-ordered pool (hipMallocAsync /

@@ -89,7 +89,7 @@ def codebook_tables(d: int, bits: int, m: int | None = None, seed: int = 42):
     m = d if m is None else m
     L = 1 << (bits - 1)
     out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
-               delta=np.empty(d, np.int8), S=np.empty((m, d), np.float32),
+               delta=np.empty(d, np.int8), S=np.empty((m, d), np.float64),
                S_rot=np.empty((m, d), np.float64))
     _check(library().tq_codebook_tables(d, bits, m, seed, *(_ptr(out[k]) for k in
                                         ("levels", "thresholds", "delta", "S", "S_rot"))),
@@ -125,7 +125,7 @@ class Codebook:
     def export(self):
         L = 1 << (self.bits - 1)
         out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
-                   delta=np.empty(self.d, np.int8), S=np.empty((self.m, self.d), np.float32),
+                   delta=np.empty(self.d, np.int8), S=np.empty((self.m, self.d), np.float64),
                    S_rot=np.empty((self.m, self.d), np.float64))
         _check(library().tq_codebook_export(self._h, *(_ptr(out[k]) for k in
                                             ("levels", "thresholds", "delta", "S", "S_rot"))),

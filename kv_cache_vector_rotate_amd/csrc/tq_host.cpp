@@ -54,7 +54,9 @@ void make_delta(uint64_t seed, int d, int8_t* out) {
   for (int i = 0; i < d; ++i) out[i] = (s(static_cast<uint64_t>(i)) >> 63) ? int8_t(-1) : int8_t(1);
 }
 
-void make_sketch(uint64_t seed, int m, int d, float* out) {
+// The sketch seen from the rotated domain, S R^T: Box-Muller N(0,1) draws
+// rounded to float16 (nearest even), held exactly in float64.
+void make_sketch_rot(uint64_t seed, int m, int d, double* out) {
   Stream s(seed, 2);
   const double two_pi = 2.0 * M_PI;
   const double ulp53 = std::ldexp(1.0, -53);
@@ -63,7 +65,7 @@ void make_sketch(uint64_t seed, int m, int d, float* out) {
     const double u1 = double((x >> 11) + 1) * ulp53;   // (0, 1]
     const double u2 = double(y >> 11) * ulp53;         // [0, 1)
     const double z = std::sqrt(-2.0 * std::log(u1)) * std::cos(two_pi * u2);  // Box-Muller
-    out[t] = static_cast<float>(z);
+    out[t] = double(static_cast<_Float16>(z));
   }
 }
 
@@ -103,13 +105,13 @@ void lloyd_max_normal(int L, double* levels, double* thresholds) {
   }
 }
 
-// S R^T = S D H / sqrt(d) (H symmetric): a Hadamard transform of each row of
-// S * delta, in float64.
-void sketch_rotated(const float* S, const int8_t* delta, int m, int d, double* out) {
+// S = (S R^T) R = S_rot H D / sqrt(d) (R orthogonal, H symmetric): a
+// Hadamard transform of each row of S_rot, then D, in float64.
+void sketch_from_rotated(const double* S_rot, const int8_t* delta, int m, int d, double* out) {
   const double scale = 1.0 / std::sqrt(double(d));
   for (int j = 0; j < m; ++j) {
     double* row = out + int64_t(j) * d;
-    for (int i = 0; i < d; ++i) row[i] = double(S[int64_t(j) * d + i]) * delta[i];
+    for (int i = 0; i < d; ++i) row[i] = S_rot[int64_t(j) * d + i];
     for (int h = 1; h < d; h <<= 1)
       for (int i0 = 0; i0 < d; i0 += 2 * h)
         for (int i = i0; i < i0 + h; ++i) {
@@ -117,7 +119,7 @@ void sketch_rotated(const float* S, const int8_t* delta, int m, int d, double* o
           row[i] = a + c;
           row[i + h] = a - c;
         }
-    for (int i = 0; i < d; ++i) row[i] *= scale;
+    for (int i = 0; i < d; ++i) row[i] *= scale * delta[i];
   }
 }
 
@@ -145,8 +147,7 @@ uint16_t half_bits(double v) {
 // coordinates coord(L/32, 8*kc + t), t = 0..7.  Stored negated (see the encoder).
 void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>& frag) {
   const int d = 128;
-  frag.assign(2 * 8 * 4 * 64 * 8, 0);
-  const size_t lo_off = size_t(8) * 4 * 64 * 8;
+  frag.assign(8 * 4 * 64 * 8, 0);
   for (int kc = 0; kc < 8; ++kc)
     for (int jb = 0; jb < 4; ++jb)
       for (int L = 0; L < 64; ++L) {
@@ -154,35 +155,26 @@ void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>
         for (int t = 0; t < 8; ++t) {
           const int r = 8 * kc + t;
           const int coord = (r & 31) + 32 * (h + 2 * (r >> 5));
-          // negated: the encoder forms the negated residual c[code] - y
-          const double v = -S_rot[size_t(j) * d + coord];
-          const _Float16 hi = static_cast<_Float16>(v);
-          const _Float16 lo = static_cast<_Float16>(v - static_cast<double>(hi));
-          const size_t at = ((size_t(kc) * 4 + jb) * 64 + L) * 8 + t;
-          std::memcpy(&frag[at], &hi, 2);
-          std::memcpy(&frag[lo_off + at], &lo, 2);
+          // negated (the encoder forms the negated residual c[code] - y);
+          // S_rot holds float16 values, so the half is exact
+          frag[((size_t(kc) * 4 + jb) * 64 + L) * 8 + t] = half_bits(-S_rot[size_t(j) * d + coord]);
         }
       }
 }
 
-// d = 1024: fragment (rb, ks, hl, lane L) holds row 32 rb + L % 32 of S R^T
-// at coordinates 16 ks + 8 (L / 32) + t, t = 0..7 (matrix-core A order for
-// 32x32x16), hl = 0 the float16 value, hl = 1 the float16 remainder.
+// d = 1024: fragment (rb, ks, lane L) holds row 32 rb + L % 32 of S R^T at
+// coordinates 16 ks + 8 (L / 32) + t, t = 0..7 (matrix-core A order for
+// 32x32x16); the values are exact in float16.
 void build_fragments_wide(const std::vector<double>& S_rot, int d, std::vector<uint16_t>& frag) {
   const int nrb = d / 32, nks = d / 16;
-  frag.assign(size_t(nrb) * nks * 2 * 64 * 8, 0);
+  frag.assign(size_t(nrb) * nks * 64 * 8, 0);
   for (int rb = 0; rb < nrb; ++rb)
     for (int ks = 0; ks < nks; ++ks)
       for (int L = 0; L < 64; ++L) {
         const int j = 32 * rb + (L & 31);
         for (int t = 0; t < 8; ++t) {
           const int k = 16 * ks + 8 * (L >> 5) + t;
-          const double v = S_rot[size_t(j) * d + k];
-          const _Float16 hi = static_cast<_Float16>(v);
-          const _Float16 lo = static_cast<_Float16>(v - static_cast<double>(hi));
-          const size_t base = ((size_t(rb) * nks + ks) * 2) * 64 * 8;
-          std::memcpy(&frag[base + size_t(L) * 8 + t], &hi, 2);
-          std::memcpy(&frag[base + 64 * 8 + size_t(L) * 8 + t], &lo, 2);
+          frag[((size_t(rb) * nks + ks) * 64 + L) * 8 + t] = half_bits(S_rot[size_t(j) * d + k]);
         }
       }
 }
@@ -236,8 +228,8 @@ int build_tables(tq::Codebook& cb) {
   for (double& v : cb.levels) v *= sigma;
   for (double& v : cb.thresholds) v *= sigma;
   make_delta(cb.seed, d, cb.delta.data());
-  make_sketch(cb.seed, m, d, cb.S.data());
-  sketch_rotated(cb.S.data(), cb.delta.data(), m, d, cb.S_rot.data());
+  make_sketch_rot(cb.seed, m, d, cb.S_rot.data());
+  sketch_from_rotated(cb.S_rot.data(), cb.delta.data(), m, d, cb.S.data());
   fill_consts(cb);
   return TQ_OK;
 }
@@ -279,7 +271,7 @@ int upload_device(tq::Codebook& cb) {
   if (e == hipSuccess) {   // the scorer reads S column by column: store its transpose
     std::vector<float> st(cb.S.size());
     for (int j = 0; j < cb.m; ++j)
-      for (int c = 0; c < cb.d; ++c) st[size_t(c) * cb.m + j] = cb.S[size_t(j) * cb.d + c];
+      for (int c = 0; c < cb.d; ++c) st[size_t(c) * cb.m + j] = float(cb.S[size_t(j) * cb.d + c]);
     e = upload(&cb.d_St, st.data(), st.size() * sizeof(float));
   }
   if (e == hipSuccess && cb.d == 128) {
@@ -323,7 +315,7 @@ int check_device(const tq::Codebook& cb) {
 extern "C" {
 
 int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed, double* levels,
-                       double* thresholds, int8_t* delta, float* S, double* S_rot) {
+                       double* thresholds, int8_t* delta, double* S, double* S_rot) {
   if (!valid_params(d, bits, m)) return TQ_ERR_UNSUPPORTED;
   tq::Codebook cb;
   cb.d = d;
@@ -336,7 +328,7 @@ int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed, double
   if (levels) std::memcpy(levels, cb.levels.data(), L * sizeof(double));
   if (thresholds) std::memcpy(thresholds, cb.thresholds.data(), (L - 1) * sizeof(double));
   if (delta) std::memcpy(delta, cb.delta.data(), d);
-  if (S) std::memcpy(S, cb.S.data(), cb.S.size() * sizeof(float));
+  if (S) std::memcpy(S, cb.S.data(), cb.S.size() * sizeof(double));
   if (S_rot) std::memcpy(S_rot, cb.S_rot.data(), cb.S_rot.size() * sizeof(double));
   return TQ_OK;
 }
@@ -366,13 +358,13 @@ void tq_free_codebook(tq_codebook* cb) {
 }
 
 int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds, int8_t* delta,
-                       float* S, double* S_rot) {
+                       double* S, double* S_rot) {
   if (!cb) return TQ_ERR_ARG;
   const int L = 1 << (cb->bits - 1);
   if (levels) std::memcpy(levels, cb->levels.data(), L * sizeof(double));
   if (thresholds) std::memcpy(thresholds, cb->thresholds.data(), (L - 1) * sizeof(double));
   if (delta) std::memcpy(delta, cb->delta.data(), cb->d);
-  if (S) std::memcpy(S, cb->S.data(), cb->S.size() * sizeof(float));
+  if (S) std::memcpy(S, cb->S.data(), cb->S.size() * sizeof(double));
   if (S_rot) std::memcpy(S_rot, cb->S_rot.data(), cb->S_rot.size() * sizeof(double));
   return TQ_OK;
 }

@@ -33,15 +33,15 @@ struct Codebook {
   // host tables
   std::vector<double> levels, thresholds, S_rot;
   std::vector<int8_t> delta;
-  std::vector<float> S;
+  std::vector<double> S;
   DevConsts consts{};
   // device copies
   DevConsts* d_consts = nullptr;
-  uint4* d_frag = nullptr;       // S R^T as float16 hi/lo, matrix-core A-operand order
+  uint4* d_frag = nullptr;       // -S R^T as float16 (exact), matrix-core A-operand order
   float* d_St = nullptr;         // S transposed, float32 [d][m]
   uint32_t* d_dpair = nullptr;      // [2 k-halves][8 k-steps][4] D as bf16 sign bits (d = 128)
   uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
-  uint4* d_fragW = nullptr;         // S R^T hi/lo for d = 1024: [row block 32][k-step 64][hi/lo][lane 64]
+  uint4* d_fragW = nullptr;         // S R^T for d = 1024: [row block 32][k-step 64][lane 64]
   int num_cus = 0;                  // compute units of the device
 };
 

@@ -175,15 +175,14 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
   // ---- Lloyd-Max codes (sign bit + magnitude thresholds), residual, hi/lo
   //      split, and the QJL projection p = (S R^T) r_rot on the matrix cores,
   //      interleaved: as soon as the 16 coordinates of chunk kc are split into
-  //      fp16 hi/lo, its 12 MFMAs (4 row blocks x hi*hi + hi*lo + lo*hi, fp32
-  //      accumulation) are issued, so the matrix core runs while the vector
-  //      ALU quantises the next chunk.
+  //      fp16 hi/lo, its 8 MFMAs (4 row blocks x (S R^T) r_hi + (S R^T) r_lo;
+  //      S R^T is exact in float16, fp32 accumulation) are issued, so the
+  //      matrix core runs while the vector ALU quantises the next chunk.
   // The fragment table never changes inside the tile loop; an opaque lane
   // offset keeps the compiler from hoisting its 64 reads out of the loop.
   int fl_off = lane;
   asm volatile("" : "+v"(fl_off));
   const half8* fh = reinterpret_cast<const half8*>(s_frag) + fl_off;
-  const half8* fo = reinterpret_cast<const half8*>(s_frag + 2048) + fl_off;
   uint32_t wu[2] = {0u, 0u};
   uint32_t wd[K > 1 ? K - 1 : 1][2];
 #pragma unroll
@@ -231,25 +230,22 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
       asm volatile("" : "+v"(wu[0]), "+v"(wu[1]), "+v"(wd[0][0]), "+v"(wd[0][1]));
     }
   };
-  // Software pipeline over the 8 chunks: the 12 matrix products of chunk kc
+  // Software pipeline over the 8 chunks: the 8 matrix products of chunk kc
   // share one scheduling region with the vector work of chunk kc + 1 and are
-  // interleaved with it (one product per eight vector instructions), so the
+  // interleaved with it (one product per twelve vector instructions), so the
   // matrix core runs while this wave quantises instead of stalling its issue.
   uint32_t bh[2][4], bl[2][4];
-  half8 ahi[2][4], alo[2][4];
+  half8 ahi[2][4];
   // fragments of chunk kc are read one region ahead, behind a per-chunk
   // opaque offset (no instruction) that keeps them from being hoisted out of
   // the tile loop
-  auto read_frag = [&](int kc, half8 (&fhv)[4], half8 (&flv)[4]) {
+  auto read_frag = [&](int kc, half8 (&fhv)[4]) {
     int ko = kc * 4 * 64;
     asm volatile("" : "+v"(ko));
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      fhv[jb] = fh[ko + jb * 64];
-      flv[jb] = fo[ko + jb * 64];
-    }
+    for (int jb = 0; jb < 4; ++jb) fhv[jb] = fh[ko + jb * 64];
   };
-  read_frag(0, ahi[0], alo[0]);
+  read_frag(0, ahi[0]);
   quant_chunk(0, bh[0], bl[0]);
   pin_words();
   __builtin_amdgcn_sched_barrier(0);
@@ -257,7 +253,7 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
   for (int kc = 0; kc < 8; ++kc) {
     const int cur = kc & 1;
     if (kc < 7) {
-      read_frag(kc + 1, ahi[cur ^ 1], alo[cur ^ 1]);
+      read_frag(kc + 1, ahi[cur ^ 1]);
       quant_chunk(kc + 1, bh[cur ^ 1], bl[cur ^ 1]);
     }
     const half8 bhi = __builtin_bit_cast(half8, u32x4{bh[cur][0], bh[cur][1], bh[cur][2], bh[cur][3]});
@@ -266,14 +262,13 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
     for (int jb = 0; jb < 4; ++jb) {
       acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[cur][jb], bhi, acc[jb], 0, 0, 0);
       acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[cur][jb], blo, acc[jb], 0, 0, 0);
-      acc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[cur][jb], bhi, acc[jb], 0, 0, 0);
     }
     if (kc < 7) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // next chunk's fragment reads first
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // next chunk's fragment reads first
 #pragma unroll
-      for (int i = 0; i < 12; ++i) {
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // eight VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // twelve VALU
       }
     }
     pin_words();
@@ -402,7 +397,7 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     const uint16_t* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
     uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
     const uint4* __restrict__ frag, const uint32_t* __restrict__ dmask) {
-  __shared__ uint4 s_frag[4096];                   // 64 KB: [hi | lo][kc 8][jb 4][lane 64]
+  __shared__ uint4 s_frag[2048];                   // 32 KB: [kc 8][jb 4][lane 64]
   __shared__ uint4 s_raw[kEncBfWaves][8 * 64];     // 64 KB: per-wave key tile
   __shared__ uint4 s_dm[2][8];                     // D as bf16 sign bits, [k-half][k-step]
 
@@ -415,7 +410,7 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
   uint32_t tile = blockIdx.x * kEncBfWaves + wave;
   uint4* buf = s_raw[wave];
   if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, lane, buf);
-  for (int i = tid; i < 4096; i += kEncBfThreads) s_frag[i] = frag[i];
+  for (int i = tid; i < 2048; i += kEncBfThreads) s_frag[i] = frag[i];
   if (tid < 16) reinterpret_cast<uint4*>(s_dm)[tid] = reinterpret_cast<const uint4*>(dmask)[tid];
   EncConsts ec;
   load_enc_consts(cst, ec);
@@ -484,11 +479,11 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     const float* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
     uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
     const uint4* __restrict__ frag, const uint32_t* __restrict__ flip) {
-  __shared__ uint4 s_frag[4096];       // [hi | lo][kc 8][jb 4][lane 64]
+  __shared__ uint4 s_frag[2048];       // [kc 8][jb 4][lane 64]
   __shared__ uint32_t s_flip[128];
 
   const int tid = threadIdx.x;
-  for (int i = tid; i < 4096; i += kEncThreads) s_frag[i] = frag[i];
+  for (int i = tid; i < 2048; i += kEncThreads) s_frag[i] = frag[i];
   for (int i = tid; i < 128; i += kEncThreads) s_flip[i] = flip[i];
   EncConsts ec;
   load_enc_consts(cst, ec);

@@ -6,8 +6,9 @@
 //                      lanes), Lloyd-Max codes -> code planes, nu and rho, and
 //                      the scaled residual 2^12 (y - c[code]) to a workspace;
 //   qjl1024_kernel     the QJL projection p = (S R^T) r_rot for 64 keys per
-//                      workgroup on the matrix cores (three-term fp16 split,
-//                      fp32 accumulation), then sign words [p < 0].
+//                      workgroup on the matrix cores (S R^T exact in fp16,
+//                      r_rot split into fp16 hi + lo, fp32 accumulation),
+//                      then sign words [p < 0].
 // [ICLR 2026 paper digest, "Step 1: PolarQuant" (R = H_d D / sqrt(d)) and the
 //  implementation pseudocode (zero vectors, sign convention); Qiita
 //  explainer, "Stage 2: QJL" (sign sketch of the residual).]
@@ -220,8 +221,9 @@ __global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict_
 // Workgroup tile: all 1024 sketch rows x 64 keys; wave w owns rows
 // [128 w, 128 w + 128) (four 32-row blocks) and both 32-key blocks.  The
 // residuals stream through LDS in 64-coordinate chunks (converted to fp16
-// hi/lo fragments on the way in, double-buffered); the (S R^T) fragments come
-// straight from global memory (L2-resident, 4 MB) in matrix-core A order.
+// hi/lo fragments on the way in, double-buffered); the (S R^T) fragments,
+// exact in float16, come straight from global memory (L2-resident, 2 MB) in
+// matrix-core A order, so each product is two terms: S_rot r_hi + S_rot r_lo.
 // Sixteen waves would cap registers at 128; eight waves with 128 accumulators
 // each keep the fragment reads one k-step ahead.
 constexpr int kQjlThreads = 512;
@@ -281,18 +283,16 @@ __global__ __launch_bounds__(kQjlThreads, 1) void qjl1024_kernel(const float* __
     __syncthreads();
 
     f32x16 acc[4][2] = {};
-    // A fragments (row block rb of this wave, global k-step ks): read three
-    // (row block, k-step) steps ahead into a ring of four register pairs
-    const uint4* fa = fragA + (size_t(4 * wave) * 64 * 2) * 64 + lane;
-    auto load_a = [&](int step, half8& ah, half8& al) {   // step = 4 ks + rb
+    // A fragments (row block rb of this wave, global k-step ks; exact in
+    // float16): read three (row block, k-step) steps ahead into a ring of four
+    const uint4* fa = fragA + (size_t(4 * wave) * 64) * 64 + lane;
+    auto load_a = [&](int step, half8& ah) {   // step = 4 ks + rb
       const int ks = step >> 2, rb = step & 3;
-      const uint4* f = fa + ((size_t(rb) * 64 + ks) * 2) * 64;
-      ah = __builtin_bit_cast(half8, f[0]);
-      al = __builtin_bit_cast(half8, f[64]);
+      ah = __builtin_bit_cast(half8, fa[(size_t(rb) * 64 + ks) * 64]);
     };
-    half8 ah[4], al[4];
+    half8 ah[4];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) load_a(i, ah[i], al[i]);
+    for (int i = 0; i < 3; ++i) load_a(i, ah[i]);
 #pragma unroll 1
     for (int c = 0; c < 16; ++c) {
       const int buf = c & 1;
@@ -308,12 +308,11 @@ __global__ __launch_bounds__(kQjlThreads, 1) void qjl1024_kernel(const float* __
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
           const int step = 16 * c + 4 * ks + rb;           // ring slot = step % 4 = rb
-          if (step + 3 < 256) load_a(step + 3, ah[(rb + 3) & 3], al[(rb + 3) & 3]);
+          if (step + 3 < 256) load_a(step + 3, ah[(rb + 3) & 3]);
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
             acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[rb], bh[cb], acc[rb][cb], 0, 0, 0);
             acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[rb], bl[cb], acc[rb][cb], 0, 0, 0);
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[rb], bh[cb], acc[rb][cb], 0, 0, 0);
           }
         }
       }

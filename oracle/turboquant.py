@@ -23,6 +23,8 @@ DESIGN.md):
 * code_i = number of thresholds t_j with y_i >= t_j (a tie goes up).
 * QJL sign bit = [ (S r)_j < 0 ]  (0 = positive, -0.0 counts as positive).
 * S has i.i.d. N(0, 1) entries, m rows; r is formed in the original domain.
+  S is drawn as S = S_rot R with S_rot's entries N(0, 1) draws rounded to
+  float16: the same law (R is orthogonal) up to that rounding.
 * both norms are stored as IEEE half (round to nearest even) and the
   estimator uses the stored values.
 * delta and S come from a counter-based SplitMix64 stream (below), not from
@@ -104,13 +106,14 @@ def rademacher_signs(seed: int, d: int) -> np.ndarray:
 
 
 def gaussian_sketch(seed: int, m: int, d: int) -> np.ndarray:
-    """S[j, i] ~ N(0, 1) by Box-Muller from stream-2 draws 2(jd+i), 2(jd+i)+1.
+    """G[j, i] ~ N(0, 1) by Box-Muller from stream-2 draws 2(jd+i), 2(jd+i)+1.
 
     u1 = ((x >> 11) + 1) * 2**-53 in (0, 1], u2 = (y >> 11) * 2**-53 in [0, 1),
-    z = sqrt(-2 ln u1) cos(2 pi u2), rounded to float32 (nearest even).  The
-    QJL projection is a Gaussian random matrix [Qiita explainer, Stage 2].
-    libm's log/cos (math module) are used so that the host library, which
-    also calls libm, draws the same fp64 values.
+    z = sqrt(-2 ln u1) cos(2 pi u2), rounded to float16 (nearest even).  The
+    QJL projection is a Gaussian random matrix [Qiita explainer, Stage 2];
+    make_codebook uses G as the sketch seen from the rotated domain,
+    S R^T = G.  libm's log/cos (math module) are used so that the host
+    library, which also calls libm, draws the same fp64 values.
     """
     n = m * d
     draws = splitmix64_draw(seed, 2, np.arange(2 * n, dtype=np.uint64))
@@ -123,7 +126,7 @@ def gaussian_sketch(seed: int, m: int, d: int) -> np.ndarray:
         u1 = (xs[t] + 1) * two53
         u2 = ys[t] * two53
         out[t] = sqrt(-2.0 * log(u1)) * cos(tau * u2)
-    return out.astype(np.float32).reshape(m, d)
+    return out.astype(np.float16).reshape(m, d)
 
 
 # --------------------------------------------------------------------------
@@ -205,8 +208,9 @@ class Codebook:
     levels: np.ndarray   # [L] ascending, for N(0, 1/d)
     thresholds: np.ndarray  # [L-1] ascending
     delta: np.ndarray    # [d] int8 Rademacher signs
-    S: np.ndarray        # [m, d] float64 holding float32-rounded N(0,1) draws
+    S: np.ndarray        # [m, d] float64 sketch, S = S_rot R
     R: np.ndarray        # [d, d] float64 dense rotation
+    S_rot: np.ndarray    # [m, d] float64 = S R^T: float16-rounded N(0,1) draws
 
     @property
     def B(self) -> int:
@@ -221,16 +225,21 @@ def make_codebook(d: int, bits: int, m: int, seed: int) -> Codebook:
     """Quantizer state: Lloyd-Max for N(0,1/d) with L = 2**(bits-1) levels
     (scale equivariance: N(0,1) levels times 1/sqrt(d)), delta and S from the
     seed, and the dense rotation.  [ai.spot.hk, 無偏內積估計: (b-1)-bit MSE
-    stage; ICLR 2026 digest, Step 1: coordinates ~ N(0, 1/d)]."""
+    stage; ICLR 2026 digest, Step 1: coordinates ~ N(0, 1/d)].
+
+    The sketch is drawn in the rotated basis: S_rot has i.i.d. N(0,1)
+    entries (rounded to float16) and S = S_rot R.  R is orthogonal, so S has
+    the same i.i.d. N(0,1) law [Qiita explainer, Stage 2: Gaussian random
+    projection], and S r = S_rot (R r)."""
     if bits < 2:
         raise ValueError("bits >= 2 (one bit is the QJL sign)")
     lv, th = lloyd_max_std_normal(bits - 1)
     sigma = 1.0 / math.sqrt(d)
     delta = rademacher_signs(seed, d)
-    S = gaussian_sketch(seed, m, d).astype(np.float64)
+    R = rotation_matrix(delta)
+    S_rot = gaussian_sketch(seed, m, d).astype(np.float64)
     return Codebook(d=d, bits=bits, m=m, seed=seed, levels=lv * sigma,
-                    thresholds=th * sigma, delta=delta, S=S,
-                    R=rotation_matrix(delta))
+                    thresholds=th * sigma, delta=delta, S=S_rot @ R, R=R, S_rot=S_rot)
 
 
 # --------------------------------------------------------------------------

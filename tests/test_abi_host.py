@@ -37,8 +37,9 @@ def test_host_tables_match_oracle(d, bits, seed):
     assert np.max(np.abs(t["levels"] - cb.levels)) < 1e-12 / np.sqrt(d)
     assert np.max(np.abs(t["thresholds"] - cb.thresholds)) < 1e-12 / np.sqrt(d)
     assert np.array_equal(t["delta"], cb.delta)
-    assert np.array_equal(t["S"], cb.S.astype(np.float32))           # bit-identical draws
-    assert np.max(np.abs(t["S_rot"] - cb.S @ cb.R.T)) < 1e-12
+    assert np.array_equal(t["S_rot"], cb.S_rot)                      # bit-identical draws
+    assert np.max(np.abs(t["S"] - cb.S)) < 1e-12
+    assert np.max(np.abs(t["S"] @ cb.R.T - cb.S_rot)) < 1e-12
 
 
 def test_host_tables_reject_unsupported():

@@ -105,14 +105,19 @@ def test_rademacher_balanced_and_seeded():
 
 
 def test_sketch_is_standard_normal():
-    """S entries pass a Kolmogorov-Smirnov test against N(0,1), rows are
-    uncorrelated, and the values are exactly float32."""
-    S = O.gaussian_sketch(42, 128, 128)
-    assert S.dtype == np.float32
-    ks = stats.kstest(S.ravel().astype(np.float64), "norm")
-    assert ks.pvalue > 1e-3
-    c = np.corrcoef(S[:8].astype(np.float64))
-    assert np.max(np.abs(c - np.eye(8))) < 0.35
+    """The draws are exactly float16 and pass a Kolmogorov-Smirnov test
+    against N(0,1); so do the entries of S = S_rot R (R orthogonal keeps the
+    law); rows of both are uncorrelated, and S R^T gives the draws back."""
+    G = O.gaussian_sketch(42, 128, 128)
+    assert G.dtype == np.float16
+    assert stats.kstest(G.ravel().astype(np.float64), "norm").pvalue > 1e-3
+    cb = O.make_codebook(128, 3, 128, 42)
+    assert np.array_equal(cb.S_rot, G.astype(np.float64))
+    assert stats.kstest(cb.S.ravel(), "norm").pvalue > 1e-3
+    for M in (cb.S, cb.S_rot):
+        c = np.corrcoef(M[:8])
+        assert np.max(np.abs(c - np.eye(8))) < 0.35
+    assert np.max(np.abs(cb.S @ cb.R.T - cb.S_rot)) < 1e-12
 
 
 # ---------------------------------------------------------------- Lloyd-Max
