@@ -205,9 +205,16 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
         float mag = ec.cpos[0];
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) {
-          const float dk = a - tu[k];
-          wd[k][ws] = push_sign(wd[k][ws], dk);
-          mag = (dk >= 0.f) ? ec.cpos[k + 1] : mag;
+          // one compare feeds both the bit push (shift-add with the compare
+          // as carry-in) and the level select
+          // the lane mask of one compare is the carry-in of a doubling add
+          // (pushes the bit) and the select of the level
+          const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
+          uint64_t co;
+          const float up = ec.cpos[k + 1];
+          asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3"
+              : "=v"(wd[k][ws]), "=s"(co) : "v"(wd[k][ws]), "s"(below));
+          asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(mag) : "v"(up), "v"(mag), "s"(below));
         }
         const float yh = copysignf(mag, u);
         // the negated residual yh - u g = 2^12 (c[code] - y): one fma with a
@@ -431,11 +438,13 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
     const bool valid = n < N;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    u32x4 raw[8];
+    u32x4 raw[8], dmv[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint4 v = buf[c * 64 + lane];
       raw[c] = u32x4{v.x, v.y, v.z, v.w};
+      const uint4 dm = s_dm[h][c];
+      dmv[c] = u32x4{dm.x, dm.y, dm.z, dm.w};
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
     if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, lane, buf);
@@ -445,8 +454,7 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     f32x16 y[4] = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const uint4 dm = s_dm[h][ks];
-      const u32x4 kv = raw[ks] ^ u32x4{dm.x, dm.y, dm.z, dm.w};
+      const u32x4 kv = raw[ks] ^ dmv[ks];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const bf16x2 p = __builtin_bit_cast(bf16x2, uint32_t(raw[ks][t]));
