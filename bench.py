@@ -344,7 +344,7 @@ def run_search(args):
     enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed), max(2, args.steps // 50), warm=1)
     ws = torch.empty(K.score_topk_workspace_nbytes(cb, 1, Qn, N, 10), dtype=torch.uint8, device=dev)
     tk = _event_times(lambda i: K.score_topk(cb, q, packed, N, 10, ws=ws), 1, warm=1)
-    enc_flops = 2.0 * d * d * N * 3        # three fp16 products per output of S R^T r
+    enc_flops = 2.0 * d * d * N * 2        # two fp16 products per output: S R^T (r_hi + r_lo)
     enc_s = float(enc.mean()) * 1e-3
     out = {"metric": "vectors encoded/s; (vector, query) pairs scored/s with top-10",
            "config": {"workload": wl.name, "vectors": N, "d": d, "bits": bits, "queries": Qn, "k": 10},
