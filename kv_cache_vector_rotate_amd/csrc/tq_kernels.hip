@@ -164,10 +164,13 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
   constexpr int P = B + 1;             // planes per key
   const int h = lane >> 5;
   nu2 = xor32_sum(nu2);
-  const float nu = sqrtf(nu2);
+  // hardware square root and reciprocal (1 ulp): the norms are stored as
+  // half, and a relative error of 1e-7 in the residual scale moves no sign
+  // or code outside the band where the two roundings may differ anyway
+  const float nu = __builtin_amdgcn_sqrtf(nu2);
   const bool zero = !(nu >= 1e-10f);
   const float nsd = nu * ec.sqrt_d;                       // u = y * nu * sqrt(d)
-  const float gsc = zero ? 0.f : kResidualScale / nsd;    // u -> 2^12 y
+  const float gsc = zero ? 0.f : kResidualScale * __builtin_amdgcn_rcpf(nsd);   // u -> 2^12 y
   float tu[K > 1 ? K - 1 : 1];
 #pragma unroll
   for (int k = 0; k < K - 1; ++k) tu[k] = ec.tpos[k] * nsd;
@@ -247,10 +250,8 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
   // opaque offset (no instruction) that keeps them from being hoisted out of
   // the tile loop
   auto read_frag = [&](int kc, half8 (&fhv)[4]) {
-    int ko = kc * 4 * 64;
-    asm volatile("" : "+v"(ko));
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) fhv[jb] = fh[ko + jb * 64];
+    for (int jb = 0; jb < 4; ++jb) fhv[jb] = fh[kc * 4 * 64 + jb * 64];
   };
   read_frag(0, ahi[0]);
   quant_chunk(0, bh[0], bl[0]);
@@ -282,7 +283,7 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
     __builtin_amdgcn_sched_barrier(0);
   }
   rho2 = xor32_sum(rho2);
-  const float rho = zero ? 0.f : sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+  const float rho = zero ? 0.f : __builtin_amdgcn_sqrtf(rho2) * (nu * (1.0f / kResidualScale));
 
   // words were filled oldest-bit-first: bit (r % 32) sits at 31 - r % 32
   uint32_t pw[P - 1][2];
