@@ -209,9 +209,42 @@ def run_decode(args):
         "roofline": roof,
         "rotation": {"key_copies": nk, "packed_copies": npk, "logit_copies": nl},
     }
+    out["append"] = run_append(K, cb, keys0, q, G, N, Qg)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def run_append(K, cb, keys0, q, G, N, Qg, steps=64):
+    """Decode loop on the same shapes: a cache of N + steps records per group,
+    prefilled with the N keys, then per step one new key per group appended
+    (tq_append_keys, T = 1) and the filled prefix scored (tq_score_cache).
+    Event times of each call; the append is launch-latency bound."""
+    import torch
+    Ncap = N + steps
+    cache = torch.empty(K.packed_nbytes(cb, G, Ncap), dtype=torch.uint8, device=keys0.device)
+    K.append_keys(cb, keys0, cache, Ncap, 0)
+    new = [keys0[:, i:i + 1].contiguous() for i in range(steps)]   # stand-in new tokens
+    lg = torch.empty(G * Qg * Ncap, dtype=torch.float32, device=keys0.device)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        L = N + i + 1
+        ev[i][0].record()
+        K.append_keys(cb, new[i], cache, Ncap, L - 1)
+        ev[i][1].record()
+        K.score_cache(cb, q, cache, Ncap, L, out=lg[:G * Qg * L].view(G, Qg, L))
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    ap = np.array([e[0].elapsed_time(e[1]) for e in ev[4:]])
+    sc = np.array([e[1].elapsed_time(e[2]) for e in ev[4:]])
+    return {"note": "one decode step: append 1 key per group into a cache of N + 64 records, "
+                    "then score the filled prefix; the cache fits the Infinity Cache here",
+            "keys_per_append": G,
+            "append_us_median": round(float(np.median(ap)) * 1e3, 2),
+            "append_us_p90": round(float(np.percentile(ap, 90)) * 1e3, 2),
+            "score_cache_us_median": round(float(np.median(sc)) * 1e3, 2),
+            "score_cache_us_p90": round(float(np.percentile(sc, 90)) * 1e3, 2)}
 
 
 def _event_times(fn, reps, warm=2):

@@ -128,6 +128,22 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
 int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype,
                    int64_t G, int64_t N, void* packed, void* stream);
 
+/*
+ * Append new keys to a packed cache at write time (compression happens when
+ * the cache is written; nothing is retrained [ICLR 2026 paper digest,
+ * "実装のポイント"; ai.spot.hk article, online / data-oblivious quantisation]).
+ * keys: [G][T][d] device rows (TQ_F32 or TQ_BF16), typically T = 1 new
+ * token per (batch, KV head) per decode step.  packed: a device buffer laid
+ * out as above for G groups of Ncap records (tq_packed_bytes(cb, G, Ncap)).
+ * Key t of group g is encoded exactly as tq_encode_keys would encode it and
+ * written to record pos + t of group g; no other record is touched.
+ * Requires 0 <= pos and pos + T <= Ncap.  G*T == 0 is a no-op.  d = 128 only.
+ * Allocates nothing.  Errors: TQ_ERR_ARG (also pos + T > Ncap),
+ * TQ_ERR_UNSUPPORTED (d != 128), TQ_ERR_HIP.
+ */
+int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, int64_t G,
+                   int64_t T, void* packed, int64_t Ncap, int64_t pos, void* stream);
+
 /* Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
  * d = 128 (each workgroup prepares its queries on chip; ws may be NULL);
  * G*Qg*(2*1024 + 4)*4 for d = 1024 (the prepared queries 2 R q, 2 S q and
@@ -151,6 +167,18 @@ size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
 int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
                     int32_t Qg, const void* packed, int64_t N, float* logits, void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * tq_score_logits over the first len records of each group of a packed cache
+ * that holds Ncap records per group (the layout tq_append_keys writes into):
+ * logits is float32 [G][Qg][len], same estimator and same kernel as
+ * tq_score_logits (which is the case len = Ncap = N).  Requires
+ * 0 <= len <= Ncap.  d = 128 only; needs no workspace.
+ * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128, Qg > 256,
+ * G > 2^31 - 1), TQ_ERR_HIP.
+ */
+int tq_score_cache(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                   const void* packed, int64_t Ncap, int64_t len, float* logits, void* stream);
 
 /*
  * Vector-search top-k by the same estimated inner product as tq_score_logits

@@ -8,7 +8,8 @@ raise instead of falling back to anything else.
 """
 
 from ._binding import (  # noqa: F401
-    TQ_F32, TQ_BF16, TQError, Codebook, codebook_tables, encode_keys, score_logits,
+    TQ_F32, TQ_BF16, TQError, Codebook, codebook_tables, encode_keys, append_keys, score_logits,
+    score_cache,
     score_topk, score_topk_workspace_nbytes, decode_mse, dense_logits_bf16, packed_nbytes,
     score_workspace_nbytes, library, library_path, EXPORTED_SYMBOLS,
 )

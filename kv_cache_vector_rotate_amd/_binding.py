@@ -18,8 +18,8 @@ library_path = os.path.join(_HERE, "libtq.so")
 # Every entry point declared in include/tq.h.
 EXPORTED_SYMBOLS = (
     "tq_codebook_tables", "tq_make_codebook", "tq_free_codebook", "tq_codebook_export",
-    "tq_codebook_info", "tq_packed_bytes", "tq_encode_keys", "tq_score_workspace_bytes",
-    "tq_score_logits", "tq_score_topk_workspace_bytes", "tq_score_topk", "tq_decode_mse",
+    "tq_codebook_info", "tq_packed_bytes", "tq_encode_keys", "tq_append_keys",
+    "tq_score_workspace_bytes", "tq_score_logits", "tq_score_cache", "tq_score_topk_workspace_bytes", "tq_score_topk", "tq_decode_mse",
     "tq_dense_logits_bf16", "tq_status_string", "tq_last_hip_error",
 )
 
@@ -32,6 +32,8 @@ _SIGS = {
     "tq_codebook_info": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
     "tq_packed_bytes": (_c_sz, [_vp, _c_i64, _c_i64]),
     "tq_encode_keys": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _vp]),
+    "tq_append_keys": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp]),
+    "tq_score_cache": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _c_i64, _vp, _vp]),
     "tq_score_workspace_bytes": (_c_sz, [_vp, _c_i64, _c_i32]),
     "tq_score_logits": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp,
                                        _c_sz, _vp]),
@@ -181,6 +183,44 @@ def encode_keys(cb: Codebook, keys, out=None):
     return out
 
 
+def _need_out(out, n: int):
+    torch = _torch()
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() < n:
+        raise ValueError("logits must be a contiguous float32 tensor of G*Qg*N elements")
+
+
+def append_keys(cb: Codebook, keys, packed, Ncap: int, pos: int):
+    """Encode keys [G, T, d] into records pos .. pos+T-1 of each group of a
+    packed cache holding Ncap records per group (in place)."""
+    _need_cuda(keys, "keys")
+    _need_cuda(packed, "packed")
+    G, T, d = keys.shape
+    if d != cb.d:
+        raise ValueError("key dimension does not match the codebook")
+    if packed.numel() * packed.element_size() < packed_nbytes(cb, G, Ncap):
+        raise ValueError("packed buffer too small for Ncap records per group")
+    _check(library().tq_append_keys(cb.handle, _ptr(keys), _dtype_code(keys), G, T, _ptr(packed),
+                                    Ncap, pos, _stream()), "tq_append_keys")
+    return packed
+
+
+def score_cache(cb: Codebook, q, packed, Ncap: int, length: int, out=None):
+    """q [G, Qg, d] against the first `length` records of a packed cache of
+    Ncap records per group -> float32 [G, Qg, length]."""
+    torch = _torch()
+    _need_cuda(q, "q")
+    _need_cuda(packed, "packed")
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    if out is None:
+        out = torch.empty((G, Qg, length), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * length)
+    _check(library().tq_score_cache(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(packed), Ncap,
+                                    length, _ptr(out), _stream()), "tq_score_cache")
+    return out
+
+
 def score_logits(cb: Codebook, q, packed, N: int, out=None, ws=None):
     """q [G, Qg, d] against packed keys of N per group -> float32 [G, Qg, N]."""
     torch = _torch()
@@ -191,6 +231,7 @@ def score_logits(cb: Codebook, q, packed, N: int, out=None, ws=None):
         raise ValueError("query dimension does not match the codebook")
     if out is None:
         out = torch.empty((G, Qg, N), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * N)
     wsb = score_workspace_nbytes(cb, G, Qg)
     if ws is None:
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)

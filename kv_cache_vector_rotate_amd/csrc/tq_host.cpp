@@ -394,7 +394,23 @@ int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
   if (G * ((N + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;   // 32-key tiles < 2^31
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
-  hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, N, packed,
+  hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, N, N, 0, packed,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, int64_t G, int64_t T,
+                   void* packed, int64_t Ncap, int64_t pos, void* stream) {
+  if (!cb || G < 0 || T < 0 || Ncap < 0 || pos < 0 || (key_dtype != TQ_F32 && key_dtype != TQ_BF16))
+    return TQ_ERR_ARG;
+  if (pos > Ncap || T > Ncap - pos) return TQ_ERR_ARG;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (!keys || !packed || !aligned16(keys) || !aligned16(packed)) return TQ_ERR_ARG;
+  if (cb->d != 128) return TQ_ERR_UNSUPPORTED;
+  if (G * ((T + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, T, Ncap, pos, packed,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
@@ -418,7 +434,23 @@ int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64
   if (!tq::score_supported(*cb)) return TQ_ERR_UNSUPPORTED;
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
-  hipError_t e = tq::launch_score(*cb, q, q_dtype, G, Qg, packed, N, logits, ws,
+  hipError_t e = tq::launch_score(*cb, q, q_dtype, G, Qg, packed, N, N, logits, ws,
+                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_score_cache(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                   const void* packed, int64_t Ncap, int64_t len, float* logits, void* stream) {
+  if (!cb || G < 0 || Qg < 0 || Ncap < 0 || len < 0 || len > Ncap ||
+      (q_dtype != TQ_F32 && q_dtype != TQ_BF16))
+    return TQ_ERR_ARG;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || len == 0 || Qg == 0) return TQ_OK;
+  if (!q || !packed || !logits || !aligned16(q) || !aligned16(packed) || !aligned16(logits))
+    return TQ_ERR_ARG;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_score(*cb, q, q_dtype, G, Qg, packed, len, Ncap, logits, nullptr,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }

@@ -46,10 +46,16 @@ struct Codebook {
 };
 
 // Launchers (tq_kernels.hip).  Return hipSuccess or the launch error.
+// Encode G x N keys into positions [pos, pos + N) of a packed buffer that
+// holds Ncap records per group (tq_encode_keys: Ncap = N, pos = 0; d = 1024
+// supports only that case).
 hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
-                         void* packed, hipStream_t s);
+                         int64_t Ncap, int64_t pos, void* packed, hipStream_t s);
+// Score records [0, N) of a packed buffer holding Ncap per group (d = 1024:
+// Ncap = N only).
 hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
-                        const void* packed, int64_t N, float* logits, void* ws, hipStream_t s);
+                        const void* packed, int64_t N, int64_t Ncap, float* logits, void* ws,
+                        hipStream_t s);
 hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
                          int odtype, hipStream_t s);
 hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg, int64_t N, int d,

@@ -144,16 +144,16 @@ struct TileOut {
 };
 
 template <int B>
-__device__ __forceinline__ void store_tile(const TileOut& o, int lane, int64_t N,
+__device__ __forceinline__ void store_tile(const TileOut& o, int lane, int64_t Ncap,
                                            uint32_t* __restrict__ planes,
                                            uint32_t* __restrict__ norms) {
   constexpr int P = B + 1;
   if (!o.valid) return;
   const int h = lane >> 5;
-  uint32_t* pl = planes + (o.g * P) * N * 4;
+  uint32_t* pl = planes + (o.g * P) * Ncap * 4;
 #pragma unroll
-  for (int p = 0; p < P; ++p) *reinterpret_cast<uint2*>(pl + (p * N + o.n) * 4 + 2 * h) = o.w[p];
-  if (h == 0) norms[o.g * N + o.n] = o.norm;
+  for (int p = 0; p < P; ++p) *reinterpret_cast<uint2*>(pl + (p * Ncap + o.n) * 4 + 2 * h) = o.w[p];
+  if (h == 0) norms[o.g * Ncap + o.n] = o.norm;
 }
 
 template <int B>
@@ -402,7 +402,8 @@ __device__ __forceinline__ void hadamard_frags(int lane, u32x4 (&g)[4]) {
 
 template <int B>
 __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
-    const uint16_t* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
+    const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
+    uint32_t* __restrict__ planes,
     uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
     const uint4* __restrict__ frag, const uint32_t* __restrict__ dmask) {
   __shared__ uint4 s_frag[2048];                   // 32 KB: [kc 8][jb 4][lane 64]
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
     if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, lane, buf);
-    store_tile<B>(prev, lane, N, planes, norms);
+    store_tile<B>(prev, lane, Ncap, planes, norms);
 
     float nu2 = 0.f;
     f32x16 y[4] = {};
@@ -474,9 +475,9 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int a = 0; a < 16; ++a) x[16 * mb + a] = y[mb][a];
-    encode_tail<B>(x, nu2, ec, s_frag, lane, g, n, valid, prev);
+    encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, prev);
   }
-  store_tile<B>(prev, lane, N, planes, norms);
+  store_tile<B>(prev, lane, Ncap, planes, norms);
 }
 
 // ---- float32 keys (register loads, four waves per workgroup).
@@ -485,7 +486,8 @@ constexpr int kEncWaves = kEncThreads / 64;
 
 template <int B>
 __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
-    const float* __restrict__ keys, int64_t G, int64_t N, uint32_t* __restrict__ planes,
+    const float* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
+    uint32_t* __restrict__ planes,
     uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
     const uint4* __restrict__ frag, const uint32_t* __restrict__ flip) {
   __shared__ uint4 s_frag[2048];       // [kc 8][jb 4][lane 64]
@@ -535,8 +537,8 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     }
     butterfly_rest(x, 2);
     TileOut out;
-    encode_tail<B>(x, nu2, ec, s_frag, lane, g, n, valid, out);
-    store_tile<B>(out, lane, N, planes, norms);
+    encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, out);
+    store_tile<B>(out, lane, Ncap, planes, norms);
   }
 }
 
@@ -608,8 +610,8 @@ __device__ __forceinline__ float butterfly_lane32(float y, bool up) {
 template <int B, bool QBF16>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
-    int64_t N, int Qg, int64_t chunk, float* __restrict__ logits, const DevConsts* __restrict__ cst,
-    const float* __restrict__ St) {
+    int64_t N, int64_t Ncap, int Qg, int64_t chunk, float* __restrict__ logits,
+    const DevConsts* __restrict__ cst, const float* __restrict__ St) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
   constexpr int D = B == 3 ? 2 : 3;        // key tiles in flight per wave
@@ -622,8 +624,9 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const int qc = blockIdx.y;
   const int64_t n0 = int64_t(blockIdx.z) * chunk;
   const int64_t n1 = std::min<int64_t>(N, n0 + chunk);   // n0 < n1: the host sizes the grid so
-  const uint4* pg = planes + g * P * N;
-  const uint32_t* ng = norms + g * N;
+  // keys [0, N) of a cache holding Ncap records per group; logits [G][Qg][N]
+  const uint4* pg = planes + g * P * Ncap;
+  const uint32_t* ng = norms + g * Ncap;
 
   // ---- loads: S columns, the R q input, the first D key tiles
   const int seg = wave >> 1;
@@ -652,7 +655,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pg + p * N) + off16));
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pg + p * Ncap) + off16));
       wv[p] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     nv = __builtin_nontemporal_load(
@@ -985,17 +988,18 @@ size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg) {
 }
 
 hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
-                         void* packed, hipStream_t s) {
+                         int64_t Ncap, int64_t pos, void* packed, hipStream_t s) {
   if (cb.d == 1024) return launch_encode_wide(cb, keys, dtype, G, N, packed, s);
   const int64_t ntiles = G * ((N + 31) / 32);
   uint32_t* planes = static_cast<uint32_t*>(packed);
-  uint32_t* norms = planes + G * N * int64_t(cb.bits) * (cb.d / 32);
+  uint32_t* norms = planes + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
   if (dtype == 1) {
     const int64_t want = (ntiles + kEncBfWaves - 1) / kEncBfWaves;
     const int grid = int(std::min<int64_t>(want, int64_t(num_cus())));
     const uint16_t* kb = static_cast<const uint16_t*>(keys);
 #define TQ_ENCB(BB)                                                                              \
   hipLaunchKernelGGL((encode128_bf16_kernel<BB>), dim3(grid), dim3(kEncBfThreads), 0, s, kb, G, N, \
+                     Ncap, pos, \
                      planes, norms, cb.d_consts, cb.d_frag, cb.d_dpair)
     switch (cb.bits - 1) {
       case 1: TQ_ENCB(1); break;
@@ -1009,6 +1013,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
     const float* kf = static_cast<const float*>(keys);
 #define TQ_ENCF(BB)                                                                             \
   hipLaunchKernelGGL((encode128_f32_kernel<BB>), dim3(grid), dim3(kEncThreads), 0, s, kf, G, N, \
+                     Ncap, pos, \
                      planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32)
     switch (cb.bits - 1) {
       case 1: TQ_ENCF(1); break;
@@ -1021,7 +1026,8 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
 }
 
 hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
-                        const void* packed, int64_t N, float* logits, void* ws, hipStream_t s) {
+                        const void* packed, int64_t N, int64_t Ncap, float* logits, void* ws,
+                        hipStream_t s) {
   if (cb.d == 1024) return launch_score_wide(cb, q, qdtype, G, Qg, packed, N, logits, ws, s);
   // enough workgroups for every CU: split each (group, query chunk) unit's
   // keys into ranges of at least 512 keys, a multiple of 64 each
@@ -1035,11 +1041,11 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const dim3 grid{unsigned(G), unsigned(nqc), unsigned(splits)};
   const uint4* planes = static_cast<const uint4*>(packed);
   const uint32_t* norms =
-      static_cast<const uint32_t*>(packed) + G * N * int64_t(cb.bits) * (cb.d / 32);
+      static_cast<const uint32_t*>(packed) + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
   const bool bf = qdtype == 1;
 #define TQ_SC(BB, QB)                                                                   \
   hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, Qg, chunk, logits, cb.d_consts, cb.d_St)
+                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_St)
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;

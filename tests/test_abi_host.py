@@ -61,6 +61,8 @@ def test_argument_validation_without_gpu():
     assert lib.tq_encode_keys(None, None, 0, 1, 1, None, None) == -1
     assert lib.tq_score_logits(None, None, 0, 1, 1, None, 1, None, None, 0, None) == -1
     assert lib.tq_decode_mse(None, None, 1, 1, None, 0, None) == -1
+    assert lib.tq_append_keys(None, None, 0, 1, 1, None, 8, 0, None) == -1
+    assert lib.tq_score_cache(None, None, 0, 1, 1, None, 8, 8, None, None) == -1
     assert lib.tq_codebook_export(None, None, None, None, None, None) == -1
     assert lib.tq_codebook_info(None, None, None, None, None) == -1
     assert lib.tq_packed_bytes(None, 1, 1) == 0
