@@ -46,6 +46,8 @@ __all__ = [
     "packed_nbytes", "decode_mse", "score", "estimate_inner_product",
     "exact_logits", "top_k", "fp16_midpoint_flag", "ZERO_NORM",
     "FLAG_BAND", "kv_bytes_per_vector",
+    "value_quantizer", "ValueEncodeResult", "encode_values", "value_packed_nbytes",
+    "pack_values", "unpack_values", "decode_values", "attention_from_logits", "attention",
 ]
 
 ZERO_NORM = 1e-10      # zero-vector rule [ICLR 2026 digest, 実装の擬似コード]
@@ -458,3 +460,122 @@ def kv_bytes_per_vector(d: int, bits: int):
     key = (bits - 1) * d // 8 + d // 8 + 4
     val = bits * d // 8 + 2
     return key, val
+
+
+# --------------------------------------------------------------------------
+# Value path: MSE-only compression of value vectors and decode attention
+# over packed keys and values.  The community implementation on the Qiita
+# explainer (API table) compresses values with the Stage-1 quantizer alone
+# (rotation + Lloyd-Max, "TurboQuantCompressorMSE"); its byte table counts
+# b-bit value codes plus one half-precision norm per value (reproduced by
+# kv_bytes_per_vector).  Readings: values use the same rotation R as keys
+# and a b-bit Lloyd-Max quantizer for N(0, 1/d) (all b bits, no QJL bit);
+# attention is softmax(scale * logits) V with scale = 1/sqrt(d) by default
+# (scaled dot-product attention; the pages do not restate it).
+# --------------------------------------------------------------------------
+
+_VQ_CACHE = {}
+
+
+def value_quantizer(cb: Codebook):
+    """(levels [2**bits], thresholds [2**bits - 1]) of the b-bit value
+    quantizer: Lloyd-Max for N(0,1) times 1/sqrt(d)."""
+    key = (cb.bits, cb.d)
+    if key not in _VQ_CACHE:
+        lv, th = lloyd_max_std_normal(cb.bits)
+        s = 1.0 / math.sqrt(cb.d)
+        _VQ_CACHE[key] = (lv * s, th * s)
+    return _VQ_CACHE[key]
+
+
+@dataclasses.dataclass
+class ValueEncodeResult:
+    codes: np.ndarray      # [n, d] uint8 level index (bits bits)
+    nu: np.ndarray         # [n] fp64 ||v||
+    nu16: np.ndarray       # [n] float16 stored norm
+    y: np.ndarray          # [n, d] rotated unit value
+    zero: np.ndarray       # [n] bool
+    code_flag: np.ndarray  # [n, d] y within FLAG_BAND of a threshold
+    nu16_flag: np.ndarray  # [n]
+
+
+def encode_values(cb: Codebook, values: np.ndarray) -> ValueEncodeResult:
+    """Per value v: nu = ||v|| (zero record below ZERO_NORM), y = R v / nu,
+    code_i = #{t_j <= y_i} over the b-bit thresholds, nu stored as float16
+    [Qiita explainer, API table (value compression = Stage 1); ICLR 2026
+    digest, Step 1 and the zero-vector rule]."""
+    lv, th = value_quantizer(cb)
+    v = np.asarray(values, dtype=np.float64)
+    n, d = v.shape
+    assert d == cb.d
+    nu = np.sqrt(np.sum(v * v, axis=1))
+    zero = nu < ZERO_NORM
+    safe = np.where(zero, 1.0, nu)
+    H = sylvester_hadamard(d).astype(np.float64)
+    u = (v * cb.delta.astype(np.float64)[None, :]) @ H.T      # exact zeros stay exact
+    y = u / (safe[:, None] * math.sqrt(d))
+    codes = np.searchsorted(th, y, side="right").astype(np.uint8)
+    codes[zero] = 0
+    nu_st = np.where(zero, 0.0, nu)
+    dist = np.min(np.abs(y[:, :, None] - th[None, None, :]), axis=2)
+    return ValueEncodeResult(codes=codes, nu=nu_st, nu16=nu_st.astype(np.float16), y=y, zero=zero,
+                             code_flag=(dist <= FLAG_BAND) & ~zero[:, None],
+                             nu16_flag=fp16_midpoint_flag(nu_st) & ~zero)
+
+
+# Packed value layout: planes uint32 [G][bits][N][d/32] (bit p of the level
+# index, LSB first; bit j of word w is coordinate 32 w + j), then norms
+# uint16 [G][N] = half(nu).
+
+def value_packed_nbytes(cb: Codebook, G: int, N: int) -> int:
+    return G * N * (cb.bits * cb.d // 8 + 2)
+
+
+def pack_values(cb: Codebook, codes, nu16) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    G, N, d = codes.shape
+    planes = np.empty((G, cb.bits, N, d // 32), dtype=np.uint32)
+    for p in range(cb.bits):
+        planes[:, p] = _bits_to_words((codes >> p) & 1)
+    norms = np.asarray(nu16, dtype=np.float16).reshape(G, N).view(np.uint16)
+    return np.concatenate([planes.reshape(-1).view(np.uint8), norms.reshape(-1).view(np.uint8)])
+
+
+def unpack_values(cb: Codebook, buf: np.ndarray, G: int, N: int):
+    """Inverse of :func:`pack_values`: (codes [G, N, d], nu16 [G, N])."""
+    buf = np.ascontiguousarray(np.asarray(buf).reshape(-1).view(np.uint8))
+    assert buf.size == value_packed_nbytes(cb, G, N)
+    d = cb.d
+    nplane = G * cb.bits * N * (d // 32)
+    planes = buf[: nplane * 4].view(np.uint32).reshape(G, cb.bits, N, d // 32)
+    nu16 = buf[nplane * 4:].view(np.float16).reshape(G, N)
+    codes = np.zeros((G, N, d), dtype=np.uint8)
+    for p in range(cb.bits):
+        codes |= (_words_to_bits(planes[:, p]) << p).astype(np.uint8)
+    return codes, nu16
+
+
+def decode_values(cb: Codebook, buf: np.ndarray, G: int, N: int) -> np.ndarray:
+    """v_mse = nu~ R^T c_v[code]: [G, N, d] fp64."""
+    lv, _ = value_quantizer(cb)
+    codes, nu16 = unpack_values(cb, buf, G, N)
+    return nu16.astype(np.float64)[..., None] * (lv[codes] @ cb.R)
+
+
+def attention_from_logits(cb: Codebook, logits: np.ndarray, vbuf: np.ndarray, G: int, N: int,
+                          scale: Optional[float] = None) -> np.ndarray:
+    """out[g, h] = sum_n softmax_n(scale * logits[g, h, :]) v_mse[g, n]:
+    [G, Qg, d] fp64, from the given logits and the packed values."""
+    scale = 1.0 / math.sqrt(cb.d) if scale is None else float(scale)
+    z = scale * np.asarray(logits, dtype=np.float64)
+    z = z - z.max(axis=-1, keepdims=True)
+    w = np.exp(z)
+    p = w / w.sum(axis=-1, keepdims=True)
+    return np.einsum("gqn,gnd->gqd", p, decode_values(cb, vbuf, G, N))
+
+
+def attention(cb: Codebook, kbuf: np.ndarray, vbuf: np.ndarray, G: int, N: int, q: np.ndarray,
+              scale: Optional[float] = None) -> np.ndarray:
+    """Decode attention of queries q [G, Qg, d] over packed keys and values:
+    the estimated logits of :func:`score`, then :func:`attention_from_logits`."""
+    return attention_from_logits(cb, score(cb, kbuf, G, N, q), vbuf, G, N, scale)

@@ -144,7 +144,7 @@ def test_lloyd_max_one_bit_closed_form():
     assert abs(_mse_quad(lv, th) - (1 - 2 / math.pi)) < 1e-10
 
 
-@pytest.mark.parametrize("B", [1, 2, 3])
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
 def test_lloyd_max_fixed_point(B):
     """Boundaries are the midpoints, levels are conditional means (by
     numerical quadrature, independent of the oracle's erfc formula) to 1e-10;
@@ -161,7 +161,7 @@ def test_lloyd_max_fixed_point(B):
         assert abs(c - _cond_mean_quad(a, b)) < 1e-10
 
 
-@pytest.mark.parametrize("B", [1, 2, 3])
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
 def test_lloyd_max_textbook_values(B):
     """Agreement with Max (1960) to the table's 4 significant digits."""
     ref = json.load(open(os.path.join(GOLDEN, "lloyd_max_gaussian.json")))[f"B{B}"]
