@@ -144,6 +144,50 @@ int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype,
 int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, int64_t G,
                    int64_t T, void* packed, int64_t Ncap, int64_t pos, void* stream);
 
+/*
+ * Value records (MSE-only): the community implementation on the Qiita
+ * explainer compresses values with the Stage-1 quantizer alone (API table:
+ * value compressor = rotation + Lloyd-Max), and its byte table counts b-bit
+ * value codes plus one half norm per value.  A value record uses all `bits`
+ * bits of the codebook for a Lloyd-Max code of N(0, 1/d) (2^bits levels),
+ * with the same rotation R; no sketch bit.  Layout for G groups x N values:
+ *   planes: uint32 [G][bits][N][d/32], bit p of the level index, LSB first,
+ *           bit j of word w = coordinate 32*w + j;
+ *   norms:  uint16 [G][N] = half(||v||) (RNE); zero record if ||v|| < 1e-10.
+ *   Total:  G*N*(bits*d/8 + 2) bytes.
+ * d = 128 only.
+ */
+size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
+
+/* Encode G*N values ([G][N][d] device rows, TQ_F32 or TQ_BF16) into value
+ * records.  Per value: nu = ||v||, y = R v / nu, code_i = #{t_j <= y_i} over
+ * the 2^bits - 1 thresholds, nu stored as half.  G*N == 0 is a no-op; nothing
+ * is allocated.  Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128), TQ_ERR_HIP. */
+int tq_encode_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G,
+                     int64_t N, void* vpacked, void* stream);
+
+/* Workspace bytes of tq_attention_decode (the logits plus per-range partial
+ * sums); 0 on bad arguments or d != 128. */
+size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N);
+
+/*
+ * Decode attention over packed keys and values, neither ever dequantised to
+ * memory:  out[g][h] = sum_n softmax_n(scale * logit[g][h][n]) * v_mse[g][n],
+ * logit = the estimator of tq_score_logits, v_mse = nu~ R^T c_v[code]
+ * (scale = 1/sqrt(d) for scaled dot-product attention).  q [G][Qg][d]
+ * (TQ_F32/TQ_BF16), kpacked: key records for N keys per group, vpacked: value
+ * records for N values per group, out float32 [G][Qg][d].  Three launches on
+ * the stream: the score kernel into ws, a value pass over key ranges that keeps
+ * each range's maximum, normaliser and weighted code sum (in the rotated
+ * domain), and a combine that merges the ranges and rotates back with R^T.
+ * ws: tq_attention_workspace_bytes(cb, G, Qg, N) bytes of device memory.
+ * Errors: TQ_ERR_ARG (also N == 0 with G*Qg > 0, scale not finite and > 0),
+ * TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (d != 128, Qg > 256), TQ_ERR_HIP.
+ */
+int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
+                        int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
+                        float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
  * d = 128 (each workgroup prepares its queries on chip; ws may be NULL);
  * G*Qg*(2*1024 + 4)*4 for d = 1024 (the prepared queries 2 R q, 2 S q and

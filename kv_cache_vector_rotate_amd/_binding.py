@@ -21,6 +21,8 @@ EXPORTED_SYMBOLS = (
     "tq_codebook_info", "tq_packed_bytes", "tq_encode_keys", "tq_append_keys",
     "tq_score_workspace_bytes", "tq_score_logits", "tq_score_cache", "tq_score_topk_workspace_bytes", "tq_score_topk", "tq_decode_mse",
     "tq_dense_logits_bf16", "tq_status_string", "tq_last_hip_error",
+    "tq_value_packed_bytes", "tq_encode_values", "tq_attention_workspace_bytes",
+    "tq_attention_decode",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -43,6 +45,11 @@ _SIGS = {
     "tq_decode_mse": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _vp, _c_i32, _vp]),
     "tq_dense_logits_bf16": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i32, _c_i64, _c_i32, _vp, _vp]),
     "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tq_value_packed_bytes": (_c_sz, [_vp, _c_i64, _c_i64]),
+    "tq_encode_values": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _vp]),
+    "tq_attention_workspace_bytes": (_c_sz, [_vp, _c_i64, _c_i32, _c_i64]),
+    "tq_attention_decode": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
+                                           ctypes.c_float, _vp, _vp, _c_sz, _vp]),
     "tq_last_hip_error": (ctypes.c_int, []),
 }
 
@@ -218,6 +225,54 @@ def score_cache(cb: Codebook, q, packed, Ncap: int, length: int, out=None):
     _need_out(out, G * Qg * length)
     _check(library().tq_score_cache(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(packed), Ncap,
                                     length, _ptr(out), _stream()), "tq_score_cache")
+    return out
+
+
+def value_packed_nbytes(cb: Codebook, G: int, N: int) -> int:
+    return int(library().tq_value_packed_bytes(cb.handle, G, N))
+
+
+def encode_values(cb: Codebook, values, out=None):
+    """values [G, N, d] (float32/bfloat16, device) -> value records uint8."""
+    torch = _torch()
+    _need_cuda(values, "values")
+    G, N, d = values.shape
+    if d != cb.d:
+        raise ValueError("value dimension does not match the codebook")
+    nb = value_packed_nbytes(cb, G, N)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=values.device)
+    elif out.numel() * out.element_size() < nb:
+        raise ValueError("value buffer too small")
+    _check(library().tq_encode_values(cb.handle, _ptr(values), _dtype_code(values), G, N, _ptr(out),
+                                      _stream()), "tq_encode_values")
+    return out
+
+
+def attention_workspace_nbytes(cb: Codebook, G: int, Qg: int, N: int) -> int:
+    return int(library().tq_attention_workspace_bytes(cb.handle, G, Qg, N))
+
+
+def attention_decode(cb: Codebook, q, kpacked, vpacked, N: int, scale=None, out=None, ws=None):
+    """softmax(scale * estimated logits) @ v_mse for q [G, Qg, d] over N packed
+    keys and values per group -> float32 [G, Qg, d] (scale 1/sqrt(d) by default)."""
+    torch = _torch()
+    for t, name in ((q, "q"), (kpacked, "kpacked"), (vpacked, "vpacked")):
+        _need_cuda(t, name)
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((G, Qg, d), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * d)
+    wsb = attention_workspace_nbytes(cb, G, Qg, N)
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check(library().tq_attention_decode(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(kpacked),
+                                         _ptr(vpacked), N, scale, _ptr(out), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream()),
+           "tq_attention_decode")
     return out
 
 

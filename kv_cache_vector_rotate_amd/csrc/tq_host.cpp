@@ -205,6 +205,9 @@ void fill_consts(tq::Codebook& cb) {
     asum += acc / L;
   }
   k.alpha_sum = float(asum);
+  const int LV = 1 << cb.bits, KV = LV / 2;
+  for (int i = 0; i < KV - 1; ++i) k.vtpos[i] = float(cb.vthresholds[KV + i]);
+  for (int i = 0; i < LV; ++i) k.vlevels[i] = float(cb.vlevels[i]);
   k.sqrt_d = float(std::sqrt(double(cb.d)));
   k.inv_sqrt_d = float(1.0 / std::sqrt(double(cb.d)));
   k.qjl_scale = float(std::sqrt(M_PI / 2.0) / cb.m);
@@ -227,6 +230,17 @@ int build_tables(tq::Codebook& cb) {
   const double sigma = 1.0 / std::sqrt(double(d));   // N(0,1) -> N(0, 1/d)
   for (double& v : cb.levels) v *= sigma;
   for (double& v : cb.thresholds) v *= sigma;
+  // value records: all `bits` bits go to the Lloyd-Max code (no sketch bit)
+  const int LV = 1 << cb.bits;
+  try {
+    cb.vlevels.resize(LV);
+    cb.vthresholds.resize(LV - 1);
+  } catch (const std::bad_alloc&) {
+    return TQ_ERR_ALLOC;
+  }
+  lloyd_max_normal(LV, cb.vlevels.data(), cb.vthresholds.data());
+  for (double& v : cb.vlevels) v *= sigma;
+  for (double& v : cb.vthresholds) v *= sigma;
   make_delta(cb.seed, d, cb.delta.data());
   make_sketch_rot(cb.seed, m, d, cb.S_rot.data());
   sketch_from_rotated(cb.S_rot.data(), cb.delta.data(), m, d, cb.S.data());
@@ -412,6 +426,50 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
   if (rc != TQ_OK) return rc;
   hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, T, Ncap, pos, packed,
                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N) {
+  if (!cb || G < 0 || N < 0) return 0;
+  return size_t(G) * size_t(N) * size_t(cb->bits * cb->d / 8 + 2);
+}
+
+int tq_encode_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G, int64_t N,
+                     void* vpacked, void* stream) {
+  if (!cb || G < 0 || N < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (G == 0 || N == 0) return TQ_OK;
+  if (!values || !vpacked || !aligned16(values) || !aligned16(vpacked)) return TQ_ERR_ARG;
+  if (cb->d != 128) return TQ_ERR_UNSUPPORTED;
+  if (G * ((N + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_encode_values(*cb, values, dtype, G, N, vpacked,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N) {
+  if (!cb || G <= 0 || Qg <= 0 || N <= 0 || cb->d != 128) return 0;
+  return tq::attention_workspace_bytes(*cb, G, Qg, N);
+}
+
+int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                        const void* kpacked, const void* vpacked, int64_t N, float scale, float* out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return TQ_ERR_ARG;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || G * Qg > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || Qg == 0) return TQ_OK;
+  if (N == 0) return TQ_ERR_ARG;   // softmax over no keys
+  if (!q || !kpacked || !vpacked || !out || !aligned16(q) || !aligned16(kpacked) ||
+      !aligned16(vpacked) || !aligned16(out))
+    return TQ_ERR_ARG;
+  const size_t need = tq::attention_workspace_bytes(*cb, G, Qg, N);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, N, scale, out, ws,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 

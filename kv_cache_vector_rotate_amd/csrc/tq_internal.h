@@ -16,6 +16,8 @@ struct DevConsts {
   float cpos_s[8];    // positive levels c_{L/2}..c_{L-1}, times 2^12 (encoder residual scale)
   float levels[16];   // all L levels, ascending (decoder)
   float alpha[4];     // Walsh coefficients of the levels: s0, s1, s2, s0*s1*s2 terms
+  float vtpos[8];     // value quantizer (bits bits): positive thresholds, ascending
+  float vlevels[16];  // value quantizer: all 2^bits levels, ascending
   float sqrt_d;       // sqrt(d)
   float inv_sqrt_d;   // 1/sqrt(d)
   float qjl_scale;    // sqrt(pi/2) / m
@@ -32,6 +34,7 @@ struct Codebook {
   int device = 0;
   // host tables
   std::vector<double> levels, thresholds, S_rot;
+  std::vector<double> vlevels, vthresholds;   // value quantizer: 2^bits levels
   std::vector<int8_t> delta;
   std::vector<double> S;
   DevConsts consts{};
@@ -61,6 +64,15 @@ hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int6
 hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg, int64_t N, int d,
                              float* logits, hipStream_t s);
 size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg);
+// Value records (d = 128): planes uint32 [G][bits][N][4], then uint16 half norms [G][N].
+hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtype, int64_t G,
+                                int64_t N, void* vpacked, hipStream_t s);
+// Decode attention over packed keys and values (d = 128): logits into the
+// workspace, a value pass over key ranges, a combine with the rotation back.
+size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N);
+hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                            const void* kpacked, const void* vpacked, int64_t N, float scale,
+                            float* out, void* ws, hipStream_t s);
 // d = 1024 (tq_wide.hip)
 hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                               void* packed, hipStream_t s);

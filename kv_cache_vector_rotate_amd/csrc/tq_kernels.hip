@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 namespace tq {
 namespace {
@@ -332,6 +333,91 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
   out.valid = valid;
 }
 
+// ---- values: MSE-only records (b-bit level index, one half norm).
+// Same lane layout and rotation as the keys; each positive threshold is one
+// compare whose lane mask is the carry-in of a doubling add (the bit push),
+// the sign bit is pushed with v_alignbit, and the level index bits follow
+// from the thermometer bits: with d_k = [|y| >= t_k], bit j of the magnitude
+// index is the XOR of d_k over k with (k + 1) divisible by 2^j, and the
+// stored bit j is that XOR the sign (negative levels mirror the positive
+// ones); the top bit is the complement of the sign.
+struct ValOut {
+  uint2 w[4];        // words (2h, 2h+1) of planes 0..BV-1
+  uint32_t norm;     // half(nu) in the low 16 bits
+  int64_t g, n;
+  bool valid;
+};
+
+template <int BV>
+__device__ __forceinline__ void store_vtile(const ValOut& o, int lane, int64_t Ncap,
+                                            uint32_t* __restrict__ planes,
+                                            uint16_t* __restrict__ norms) {
+  if (!o.valid) return;
+  const int h = lane >> 5;
+  uint32_t* pl = planes + (o.g * BV) * Ncap * 4;
+#pragma unroll
+  for (int p = 0; p < BV; ++p) *reinterpret_cast<uint2*>(pl + (p * Ncap + o.n) * 4 + 2 * h) = o.w[p];
+  if (h == 0) norms[o.g * Ncap + o.n] = uint16_t(o.norm);
+}
+
+template <int BV>
+__device__ __forceinline__ void value_tail(const float (&x)[64], float nu2,
+                                           const DevConsts* __restrict__ cst, int lane, int64_t g,
+                                           int64_t n, bool valid, ValOut& out) {
+  constexpr int KV = 1 << (BV - 1);    // levels on the positive half
+  nu2 = xor32_sum(nu2);
+  const float nu = __builtin_amdgcn_sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * cst->sqrt_d;
+  float tu[KV > 1 ? KV - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < KV - 1; ++k) tu[k] = cst->vtpos[k] * nsd;
+  uint32_t wu[2] = {0u, 0u};
+  uint32_t wd[KV > 1 ? KV - 1 : 1][2];
+#pragma unroll
+  for (int k = 0; k < (KV > 1 ? KV - 1 : 1); ++k) wd[k][0] = wd[k][1] = 0u;
+#pragma unroll
+  for (int r = 0; r < 64; ++r) {
+    const int ws = r >> 5;
+    const float u = x[r];
+    const float a = fabsf(u);
+    wu[ws] = push_sign(wu[ws], u);
+#pragma unroll
+    for (int k = 0; k < KV - 1; ++k) {
+      const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
+      uint64_t co;
+      asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3"
+          : "=v"(wd[k][ws]), "=s"(co) : "v"(wd[k][ws]), "s"(below));
+    }
+  }
+  const bool keep = valid && !zero;
+  uint32_t pw[BV][2];
+#pragma unroll
+  for (int ws = 0; ws < 2; ++ws) {
+    // words were filled oldest-bit-first: bit (r % 32) sits at 31 - r % 32
+    const uint32_t sg = __builtin_bitreverse32(wu[ws]);       // 1 = negative
+    pw[BV - 1][ws] = ~sg;
+#pragma unroll
+    for (int j = 0; j < BV - 1; ++j) {
+      uint32_t e = 0u;   // XOR of the "below" bits (complements of d_k); odd count
+#pragma unroll
+      for (int k = 0; k < KV - 1; ++k)
+        if (((k + 1) & ((1 << j) - 1)) == 0) e ^= __builtin_bitreverse32(wd[k][ws]);
+      pw[j][ws] = ~(e ^ sg);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < BV; ++p) {
+    // (word h, word 2+h) of each lane -> (words 2h, 2h+1): swap across halves
+    auto pr = __builtin_amdgcn_permlane32_swap(pw[p][0], pw[p][1], false, false);
+    out.w[p] = make_uint2(keep ? uint32_t(pr[0]) : 0u, keep ? uint32_t(pr[1]) : 0u);
+  }
+  out.norm = keep ? uint32_t(f2h_bits(nu)) : 0u;
+  out.g = g;
+  out.n = n;
+  out.valid = valid;
+}
+
 // ---- bf16 keys.  Eight waves per workgroup, one workgroup per CU.  Each
 // wave owns an 8 KB LDS buffer that the next tile's keys stream into
 // (global_load_lds, 16 B per lane, no registers held) while the current tile
@@ -400,13 +486,14 @@ __device__ __forceinline__ void hadamard_frags(int lane, u32x4 (&g)[4]) {
   g[3] = g[1] ^ 0x80008000u;
 }
 
-template <int B>
+// VAL: value records (B = value bits, no sketch; norms are uint16 halves).
+template <int B, bool VAL>
 __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
     uint32_t* __restrict__ planes,
-    uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
+    void* __restrict__ norms_, const DevConsts* __restrict__ cst,
     const uint4* __restrict__ frag, const uint32_t* __restrict__ dmask) {
-  __shared__ uint4 s_frag[2048];                   // 32 KB: [kc 8][jb 4][lane 64]
+  __shared__ uint4 s_frag[VAL ? 1 : 2048];         // 32 KB: [kc 8][jb 4][lane 64]
   __shared__ uint4 s_raw[kEncBfWaves][8 * 64];     // 64 KB: per-wave key tile
   __shared__ uint4 s_dm[2][8];                     // D as bf16 sign bits, [k-half][k-step]
 
@@ -419,7 +506,8 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
   uint32_t tile = blockIdx.x * kEncBfWaves + wave;
   uint4* buf = s_raw[wave];
   if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, lane, buf);
-  for (int i = tid; i < 2048; i += kEncBfThreads) s_frag[i] = frag[i];
+  if constexpr (!VAL)
+    for (int i = tid; i < 2048; i += kEncBfThreads) s_frag[i] = frag[i];
   if (tid < 16) reinterpret_cast<uint4*>(s_dm)[tid] = reinterpret_cast<const uint4*>(dmask)[tid];
   EncConsts ec;
   load_enc_consts(cst, ec);
@@ -432,7 +520,14 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
   // operations in flight), copy them to registers, start the next tile's DMA,
   // write the previous tile's results, then encode this tile.  The compiler
   // does not track the loop-carried DMA, hence the explicit wait.
-  TileOut prev;
+  using Out = std::conditional_t<VAL, ValOut, TileOut>;
+  auto store = [&](const Out& o) {
+    if constexpr (VAL)
+      store_vtile<B>(o, lane, Ncap, planes, static_cast<uint16_t*>(norms_));
+    else
+      store_tile<B>(o, lane, Ncap, planes, static_cast<uint32_t*>(norms_));
+  };
+  Out prev;
   prev.valid = false;
   for (; tile < ntiles; tile += stride) {
     const uint32_t gt = tile / tpg;
@@ -450,7 +545,7 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
     if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, lane, buf);
-    store_tile<B>(prev, lane, Ncap, planes, norms);
+    store(prev);
 
     float nu2 = 0.f;
     f32x16 y[4] = {};
@@ -475,26 +570,30 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int a = 0; a < 16; ++a) x[16 * mb + a] = y[mb][a];
-    encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, prev);
+    if constexpr (VAL)
+      value_tail<B>(x, nu2, cst, lane, g, pos + n, valid, prev);
+    else
+      encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, prev);
   }
-  store_tile<B>(prev, lane, Ncap, planes, norms);
+  store(prev);
 }
 
 // ---- float32 keys (register loads, four waves per workgroup).
 constexpr int kEncThreads = 256;
 constexpr int kEncWaves = kEncThreads / 64;
 
-template <int B>
+template <int B, bool VAL>
 __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     const float* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
     uint32_t* __restrict__ planes,
-    uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst,
+    void* __restrict__ norms_, const DevConsts* __restrict__ cst,
     const uint4* __restrict__ frag, const uint32_t* __restrict__ flip) {
-  __shared__ uint4 s_frag[2048];       // [kc 8][jb 4][lane 64]
+  __shared__ uint4 s_frag[VAL ? 1 : 2048];       // [kc 8][jb 4][lane 64]
   __shared__ uint32_t s_flip[128];
 
   const int tid = threadIdx.x;
-  for (int i = tid; i < 2048; i += kEncThreads) s_frag[i] = frag[i];
+  if constexpr (!VAL)
+    for (int i = tid; i < 2048; i += kEncThreads) s_frag[i] = frag[i];
   for (int i = tid; i < 128; i += kEncThreads) s_flip[i] = flip[i];
   EncConsts ec;
   load_enc_consts(cst, ec);
@@ -536,9 +635,15 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
       x[r + 1] = (a - b) + 0.0f;
     }
     butterfly_rest(x, 2);
-    TileOut out;
-    encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, out);
-    store_tile<B>(out, lane, Ncap, planes, norms);
+    if constexpr (VAL) {
+      ValOut out;
+      value_tail<B>(x, nu2, cst, lane, g, pos + n, valid, out);
+      store_vtile<B>(out, lane, Ncap, planes, static_cast<uint16_t*>(norms_));
+    } else {
+      TileOut out;
+      encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, out);
+      store_tile<B>(out, lane, Ncap, planes, static_cast<uint32_t*>(norms_));
+    }
   }
 }
 
@@ -976,6 +1081,156 @@ __global__ __launch_bounds__(256) void dense128_kernel(const uint16_t* __restric
   }
 }
 
+// ============================================================== decode attention, d = 128
+// out[g][h] = sum_n softmax_n(scale * logit[g][h][n]) v_mse[g][n] over packed
+// values v_mse = nu~ R^T c_v[code] (value records: b-bit Lloyd-Max codes and
+// a half norm).  R^T is linear, so the weighted sum is formed in the rotated
+// domain, A = sum_n w_n nu~_n c_v[code_n], and rotated back once per query.
+// Split over key ranges (flash-decoding style): each range keeps its own
+// maximum m_s, normaliser Z_s = sum exp(scale l - m_s) and A_s; a combine step
+// rescales by exp(m_s - M).
+constexpr int kAttnThreads = 256;
+constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, query chunk, range)
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Grid (G, query chunks of 4, key ranges).  Thread t: while weighting, key
+// t % 64 of a 64-key block for query t / 64; while accumulating, bit t % 32
+// of each of the four 32-coordinate words (coordinates t % 32 + 32 w) of
+// every eighth key of the block, starting at key t / 32.
+template <int BV>
+__global__ __launch_bounds__(kAttnThreads) void attn_values128_kernel(
+    const float* __restrict__ logits, const uint4* __restrict__ vplanes,
+    const uint16_t* __restrict__ vnorms, int64_t N, int Qg, int64_t chunk, float scale,
+    const DevConsts* __restrict__ cst, float* __restrict__ part) {
+  __shared__ f32x4 s_w[64];                 // weights of the block's keys, 4 queries
+  __shared__ uint4 s_pl[BV][64];            // value plane words of the block's keys
+  __shared__ float s_lev[16];
+  __shared__ float s_red[8][32][17];        // [key lane][coordinate bit][word x query], padded
+  __shared__ float s_m[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t g = blockIdx.x;
+  const int qc = blockIdx.y;
+  const int64_t n0 = int64_t(blockIdx.z) * chunk;
+  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
+  if (tid < 16) s_lev[tid] = cst->vlevels[tid];
+
+  // ---- range maximum of each query's scaled logits (wave q: query q)
+  const int qh = qc * 4 + wave;
+  const bool qlive = qh < Qg;
+  const float* lrow = logits + (g * Qg + (qlive ? qh : 0)) * N;
+  float mx = -INFINITY;
+  if (qlive)
+    for (int64_t n = n0 + lane; n < n1; n += 64) mx = fmaxf(mx, scale * lrow[n]);
+  mx = wave_max(mx);
+  if (!qlive) mx = 0.f;
+
+  float zs = 0.f;                    // this thread's part of Z for query `wave`
+  float acc[4][4] = {};              // [word][query]
+  const int cs = tid & 31, kq = tid >> 5;
+  for (int64_t nb = n0; nb < n1; nb += 64) {
+    {
+      const int64_t n = nb + lane;
+      const bool in = n < n1;
+      const int64_t nc = in ? n : n1 - 1;
+      float w = 0.f;
+      if (in && qlive) {
+        const float e = __expf(scale * lrow[n] - mx);
+        zs += e;
+        w = e * h2f_bits(vnorms[g * N + n]);
+      }
+      reinterpret_cast<float*>(&s_w[lane])[wave] = w;
+      if (wave < BV) s_pl[wave][lane] = vplanes[(g * BV + wave) * N + nc];
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int j = 0; j < 8; ++j) {
+      const int kk = kq + 8 * j;
+      const f32x4 wv = s_w[kk];
+      uint32_t sh[BV][4];
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        const uint4 pw = s_pl[p][kk];
+        sh[p][0] = pw.x >> cs; sh[p][1] = pw.y >> cs; sh[p][2] = pw.z >> cs; sh[p][3] = pw.w >> cs;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t code = 0;
+#pragma unroll
+        for (int p = 0; p < BV; ++p) code |= (sh[p][w] & 1u) << p;
+        const float lv = s_lev[code];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[w][q] = fmaf(wv[q], lv, acc[w][q]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- reduce over the eight key lanes, write the range's partial state
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_red[kq][cs][4 * w + q] = acc[w][q];
+  zs = wave_sum(zs);
+  if (lane == 0) { s_m[0][wave] = mx; s_m[1][wave] = zs; }
+  __syncthreads();
+  float* out = part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
+  if (tid < 8) out[tid] = s_m[tid >> 2][tid & 3];
+  for (int e = tid; e < 512; e += kAttnThreads) {
+    const int q = e >> 7, i = e & 127, w = i >> 5, c = i & 31;
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a += s_red[k][c][4 * w + q];
+    out[8 + e] = a;                 // A[q][i], coordinate i = 32 w + c
+  }
+}
+
+// One wave per (group, query): merge the ranges, divide by Z, rotate back
+// with R^T = D H / sqrt(d).  Lane L holds coordinates L and L + 64.
+__global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __restrict__ part,
+                                                              int Qg, int nqc, int splits,
+                                                              const DevConsts* __restrict__ cst,
+                                                              float* __restrict__ out) {
+  const int lane = threadIdx.x;
+  const int64_t gh = blockIdx.x;
+  const int64_t g = gh / Qg;
+  const int h = int(gh - g * Qg), qc = h >> 2, q = h & 3;
+  const float* base = part + (g * nqc + qc) * int64_t(splits) * kAttnPart;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * kAttnPart + q]);
+  float Z = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = base + s * kAttnPart;
+    const float f = __expf(ps[q] - M);
+    Z = fmaf(f, ps[4 + q], Z);
+    a0 = fmaf(f, ps[8 + q * 128 + lane], a0);
+    a1 = fmaf(f, ps[8 + q * 128 + 64 + lane], a1);
+  }
+  const float inv = 1.0f / Z;
+  float y0 = a0 * inv + a1 * inv, y1 = a0 * inv - a1 * inv;
+  y0 = butterfly_lane<1>(y0, lane & 1);   y1 = butterfly_lane<1>(y1, lane & 1);
+  y0 = butterfly_lane<2>(y0, lane & 2);   y1 = butterfly_lane<2>(y1, lane & 2);
+  y0 = butterfly_lane<4>(y0, lane & 4);   y1 = butterfly_lane<4>(y1, lane & 4);
+  y0 = butterfly_lane<8>(y0, lane & 8);   y1 = butterfly_lane<8>(y1, lane & 8);
+  y0 = butterfly_lane<16>(y0, lane & 16); y1 = butterfly_lane<16>(y1, lane & 16);
+  y0 = butterfly_lane32(y0, lane & 32);   y1 = butterfly_lane32(y1, lane & 32);
+  const float sc = cst->inv_sqrt_d;
+  const uint32_t f0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
+  const uint32_t f1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
+  float* o = out + gh * 128;
+  o[lane] = (f0 ? -y0 : y0) * sc;
+  o[64 + lane] = (f1 ? -y1 : y1) * sc;
+}
+
 }  // namespace
 
 bool encode_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
@@ -998,7 +1253,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
     const int grid = int(std::min<int64_t>(want, int64_t(num_cus())));
     const uint16_t* kb = static_cast<const uint16_t*>(keys);
 #define TQ_ENCB(BB)                                                                              \
-  hipLaunchKernelGGL((encode128_bf16_kernel<BB>), dim3(grid), dim3(kEncBfThreads), 0, s, kb, G, N, \
+  hipLaunchKernelGGL((encode128_bf16_kernel<BB, false>), dim3(grid), dim3(kEncBfThreads), 0, s, kb, G, N, \
                      Ncap, pos, \
                      planes, norms, cb.d_consts, cb.d_frag, cb.d_dpair)
     switch (cb.bits - 1) {
@@ -1012,7 +1267,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
     const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 2));
     const float* kf = static_cast<const float*>(keys);
 #define TQ_ENCF(BB)                                                                             \
-  hipLaunchKernelGGL((encode128_f32_kernel<BB>), dim3(grid), dim3(kEncThreads), 0, s, kf, G, N, \
+  hipLaunchKernelGGL((encode128_f32_kernel<BB, false>), dim3(grid), dim3(kEncThreads), 0, s, kf, G, N, \
                      Ncap, pos, \
                      planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32)
     switch (cb.bits - 1) {
@@ -1022,6 +1277,91 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
     }
 #undef TQ_ENCF
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtype, int64_t G,
+                                int64_t N, void* vpacked, hipStream_t s) {
+  const int64_t ntiles = G * ((N + 31) / 32);
+  uint32_t* planes = static_cast<uint32_t*>(vpacked);
+  uint16_t* norms = reinterpret_cast<uint16_t*>(planes + G * N * int64_t(cb.bits) * (cb.d / 32));
+  if (dtype == 1) {
+    const int64_t want = (ntiles + kEncBfWaves - 1) / kEncBfWaves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus())));
+    const uint16_t* vb = static_cast<const uint16_t*>(values);
+#define TQ_VB(BB)                                                                                  \
+  hipLaunchKernelGGL((encode128_bf16_kernel<BB, true>), dim3(grid), dim3(kEncBfThreads), 0, s, vb, \
+                     G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag, cb.d_dpair)
+    switch (cb.bits) {
+      case 2: TQ_VB(2); break;
+      case 3: TQ_VB(3); break;
+      default: TQ_VB(4); break;
+    }
+#undef TQ_VB
+  } else {
+    const int64_t want = (ntiles + kEncWaves - 1) / kEncWaves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 2));
+    const float* vf = static_cast<const float*>(values);
+#define TQ_VF(BB)                                                                                \
+  hipLaunchKernelGGL((encode128_f32_kernel<BB, true>), dim3(grid), dim3(kEncThreads), 0, s, vf, \
+                     G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32)
+    switch (cb.bits) {
+      case 2: TQ_VF(2); break;
+      case 3: TQ_VF(3); break;
+      default: TQ_VF(4); break;
+    }
+#undef TQ_VF
+  }
+  return hipGetLastError();
+}
+
+// Key ranges of the decode-attention value pass: multiples of 64 keys,
+// enough (group, query chunk, range) workgroups for four per compute unit.
+static void attn_split(int64_t G, int Qg, int64_t N, int64_t& chunk, int64_t& splits) {
+  const int64_t units = G * ((Qg + 3) / 4);
+  const int64_t want_wg = int64_t(num_cus()) * 4;
+  int64_t want = std::max<int64_t>(1, (want_wg + units - 1) / units);
+  want = std::min<int64_t>(want, std::max<int64_t>(1, (N + 255) / 256));
+  chunk = ((N + want - 1) / want + 63) / 64 * 64;
+  splits = (N + chunk - 1) / chunk;
+}
+
+size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N) {
+  (void)cb;
+  int64_t chunk, splits;
+  attn_split(G, Qg, N, chunk, splits);
+  const size_t lg = (size_t(G) * Qg * N * 4 + 255) / 256 * 256;
+  return lg + size_t(G) * ((Qg + 3) / 4) * splits * kAttnPart * 4;
+}
+
+hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                            const void* kpacked, const void* vpacked, int64_t N, float scale,
+                            float* out, void* ws, hipStream_t s) {
+  int64_t chunk, splits;
+  attn_split(G, Qg, N, chunk, splits);
+  float* logits = static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         (size_t(G) * Qg * N * 4 + 255) / 256 * 256);
+  hipError_t e = launch_score(cb, q, qdtype, G, Qg, kpacked, N, N, logits, nullptr, s);
+  if (e != hipSuccess) return e;
+  const int nqc = (Qg + 3) / 4;
+  const uint4* vpl = static_cast<const uint4*>(vpacked);
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(static_cast<const uint32_t*>(vpacked) +
+                                                         G * N * int64_t(cb.bits) * (cb.d / 32));
+  const dim3 grid{unsigned(G), unsigned(nqc), unsigned(splits)};
+#define TQ_AV(BB)                                                                                 \
+  hipLaunchKernelGGL((attn_values128_kernel<BB>), grid, dim3(kAttnThreads), 0, s, logits, vpl, vn, \
+                     N, Qg, chunk, scale, cb.d_consts, part)
+  switch (cb.bits) {
+    case 2: TQ_AV(2); break;
+    case 3: TQ_AV(3); break;
+    default: TQ_AV(4); break;
+  }
+#undef TQ_AV
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine128_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, part, Qg, nqc,
+                     int(splits), cb.d_consts, out);
   return hipGetLastError();
 }
 

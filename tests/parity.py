@@ -78,3 +78,34 @@ def check_logits(gpu, ref, q, keys_norm):
     worst = np.max(err / np.maximum(tol, 1e-300)) if err.size else 0.0
     assert np.all(err <= tol), f"logit mismatch: worst |delta|/tol = {worst:.3g}"
     return float(worst)
+
+
+def check_values(cb, values, gpu_codes, gpu_nu16):
+    """Value records (MSE-only): the code and half-norm rules above."""
+    ref = O.encode_values(cb, values)
+    n, d = ref.codes.shape
+    gc = np.asarray(gpu_codes).reshape(n, d).astype(np.int16)
+    rc = ref.codes.astype(np.int16)
+    diff = gc != rc
+    bad = diff & ~ref.code_flag
+    assert not bad.any(), f"{int(bad.sum())} unflagged value-code mismatches at {np.argwhere(bad)[:5].tolist()}"
+    assert np.all(np.abs(gc - rc)[diff] <= 1), "flagged value-code mismatch beyond an adjacent level"
+    assert _rate_ok(int(diff.sum()), diff.size), f"{int(diff.sum())} value-code mismatches in {diff.size}"
+    gb = np.asarray(gpu_nu16).reshape(n).view(np.uint16).astype(np.int32)
+    rb = ref.nu16.view(np.uint16).astype(np.int32)
+    nd = gb != rb
+    assert not (nd & ~ref.nu16_flag).any(), "value norm: unflagged half mismatch"
+    assert np.all(np.abs(gb - rb)[nd] <= 1), "value norm: flagged half mismatch beyond one ulp"
+    TOTALS["code_mismatch"] += int(diff.sum())
+    TOTALS["code_entries"] += int(diff.size)
+    return ref
+
+
+def attention_tolerance(vhat, extra=0.0):
+    """Bound for |out_gpu - out_oracle| per element when both use the same
+    logits: the weights carry fp32 exponentials (relative error ~1e-6) and the
+    sums fp32 rounding, so every output element is within 5e-5 of the largest
+    decoded value norm of its group (plus `extra`, a relative bound on the
+    softmax weights when the logits themselves differ)."""
+    vmax = np.max(np.linalg.norm(vhat, axis=-1), axis=-1)          # [G]
+    return ((5e-5 + extra) * vmax)[:, None, None]
