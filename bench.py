@@ -210,6 +210,7 @@ def run_decode(args):
         "rotation": {"key_copies": nk, "packed_copies": npk, "logit_copies": nl},
     }
     out["append"] = run_append(K, cb, keys0, q, G, N, Qg)
+    out["decode_attention"] = run_attention(K, cb, keys0, q, G, N, Qg, packed, npk, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -245,6 +246,34 @@ def run_append(K, cb, keys0, q, G, N, Qg, steps=64):
             "append_us_p90": round(float(np.percentile(ap, 90)) * 1e3, 2),
             "score_cache_us_median": round(float(np.median(sc)) * 1e3, 2),
             "score_cache_us_p90": round(float(np.percentile(sc, 90)) * 1e3, 2)}
+
+
+def run_attention(K, cb, keys0, q, G, N, Qg, packed, npk, steps):
+    """Value path on the same shapes: value records for the cache (values drawn
+    like the keys: the key rows in reverse order), then decode attention of the
+    step's queries over packed keys and values, with both caches rotating past
+    the Infinity Cache.  Reports the value encoder and the three attention
+    launches (score, value pass, combine) by HIP events."""
+    import torch
+    vals = keys0.flip(1).contiguous()
+    vbytes = K.value_packed_nbytes(cb, G, N)
+    nv = max(3, -(-3 * (256 << 20) // vbytes))
+    vpk = [K.encode_values(cb, vals) for _ in range(nv)]
+    ws = torch.empty(max(16, K.attention_workspace_nbytes(cb, G, Qg, N)), dtype=torch.uint8,
+                     device=keys0.device)
+    out = torch.empty((G, Qg, cb.d), dtype=torch.float32, device=keys0.device)
+    enc = _event_times(lambda i: K.encode_values(cb, vals, out=vpk[i % nv]), steps)
+    att = _event_times(lambda i: K.attention_decode(cb, q, packed[i % npk], vpk[i % nv], N, out=out,
+                                                    ws=ws), steps)
+    key_bytes = keys0.numel() * keys0.element_size()
+    kbytes = K.packed_nbytes(cb, G, N)
+    # attention: read key and value records and the queries, write and read
+    # back the logits, write the outputs (the range partials stay in cache)
+    att_alg = kbytes + vbytes + q.numel() * q.element_size() + 2 * G * Qg * N * 4 + G * Qg * cb.d * 4
+    return {"values_encode": _stats(enc, key_bytes + vbytes, G * N, "values"),
+            "attention": _stats(att, att_alg, G * N, "keys"),
+            "value_record_bytes": int(vbytes // (G * N)),
+            "note": "attention = score kernel (logits to workspace) + value pass + combine"}
 
 
 def _event_times(fn, reps, warm=2):

@@ -1104,93 +1104,129 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Grid (G, query chunks of 4, key ranges).  Thread t: while weighting, key
-// t % 64 of a 64-key block for query t / 64; while accumulating, bit t % 32
-// of each of the four 32-coordinate words (coordinates t % 32 + 32 w) of
-// every eighth key of the block, starting at key t / 32.
+// t % 64 of a 64-key block for query t / 64; while accumulating, the four
+// adjacent coordinates 4 (t % 32) .. 4 (t % 32) + 3 of every eighth key of the
+// block, starting at key t / 32.  A 2^(2 BV)-entry table maps the BV plane
+// bits of two adjacent coordinates to their two levels, so each pair costs one
+// 8-byte LDS read after BV two-bit field extractions.
 template <int BV>
 __global__ __launch_bounds__(kAttnThreads) void attn_values128_kernel(
     const float* __restrict__ logits, const uint4* __restrict__ vplanes,
     const uint16_t* __restrict__ vnorms, int64_t N, int Qg, int64_t chunk, float scale,
     const DevConsts* __restrict__ cst, float* __restrict__ part) {
-  __shared__ f32x4 s_w[64];                 // weights of the block's keys, 4 queries
-  __shared__ uint4 s_pl[BV][64];            // value plane words of the block's keys
-  __shared__ float s_lev[16];
-  __shared__ float s_red[8][32][17];        // [key lane][coordinate bit][word x query], padded
-  __shared__ float s_m[4][4];
+  constexpr int NL = 1 << (2 * BV);
+  __shared__ f32x4 s_w[2][64];              // weights of a block's keys, 4 queries (double-buffered)
+  __shared__ uint32_t s_pl[2][BV][64][4];   // value plane words of a block's keys
+  __shared__ float2 s_lut[NL];              // pair of levels by plane-major 2-bit fields
+  __shared__ float s_red[8][32][17];        // [key lane][coordinate quad][4 coords x 4 queries]
+  __shared__ float s_m[2][4];
+  __shared__ float s_f[2][4];               // rescale of the accumulators per block and query
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t g = blockIdx.x;
   const int qc = blockIdx.y;
   const int64_t n0 = int64_t(blockIdx.z) * chunk;
   const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
-  if (tid < 16) s_lev[tid] = cst->vlevels[tid];
+  for (int j = tid; j < NL; j += kAttnThreads) {
+    int ca = 0, cb = 0;
+#pragma unroll
+    for (int p = 0; p < BV; ++p) {
+      ca |= ((j >> (2 * p)) & 1) << p;
+      cb |= ((j >> (2 * p + 1)) & 1) << p;
+    }
+    s_lut[j] = make_float2(cst->vlevels[ca], cst->vlevels[cb]);
+  }
 
-  // ---- range maximum of each query's scaled logits (wave q: query q)
+  // Online softmax: wave q keeps query q's running maximum mx (the same in
+  // every lane) and normaliser; when a block raises the maximum, every
+  // accumulator of that query is rescaled by exp(old - new) before the block
+  // is added.
   const int qh = qc * 4 + wave;
   const bool qlive = qh < Qg;
   const float* lrow = logits + (g * Qg + (qlive ? qh : 0)) * N;
   float mx = -INFINITY;
-  if (qlive)
-    for (int64_t n = n0 + lane; n < n1; n += 64) mx = fmaxf(mx, scale * lrow[n]);
-  mx = wave_max(mx);
-  if (!qlive) mx = 0.f;
-
   float zs = 0.f;                    // this thread's part of Z for query `wave`
-  float acc[4][4] = {};              // [word][query]
-  const int cs = tid & 31, kq = tid >> 5;
-  for (int64_t nb = n0; nb < n1; nb += 64) {
+  float acc[4][4] = {};              // [coordinate][query]
+  const int cq = tid & 31, kq = tid >> 5;
+  const int wsel = cq >> 3, sh = 4 * (cq & 7);   // word and bit of the coordinate quad
+  const char* lut = reinterpret_cast<const char*>(s_lut);
+  // the next block's logit, norm and plane words are loaded into registers
+  // while the current block is accumulated (one barrier per block: a buffer
+  // is rewritten only after every thread has passed the next barrier)
+  float lg_n = 0.f;
+  uint32_t nv_n = 0;
+  uint4 pl_n = make_uint4(0, 0, 0, 0);
+  auto load_block = [&](int64_t nb) {
+    const int64_t nc = std::min<int64_t>(nb + lane, n1 - 1);
+    lg_n = lrow[nc];
+    nv_n = vnorms[g * N + nc];
+    if (wave < BV) pl_n = vplanes[(g * BV + wave) * N + nc];
+  };
+  load_block(n0);
+  int buf = 0;
+  for (int64_t nb = n0; nb < n1; nb += 64, buf ^= 1) {
     {
-      const int64_t n = nb + lane;
-      const bool in = n < n1;
-      const int64_t nc = in ? n : n1 - 1;
+      const bool in = nb + lane < n1 && qlive;
+      const float z = scale * lg_n;
+      const float mnew = fmaxf(mx, wave_max(in ? z : -INFINITY));
+      const float f = qlive ? __expf(mx - mnew) : 1.f;     // exp(-inf) = 0 on the first block
+      mx = qlive ? mnew : 0.f;
       float w = 0.f;
-      if (in && qlive) {
-        const float e = __expf(scale * lrow[n] - mx);
+      zs *= f;
+      if (in) {
+        const float e = __expf(z - mx);
         zs += e;
-        w = e * h2f_bits(vnorms[g * N + n]);
+        w = e * h2f_bits(nv_n);
       }
-      reinterpret_cast<float*>(&s_w[lane])[wave] = w;
-      if (wave < BV) s_pl[wave][lane] = vplanes[(g * BV + wave) * N + nc];
+      reinterpret_cast<float*>(&s_w[buf][lane])[wave] = w;
+      if (lane == 0) s_f[buf][wave] = f;
+      if (wave < BV) *reinterpret_cast<uint4*>(s_pl[buf][wave][lane]) = pl_n;
     }
     __syncthreads();
-#pragma unroll 2
+    {
+      const float f0 = s_f[buf][0], f1 = s_f[buf][1], f2 = s_f[buf][2], f3 = s_f[buf][3];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[c][0] *= f0; acc[c][1] *= f1; acc[c][2] *= f2; acc[c][3] *= f3;
+      }
+    }
+    if (nb + 64 < n1) load_block(nb + 64);
+#pragma unroll 4
     for (int j = 0; j < 8; ++j) {
       const int kk = kq + 8 * j;
-      const f32x4 wv = s_w[kk];
-      uint32_t sh[BV][4];
+      const f32x4 wv = s_w[buf][kk];
+      uint32_t a0 = 0, a1 = 0;   // byte offsets of the two level pairs
 #pragma unroll
       for (int p = 0; p < BV; ++p) {
-        const uint4 pw = s_pl[p][kk];
-        sh[p][0] = pw.x >> cs; sh[p][1] = pw.y >> cs; sh[p][2] = pw.z >> cs; sh[p][3] = pw.w >> cs;
+        const uint32_t x = s_pl[buf][p][kk][wsel];
+        a0 |= __builtin_amdgcn_ubfe(x, sh, 2) << (2 * p + 3);
+        a1 |= __builtin_amdgcn_ubfe(x, sh + 2, 2) << (2 * p + 3);
       }
+      const float2 l01 = *reinterpret_cast<const float2*>(lut + a0);
+      const float2 l23 = *reinterpret_cast<const float2*>(lut + a1);
+      const float lv[4] = {l01.x, l01.y, l23.x, l23.y};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t code = 0;
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int p = 0; p < BV; ++p) code |= (sh[p][w] & 1u) << p;
-        const float lv = s_lev[code];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[w][q] = fmaf(wv[q], lv, acc[w][q]);
-      }
+        for (int q = 0; q < 4; ++q) acc[c][q] = fmaf(wv[q], lv[c], acc[c][q]);
     }
-    __syncthreads();
   }
 
   // ---- reduce over the eight key lanes, write the range's partial state
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_red[kq][cs][4 * w + q] = acc[w][q];
+    for (int q = 0; q < 4; ++q) s_red[kq][cq][4 * c + q] = acc[c][q];
   zs = wave_sum(zs);
   if (lane == 0) { s_m[0][wave] = mx; s_m[1][wave] = zs; }
   __syncthreads();
   float* out = part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
   if (tid < 8) out[tid] = s_m[tid >> 2][tid & 3];
   for (int e = tid; e < 512; e += kAttnThreads) {
-    const int q = e >> 7, i = e & 127, w = i >> 5, c = i & 31;
+    const int q = e >> 7, i = e & 127, quad = i >> 2, c = i & 3;
     float a = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a += s_red[k][c][4 * w + q];
-    out[8 + e] = a;                 // A[q][i], coordinate i = 32 w + c
+    for (int k = 0; k < 8; ++k) a += s_red[k][quad][4 * c + q];
+    out[8 + e] = a;                 // A[q][i]
   }
 }
 
@@ -1206,8 +1242,10 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
   const int h = int(gh - g * Qg), qc = h >> 2, q = h & 3;
   const float* base = part + (g * nqc + qc) * int64_t(splits) * kAttnPart;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * kAttnPart + q]);
   float Z = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
     const float* ps = base + s * kAttnPart;
     const float f = __expf(ps[q] - M);
