@@ -662,6 +662,258 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- many-query top-k, matrix cores
+// With many queries per group the estimator is a dense contraction over the
+// 1024 coordinates:
+//   score(q, v) = nu~ sum_i (R q)_i c[code_v,i] + rho~ sqrt(pi/2)/m sum_j (S q)_j (1 - 2 s_v,j)
+// and both sums run on v_mfma_f32_32x32x16_f16 into one accumulator.  Query
+// side (A, per query a power of two sigma_q): R q / (sqrt(d) sigma_q) and
+// sqrt(pi/2)/m S q / sigma_q, each split into fp16 hi + lo.  Vector side (B,
+// per vector a power of two 2^-e_v that brings nu~ into [0.5, 1)):
+// nu~ 2^-e_v sqrt(d) c[code] as fp16 hi + lo, and rho~ 2^-e_v (1 - 2 s) exactly
+// in fp16.  Products hi*hi + hi*lo + lo*hi (levels) and hi*s + lo*s (signs),
+// fp32 accumulation: score = sigma_q 2^e_v C.  One LDS table maps the code
+// and sign bits of two adjacent coordinates to their two levels and sign
+// pattern.  Each wave owns 32 queries and keeps each query's best K (of
+// C 2^e_v: sigma_q > 0 does not change the order) in one 16-lane row of a
+// register pair; a workgroup walks a contiguous run of 128-vector tiles and
+// writes its lists (times sigma_q) as one range for topk_merge_kernel.
+constexpr int kMqThreads = 512;   // 8 waves, wave w = query rows 32 w .. 32 w + 31
+constexpr int kMqMaxRb = 8;       // up to 256 queries per group
+
+// A fragments: frag[g][rb][tile][ks][lane] (half8) for tiles R hi, R lo, S hi,
+// S lo: query 32 rb + lane % 32 (zero past Qg) at coordinates
+// 16 ks + 8 (lane / 32) .. + 7; sigma[g][32 rb + r].
+__global__ __launch_bounds__(256) void mqprep1024_kernel(const float* __restrict__ X, int Qg, int rbs,
+                                                         uint4* __restrict__ frag,
+                                                         float* __restrict__ sigma,
+                                                         const DevConsts* __restrict__ cst) {
+  __shared__ float s_max[8][32];
+  __shared__ float s_mul[2][32];
+  const int tid = threadIdx.x;
+  const int64_t g = blockIdx.x / rbs;
+  const int rb = int(blockIdx.x - g * rbs);
+  // X holds 2 R q and 2 S q: the A values are X times these factors over sigma
+  const float fR = 0.5f * cst->inv_sqrt_d, fS = 0.5f * cst->qjl_scale;
+  {
+    const int r = tid & 31, part = tid >> 5, qh = 32 * rb + r;
+    float m = 0.f;
+    if (qh < Qg) {
+      const float* x = X + (g * Qg + qh) * 2 * kD + 128 * part;
+      for (int c = 0; c < 128; ++c) m = fmaxf(m, fmaxf(fabsf(x[c]) * fR, fabsf(x[kD + c]) * fS));
+    }
+    s_max[part][r] = m;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float m = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) m = fmaxf(m, s_max[p][tid]);
+    int e = 0;
+    if (m > 0.f) (void)frexpf(m, &e);            // m = f 2^e, f in [0.5, 1)
+    const float sig = m > 0.f ? ldexpf(1.f, e) : 1.f;
+    s_mul[0][tid] = fR / sig;                    // exact: powers of two
+    s_mul[1][tid] = fS / sig;
+    sigma[(g * rbs + rb) * 32 + tid] = sig;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int ks = e >> 6, ln = e & 63, r = ln & 31, qh = 32 * rb + r;
+    const int c0 = 16 * ks + 8 * (ln >> 5);
+#pragma unroll
+    for (int ty = 0; ty < 2; ++ty) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v0 = 0.f, v1 = 0.f;
+        if (qh < Qg) {
+          const float* x = X + (g * Qg + qh) * 2 * kD + ty * kD + c0 + 2 * j;
+          v0 = x[0] * s_mul[ty][r];
+          v1 = x[1] * s_mul[ty][r];
+        }
+        const half2v hv = {static_cast<_Float16>(v0), static_cast<_Float16>(v1)};
+        const half2v lv = {static_cast<_Float16>(v0 - static_cast<float>(hv[0])),
+                           static_cast<_Float16>(v1 - static_cast<float>(hv[1]))};
+        hw[j] = __builtin_bit_cast(uint32_t, hv);
+        lw[j] = __builtin_bit_cast(uint32_t, lv);
+      }
+      const size_t at = (((size_t(g) * rbs + rb) * 4 + 2 * ty) * 64 + ks) * 64 + ln;
+      frag[at] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      frag[at + 64 * 64] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
+}
+
+// insert (cs, ci) into row `row` (lanes 16 row .. 16 row + K - 1) of (ls, li)
+__device__ __forceinline__ void row_insert(float& ls, int32_t& li, float cs, int32_t ci, int lane,
+                                           int row, int K) {
+  const int rl = lane & 15;
+  const bool mine = (lane >> 4) == row && rl < K;
+  const int pos = __builtin_popcountll(__builtin_amdgcn_ballot_w64(mine && better(ls, li, cs, ci)));
+  if (pos >= K) return;
+  const float ps = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ls), 0x111, 0xF, 0xF, false));
+  const int32_t pi = __builtin_amdgcn_mov_dpp(li, 0x111, 0xF, 0xF, false);   // row_shr:1
+  if (mine) {
+    if (rl == pos) { ls = cs; li = ci; }
+    else if (rl > pos) { ls = ps; li = pi; }
+  }
+}
+
+template <int B>
+__global__ __launch_bounds__(kMqThreads, 1) void mqtopk1024_kernel(
+    const uint32_t* __restrict__ planes, const uint32_t* __restrict__ norms, int64_t N, int Qg,
+    int rbs, int64_t tiles_per_wg, const uint4* __restrict__ frag, const float* __restrict__ sigma,
+    int K, float* __restrict__ tk_s, int32_t* __restrict__ tk_i, const DevConsts* __restrict__ cst) {
+  constexpr int P = B + 1;
+  constexpr int NLUT = 1 << (2 * P);
+  __shared__ uint4 s_lut[NLUT];                 // (level a, level b (times sqrt d), sign mask, 0)
+  __shared__ uint4 s_b[2][4][4][3][64];         // [buffer][k-step][vector block][tile][lane]: 96 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t g = blockIdx.y;
+  const int64_t ntiles = (N + 127) / 128;
+  const int64_t t0 = int64_t(blockIdx.x) * tiles_per_wg;
+  const int64_t t1 = std::min<int64_t>(ntiles, t0 + tiles_per_wg);
+
+  for (int j = tid; j < NLUT; j += kMqThreads) {
+    int ca = 0, cb = 0;
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      ca |= ((j >> (2 * p)) & 1) << p;
+      cb |= ((j >> (2 * p + 1)) & 1) << p;
+    }
+    const float la = cst->levels[ca] * cst->sqrt_d, lb = cst->levels[cb] * cst->sqrt_d;
+    const uint32_t sm = (((j >> (2 * B)) & 1u) << 15) | (((j >> (2 * B + 1)) & 1u) << 31);
+    s_lut[j] = make_uint4(__float_as_uint(la), __float_as_uint(lb), sm, 0u);
+  }
+
+  float ls[8];      // query r: register r / 4, lanes 16 (r % 4) .. + K - 1
+  int32_t li[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) { ls[k] = -__builtin_huge_valf(); li[k] = 0x7fffffff; }
+  float mone = -1.0f;
+  asm volatile("" : "+v"(mone));
+
+  const uint4* fa = frag + ((size_t(g) * rbs + (wave < rbs ? wave : 0)) * 4) * 64 * 64 + lane;
+  for (int64_t tile = t0; tile < t1; ++tile) {
+    const int64_t nb = tile * 128;
+    // B operand of chunk c (k-steps 4c .. 4c+3): item i = (k-step, vector block, lane)
+    auto expand = [&](int c, int buf) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int i = tid + it * kMqThreads;
+        const int ksl = i >> 8, vb = (i >> 6) & 3, ln = i & 63;
+        const int ks = 4 * c + ksl;
+        const int64_t v = std::min<int64_t>(nb + 32 * vb + (ln & 31), N - 1);
+        const int w = ks >> 1, bo = 16 * (ks & 1) + 8 * (ln >> 5);
+        uint32_t by[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) by[p] = (planes[((g * P + p) * N + v) * 32 + w] >> bo) & 0xffu;
+        const uint32_t nr = norms[g * N + v];
+        const float nu = __builtin_bit_cast(_Float16, uint16_t(nr & 0xffffu));
+        const float rho = __builtin_bit_cast(_Float16, uint16_t(nr >> 16));
+        int e = 0;
+        if (nu > 0.f) (void)frexpf(nu, &e);
+        const float nus = ldexpf(nu, -e), rhos = ldexpf(rho, -e);   // exact
+        const uint32_t rb16 = f2h_bits(rhos);                        // exact: rho~ is a half
+        const uint32_t rr = rb16 | (rb16 << 16);
+        uint32_t ch[4], cl[4], sg[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t idx = 0;
+#pragma unroll
+          for (int p = 0; p < P; ++p) idx |= ((by[p] >> (2 * j)) & 3u) << (2 * p);
+          const uint4 en = s_lut[idx];
+          const float ma = nus * __uint_as_float(en.x), mb = nus * __uint_as_float(en.y);
+          const half2v hv = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ma, mb));
+          const half2v lv = {static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hv[0]), mone, ma)),
+                             static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hv[1]), mone, mb))};
+          ch[j] = __builtin_bit_cast(uint32_t, hv);
+          cl[j] = __builtin_bit_cast(uint32_t, lv);
+          sg[j] = rr ^ en.z;
+        }
+        s_b[buf][ksl][vb][0][ln] = make_uint4(ch[0], ch[1], ch[2], ch[3]);
+        s_b[buf][ksl][vb][1][ln] = make_uint4(cl[0], cl[1], cl[2], cl[3]);
+        s_b[buf][ksl][vb][2][ln] = make_uint4(sg[0], sg[1], sg[2], sg[3]);
+      }
+    };
+    f32x16 acc[4] = {};
+    __syncthreads();             // the table (first tile) and the previous tile's last reads
+    expand(0, 0);
+    __syncthreads();
+    for (int c = 0; c < 16; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < 16) expand(c + 1, buf ^ 1);
+      if (wave < rbs) {
+#pragma unroll
+        for (int ksl = 0; ksl < 4; ++ksl) {
+          const int ks = 4 * c + ksl;
+          const half8 rh = __builtin_bit_cast(half8, fa[(0 * 64 + ks) * 64]);
+          const half8 rl = __builtin_bit_cast(half8, fa[(1 * 64 + ks) * 64]);
+          const half8 sh = __builtin_bit_cast(half8, fa[(2 * 64 + ks) * 64]);
+          const half8 sl = __builtin_bit_cast(half8, fa[(3 * 64 + ks) * 64]);
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb) {
+            const half8 bh = __builtin_bit_cast(half8, s_b[buf][ksl][vb][0][lane]);
+            const half8 bl = __builtin_bit_cast(half8, s_b[buf][ksl][vb][1][lane]);
+            const half8 bs = __builtin_bit_cast(half8, s_b[buf][ksl][vb][2][lane]);
+            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, bh, acc[vb], 0, 0, 0);
+            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, bl, acc[vb], 0, 0, 0);
+            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rl, bh, acc[vb], 0, 0, 0);
+            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sh, bs, acc[vb], 0, 0, 0);
+            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sl, bs, acc[vb], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (wave < rbs) {
+      const int h = lane >> 5;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        const int64_t v = nb + 32 * vb + (lane & 31);
+        const bool valid = v < N;
+        const uint32_t nr = norms[g * N + std::min<int64_t>(v, N - 1)];
+        const float nu = __builtin_bit_cast(_Float16, uint16_t(nr & 0xffffu));
+        int e = 0;
+        if (nu > 0.f) (void)frexpf(nu, &e);
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const float sc = ldexpf(acc[vb][a], e);      // score / sigma_q
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            const int r = 8 * (a >> 2) + 4 * hs + (a & 3);
+            const int reg = r >> 2, row = r & 3;
+            const float t_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[reg]), 16 * row + K - 1));
+            const int32_t t_i = __builtin_amdgcn_readlane(li[reg], 16 * row + K - 1);
+            uint64_t m = __builtin_amdgcn_ballot_w64(valid && h == hs && better(sc, int32_t(v), t_s, t_i));
+            while (m) {
+              const int b = __builtin_ctzll(m);
+              m &= m - 1;
+              const float cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), b));
+              const int32_t ci = __builtin_amdgcn_readlane(int32_t(v), b);
+              row_insert(ls[reg], li[reg], cs, ci, lane, row, K);
+            }
+          }
+        }
+      }
+    }
+  }
+  if (wave < rbs && (lane & 15) < K) {
+    const int row = lane >> 4;
+#pragma unroll
+    for (int reg = 0; reg < 8; ++reg) {
+      const int qh = 32 * wave + 4 * reg + row;
+      if (qh < Qg) {
+        const float sig = sigma[(g * rbs + wave) * 32 + 4 * reg + row];
+        const int64_t at = ((g * Qg + qh) * int64_t(gridDim.x) + blockIdx.x) * K + (lane & 15);
+        tk_s[at] = ls[reg] * sig;
+        tk_i[at] = li[reg];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t encode_wide_chunk_keys() { return size_t(1) << 16; }   // 64K keys: 256 MiB of residuals
@@ -714,7 +966,28 @@ int64_t score_wide_ranges(const Codebook& cb, int64_t G, int Qg, int64_t N, int6
   return (N + chunk - 1) / chunk;
 }
 
+// Many queries per group take the matrix-core top-k (one row block of 32
+// queries per wave); fewer take the table scorer.
+static bool use_mq(int Qg) { return Qg >= 32 && Qg <= 32 * kMqMaxRb; }
+
+static int64_t mq_ranges(const Codebook& cb, int64_t G, int64_t N, int64_t* tiles_per_wg) {
+  const int64_t ntiles = (N + 127) / 128;
+  const int64_t cus = std::max(1, cb.num_cus);
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(ntiles, (cus + G - 1) / G));
+  const int64_t per = (ntiles + want - 1) / want;
+  if (tiles_per_wg) *tiles_per_wg = per;
+  return (ntiles + per - 1) / per;
+}
+
+static size_t mq_frag_bytes(int64_t G, int Qg) {
+  const int rbs = (Qg + 31) / 32;
+  return size_t(G) * rbs * 4 * 64 * 64 * 16 + size_t(G) * rbs * 32 * 4;
+}
+
 size_t topk_wide_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N, int K) {
+  if (use_mq(Qg))
+    return score_wide_prep_bytes(G, Qg) + mq_frag_bytes(G, Qg) +
+           size_t(G) * Qg * mq_ranges(cb, G, N, nullptr) * K * 8;
   const int64_t ranges = score_wide_ranges(cb, G, Qg, N, nullptr);
   return score_wide_prep_bytes(G, Qg) + size_t(G) * Qg * ranges * K * 8;
 }
@@ -766,6 +1039,37 @@ hipError_t launch_topk_wide(const Codebook& cb, const void* q, int qdtype, int64
                             void* ws, hipStream_t s) {
   float* X = static_cast<float*>(ws);
   float* sums = X + G * Qg * 2 * kD;
+  if (use_mq(Qg)) {
+    const int rbs = (Qg + 31) / 32;
+    char* base = static_cast<char*>(ws) + score_wide_prep_bytes(G, Qg);
+    uint4* frag = reinterpret_cast<uint4*>(base);
+    float* sigma = reinterpret_cast<float*>(base + size_t(G) * rbs * 4 * 64 * 64 * 16);
+    int64_t per = 0;
+    const int64_t ranges = mq_ranges(cb, G, N, &per);
+    float* tk_s = reinterpret_cast<float*>(base + mq_frag_bytes(G, Qg));
+    int32_t* tk_i = reinterpret_cast<int32_t*>(tk_s + G * Qg * ranges * K);
+    hipError_t e = prep_wide(cb, q, qdtype, G, Qg, X, sums, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mqprep1024_kernel, dim3(unsigned(G * rbs)), dim3(256), 0, s, X, Qg, rbs, frag,
+                       sigma, cb.d_consts);
+    const dim3 grid{unsigned(ranges), unsigned(G)};
+    const uint32_t* pl = static_cast<const uint32_t*>(packed);
+    const uint32_t* nr = pl + G * N * int64_t(cb.bits) * (kD / 32);
+#define TQ_MQ(BB)                                                                                \
+    hipLaunchKernelGGL((mqtopk1024_kernel<BB>), grid, dim3(kMqThreads), 0, s, pl, nr, N, Qg, rbs, \
+                       per, frag, sigma, K, tk_s, tk_i, cb.d_consts)
+    switch (cb.bits - 1) {
+      case 1: TQ_MQ(1); break;
+      case 2: TQ_MQ(2); break;
+      default: TQ_MQ(3); break;
+    }
+#undef TQ_MQ
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, tk_s, tk_i,
+                       int(ranges), K, idx, scores);
+    return hipGetLastError();
+  }
   const int64_t ranges = score_wide_ranges(cb, G, Qg, N, nullptr);
   float* tk_s = reinterpret_cast<float*>(static_cast<char*>(ws) + score_wide_prep_bytes(G, Qg));
   int32_t* tk_i = reinterpret_cast<int32_t*>(tk_s + G * Qg * ranges * K);

@@ -191,6 +191,24 @@ def test_wide_topk_ragged(N, k):
     _check_topk(idx.cpu().numpy(), sc.cpu().numpy(), ref, q, np.linalg.norm(keys, axis=-1), k)
 
 
+@pytest.mark.parametrize("bits,N,Qg,k", [(4, 1000, 40, 10), (3, 333, 32, 16), (2, 5000, 70, 5), (4, 129, 256, 1)])
+def test_wide_topk_many_queries(bits, N, Qg, k):
+    """32 or more queries per group take the matrix-core top-k: ragged vector
+    tiles, ragged query blocks, every supported code width."""
+    rng = np.random.default_rng(N + Qg + k + bits)
+    G = 1 if Qg > 64 else 2
+    keys = _keys(rng, G, N)
+    q = rng.standard_normal((G, Qg, D)).astype(np.float32) * np.exp(rng.normal(0, 1, (G, Qg, 1)))
+    cb = K.Codebook(D, bits)
+    cbo = O.make_codebook(D, bits, D, 42)
+    print(f"[case] wide matrix-core top-{k} bits={bits} N={N} Qg={Qg}", flush=True)
+    packed = K.encode_keys(cb, _dev(keys, torch.float32))
+    idx, sc = K.score_topk(cb, _dev(q, torch.float32), packed, N, k)
+    torch.cuda.synchronize()
+    ref = O.score(cbo, packed.cpu().numpy(), G, N, q)
+    _check_topk(idx.cpu().numpy(), sc.cpu().numpy(), ref, q, np.linalg.norm(keys, axis=-1), k)
+
+
 def test_wide_topk_argument_errors():
     import ctypes
     cb = K.Codebook(D, 4)
