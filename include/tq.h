@@ -56,6 +56,15 @@ enum {
 /* Element types of keys, queries and decoded outputs. */
 enum { TQ_F32 = 0, TQ_BF16 = 1 };
 
+/* Coordinate law the Lloyd-Max tables are optimal for.  TQ_CODEBOOK_GAUSSIAN:
+ * N(0, 1/d), the limit the pages give for a rotated coordinate (the default).
+ * TQ_CODEBOOK_BETA: the exact law of one coordinate of a uniformly random
+ * unit vector in R^d, density proportional to (1 - y^2)^((d-3)/2) on [-1, 1]
+ * (y^2 ~ Beta(1/2, (d-1)/2)) [ai.spot.hk article, "隨機旋轉與Beta分佈";
+ * ICLR 2026 paper digest, "Step 1: PolarQuant"].  Both are symmetric with the
+ * middle threshold at 0; only the level and threshold values differ. */
+enum { TQ_CODEBOOK_GAUSSIAN = 0, TQ_CODEBOOK_BETA = 1 };
+
 typedef struct tq_codebook tq_codebook;
 
 /*
@@ -82,6 +91,13 @@ int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed,
                        double* levels, double* thresholds, int8_t* delta,
                        double* S, double* S_rot);
 
+/* tq_codebook_tables for a chosen coordinate law (TQ_CODEBOOK_*); kind
+ * TQ_CODEBOOK_GAUSSIAN is tq_codebook_tables.  Errors as above, plus
+ * TQ_ERR_ARG for an unknown kind. */
+int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32_t kind,
+                          double* levels, double* thresholds, int8_t* delta, double* S,
+                          double* S_rot);
+
 /*
  * Build the quantizer state for (d, bits, m, seed) on the current HIP device:
  * the tables above plus the kernels' constant blocks (thresholds and levels in
@@ -93,6 +109,13 @@ int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed,
  * Errors: TQ_ERR_ARG (out NULL), TQ_ERR_UNSUPPORTED, TQ_ERR_ALLOC, TQ_ERR_HIP.
  */
 int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out);
+
+/* tq_make_codebook for a chosen coordinate law (TQ_CODEBOOK_*): every
+ * entry point then encodes, scores and decodes with those levels and
+ * thresholds (keys: bits-1 bit codes, values: bits bit codes).  Errors as
+ * above, plus TQ_ERR_ARG for an unknown kind. */
+int tq_make_codebook_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32_t kind,
+                        tq_codebook** out);
 
 /* Release a codebook (NULL is a no-op).  The caller must ensure no launch
  * that uses it is still in flight. */

@@ -12,6 +12,8 @@ import os
 import numpy as np
 
 TQ_F32, TQ_BF16 = 0, 1
+TQ_CODEBOOK_GAUSSIAN, TQ_CODEBOOK_BETA = 0, 1
+_KINDS = {"gaussian": TQ_CODEBOOK_GAUSSIAN, "beta": TQ_CODEBOOK_BETA}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libtq.so")
 
@@ -22,13 +24,16 @@ EXPORTED_SYMBOLS = (
     "tq_score_workspace_bytes", "tq_score_logits", "tq_score_cache", "tq_score_topk_workspace_bytes", "tq_score_topk", "tq_decode_mse",
     "tq_dense_logits_bf16", "tq_status_string", "tq_last_hip_error",
     "tq_value_packed_bytes", "tq_encode_values", "tq_attention_workspace_bytes",
-    "tq_attention_decode",
+    "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
 _SIGS = {
     "tq_codebook_tables": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, _vp, _vp, _vp, _vp, _vp]),
     "tq_make_codebook": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, ctypes.POINTER(_vp)]),
+    "tq_codebook_tables_ex": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, _c_i32, _vp, _vp, _vp, _vp,
+                                             _vp]),
+    "tq_make_codebook_ex": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, _c_i32, ctypes.POINTER(_vp)]),
     "tq_free_codebook": (None, [_vp]),
     "tq_codebook_export": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "tq_codebook_info": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
@@ -93,27 +98,31 @@ def _ptr(a):
     return None if a is None else ctypes.c_void_p(a.ctypes.data if isinstance(a, np.ndarray) else a.data_ptr())
 
 
-def codebook_tables(d: int, bits: int, m: int | None = None, seed: int = 42):
-    """Host-only quantizer tables (no GPU): levels, thresholds, delta, S, S R^T."""
+def codebook_tables(d: int, bits: int, m: int | None = None, seed: int = 42, kind: str = "gaussian"):
+    """Host-only quantizer tables (no GPU): levels, thresholds, delta, S, S R^T
+    (kind: "gaussian" = N(0, 1/d) Lloyd-Max, "beta" = the exact coordinate law)."""
     m = d if m is None else m
     L = 1 << (bits - 1)
     out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
                delta=np.empty(d, np.int8), S=np.empty((m, d), np.float64),
                S_rot=np.empty((m, d), np.float64))
-    _check(library().tq_codebook_tables(d, bits, m, seed, *(_ptr(out[k]) for k in
-                                        ("levels", "thresholds", "delta", "S", "S_rot"))),
-           "tq_codebook_tables")
+    _check(library().tq_codebook_tables_ex(d, bits, m, seed, _KINDS[kind], *(_ptr(out[k]) for k in
+                                           ("levels", "thresholds", "delta", "S", "S_rot"))),
+           "tq_codebook_tables_ex")
     return out
 
 
 class Codebook:
     """Device-resident quantizer state for (d, bits, m, seed)."""
 
-    def __init__(self, d: int = 128, bits: int = 3, m: int | None = None, seed: int = 42):
+    def __init__(self, d: int = 128, bits: int = 3, m: int | None = None, seed: int = 42,
+                 kind: str = "gaussian"):
         lib = library()
         self.d, self.bits, self.m, self.seed = d, bits, d if m is None else m, seed
+        self.kind = kind
         h = ctypes.c_void_p()
-        _check(lib.tq_make_codebook(d, bits, self.m, seed, ctypes.byref(h)), "tq_make_codebook")
+        _check(lib.tq_make_codebook_ex(d, bits, self.m, seed, _KINDS[kind], ctypes.byref(h)),
+               "tq_make_codebook_ex")
         self._h = h
 
     @property

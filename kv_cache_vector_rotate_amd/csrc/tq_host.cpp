@@ -105,6 +105,90 @@ void lloyd_max_normal(int L, double* levels, double* thresholds) {
   }
 }
 
+// ------------------------------------------------------- Lloyd-Max, Beta law
+// One coordinate of a uniformly random unit vector in R^d has density
+// proportional to (1 - y^2)^((d-3)/2) on [-1, 1] (y^2 ~ Beta(1/2, (d-1)/2)).
+// Tail mass P(Y >= y) = I_{1-y^2}((d-1)/2, 1/2) / 2 with the regularised
+// incomplete beta function I evaluated by its continued fraction (modified
+// Lentz), switching to I_x(a, b) = 1 - I_{1-x}(b, a) where the fraction
+// converges slowly; the first moment of a cell has a closed form.
+double incbeta_cf(double a, double b, double x) {
+  const double tiny = 1e-300;
+  double c = 1.0, dd = 1.0 - (a + b) * x / (a + 1.0);
+  if (std::fabs(dd) < tiny) dd = tiny;
+  dd = 1.0 / dd;
+  double f = dd;
+  for (int m = 1; m < 100000; ++m) {
+    // even step
+    double num = m * (b - m) * x / ((a + 2 * m - 1) * (a + 2 * m));
+    dd = 1.0 + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    c = 1.0 + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    dd = 1.0 / dd;
+    f *= dd * c;
+    // odd step
+    num = -(a + m) * (a + b + m) * x / ((a + 2 * m) * (a + 2 * m + 1));
+    dd = 1.0 + num * dd;
+    if (std::fabs(dd) < tiny) dd = tiny;
+    c = 1.0 + num / c;
+    if (std::fabs(c) < tiny) c = tiny;
+    dd = 1.0 / dd;
+    const double del = dd * c;
+    f *= del;
+    if (std::fabs(del - 1.0) < 1e-16) break;
+  }
+  return f;
+}
+
+double incbeta(double a, double b, double x) {
+  if (x <= 0.0) return 0.0;
+  if (x >= 1.0) return 1.0;
+  const double lfront = std::lgamma(a + b) - std::lgamma(a) - std::lgamma(b) + a * std::log(x) +
+                        b * std::log1p(-x);
+  if (x < (a + 1.0) / (a + b + 2.0)) return std::exp(lfront) * incbeta_cf(a, b, x) / a;
+  return 1.0 - std::exp(lfront) * incbeta_cf(b, a, 1.0 - x) / b;
+}
+
+void lloyd_max_beta(int d, int L, double* levels, double* thresholds) {
+  const int K = L / 2;
+  const double h = 0.5 * (d - 1);
+  const double cnorm = std::exp(std::lgamma(0.5 * d) - std::lgamma(h) - 0.5 * std::log(M_PI));
+  auto upper = [&](double y) { return y >= 1.0 ? 0.0 : 0.5 * incbeta(h, 0.5, 1.0 - y * y); };
+  auto moment = [&](double a, double b) {
+    const double fa = a < 1.0 ? std::pow(1.0 - a * a, h) : 0.0;
+    const double fb = b < 1.0 ? std::pow(1.0 - b * b, h) : 0.0;
+    return cnorm * (fa - fb) / (d - 1);
+  };
+  const double sd = 1.0 / std::sqrt(double(d));
+  std::vector<double> c(K), t(K + 1);
+  for (int k = 0; k < K; ++k) c[k] = sd * (k + 0.5) * 1.5 / K;
+  // stops once the levels move less than 1e-14 of the coordinate scale (the
+  // continued fraction's own rounding keeps them moving at the ulp level)
+  for (int it = 0; it < 100000; ++it) {
+    t[0] = 0.0;
+    t[K] = 1.0;
+    for (int k = 1; k < K; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    double moved = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double nc = moment(t[k], t[k + 1]) / (upper(t[k]) - upper(t[k + 1]));
+      moved = std::fmax(moved, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (moved < 1e-14 * sd) break;
+  }
+  for (int k = 0; k < K; ++k) {
+    levels[K + k] = c[k];
+    levels[K - 1 - k] = -c[k];
+  }
+  thresholds[K - 1] = 0.0;
+  for (int k = 1; k < K; ++k) {
+    const double tt = 0.5 * (c[k - 1] + c[k]);
+    thresholds[K - 1 + k] = tt;
+    thresholds[K - 1 - k] = -tt;
+  }
+}
+
 // S = (S R^T) R = S_rot H D / sqrt(d) (R orthogonal, H symmetric): a
 // Hadamard transform of each row of S_rot, then D, in float64.
 void sketch_from_rotated(const double* S_rot, const int8_t* delta, int m, int d, double* out) {
@@ -226,10 +310,19 @@ int build_tables(tq::Codebook& cb) {
   } catch (const std::bad_alloc&) {
     return TQ_ERR_ALLOC;
   }
-  lloyd_max_normal(L, cb.levels.data(), cb.thresholds.data());
+  // Lloyd-Max tables on the unit-vector coordinate scale: the N(0, 1/d) law
+  // (kind 0) or the exact coordinate law of a random unit vector (kind 1)
   const double sigma = 1.0 / std::sqrt(double(d));   // N(0,1) -> N(0, 1/d)
-  for (double& v : cb.levels) v *= sigma;
-  for (double& v : cb.thresholds) v *= sigma;
+  auto tables = [&](int LL, double* lv, double* th) {
+    if (cb.kind == TQ_CODEBOOK_BETA) {
+      lloyd_max_beta(d, LL, lv, th);
+    } else {
+      lloyd_max_normal(LL, lv, th);
+      for (int i = 0; i < LL; ++i) lv[i] *= sigma;
+      for (int i = 0; i + 1 < LL; ++i) th[i] *= sigma;
+    }
+  };
+  tables(L, cb.levels.data(), cb.thresholds.data());
   // value records: all `bits` bits go to the Lloyd-Max code (no sketch bit)
   const int LV = 1 << cb.bits;
   try {
@@ -238,9 +331,7 @@ int build_tables(tq::Codebook& cb) {
   } catch (const std::bad_alloc&) {
     return TQ_ERR_ALLOC;
   }
-  lloyd_max_normal(LV, cb.vlevels.data(), cb.vthresholds.data());
-  for (double& v : cb.vlevels) v *= sigma;
-  for (double& v : cb.vthresholds) v *= sigma;
+  tables(LV, cb.vlevels.data(), cb.vthresholds.data());
   make_delta(cb.seed, d, cb.delta.data());
   make_sketch_rot(cb.seed, m, d, cb.S_rot.data());
   sketch_from_rotated(cb.S_rot.data(), cb.delta.data(), m, d, cb.S.data());
@@ -330,8 +421,17 @@ extern "C" {
 
 int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed, double* levels,
                        double* thresholds, int8_t* delta, double* S, double* S_rot) {
+  return tq_codebook_tables_ex(d, bits, m, seed, TQ_CODEBOOK_GAUSSIAN, levels, thresholds, delta, S,
+                               S_rot);
+}
+
+int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32_t kind,
+                          double* levels, double* thresholds, int8_t* delta, double* S,
+                          double* S_rot) {
   if (!valid_params(d, bits, m)) return TQ_ERR_UNSUPPORTED;
+  if (kind != TQ_CODEBOOK_GAUSSIAN && kind != TQ_CODEBOOK_BETA) return TQ_ERR_ARG;
   tq::Codebook cb;
+  cb.kind = kind;
   cb.d = d;
   cb.bits = bits;
   cb.m = m;
@@ -348,11 +448,18 @@ int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed, double
 }
 
 int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out) {
+  return tq_make_codebook_ex(d, bits, m, seed, TQ_CODEBOOK_GAUSSIAN, out);
+}
+
+int tq_make_codebook_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32_t kind,
+                        tq_codebook** out) {
   if (!out) return TQ_ERR_ARG;
   *out = nullptr;
+  if (kind != TQ_CODEBOOK_GAUSSIAN && kind != TQ_CODEBOOK_BETA) return TQ_ERR_ARG;
   if (!valid_params(d, bits, m) || !device_params(d)) return TQ_ERR_UNSUPPORTED;
   std::unique_ptr<tq_codebook> cb(new (std::nothrow) tq_codebook());
   if (!cb) return TQ_ERR_ALLOC;
+  cb->kind = kind;
   cb->d = d;
   cb->bits = bits;
   cb->m = m;

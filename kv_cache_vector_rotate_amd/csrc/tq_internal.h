@@ -30,6 +30,7 @@ constexpr float kResidualScale = 4096.0f;  // 2^12: keeps residual hi/lo halves 
 
 struct Codebook {
   int d = 0, bits = 0, m = 0;
+  int kind = 0;               // TQ_CODEBOOK_GAUSSIAN or TQ_CODEBOOK_BETA
   uint64_t seed = 0;
   int device = 0;
   // host tables

@@ -46,7 +46,7 @@ __all__ = [
     "packed_nbytes", "decode_mse", "score", "estimate_inner_product",
     "exact_logits", "top_k", "fp16_midpoint_flag", "ZERO_NORM",
     "FLAG_BAND", "kv_bytes_per_vector",
-    "value_quantizer", "ValueEncodeResult", "encode_values", "value_packed_nbytes",
+    "lloyd_max_beta", "haar_rotation", "value_quantizer", "ValueEncodeResult", "encode_values", "value_packed_nbytes",
     "pack_values", "unpack_values", "decode_values", "attention_from_logits", "attention",
 ]
 
@@ -197,6 +197,60 @@ def lloyd_max_std_normal(B: int, tol: float = 1e-15, max_iter: int = 100000):
     return levels, thresholds
 
 
+def lloyd_max_beta(d: int, B: int, tol: float = 1e-15, max_iter: int = 200000):
+    """(levels, thresholds) of the MSE-optimal 2**B-level quantizer for one
+    coordinate of a uniformly random unit vector in R^d, the law the pages
+    give for a rotated coordinate before its Gaussian limit [ai.spot.hk,
+    隨機旋轉與Beta分佈; ICLR 2026 digest, Step 1]: density proportional to
+    (1 - y^2)^((d-3)/2) on [-1, 1] (y^2 ~ Beta(1/2, (d-1)/2)).
+
+    The same two Lloyd conditions as :func:`lloyd_max_std_normal`, on the
+    positive half with the middle threshold fixed at 0: a cell's mass is
+    P(|Y| <= y) = I_{y^2}(1/2, (d-1)/2) (the regularised incomplete beta
+    function), and its first moment has the closed form
+    int_a^b y (1 - y^2)^((d-3)/2) dy = ((1-a^2)^((d-1)/2) - (1-b^2)^((d-1)/2)) / (d-1).
+    Scale: unit-vector coordinates (no 1/sqrt(d) factor to apply)."""
+    from scipy import special
+    if d < 2 or B < 1:
+        raise ValueError("d >= 2, B >= 1")
+    K = (1 << B) // 2
+    h = (d - 1) / 2.0
+    # normalising constant of the density on [-1, 1]
+    cnorm = math.exp(special.gammaln(d / 2.0) - special.gammaln(h) - 0.5 * math.log(math.pi))
+
+    def upper(y):          # P(Y >= y) for y >= 0, via the complementary incomplete beta
+        return 0.0 if y >= 1.0 else 0.5 * special.betainc(h, 0.5, 1.0 - y * y)
+
+    def moment(a, b):      # int_a^b y f(y) dy, 0 <= a <= b <= 1
+        fa = (1.0 - a * a) ** h if a < 1.0 else 0.0
+        fb = (1.0 - b * b) ** h if b < 1.0 else 0.0
+        return cnorm * (fa - fb) / (d - 1)
+
+    sd = 1.0 / math.sqrt(d)
+    c = [sd * (0.5 + 2.0 * (k + 0.5) / K) / 2.0 for k in range(K)]
+    for _ in range(max_iter):
+        t = [0.0] + [(c[k - 1] + c[k]) / 2.0 for k in range(1, K)] + [1.0]
+        new = [moment(t[k], t[k + 1]) / (upper(t[k]) - upper(t[k + 1])) for k in range(K)]
+        delta = max(abs(x - y) for x, y in zip(new, c))
+        c = new
+        if delta < tol * sd:
+            break
+    pos_levels = np.array(c, dtype=np.float64)
+    pos_thr = np.array([(c[k - 1] + c[k]) / 2.0 for k in range(1, K)], dtype=np.float64)
+    return (np.concatenate([-pos_levels[::-1], pos_levels]),
+            np.concatenate([-pos_thr[::-1], [0.0], pos_thr]))
+
+
+def haar_rotation(seed: int, d: int) -> np.ndarray:
+    """A Haar-distributed orthogonal matrix (QR of a Gaussian matrix with the
+    signs of R's diagonal moved into Q).  Cross-check only: the library uses
+    the randomized Hadamard rotation of the pages; under a Haar rotation each
+    rotated coordinate has exactly the Beta law of :func:`lloyd_max_beta`."""
+    g = np.random.default_rng(seed).standard_normal((d, d))
+    q, r = np.linalg.qr(g)
+    return q * np.sign(np.diag(r))[None, :]
+
+
 # --------------------------------------------------------------------------
 # Codebook = every piece of quantizer state derived from (d, b, m, seed).
 # --------------------------------------------------------------------------
@@ -213,6 +267,7 @@ class Codebook:
     S: np.ndarray        # [m, d] float64 sketch, S = S_rot R
     R: np.ndarray        # [d, d] float64 dense rotation
     S_rot: np.ndarray    # [m, d] float64 = S R^T: float16-rounded N(0,1) draws
+    kind: str = "gaussian"   # coordinate law of the Lloyd-Max tables: "gaussian" or "beta"
 
     @property
     def B(self) -> int:
@@ -223,7 +278,17 @@ class Codebook:
         return 1 << (self.bits - 1)
 
 
-def make_codebook(d: int, bits: int, m: int, seed: int) -> Codebook:
+def _lloyd_tables(d: int, B: int, kind: str):
+    """Lloyd-Max levels/thresholds on the unit-vector coordinate scale."""
+    if kind == "gaussian":
+        lv, th = lloyd_max_std_normal(B)
+        return lv / math.sqrt(d), th / math.sqrt(d)
+    if kind == "beta":
+        return lloyd_max_beta(d, B)
+    raise ValueError(kind)
+
+
+def make_codebook(d: int, bits: int, m: int, seed: int, kind: str = "gaussian") -> Codebook:
     """Quantizer state: Lloyd-Max for N(0,1/d) with L = 2**(bits-1) levels
     (scale equivariance: N(0,1) levels times 1/sqrt(d)), delta and S from the
     seed, and the dense rotation.  [ai.spot.hk, 無偏內積估計: (b-1)-bit MSE
@@ -235,13 +300,12 @@ def make_codebook(d: int, bits: int, m: int, seed: int) -> Codebook:
     projection], and S r = S_rot (R r)."""
     if bits < 2:
         raise ValueError("bits >= 2 (one bit is the QJL sign)")
-    lv, th = lloyd_max_std_normal(bits - 1)
-    sigma = 1.0 / math.sqrt(d)
+    lv, th = _lloyd_tables(d, bits - 1, kind)
     delta = rademacher_signs(seed, d)
     R = rotation_matrix(delta)
     S_rot = gaussian_sketch(seed, m, d).astype(np.float64)
-    return Codebook(d=d, bits=bits, m=m, seed=seed, levels=lv * sigma,
-                    thresholds=th * sigma, delta=delta, S=S_rot @ R, R=R, S_rot=S_rot)
+    return Codebook(d=d, bits=bits, m=m, seed=seed, levels=lv, thresholds=th, delta=delta,
+                    S=S_rot @ R, R=R, S_rot=S_rot, kind=kind)
 
 
 # --------------------------------------------------------------------------
@@ -480,11 +544,9 @@ _VQ_CACHE = {}
 def value_quantizer(cb: Codebook):
     """(levels [2**bits], thresholds [2**bits - 1]) of the b-bit value
     quantizer: Lloyd-Max for N(0,1) times 1/sqrt(d)."""
-    key = (cb.bits, cb.d)
+    key = (cb.bits, cb.d, cb.kind)
     if key not in _VQ_CACHE:
-        lv, th = lloyd_max_std_normal(cb.bits)
-        s = 1.0 / math.sqrt(cb.d)
-        _VQ_CACHE[key] = (lv * s, th * s)
+        _VQ_CACHE[key] = _lloyd_tables(cb.d, cb.bits, cb.kind)
     return _VQ_CACHE[key]
 
 
