@@ -205,7 +205,7 @@ size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg
  * domain), and a combine that merges the ranges and rotates back with R^T.
  * ws: tq_attention_workspace_bytes(cb, G, Qg, N) bytes of device memory.
  * Errors: TQ_ERR_ARG (also N == 0 with G*Qg > 0, scale not finite and > 0),
- * TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (d != 128, Qg > 256), TQ_ERR_HIP.
+ * TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (d != 128, Qg > 256, N >= 2^28), TQ_ERR_HIP.
  */
 int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
                         int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
@@ -228,8 +228,9 @@ size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
  * tq_score_workspace_bytes(cb, G, Qg) bytes (may be NULL when that is 0).
  * G*N*Qg == 0 is a no-op.  d = 1024 runs a query-preparation kernel into ws
  * first, then scores with nibble subset-sum tables (same estimator).
- * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256 or G > 2^31 - 1),
- * TQ_ERR_HIP.
+ * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256, G > 2^31 - 1,
+ * or N >= 2^28 at d = 128: records and logits of a group are addressed with
+ * 32-bit byte offsets), TQ_ERR_HIP.
  */
 int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
                     int32_t Qg, const void* packed, int64_t N, float* logits, void* ws,
@@ -242,7 +243,7 @@ int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64
  * tq_score_logits (which is the case len = Ncap = N).  Requires
  * 0 <= len <= Ncap.  d = 128 only; needs no workspace.
  * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED (d != 128, Qg > 256,
- * G > 2^31 - 1), TQ_ERR_HIP.
+ * G > 2^31 - 1, Ncap >= 2^28), TQ_ERR_HIP.
  */
 int tq_score_cache(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
                    const void* packed, int64_t Ncap, int64_t len, float* logits, void* stream);

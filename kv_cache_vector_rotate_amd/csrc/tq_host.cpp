@@ -565,7 +565,9 @@ int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, i
                         void* ws, size_t ws_bytes, void* stream) {
   if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_ERR_ARG;
   if (!(scale > 0.f) || !(scale < INFINITY)) return TQ_ERR_ARG;
-  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || G * Qg > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || G * Qg > INT32_MAX ||
+      N >= (int64_t(1) << 28))
+    return TQ_ERR_UNSUPPORTED;
   if (G == 0 || Qg == 0) return TQ_OK;
   if (N == 0) return TQ_ERR_ARG;   // softmax over no keys
   if (!q || !kpacked || !vpacked || !out || !aligned16(q) || !aligned16(kpacked) ||
@@ -590,7 +592,9 @@ int tq_score_logits(const tq_codebook* cb, const void* q, int32_t q_dtype, int64
                     void* stream) {
   if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16))
     return TQ_ERR_ARG;
-  if (Qg > 256 || G > INT32_MAX) return TQ_ERR_UNSUPPORTED;   // one grid row per group
+  if (Qg > 256 || G > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+  // d = 128 addresses records and logits of a group with 32-bit byte offsets
+  if (cb->d == 128 && N >= (int64_t(1) << 28)) return TQ_ERR_UNSUPPORTED;
   if (G == 0 || N == 0 || Qg == 0) return TQ_OK;
   if (!q || !packed || !logits || !aligned16(q) || !aligned16(packed) || !aligned16(logits))
     return TQ_ERR_ARG;
@@ -609,7 +613,8 @@ int tq_score_cache(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_
   if (!cb || G < 0 || Qg < 0 || Ncap < 0 || len < 0 || len > Ncap ||
       (q_dtype != TQ_F32 && q_dtype != TQ_BF16))
     return TQ_ERR_ARG;
-  if (cb->d != 128 || Qg > 256 || G > INT32_MAX) return TQ_ERR_UNSUPPORTED;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || Ncap >= (int64_t(1) << 28))
+    return TQ_ERR_UNSUPPORTED;
   if (G == 0 || len == 0 || Qg == 0) return TQ_OK;
   if (!q || !packed || !logits || !aligned16(q) || !aligned16(packed) || !aligned16(logits))
     return TQ_ERR_ARG;

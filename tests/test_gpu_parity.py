@@ -226,6 +226,14 @@ def test_gpu_argument_errors():
     assert lib.tq_score_logits(cb.handle, ctypes.c_void_p(q.data_ptr()), 0, 1, 300,
                                ctypes.c_void_p(packed.data_ptr()), 8, ctypes.c_void_p(out.data_ptr()),
                                None, 0, None) == -2
+    # key counts whose byte offsets would not fit 32 bits are refused before any launch
+    big = 1 << 28
+    assert lib.tq_score_logits(cb.handle, ctypes.c_void_p(q.data_ptr()), 0, 1, 4,
+                               ctypes.c_void_p(packed.data_ptr()), big, ctypes.c_void_p(out.data_ptr()),
+                               None, 0, None) == -2
+    assert lib.tq_score_cache(cb.handle, ctypes.c_void_p(q.data_ptr()), 0, 1, 4,
+                              ctypes.c_void_p(packed.data_ptr()), big, 8, ctypes.c_void_p(out.data_ptr()),
+                              None) == -2
     # empty inputs are no-ops
     assert lib.tq_encode_keys(cb.handle, None, 0, 0, 8, None, None) == 0
     with pytest.raises(K.TQError):
