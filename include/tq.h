@@ -27,6 +27,16 @@
  *   norms:  uint32 [G][N] = half(||k||) | half(||r||) << 16  (IEEE half, RNE).
  *   Total:  G*N*((bits-1)*d/8 + d/8 + 4) bytes.
  *
+ * Dimensions that are not a power of two: the method needs a power of two
+ * for the Hadamard transform, and a shorter vector is zero-padded up to the
+ * next one [ICLR 2026 paper digest, "実装のポイント": zero padding to the
+ * nearest power of two, with negligible accuracy loss reported].  A codebook
+ * made for such a d (a multiple of 16) runs in D = tq_rotation_dim(d):
+ * delta has D entries, S is m x D with m = D, the levels are those for
+ * N(0, 1/D), and records are D-dimensional.  Keys, values and queries are
+ * passed as rows of d elements and decoded vectors come back as rows of d
+ * elements; the kernels read the missing coordinates as zeros.
+ *
  * Status: every entry point returns TQ_OK (0) or a negative TQ_ERR_* code.
  * No C++ exception crosses this boundary.  Launches are asynchronous on the
  * given stream; device faults surface at the caller's next synchronisation.
@@ -67,9 +77,16 @@ enum { TQ_CODEBOOK_GAUSSIAN = 0, TQ_CODEBOOK_BETA = 1 };
 
 typedef struct tq_codebook tq_codebook;
 
+/* The power of two D the method runs in for vectors of d elements: d when d
+ * is a power of two in [32, 1024]; otherwise the next power of two >= 32
+ * when d is a multiple of 16 below 1024 (zero padding, see above); 0 when d
+ * is unsupported.  Pure host function. */
+int32_t tq_rotation_dim(int32_t d);
+
 /*
  * Host-only: the quantizer tables derived from (d, bits, m, seed), written to
- * caller-owned host arrays (any may be NULL):
+ * caller-owned host arrays (any may be NULL).  Below, d stands for
+ * tq_rotation_dim(d) (the same value unless d is zero-padded):
  *   levels[L], thresholds[L-1]  Lloyd-Max levels/boundaries for N(0, 1/d),
  *                               L = 2^(bits-1), ascending, float64;
  *   delta[d]                    Rademacher signs (+1/-1) of D;
@@ -84,8 +101,8 @@ typedef struct tq_codebook tq_codebook;
  * iff bit 63 of draw(seed,1,i) is 0; S_rot[j][i] = fp16(sqrt(-2 ln u1)
  * cos(2 pi u2)), u1 = ((x>>11)+1) 2^-53, u2 = (y>>11) 2^-53,
  * x,y = draw(seed,2,2(jd+i)+{0,1}).
- * Touches no GPU.  Errors: TQ_ERR_UNSUPPORTED (d not a power of two in
- * [32, 1024], bits not in {2,3,4}, m != d), TQ_ERR_ALLOC.
+ * Touches no GPU.  Errors: TQ_ERR_UNSUPPORTED (tq_rotation_dim(d) == 0,
+ * bits not in {2,3,4}, m != tq_rotation_dim(d)), TQ_ERR_ALLOC.
  */
 int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed,
                        double* levels, double* thresholds, int8_t* delta,
@@ -105,7 +122,9 @@ int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int
  * cores, Walsh coefficients of the levels for the scorer).  The handle owns
  * its device memory (hipMalloc) and is immutable afterwards, so it may be
  * shared by streams and threads; it is valid on the device that was current
- * here.  Supported: d in {128, 1024}, bits in {2, 3, 4}, m == d.
+ * here.  Supported: tq_rotation_dim(d) in {128, 1024}, i.e. d = 128 or 1024,
+ * or d in {80, 96, 112} or a multiple of 16 in [528, 1008] (zero-padded),
+ * bits in {2, 3, 4}, m == tq_rotation_dim(d).
  * Errors: TQ_ERR_ARG (out NULL), TQ_ERR_UNSUPPORTED, TQ_ERR_ALLOC, TQ_ERR_HIP.
  */
 int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out);
@@ -121,12 +140,14 @@ int tq_make_codebook_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32
  * that uses it is still in flight. */
 void tq_free_codebook(tq_codebook* cb);
 
-/* Host copies of a codebook's tables (same meaning as tq_codebook_tables;
- * any pointer may be NULL).  Errors: TQ_ERR_ARG (cb NULL). */
+/* Host copies of a codebook's tables (same meaning and sizes as
+ * tq_codebook_tables: delta has tq_rotation_dim(d) entries; any pointer may
+ * be NULL).  Errors: TQ_ERR_ARG (cb NULL). */
 int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds,
                        int8_t* delta, double* S, double* S_rot);
 
-/* (d, bits, m, seed) of a codebook; any pointer may be NULL. */
+/* (d, bits, m, seed) of a codebook as passed to tq_make_codebook (d is the
+ * caller's vector length, before any zero padding); any pointer may be NULL. */
 int tq_codebook_info(const tq_codebook* cb, int32_t* d, int32_t* bits, int32_t* m,
                      uint64_t* seed);
 

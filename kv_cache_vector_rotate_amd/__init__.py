@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     TQ_F32, TQ_BF16, TQError, Codebook, codebook_tables, encode_keys, append_keys, score_logits,
     score_cache, value_packed_nbytes, encode_values, attention_workspace_nbytes, attention_decode,
     score_topk, score_topk_workspace_nbytes, decode_mse, dense_logits_bf16, packed_nbytes,
-    score_workspace_nbytes, library, library_path, EXPORTED_SYMBOLS,
+    score_workspace_nbytes, rotation_dim, library, library_path, EXPORTED_SYMBOLS,
 )

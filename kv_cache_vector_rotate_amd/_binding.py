@@ -24,7 +24,7 @@ EXPORTED_SYMBOLS = (
     "tq_score_workspace_bytes", "tq_score_logits", "tq_score_cache", "tq_score_topk_workspace_bytes", "tq_score_topk", "tq_decode_mse",
     "tq_dense_logits_bf16", "tq_status_string", "tq_last_hip_error",
     "tq_value_packed_bytes", "tq_encode_values", "tq_attention_workspace_bytes",
-    "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex",
+    "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex", "tq_rotation_dim",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -35,6 +35,7 @@ _SIGS = {
                                              _vp]),
     "tq_make_codebook_ex": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _c_u64, _c_i32, ctypes.POINTER(_vp)]),
     "tq_free_codebook": (None, [_vp]),
+    "tq_rotation_dim": (_c_i32, [_c_i32]),
     "tq_codebook_export": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp]),
     "tq_codebook_info": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp]),
     "tq_packed_bytes": (_c_sz, [_vp, _c_i64, _c_i64]),
@@ -98,14 +99,24 @@ def _ptr(a):
     return None if a is None else ctypes.c_void_p(a.ctypes.data if isinstance(a, np.ndarray) else a.data_ptr())
 
 
+def rotation_dim(d: int) -> int:
+    """The power of two the method runs in for d-element vectors (d, or the
+    next power of two for a zero-padded d); 0 when unsupported."""
+    return int(library().tq_rotation_dim(d))
+
+
 def codebook_tables(d: int, bits: int, m: int | None = None, seed: int = 42, kind: str = "gaussian"):
     """Host-only quantizer tables (no GPU): levels, thresholds, delta, S, S R^T
-    (kind: "gaussian" = N(0, 1/d) Lloyd-Max, "beta" = the exact coordinate law)."""
-    m = d if m is None else m
+    (kind: "gaussian" = N(0, 1/D) Lloyd-Max, "beta" = the exact coordinate law;
+    D = rotation_dim(d), the arrays are D-dimensional)."""
+    D = rotation_dim(d)
+    if D == 0:
+        raise TQError(-2, "tq_rotation_dim")
+    m = D if m is None else m
     L = 1 << (bits - 1)
     out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
-               delta=np.empty(d, np.int8), S=np.empty((m, d), np.float64),
-               S_rot=np.empty((m, d), np.float64))
+               delta=np.empty(D, np.int8), S=np.empty((m, D), np.float64),
+               S_rot=np.empty((m, D), np.float64))
     _check(library().tq_codebook_tables_ex(d, bits, m, seed, _KINDS[kind], *(_ptr(out[k]) for k in
                                            ("levels", "thresholds", "delta", "S", "S_rot"))),
            "tq_codebook_tables_ex")
@@ -113,12 +124,15 @@ def codebook_tables(d: int, bits: int, m: int | None = None, seed: int = 42, kin
 
 
 class Codebook:
-    """Device-resident quantizer state for (d, bits, m, seed)."""
+    """Device-resident quantizer state for (d, bits, m, seed).  d is the
+    length of the caller's vectors; D = rotation_dim(d) the dimension the
+    method runs in (m defaults to D)."""
 
     def __init__(self, d: int = 128, bits: int = 3, m: int | None = None, seed: int = 42,
                  kind: str = "gaussian"):
         lib = library()
-        self.d, self.bits, self.m, self.seed = d, bits, d if m is None else m, seed
+        self.D = rotation_dim(d)
+        self.d, self.bits, self.m, self.seed = d, bits, (self.D or d) if m is None else m, seed
         self.kind = kind
         h = ctypes.c_void_p()
         _check(lib.tq_make_codebook_ex(d, bits, self.m, seed, _KINDS[kind], ctypes.byref(h)),
@@ -143,8 +157,8 @@ class Codebook:
     def export(self):
         L = 1 << (self.bits - 1)
         out = dict(levels=np.empty(L, np.float64), thresholds=np.empty(L - 1, np.float64),
-                   delta=np.empty(self.d, np.int8), S=np.empty((self.m, self.d), np.float64),
-                   S_rot=np.empty((self.m, self.d), np.float64))
+                   delta=np.empty(self.D, np.int8), S=np.empty((self.m, self.D), np.float64),
+                   S_rot=np.empty((self.m, self.D), np.float64))
         _check(library().tq_codebook_export(self._h, *(_ptr(out[k]) for k in
                                             ("levels", "thresholds", "delta", "S", "S_rot"))),
                "tq_codebook_export")

@@ -207,13 +207,28 @@ void sketch_from_rotated(const double* S_rot, const int8_t* delta, int m, int d,
   }
 }
 
-bool valid_params(int d, int bits, int m) {
-  if (d < 32 || d > 1024 || (d & (d - 1))) return false;
-  if (bits < 2 || bits > 4) return false;
-  return m == d;
+// The power of two D the method runs in for d-dimensional vectors: d itself,
+// or the next power of two when d is a multiple of 16 (rows are zero-padded
+// to D [ICLR 2026 paper digest, "実装のポイント": zero padding up to the
+// nearest power of two for the Hadamard transform]); 0 when unsupported.
+int rotation_dim(int d) {
+  if (d < 1 || d > 1024) return 0;
+  int D = 32;
+  while (D < d) D <<= 1;
+  return (D == d || d % 16 == 0) ? D : 0;
 }
 
-bool device_params(int d) { return d == 128 || d == 1024; }
+bool valid_params(int d, int bits, int m) {
+  const int D = rotation_dim(d);
+  if (D == 0) return false;
+  if (bits < 2 || bits > 4) return false;
+  return m == D;
+}
+
+bool device_params(int d) {
+  const int D = rotation_dim(d);
+  return D == 128 || D == 1024;
+}
 
 uint16_t half_bits(double v) {
   const _Float16 h = static_cast<_Float16>(v);   // round to nearest even
@@ -295,6 +310,7 @@ void fill_consts(tq::Codebook& cb) {
   k.sqrt_d = float(std::sqrt(double(cb.d)));
   k.inv_sqrt_d = float(1.0 / std::sqrt(double(cb.d)));
   k.qjl_scale = float(std::sqrt(M_PI / 2.0) / cb.m);
+  k.din = uint32_t(cb.d_in);
   for (int i = 0; i < cb.d; ++i)
     if (cb.delta[i] < 0) k.dneg[i >> 5] |= 1u << (i & 31);
 }
@@ -419,6 +435,8 @@ int check_device(const tq::Codebook& cb) {
 
 extern "C" {
 
+int32_t tq_rotation_dim(int32_t d) { return rotation_dim(d); }
+
 int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed, double* levels,
                        double* thresholds, int8_t* delta, double* S, double* S_rot) {
   return tq_codebook_tables_ex(d, bits, m, seed, TQ_CODEBOOK_GAUSSIAN, levels, thresholds, delta, S,
@@ -432,7 +450,8 @@ int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int
   if (kind != TQ_CODEBOOK_GAUSSIAN && kind != TQ_CODEBOOK_BETA) return TQ_ERR_ARG;
   tq::Codebook cb;
   cb.kind = kind;
-  cb.d = d;
+  cb.d = rotation_dim(d);
+  cb.d_in = d;
   cb.bits = bits;
   cb.m = m;
   cb.seed = seed;
@@ -441,7 +460,7 @@ int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int
   const int L = 1 << (bits - 1);
   if (levels) std::memcpy(levels, cb.levels.data(), L * sizeof(double));
   if (thresholds) std::memcpy(thresholds, cb.thresholds.data(), (L - 1) * sizeof(double));
-  if (delta) std::memcpy(delta, cb.delta.data(), d);
+  if (delta) std::memcpy(delta, cb.delta.data(), cb.d);
   if (S) std::memcpy(S, cb.S.data(), cb.S.size() * sizeof(double));
   if (S_rot) std::memcpy(S_rot, cb.S_rot.data(), cb.S_rot.size() * sizeof(double));
   return TQ_OK;
@@ -460,7 +479,8 @@ int tq_make_codebook_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32
   std::unique_ptr<tq_codebook> cb(new (std::nothrow) tq_codebook());
   if (!cb) return TQ_ERR_ALLOC;
   cb->kind = kind;
-  cb->d = d;
+  cb->d = rotation_dim(d);
+  cb->d_in = d;
   cb->bits = bits;
   cb->m = m;
   cb->seed = seed;
@@ -493,7 +513,7 @@ int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds
 int tq_codebook_info(const tq_codebook* cb, int32_t* d, int32_t* bits, int32_t* m,
                      uint64_t* seed) {
   if (!cb) return TQ_ERR_ARG;
-  if (d) *d = cb->d;
+  if (d) *d = cb->d_in;
   if (bits) *bits = cb->bits;
   if (m) *m = cb->m;
   if (seed) *seed = cb->seed;

@@ -23,13 +23,15 @@ struct DevConsts {
   float qjl_scale;    // sqrt(pi/2) / m
   float alpha_sum;    // alpha[0] + ... + alpha[3]
   uint32_t dneg[32];  // bit (i % 32) of word i/32 set where delta_i = -1 (d <= 1024)
-  uint32_t pad[4];
+  uint32_t din;       // length of input rows (and of decoded rows): d, or less when zero-padded to d
+  uint32_t pad[3];
 };
 
 constexpr float kResidualScale = 4096.0f;  // 2^12: keeps residual hi/lo halves normal
 
 struct Codebook {
-  int d = 0, bits = 0, m = 0;
+  int d = 0, bits = 0, m = 0;   // d: the power of two the method runs in
+  int d_in = 0;                 // caller's vector length (d_in <= d; rows are zero-padded to d)
   int kind = 0;               // TQ_CODEBOOK_GAUSSIAN or TQ_CODEBOOK_BETA
   uint64_t seed = 0;
   int device = 0;

@@ -447,17 +447,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Rows hold din <= 128 elements (din a multiple of 16); k-steps at or past
+// din / 16 are zero padding: they re-read step 0 (valid memory) and the
+// consumer replaces them by zeros.
 __device__ __forceinline__ void issue_tile_dma(const uint16_t* __restrict__ keys, uint32_t tile,
-                                               uint32_t tpg, int64_t N, int lane, uint4* buf) {
+                                               uint32_t tpg, int64_t N, uint32_t din, int lane,
+                                               uint4* buf) {
   const int h = lane >> 5, kl = lane & 31;
   const uint32_t gt = tile / tpg;
   const int64_t g = gt;
   const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
   const int64_t nl = n < N ? n : N - 1;
-  const uint4* src = reinterpret_cast<const uint4*>(keys + (g * N + nl) * 128) + h;
+  const uint4* src = reinterpret_cast<const uint4*>(keys + (g * N + nl) * din) + h;
+  const uint32_t kval = din >> 4;
 #pragma unroll
   for (int c = 0; c < 8; ++c)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * c),
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * (uint32_t(c) < kval ? c : 0)),
                                      (lds_void*)(buf + c * 64), 16, 0, 0);
 }
 
@@ -505,7 +510,8 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
   const uint32_t stride = gridDim.x * kEncBfWaves;
   uint32_t tile = blockIdx.x * kEncBfWaves + wave;
   uint4* buf = s_raw[wave];
-  if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, lane, buf);
+  const uint32_t din = cst->din, kval = din >> 4;   // k-steps that hold input coordinates
+  if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, din, lane, buf);
   if constexpr (!VAL)
     for (int i = tid; i < 2048; i += kEncBfThreads) s_frag[i] = frag[i];
   if (tid < 16) reinterpret_cast<uint4*>(s_dm)[tid] = reinterpret_cast<const uint4*>(dmask)[tid];
@@ -544,7 +550,12 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
       dmv[c] = u32x4{dm.x, dm.y, dm.z, dm.w};
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
-    if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, lane, buf);
+    if (kval < 8) {   // zero padding past din
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (uint32_t(c) >= kval) raw[c] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, din, lane, buf);
     store(prev);
 
     float nu2 = 0.f;
@@ -603,6 +614,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t tpg = uint32_t((N + 31) / 32);
   const uint32_t ntiles = uint32_t(G) * tpg;
+  const uint32_t din = cst->din;   // row length (128, or less when zero-padded)
   for (uint32_t tile = blockIdx.x * kEncWaves + wave; tile < ntiles; tile += gridDim.x * kEncWaves) {
     const uint32_t gt = tile / tpg;
     const int64_t g = gt;
@@ -611,18 +623,34 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     // lanes past the end of a ragged group load the group's last key; their
     // results are never stored and each key has its own matrix column
     const int64_t nl = valid ? n : N - 1;
-    const uint4* src = reinterpret_cast<const uint4*>(keys + ((g * N + nl) * 128 + 64 * h));
+    const float* row = keys + (g * N + nl) * din;
+    const uint4* src = reinterpret_cast<const uint4*>(row + 64 * h);
     const uint4* fl = reinterpret_cast<const uint4*>(s_flip) + h * 16;
     float x[64];
     float nu2 = 0.f;
+    if (din == 128) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint4 v = src[c];
-      const uint4 f = fl[c];
-      x[4 * c + 0] = __uint_as_float(v.x ^ f.x);
-      x[4 * c + 1] = __uint_as_float(v.y ^ f.y);
-      x[4 * c + 2] = __uint_as_float(v.z ^ f.z);
-      x[4 * c + 3] = __uint_as_float(v.w ^ f.w);
+      for (int c = 0; c < 16; ++c) {
+        const uint4 v = src[c];
+        const uint4 f = fl[c];
+        x[4 * c + 0] = __uint_as_float(v.x ^ f.x);
+        x[4 * c + 1] = __uint_as_float(v.y ^ f.y);
+        x[4 * c + 2] = __uint_as_float(v.z ^ f.z);
+        x[4 * c + 3] = __uint_as_float(v.w ^ f.w);
+      }
+    } else {
+      // zero padding: 4-coordinate chunk c of this lane half is an input
+      // coordinate when 64 h + 4 c < din; the others read as +0
+      const int cval = std::min(16, std::max(0, (int(din) - 64 * h) / 4));
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const uint4 v = c < cval ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 f = c < cval ? fl[c] : make_uint4(0u, 0u, 0u, 0u);
+        x[4 * c + 0] = __uint_as_float(v.x ^ f.x);
+        x[4 * c + 1] = __uint_as_float(v.y ^ f.y);
+        x[4 * c + 2] = __uint_as_float(v.z ^ f.z);
+        x[4 * c + 3] = __uint_as_float(v.w ^ f.w);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 64; ++r) nu2 = fmaf(x[r], x[r], nu2);
@@ -739,16 +767,20 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   float sv[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m) sv[m] = St[(16 * seg + m) * 128 + jrow];
+  // query rows hold din <= 128 elements; coordinates at or past din are zero
+  // padding (the loads are clamped to the row and their values dropped)
+  const int din = int(cst->din);
   uint32_t u0, u1;   // raw bits of the R q input (converted after the pin below)
   {
     const int qr = std::min(qc * 4 + (wave & 3), Qg - 1);
-    const int64_t at = (g * Qg + qr) * 128 + lane;
+    const int64_t at = (g * Qg + qr) * din;
+    const int i0 = std::min(lane, din - 1), i1 = std::min(lane + 64, din - 1);
     if constexpr (QBF16) {
-      u0 = static_cast<const uint16_t*>(q)[at];
-      u1 = static_cast<const uint16_t*>(q)[at + 64];
+      u0 = static_cast<const uint16_t*>(q)[at + i0];
+      u1 = static_cast<const uint16_t*>(q)[at + i1];
     } else {
-      u0 = static_cast<const uint32_t*>(q)[at];
-      u1 = static_cast<const uint32_t*>(q)[at + 64];
+      u0 = static_cast<const uint32_t*>(q)[at + i0];
+      u1 = static_cast<const uint32_t*>(q)[at + i1];
     }
   }
   uint32_t dn0 = cst->dneg[lane >> 5], dn1 = cst->dneg[2 + (lane >> 5)];
@@ -774,7 +806,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   // (an empty use outside the branch below keeps these loads ahead of the key
   // tiles: issued later, waiting for them would also wait for the tiles)
   asm volatile("" : "+v"(u0), "+v"(u1), "+v"(dn0), "+v"(dn1));
-  const float v0 = __uint_as_float(QBF16 ? u0 << 16 : u0), v1 = __uint_as_float(QBF16 ? u1 << 16 : u1);
+  const float v0 = lane < din ? __uint_as_float(QBF16 ? u0 << 16 : u0) : 0.f;
+  const float v1 = lane + 64 < din ? __uint_as_float(QBF16 ? u1 << 16 : u1) : 0.f;
 
   // ---- S q partial sums over this wave's sixteen columns
   {
@@ -782,7 +815,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
       const int qh = qc * 4 + qq;
-      const int64_t at = (g * Qg + std::min(qh, Qg - 1)) * 128 + 16 * seg;
+      const bool seg_in = 16 * seg < din;   // this wave's sixteen coordinates are input, not padding
+      const int64_t at = (g * Qg + std::min(qh, Qg - 1)) * din + (seg_in ? 16 * seg : 0);
       float qv[16];
       if constexpr (QBF16) {
         const uint32_t* qp = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + at);
@@ -799,7 +833,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
       float a = 0.f;
 #pragma unroll
       for (int m = 0; m < 16; ++m) a = fmaf(sv[m], qv[m], a);
-      acc[qq] = qh < Qg ? a : 0.f;
+      acc[qq] = qh < Qg && seg_in ? a : 0.f;
     }
     sm.part[seg][jrow] = f32x4{acc[0], acc[1], acc[2], acc[3]};
   }
@@ -1017,14 +1051,16 @@ __global__ __launch_bounds__(256) void decode128_kernel(const uint32_t* __restri
   const uint32_t n1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
   y0 = (n0 ? -y0 : y0) * sc;
   y1 = (n1 ? -y1 : y1) * sc;
+  // rows of din elements: the coordinates a zero-padded input never had are dropped
+  const int din = int(cst->din);
   if constexpr (BF16OUT) {
-    __bf16* o = static_cast<__bf16*>(out) + key * 128;
-    o[lane] = static_cast<__bf16>(y0);
-    o[lane + 64] = static_cast<__bf16>(y1);
+    __bf16* o = static_cast<__bf16*>(out) + key * din;
+    if (lane < din) o[lane] = static_cast<__bf16>(y0);
+    if (lane + 64 < din) o[lane + 64] = static_cast<__bf16>(y1);
   } else {
-    float* o = static_cast<float*>(out) + key * 128;
-    o[lane] = y0;
-    o[lane + 64] = y1;
+    float* o = static_cast<float*>(out) + key * din;
+    if (lane < din) o[lane] = y0;
+    if (lane + 64 < din) o[lane + 64] = y1;
   }
 }
 
@@ -1264,9 +1300,10 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
   const float sc = cst->inv_sqrt_d;
   const uint32_t f0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
   const uint32_t f1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
-  float* o = out + gh * 128;
-  o[lane] = (f0 ? -y0 : y0) * sc;
-  o[64 + lane] = (f1 ? -y1 : y1) * sc;
+  const int din = int(cst->din);   // output rows keep the input coordinates only
+  float* o = out + gh * din;
+  if (lane < din) o[lane] = (f0 ? -y0 : y0) * sc;
+  if (64 + lane < din) o[64 + lane] = (f1 ? -y1 : y1) * sc;
 }
 
 }  // namespace

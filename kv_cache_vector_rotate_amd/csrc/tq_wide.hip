@@ -106,13 +106,19 @@ __global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict_
   for (int k = 0; k < K; ++k) cpos[k] = cst->cpos_s[k];
   const float sqrt_d = cst->sqrt_d;
   const uint32_t dn = (cst->dneg[lane >> 1] >> (16 * (lane & 1))) & 0xffffu;
+  // rows of din <= 1024 elements (a multiple of 16): lanes at or past
+  // din / 16 hold zero padding (their loads re-read the row's first chunk)
+  const int din = int(cst->din);
+  const bool lane_in = 16 * lane < din;
+  const int col = lane_in ? 16 * lane : 0;
 
   for (int64_t w = wave0; w < nk; w += wstride) {
     const int64_t kk = k0 + w;   // key index over [G][N]
     float x[16];
     if constexpr (BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + kk * kD + 16 * lane);
-      const uint4 a = src[0], b = src[1];
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + kk * din + col);
+      uint4 a = src[0], b = src[1];
+      if (!lane_in) a = b = make_uint4(0u, 0u, 0u, 0u);
       const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -120,10 +126,11 @@ __global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict_
         x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
       }
     } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + kk * kD + 16 * lane);
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + kk * din + col);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 v = src[i];
+        float4 v = src[i];
+        if (!lane_in) v = make_float4(0.f, 0.f, 0.f, 0.f);
         x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
       }
     }
@@ -366,10 +373,13 @@ __global__ __launch_bounds__(1024) void qprep1024_kernel(const void* __restrict_
   __shared__ float s_part[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t gq = blockIdx.x;
-  if constexpr (QBF16)
-    s_q[tid] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[gq * kD + tid]) << 16);
+  const int din = int(cst->din);   // query rows of din elements; the rest is zero padding
+  if (tid >= din)
+    s_q[tid] = 0.f;
+  else if constexpr (QBF16)
+    s_q[tid] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(q)[gq * din + tid]) << 16);
   else
-    s_q[tid] = static_cast<const float*>(q)[gq * kD + tid];
+    s_q[tid] = static_cast<const float*>(q)[gq * din + tid];
   __syncthreads();
   float* xr = X + gq * 2 * kD;
   if (wave == 0) {

@@ -29,6 +29,11 @@ DESIGN.md):
   estimator uses the stored values.
 * delta and S come from a counter-based SplitMix64 stream (below), not from
   numpy's RandomState: only their distribution matters to the method.
+* a dimension d that is not a power of two is zero-padded to the next power
+  of two D and the method runs in D dimensions (delta of length D, S with
+  m = D rows over D columns, the N(0, 1/D) codebook); decoded vectors keep
+  their first d coordinates [ICLR 2026 digest, 実装のポイント: zero padding
+  to the nearest power of two for the Hadamard transform].
 """
 
 from __future__ import annotations
@@ -46,7 +51,7 @@ __all__ = [
     "packed_nbytes", "decode_mse", "score", "estimate_inner_product",
     "exact_logits", "top_k", "fp16_midpoint_flag", "ZERO_NORM",
     "FLAG_BAND", "kv_bytes_per_vector",
-    "lloyd_max_beta", "haar_rotation", "value_quantizer", "ValueEncodeResult", "encode_values", "value_packed_nbytes",
+    "lloyd_max_beta", "haar_rotation", "rotation_dim", "value_quantizer", "ValueEncodeResult", "encode_values", "value_packed_nbytes",
     "pack_values", "unpack_values", "decode_values", "attention_from_logits", "attention",
 ]
 
@@ -268,6 +273,12 @@ class Codebook:
     R: np.ndarray        # [d, d] float64 dense rotation
     S_rot: np.ndarray    # [m, d] float64 = S R^T: float16-rounded N(0,1) draws
     kind: str = "gaussian"   # coordinate law of the Lloyd-Max tables: "gaussian" or "beta"
+    d_in: int = 0        # length of input rows when they are zero-padded to d (0: d)
+
+    @property
+    def din(self) -> int:
+        """Length of the vectors the caller passes (and gets back)."""
+        return self.d_in or self.d
 
     @property
     def B(self) -> int:
@@ -288,6 +299,26 @@ def _lloyd_tables(d: int, B: int, kind: str):
     raise ValueError(kind)
 
 
+def rotation_dim(d: int) -> int:
+    """The power of two the method runs in for d-dimensional vectors: d
+    itself, or the next power of two (zero padding) [ICLR 2026 digest,
+    実装のポイント]."""
+    if d < 1:
+        raise ValueError("d >= 1")
+    return 1 << (d - 1).bit_length()
+
+
+def _pad_rows(cb: Codebook, x) -> np.ndarray:
+    """Rows of length cb.din as float64, zero-padded to cb.d."""
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] == cb.din, (x.shape, cb.din)
+    if cb.din == cb.d:
+        return x
+    out = np.zeros(x.shape[:-1] + (cb.d,))
+    out[..., :cb.din] = x
+    return out
+
+
 def make_codebook(d: int, bits: int, m: int, seed: int, kind: str = "gaussian") -> Codebook:
     """Quantizer state: Lloyd-Max for N(0,1/d) with L = 2**(bits-1) levels
     (scale equivariance: N(0,1) levels times 1/sqrt(d)), delta and S from the
@@ -297,15 +328,20 @@ def make_codebook(d: int, bits: int, m: int, seed: int, kind: str = "gaussian") 
     The sketch is drawn in the rotated basis: S_rot has i.i.d. N(0,1)
     entries (rounded to float16) and S = S_rot R.  R is orthogonal, so S has
     the same i.i.d. N(0,1) law [Qiita explainer, Stage 2: Gaussian random
-    projection], and S r = S_rot (R r)."""
+    projection], and S r = S_rot (R r).
+
+    A d that is not a power of two gives the codebook of D = rotation_dim(d)
+    (same seed, so the same delta, S and levels) that takes rows of length d
+    and zero-pads them."""
     if bits < 2:
         raise ValueError("bits >= 2 (one bit is the QJL sign)")
+    d_in, d = d, rotation_dim(d)
     lv, th = _lloyd_tables(d, bits - 1, kind)
     delta = rademacher_signs(seed, d)
     R = rotation_matrix(delta)
     S_rot = gaussian_sketch(seed, m, d).astype(np.float64)
     return Codebook(d=d, bits=bits, m=m, seed=seed, levels=lv, thresholds=th, delta=delta,
-                    S=S_rot @ R, R=R, S_rot=S_rot, kind=kind)
+                    S=S_rot @ R, R=R, S_rot=S_rot, kind=kind, d_in=d_in if d_in != d else 0)
 
 
 # --------------------------------------------------------------------------
@@ -350,7 +386,8 @@ def quantize_rotated(cb: Codebook, y: np.ndarray) -> np.ndarray:
 
 def encode(cb: Codebook, keys: np.ndarray, S: Optional[np.ndarray] = None,
            codes: Optional[np.ndarray] = None) -> EncodeResult:
-    """Encode rows of ``keys`` ([n, d], any float dtype, used as exact fp64).
+    """Encode rows of ``keys`` ([n, din], any float dtype, used as exact fp64;
+    zero-padded to d when din < d).
 
     Per key k: nu = ||k||; if nu < 1e-10 the record is all zero.  Otherwise
     x = k / nu, y = R x, code_i = #{t_j <= y_i}, k_mse = nu R^T c[code],
@@ -361,7 +398,7 @@ def encode(cb: Codebook, keys: np.ndarray, S: Optional[np.ndarray] = None,
     chose at a flagged boundary coordinate.
     """
     S = cb.S if S is None else np.asarray(S, dtype=np.float64)
-    k = np.asarray(keys, dtype=np.float64)
+    k = _pad_rows(cb, keys)
     n, d = k.shape
     assert d == cb.d
     nu = np.sqrt(np.sum(k * k, axis=1))
@@ -462,11 +499,11 @@ def unpack(cb: Codebook, buf: np.ndarray, G: int, N: int):
 # --------------------------------------------------------------------------
 
 def decode_mse(cb: Codebook, buf: np.ndarray, G: int, N: int) -> np.ndarray:
-    """k_mse = nu~ R^T c[code] for every record: [G, N, d] fp64.  The MSE-only
-    reconstruction (what the community API calls the MSE compressor
-    [Qiita explainer, API table])."""
+    """k_mse = nu~ R^T c[code] for every record: [G, N, din] fp64 (the first
+    din coordinates).  The MSE-only reconstruction (what the community API
+    calls the MSE compressor [Qiita explainer, API table])."""
     codes, _, nu16, _ = unpack(cb, buf, G, N)
-    return nu16.astype(np.float64)[..., None] * (cb.levels[codes] @ cb.R)
+    return (nu16.astype(np.float64)[..., None] * (cb.levels[codes] @ cb.R))[..., :cb.din]
 
 
 def estimate_inner_product(q, k_mse, rho, S, sign_bits) -> np.ndarray:
@@ -484,11 +521,11 @@ def estimate_inner_product(q, k_mse, rho, S, sign_bits) -> np.ndarray:
 
 
 def score(cb: Codebook, buf: np.ndarray, G: int, N: int, q: np.ndarray) -> np.ndarray:
-    """Logits [G, Qg, N] of queries q [G, Qg, d] against the packed keys of
+    """Logits [G, Qg, N] of queries q [G, Qg, din] against the packed keys of
     their group, from the stored record only (so it can score any producer's
     buffer).  Queries stay full precision; keys are never dequantised by the
     estimator's definition beyond k_mse."""
-    q = np.asarray(q, dtype=np.float64)
+    q = _pad_rows(cb, q)
     codes, signs, nu16, rho16 = unpack(cb, buf, G, N)
     k_mse = nu16.astype(np.float64)[..., None] * (cb.levels[codes] @ cb.R)   # [G,N,d]
     sgn = 1.0 - 2.0 * signs.astype(np.float64)                                # [G,N,m]
@@ -567,7 +604,7 @@ def encode_values(cb: Codebook, values: np.ndarray) -> ValueEncodeResult:
     [Qiita explainer, API table (value compression = Stage 1); ICLR 2026
     digest, Step 1 and the zero-vector rule]."""
     lv, th = value_quantizer(cb)
-    v = np.asarray(values, dtype=np.float64)
+    v = _pad_rows(cb, values)
     n, d = v.shape
     assert d == cb.d
     nu = np.sqrt(np.sum(v * v, axis=1))
@@ -618,17 +655,18 @@ def unpack_values(cb: Codebook, buf: np.ndarray, G: int, N: int):
 
 
 def decode_values(cb: Codebook, buf: np.ndarray, G: int, N: int) -> np.ndarray:
-    """v_mse = nu~ R^T c_v[code]: [G, N, d] fp64."""
+    """v_mse = nu~ R^T c_v[code]: [G, N, din] fp64 (the first din coordinates)."""
     lv, _ = value_quantizer(cb)
     codes, nu16 = unpack_values(cb, buf, G, N)
-    return nu16.astype(np.float64)[..., None] * (lv[codes] @ cb.R)
+    return (nu16.astype(np.float64)[..., None] * (lv[codes] @ cb.R))[..., :cb.din]
 
 
 def attention_from_logits(cb: Codebook, logits: np.ndarray, vbuf: np.ndarray, G: int, N: int,
                           scale: Optional[float] = None) -> np.ndarray:
     """out[g, h] = sum_n softmax_n(scale * logits[g, h, :]) v_mse[g, n]:
-    [G, Qg, d] fp64, from the given logits and the packed values."""
-    scale = 1.0 / math.sqrt(cb.d) if scale is None else float(scale)
+    [G, Qg, din] fp64, from the given logits and the packed values (scale
+    1/sqrt(din) by default)."""
+    scale = 1.0 / math.sqrt(cb.din) if scale is None else float(scale)
     z = scale * np.asarray(logits, dtype=np.float64)
     z = z - z.max(axis=-1, keepdims=True)
     w = np.exp(z)

@@ -91,3 +91,28 @@ def test_packed_bytes_formula():
         assert kb == (bits - 1) * d // 8 + d // 8 + 4
     assert O.kv_bytes_per_vector(128, 3)[0] == 52
     assert O.kv_bytes_per_vector(1024, 4)[0] == 516
+
+
+def test_rotation_dim_and_padded_tables():
+    """Zero padding to the next power of two [ICLR 2026 digest, 実装のポイント]:
+    the host rule, and the padded codebook's tables are the D-dimensional
+    oracle's (same seed)."""
+    lib = K.library()
+    for d, D in ((96, 128), (80, 128), (112, 128), (128, 128), (32, 32), (16, 32), (48, 64),
+                 (768, 1024), (1008, 1024), (1024, 1024), (100, 0), (1000, 0), (2048, 0), (0, 0)):
+        assert lib.tq_rotation_dim(d) == D, d
+        assert K.rotation_dim(d) == D
+    for d in (96, 768):
+        D = lib.tq_rotation_dim(d)
+        t = K.codebook_tables(d, 4, D, 42)
+        cb = O.make_codebook(d, 4, D, 42)
+        assert cb.d == D and cb.din == d
+        assert np.max(np.abs(t["levels"] - cb.levels)) < 1e-12 / np.sqrt(D)
+        assert np.array_equal(t["delta"], cb.delta)
+        assert np.array_equal(t["S_rot"], cb.S_rot)
+        assert np.max(np.abs(t["S"] - cb.S)) < 1e-12
+    # m must be the padded dimension; 256 and 512 have no device kernels
+    assert lib.tq_codebook_tables(96, 3, 96, 1, None, None, None, None, None) == -2
+    h = ctypes.c_void_p()
+    assert lib.tq_make_codebook(192, 3, 256, 1, ctypes.byref(h)) == -2
+    assert lib.tq_make_codebook(48, 3, 64, 1, ctypes.byref(h)) == -2
