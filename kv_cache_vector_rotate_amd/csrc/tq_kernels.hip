@@ -460,10 +460,17 @@ __device__ __forceinline__ void issue_tile_dma(const uint16_t* __restrict__ keys
   const int64_t nl = n < N ? n : N - 1;
   const uint4* src = reinterpret_cast<const uint4*>(keys + (g * N + nl) * din) + h;
   const uint32_t kval = din >> 4;
+  if (kval == 8) {   // full rows: constant offsets
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * (uint32_t(c) < kval ? c : 0)),
-                                     (lds_void*)(buf + c * 64), 16, 0, 0);
+    for (int c = 0; c < 8; ++c)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * c),
+                                       (lds_void*)(buf + c * 64), 16, 0, 0);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * (uint32_t(c) < kval ? c : 0)),
+                                       (lds_void*)(buf + c * 64), 16, 0, 0);
+  }
 }
 
 // Hadamard A fragments of this lane (row rho = lane % 32, k-half e = lane / 32):
