@@ -19,13 +19,14 @@
  *    all-zero record [ICLR 2026 paper digest, "実装の擬似コード",
  *    "実装のポイント"].
  *
- * Packed key record layout (one buffer for G groups x N keys, m = d):
- *   planes: uint32 [G][bits][N][d/32].  Planes 0..bits-2 hold bit p of the
+ * Packed key record layout (one buffer for G groups x N keys; D =
+ * tq_rotation_dim(d), which is d itself unless d is zero-padded, and m = D):
+ *   planes: uint32 [G][bits][N][D/32].  Planes 0..bits-2 hold bit p of the
  *           level index (LSB first; levels ascending, code 0 = most negative
  *           level); plane bits-1 holds the QJL sign bits, 1 = negative.
  *           Bit j of word w is coordinate (or sketch row) 32*w + j.
  *   norms:  uint32 [G][N] = half(||k||) | half(||r||) << 16  (IEEE half, RNE).
- *   Total:  G*N*((bits-1)*d/8 + d/8 + 4) bytes.
+ *   Total:  G*N*((bits-1)*D/8 + D/8 + 4) bytes.
  *
  * Dimensions that are not a power of two: the method needs a power of two
  * for the Hadamard transform, and a shorter vector is zero-padded up to the
@@ -35,7 +36,9 @@
  * delta has D entries, S is m x D with m = D, the levels are those for
  * N(0, 1/D), and records are D-dimensional.  Keys, values and queries are
  * passed as rows of d elements and decoded vectors come back as rows of d
- * elements; the kernels read the missing coordinates as zeros.
+ * elements; the kernels read the missing coordinates as zeros.  Where a call
+ * below is limited to "d = 128" or "d = 1024", that names D: a zero-padded
+ * codebook follows the rules of its D.
  *
  * Status: every entry point returns TQ_OK (0) or a negative TQ_ERR_* code.
  * No C++ exception crosses this boundary.  Launches are asynchronous on the
@@ -195,10 +198,10 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
  * value codes plus one half norm per value.  A value record uses all `bits`
  * bits of the codebook for a Lloyd-Max code of N(0, 1/d) (2^bits levels),
  * with the same rotation R; no sketch bit.  Layout for G groups x N values:
- *   planes: uint32 [G][bits][N][d/32], bit p of the level index, LSB first,
+ *   planes: uint32 [G][bits][N][D/32], bit p of the level index, LSB first,
  *           bit j of word w = coordinate 32*w + j;
  *   norms:  uint16 [G][N] = half(||v||) (RNE); zero record if ||v|| < 1e-10.
- *   Total:  G*N*(bits*d/8 + 2) bytes.
+ *   Total:  G*N*(bits*D/8 + 2) bytes.
  * d = 128 only.
  */
 size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
