@@ -116,3 +116,10 @@ def test_rotation_dim_and_padded_tables():
     h = ctypes.c_void_p()
     assert lib.tq_make_codebook(192, 3, 256, 1, ctypes.byref(h)) == -2
     assert lib.tq_make_codebook(48, 3, 64, 1, ctypes.byref(h)) == -2
+
+
+def test_padded_beta_tables_are_the_power_of_two_tables():
+    a = K.codebook_tables(96, 3, 128, 42, kind="beta")
+    b = K.codebook_tables(128, 3, 128, 42, kind="beta")
+    for f in ("levels", "thresholds", "delta", "S", "S_rot"):
+        assert np.array_equal(a[f], b[f]), f
