@@ -238,3 +238,48 @@ def test_gpu_argument_errors():
     assert lib.tq_encode_keys(cb.handle, None, 0, 0, 8, None, None) == 0
     with pytest.raises(K.TQError):
         K.Codebook(128, 7)
+
+
+def _sampled_full_size(wl, cb, cbo, groups, rows):
+    """Encode and score a whole workload in the benchmark's launch
+    configuration; the oracle re-encodes and re-scores sampled rows of
+    sampled groups from the GPU's records."""
+    keys_bits = W.all_keys(wl)
+    q_bits = W.all_queries(wl)
+    keys = torch.from_numpy(keys_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    q = torch.from_numpy(q_bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    print(f"[case] full-size encode + score G={wl.G} N={wl.N} Qg={wl.Qg} b={wl.bits}", flush=True)
+    packed = K.encode_keys(cb, keys)
+    lg = K.score_logits(cb, q, packed, wl.N)
+    torch.cuda.synchronize()
+    del keys
+    codes, signs, nu16, rho16 = O.unpack(cbo, packed.cpu().numpy(), wl.G, wl.N)
+    lgh = lg.cpu().numpy()
+    for g in groups:
+        kg = W.bf16_bits_to_f32(keys_bits[g, rows])
+        check_encode(cbo, kg, codes[g, rows], signs[g, rows], nu16[g, rows], rho16[g, rows])
+        n = len(rows)
+        one = O.pack(cbo, codes[g:g + 1, rows], signs[g:g + 1, rows], nu16[g:g + 1, rows],
+                     rho16[g:g + 1, rows])
+        qg = W.bf16_bits_to_f32(q_bits[g])[None]
+        ref = O.score(cbo, one, 1, n, qg)
+        check_logits(lgh[g:g + 1][:, :, rows], ref, qg, np.linalg.norm(kg.astype(np.float64), axis=-1)[None])
+
+
+def test_config2_full_size_sampled():
+    """Long-context decode (G = 32, N = 131072, bf16, b = 4) in full; the
+    oracle checks the first and last 3000 keys and 2000 spread ones of three
+    groups."""
+    wl = W.workload(2)
+    rows = np.concatenate([np.arange(3000), np.arange(wl.N - 3000, wl.N),
+                           np.random.default_rng(5).choice(np.arange(3000, wl.N - 3000), 2000, replace=False)])
+    _sampled_full_size(wl, K.Codebook(128, 4), O.make_codebook(128, 4, 128, 42), (0, 17, 31), np.sort(rows))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_config3_full_size_sampled(bits):
+    """The per-layer cache (36 layers x 2 KV heads, N = 8192, 8 queries per
+    group, bf16) at each bit width; two groups checked in full."""
+    wl = W.workload(3, bits=bits)
+    _sampled_full_size(wl, K.Codebook(128, bits), O.make_codebook(128, bits, 128, 42), (3, 70),
+                       np.arange(wl.N))
