@@ -15,8 +15,7 @@ Sources (cited by page title and section; see oracle/__init__.py):
   "実装の擬似コード" (zero-vector rule, sign convention 0 = positive),
   "実装のポイント" (norm stored on the side, 8 sign bits per byte).
 
-Readings where the pages are silent or disagree (each also listed in
-DESIGN.md):
+Readings where the pages are silent or disagree:
 
 * b counts all bits: (b-1) Lloyd-Max bits + 1 QJL bit per coordinate.
 * the codebook is Lloyd-Max for N(0, 1/d); the middle threshold is exactly 0.
