@@ -400,15 +400,15 @@ int upload_device(tq::Codebook& cb) {
     build_fragments_128(cb.S_rot, frag);
     e = upload(&cb.d_frag, frag.data(), frag.size() * sizeof(uint16_t));
     // D as bf16 sign bits in the order the rotation product reads the keys:
-    // [k-half e][k-step ks][word j] covers coordinates 16 ks + 8 e + 2 j, +1;
+    // [k-half kh][k-step ks][word j] covers coordinates 16 ks + 8 kh + 2 j, +1;
     // for float32 keys sign-flip words for the lane holding [64h, 64h + 64).
     std::vector<uint32_t> dp(64, 0), ff(128, 0);
-    for (int e = 0; e < 2; ++e)
+    for (int kh = 0; kh < 2; ++kh)
       for (int ks = 0; ks < 8; ++ks)
         for (int j = 0; j < 4; ++j) {
-          const int i0 = 16 * ks + 8 * e + 2 * j;
-          dp[(e * 8 + ks) * 4 + j] = (cb.delta[i0] < 0 ? 0x8000u : 0u) |
-                                     (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
+          const int i0 = 16 * ks + 8 * kh + 2 * j;
+          dp[(kh * 8 + ks) * 4 + j] = (cb.delta[i0] < 0 ? 0x8000u : 0u) |
+                                      (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
         }
     for (int i = 0; i < 128; ++i)
       if (cb.delta[i] < 0) ff[(i >> 6) * 64 + (i & 63)] = 0x80000000u;
