@@ -173,7 +173,8 @@ def run_decode(args):
     dominant = "encode" if enc_avg_s >= sc_avg_s else "score"
     traffic = read_traffic(f"encode128_{wl.key_dtype}_b{bits}_workload{args.config}.txt" if dominant == "encode"
                            else f"score128_b{bits}_workload{args.config}.txt")
-    enc_kernel = f"encode128_{wl.key_dtype}_kernel<{bits - 1}>"
+    enc_kernel = (f"encode128_bf16_t16_kernel<{bits - 1}>" if wl.key_dtype == "bf16"
+                  else f"encode128_f32_kernel<{bits - 1}>")
     sc_kernel = f"score128_kernel<{bits - 1}, {'true' if wl.key_dtype == 'bf16' else 'false'}>"
     roof = {"bound": "hbm", "kernel": enc_kernel if dominant == "encode" else sc_kernel,
             "achieved": round(enc_gbps if dominant == "encode" else sc_gbps, 1),

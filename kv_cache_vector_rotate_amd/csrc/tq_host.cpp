@@ -261,6 +261,30 @@ void build_fragments_128(const std::vector<double>& S_rot, std::vector<uint16_t>
       }
 }
 
+// Lane layout of the 16-key bf16 encoder: lane L = 16 w + n serves key n and
+// owns the 32 coordinates [32 w, 32 w + 32) (word w of every bit plane).
+// Rotation block b leaves value i of that lane at coordinate 32 w + 4 b + i,
+// and sketch k-step t takes the lane's blocks 2t and 2t + 1, so the matrix
+// core's K index 8 w + j of step t is coordinate 32 w + 8 t + j.  The A
+// operand of step t, row block b (16 x 16 x 32 products) puts row
+// 32 (m / 4) + 4 b + m % 4 of S R^T on matrix row m = L % 16, so the lane
+// holding rows 4 w .. 4 w + 3 of block b gets sketch rows 32 w + 4 b + i:
+// fragment (t, b, lane L) holds that row at coordinates 32 (L / 16) + 8 t + j,
+// j = 0..7, negated like the two-lane table.
+void build_fragments_128_t16(const std::vector<double>& S_rot, std::vector<uint16_t>& frag) {
+  const int d = 128;
+  frag.assign(4 * 8 * 64 * 8, 0);
+  for (int t = 0; t < 4; ++t)
+    for (int b = 0; b < 8; ++b)
+      for (int L = 0; L < 64; ++L) {
+        const int m = L & 15, row = 32 * (m >> 2) + 4 * b + (m & 3);
+        for (int j = 0; j < 8; ++j) {
+          const int coord = 32 * (L >> 4) + 8 * t + j;
+          frag[((size_t(t) * 8 + b) * 64 + L) * 8 + j] = half_bits(-S_rot[size_t(row) * d + coord]);
+        }
+      }
+}
+
 // d = 1024: fragment (rb, ks, lane L) holds row 32 rb + L % 32 of S R^T at
 // coordinates 16 ks + 8 (L / 32) + t, t = 0..7 (matrix-core A order for
 // 32x32x16); the values are exact in float16.
@@ -362,7 +386,11 @@ void release_device(tq::Codebook& cb) {
   if (cb.d_dpair) (void)hipFree(cb.d_dpair);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
   if (cb.d_fragW) (void)hipFree(cb.d_fragW);
+  if (cb.d_frag16) (void)hipFree(cb.d_frag16);
+  if (cb.d_dm16) (void)hipFree(cb.d_dm16);
   cb.d_fragW = nullptr;
+  cb.d_frag16 = nullptr;
+  cb.d_dm16 = nullptr;
   cb.d_consts = nullptr;
   cb.d_frag = nullptr;
   cb.d_St = nullptr;
@@ -414,6 +442,20 @@ int upload_device(tq::Codebook& cb) {
       if (cb.delta[i] < 0) ff[(i >> 6) * 64 + (i & 63)] = 0x80000000u;
     if (e == hipSuccess) e = upload(&cb.d_dpair, dp.data(), dp.size() * 4);
     if (e == hipSuccess) e = upload(&cb.d_flip_f32, ff.data(), ff.size() * 4);
+    // 16-key encoder: [word w][k-step t][register j] covers coordinates
+    // 32 w + 8 t + 2 j, +1 (low, high half)
+    std::vector<uint16_t> f16;
+    build_fragments_128_t16(cb.S_rot, f16);
+    std::vector<uint32_t> dm(64, 0);
+    for (int w = 0; w < 4; ++w)
+      for (int t = 0; t < 4; ++t)
+        for (int j = 0; j < 4; ++j) {
+          const int i0 = 32 * w + 8 * t + 2 * j;
+          dm[(w * 4 + t) * 4 + j] = (cb.delta[i0] < 0 ? 0x8000u : 0u) |
+                                    (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
+        }
+    if (e == hipSuccess) e = upload(&cb.d_frag16, f16.data(), f16.size() * sizeof(uint16_t));
+    if (e == hipSuccess) e = upload(&cb.d_dm16, dm.data(), dm.size() * 4);
   }
   if (e != hipSuccess) {
     release_device(cb);

@@ -1,7 +1,8 @@
 // HIP kernels (gfx950 / MI355X) of the TurboQuant key path, d = 128.
 //
-//  encode:  rotation y = H D k / (||k|| sqrt(d)) as a register-resident
-//           Hadamard butterfly, Lloyd-Max codes by threshold comparison,
+//  encode:  rotation y = H D k / (||k|| sqrt(d)) on the matrix cores (bf16
+//           keys) or as a register-resident Hadamard butterfly (float32
+//           keys), Lloyd-Max codes by threshold comparison,
 //           bit-plane packing, residual, and the QJL projection S r on the
 //           matrix cores [ICLR 2026 paper digest (0h-n0), "Step 1:
 //           PolarQuant"; Qiita explainer (kai_kou), "Stage 2: QJL"].
@@ -594,6 +595,380 @@ __global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
       encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, prev);
   }
   store(prev);
+}
+
+// ---- bf16 keys, 16 keys per wave-tile (16 x 16 x 32 matrix products).
+// Lane L = 16 w + n serves key n of the tile and owns the coordinates
+// [32 w, 32 w + 32): the bits it produces are word w of every bit plane, so
+// codes and sign words leave the lane in natural order with no cross-lane
+// packing, and each lane holds 32 rotated values instead of 64 (registers
+// for three waves per SIMD).
+//
+// Rotation.  Split coordinates as c = 32 c_hi + c_lo; the Sylvester matrix
+// factors as H_128[r][c] = H_4[r_hi][c_hi] H_32[r_lo][c_lo].  Product step t
+// feeds the lane's input coordinates 32 w + 8 t + j (K index 8 w + j), and
+// output row m of block b is coordinate 32 (m / 4) + 4 b + m % 4.  The A
+// operand of (b, t) is then sigma(b / 2, t) P_{b % 2}: two per-lane +-1
+// patterns (the H_4 factor of the lane's (m / 4, w) and the low H_32 bits)
+// times the wave-uniform sign sigma(s, t) = (-1)^popcount(s & t).  For each
+// pattern the four blocks b = p + 2 s are the 4-point Hadamard over t of the
+// products P_p B_t, accumulated as a tree with shared prefixes: 11 products
+// per pattern, 22 per 16 keys.
+constexpr int kEnc16Threads = 256;
+constexpr int kEnc16Waves = kEnc16Threads / 64;
+
+// A-operand patterns of this lane (row m = lane % 16, K group lane / 16):
+// p[0] = P_0, p[1] = P_1, p[2] = -P_0, p[3] = -P_1 (bf16 +-1).
+__device__ __forceinline__ void hadamard_frags16(int lane, u32x4 (&p)[4]) {
+  const int m = lane & 15, kg = lane >> 4;
+  const int base = __builtin_popcount((m >> 2) & kg) & 1;
+  uint32_t w0[4], w1[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t v0 = 0, v1 = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * r + u;
+      const int s0 = base ^ (__builtin_popcount((m & 3) & (j & 3)) & 1);
+      const int s1 = s0 ^ (j >> 2);
+      v0 |= (s0 ? 0xBF80u : 0x3F80u) << (16 * u);
+      v1 |= (s1 ? 0xBF80u : 0x3F80u) << (16 * u);
+    }
+    w0[r] = v0;
+    w1[r] = v1;
+  }
+  p[0] = u32x4{w0[0], w0[1], w0[2], w0[3]};
+  p[1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
+  p[2] = p[0] ^ 0x80008000u;
+  p[3] = p[1] ^ 0x80008000u;
+}
+
+// Rows hold din <= 128 elements (din a multiple of 16): a lane whose eight
+// coordinates 32 w + 8 t + j lie at or past din reads the row start instead
+// (valid memory) and the consumer replaces the data by zeros.
+__device__ __forceinline__ void issue_tile_dma16(const uint16_t* __restrict__ keys, uint32_t tile,
+                                                 uint32_t tpg, int64_t N, uint32_t din, int lane,
+                                                 uint4* buf) {
+  const int w = lane >> 4, kl = lane & 15;
+  const uint32_t gt = tile / tpg;
+  const int64_t g = gt;
+  const int64_t n = int64_t(tile - gt * tpg) * 16 + kl;
+  const int64_t nl = n < N ? n : N - 1;
+  const uint4* src = reinterpret_cast<const uint4*>(keys + (g * N + nl) * din) + 4 * w;
+  if (din == 128) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + t), (lds_void*)(buf + t * 64),
+                                       16, 0, 0);
+  } else {
+    const uint4* row = src - 4 * w;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(uint32_t(32 * w + 8 * t) < din ? src + t : row),
+          (lds_void*)(buf + t * 64), 16, 0, 0);
+  }
+}
+
+struct TileOut16 {
+  uint32_t w[4];     // word (lane / 16) of planes 0..B (code planes, then the sign plane)
+  uint32_t norm;
+  int64_t g, n;
+  bool valid;
+};
+
+template <int B>
+__device__ __forceinline__ void store_tile16(const TileOut16& o, int lane, int64_t Ncap,
+                                             uint32_t* __restrict__ planes,
+                                             uint32_t* __restrict__ norms) {
+  constexpr int P = B + 1;
+  if (!o.valid) return;
+  const int w = lane >> 4;
+  uint32_t* pl = planes + (o.g * P) * Ncap * 4;
+#pragma unroll
+  for (int p = 0; p < P; ++p) pl[(p * Ncap + o.n) * 4 + w] = o.w[p];
+  if (w == 0) norms[o.g * Ncap + o.n] = o.norm;
+}
+
+// sum over the four lanes of a key (lanes n, n + 16, n + 32, n + 48)
+__device__ __forceinline__ float key16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));   // lane ^ 16
+  return xor32_sum(v);
+}
+
+// A tile between its products and its packing: the sketch accumulators are
+// read one iteration later, after the next tile's rotation products are
+// issued, so no wave waits for its own matrix products to drain.
+struct Pending16 {
+  f32x4 acc[8];
+  uint32_t wu, wd[3];
+  float rho2, nu;
+  bool zero, valid;
+  int64_t g, n;
+};
+
+template <int B>
+__device__ __forceinline__ void quant_sketch16(const f32x4 (&y)[8], float nu2, const EncConsts& ec,
+                                               const uint4* __restrict__ s_frag, int lane,
+                                               int64_t g, int64_t n, bool valid, Pending16& pd) {
+  constexpr int K = 1 << (B - 1);      // levels on the positive half
+  nu2 = key16_sum(nu2);
+  // hardware square root and reciprocal, as in the two-lane encoder
+  const float nu = __builtin_amdgcn_sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * ec.sqrt_d;                       // u = y * nu * sqrt(d)
+  const float gsc = zero ? 0.f : kResidualScale * __builtin_amdgcn_rcpf(nsd);   // u -> 2^12 y
+  float tu[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) tu[k] = ec.tpos[k] * nsd;
+
+  // fragment reads go through a per-tile opaque lane offset (no instruction)
+  // so the compiler cannot hoist the loop-invariant table out of the tile loop
+  int fl_off = lane;
+  asm volatile("" : "+v"(fl_off));
+  const half8* fh = reinterpret_cast<const half8*>(s_frag) + fl_off;
+  uint32_t wu = 0u;
+  uint32_t wd[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k] = 0u;
+  f32x4 acc[8] = {};
+  float rho2 = 0.f;
+  float mone = -1.0f;
+  asm volatile("" : "+v"(mone));
+  // chunk c = rotation blocks 2c, 2c + 1: codes, residual and fp16 hi/lo
+  // split of the lane's coordinates 32 w + 8 c + j, j = 0..7 (register pair
+  // r holds j = 2r, 2r + 1)
+  auto quant_chunk = [&](int c, uint32_t (&bh)[4], uint32_t (&bl)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float ep[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int j = 2 * r + t;
+        const float u = y[2 * c + (j >> 2)][j & 3];
+        const float a = fabsf(u);
+        wu = push_sign(wu, u);
+        float mag = ec.cpos[0];
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) {
+          // the lane mask of one compare is the carry-in of a doubling add
+          // (pushes the bit) and the select of the level
+          const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
+          uint64_t co;
+          const float up = ec.cpos[k + 1];
+          asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(wd[k]), "=s"(co) : "v"(wd[k]), "s"(below));
+          asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(mag) : "v"(up), "v"(mag), "s"(below));
+        }
+        const float yh = copysignf(mag, u);
+        // negated residual 2^12 (c[code] - y); the table holds -S R^T
+        ep[t] = fmaf(-u, gsc, yh);
+        rho2 = fmaf(ep[t], ep[t], rho2);
+      }
+      split_f16_pair(ep[0], ep[1], mone, bh[r], bl[r]);
+    }
+  };
+  auto pin_words = [&]() {
+    if constexpr (K > 2) {
+      asm volatile("" : "+v"(wu), "+v"(wd[0]), "+v"(wd[1]), "+v"(wd[2]));
+    } else {
+      asm volatile("" : "+v"(wu), "+v"(wd[0]));
+    }
+  };
+  // Software pipeline over the 4 chunks: the 16 products of chunk c share a
+  // scheduling region with the vector work of chunk c + 1, one product per
+  // five vector instructions; the fragment of row block b for chunk c + 1 is
+  // read right after the two products of chunk c that use its register.
+  uint32_t bh[2][4], bl[2][4];
+  half8 f[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) f[b] = fh[b * 64];
+  quant_chunk(0, bh[0], bl[0]);
+  pin_words();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int cur = c & 1;
+    if (c < 3) quant_chunk(c + 1, bh[cur ^ 1], bl[cur ^ 1]);
+    const half8 bhi = __builtin_bit_cast(half8, u32x4{bh[cur][0], bh[cur][1], bh[cur][2], bh[cur][3]});
+    const half8 blo = __builtin_bit_cast(half8, u32x4{bl[cur][0], bl[cur][1], bl[cur][2], bl[cur][3]});
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[b], bhi, acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[b], blo, acc[b], 0, 0, 0);
+      if (c < 3) f[b] = fh[((c + 1) * 8 + b) * 64];
+    }
+    if (c < 3) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // five VALU
+        if (i & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read
+      }
+    }
+    pin_words();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int b = 0; b < 8; ++b) pd.acc[b] = acc[b];
+  pd.wu = wu;
+#pragma unroll
+  for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) pd.wd[k] = wd[k];
+  pd.rho2 = rho2;
+  pd.nu = nu;
+  pd.zero = zero;
+  pd.valid = valid;
+  pd.g = g;
+  pd.n = n;
+}
+
+template <int B>
+__device__ __forceinline__ void finish16(const Pending16& pd, TileOut16& out) {
+  constexpr int P = B + 1;
+  const float rho2 = key16_sum(pd.rho2);
+  const float nu = pd.nu;
+  const bool zero = pd.zero, valid = pd.valid;
+  const uint32_t wu = pd.wu;
+  const uint32_t* wd = pd.wd;
+  const f32x4* acc = pd.acc;
+  const float rho = zero ? 0.f : __builtin_amdgcn_sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+
+  // words were filled oldest-bit-first: bit r sits at 31 - r
+  const bool keep = valid && !zero;
+  const uint32_t u_ = __builtin_bitreverse32(wu);
+  uint32_t pw[P - 1];
+  if constexpr (B == 1) {
+    pw[0] = ~u_;
+  } else if constexpr (B == 2) {
+    pw[1] = ~u_;
+    pw[0] = ~(u_ ^ __builtin_bitreverse32(wd[0]));
+  } else {
+    const uint32_t d0 = __builtin_bitreverse32(wd[0]);
+    const uint32_t d1 = __builtin_bitreverse32(wd[1]);
+    const uint32_t d2 = __builtin_bitreverse32(wd[2]);
+    pw[2] = ~u_;
+    pw[1] = ~(u_ ^ d1);
+    pw[0] = ~(u_ ^ d0 ^ d1 ^ d2);
+  }
+#pragma unroll
+  for (int p = 0; p < P - 1; ++p) out.w[p] = keep ? pw[p] : 0u;
+
+  // sign word: value i of block b is sketch row 32 w + 4 b + i; pushed from
+  // the top row down, row r lands at bit r
+  uint32_t sw = 0u;
+#pragma unroll
+  for (int b = 7; b >= 0; --b)
+#pragma unroll
+    for (int i = 3; i >= 0; --i) sw = push_sign(sw, acc[b][i]);
+  const bool keep_s = keep && rho2 > 0.f;
+  out.w[P - 1] = keep_s ? sw : 0u;
+  out.norm = keep ? (uint32_t(f2h_bits(nu)) | (uint32_t(f2h_bits(rho)) << 16)) : 0u;
+  out.g = pd.g;
+  out.n = pd.n;
+  out.valid = valid;
+}
+
+template <int B>
+__global__ __launch_bounds__(kEnc16Threads, 3) void encode128_bf16_t16_kernel(
+    const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
+    uint32_t* __restrict__ planes, uint32_t* __restrict__ norms,
+    const DevConsts* __restrict__ cst, const uint4* __restrict__ frag,
+    const uint4* __restrict__ dmask) {
+  __shared__ uint4 s_frag[2048];                     // 32 KB: [t 4][b 8][lane 64]
+  __shared__ uint4 s_raw[kEnc16Waves][4 * 64];       // 16 KB: per-wave key tile
+  __shared__ uint4 s_dm[16];                         // D as bf16 sign bits, [word][k-step]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = lane >> 4, kl = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t tpg = uint32_t((N + 15) / 16);
+  const uint64_t ntiles = uint64_t(G) * tpg;   // < 2^32 (the host bounds G x N)
+  const uint64_t stride = uint64_t(gridDim.x) * kEnc16Waves;
+  uint64_t tile = uint64_t(blockIdx.x) * kEnc16Waves + wave;
+  uint4* buf = s_raw[wave];
+  const uint32_t din = cst->din;
+  if (tile < ntiles) issue_tile_dma16(keys, uint32_t(tile), tpg, N, din, lane, buf);
+  for (int i = tid; i < 2048; i += kEnc16Threads) s_frag[i] = frag[i];
+  if (tid < 16) s_dm[tid] = dmask[tid];
+  EncConsts ec;
+  load_enc_consts(cst, ec);
+  u32x4 hp[4];
+  hadamard_frags16(lane, hp);
+  __syncthreads();
+
+  // Each iteration: wait for this tile's keys (the DMA issued one iteration
+  // earlier and the stores of two tiles back are the only vector memory
+  // operations in flight), copy them to registers, start the next tile's DMA,
+  // issue this tile's rotation products, pack and store the previous tile,
+  // then quantise this tile and issue its sketch products.
+  Pending16 pend;
+  TileOut16 out;
+  bool have = false;   // pend holds the previous tile (wave-uniform)
+  for (; tile < ntiles; tile += stride) {
+    const uint32_t t32 = uint32_t(tile);
+    const uint32_t gt = t32 / tpg;
+    const int64_t g = gt;
+    const int64_t n = int64_t(t32 - gt * tpg) * 16 + kl;
+    const bool valid = n < N;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    u32x4 raw[4], dmv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint4 v = buf[t * 64 + lane];
+      raw[t] = u32x4{v.x, v.y, v.z, v.w};
+      const uint4 dm = s_dm[w * 4 + t];
+      dmv[t] = u32x4{dm.x, dm.y, dm.z, dm.w};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
+    if (din < 128) {   // zero padding past din
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (uint32_t(32 * w + 8 * t) >= din) raw[t] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tile + stride < ntiles) issue_tile_dma16(keys, uint32_t(tile + stride), tpg, N, din, lane, buf);
+
+    float nu2 = 0.f;
+    bf16x8 kv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16x2 q = __builtin_bit_cast(bf16x2, uint32_t(raw[t][r]));
+        nu2 = __builtin_amdgcn_fdot2_f32_bf16(q, q, nu2, false);
+      }
+      kv[t] = __builtin_bit_cast(bf16x8, raw[t] ^ dmv[t]);
+    }
+    // y[p + 2 s] = sum_t (-1)^popcount(s & t) P_p B_t, as a prefix tree
+    f32x4 y[8];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bf16x8 pp = __builtin_bit_cast(bf16x8, hp[p]), pn = __builtin_bit_cast(bf16x8, hp[p + 2]);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[0], z, 0, 0, 0);
+      const f32x4 ap = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[1], a, 0, 0, 0);
+      const f32x4 am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pn, kv[1], a, 0, 0, 0);
+      const f32x4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[2], ap, 0, 0, 0);
+      const f32x4 c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pn, kv[2], ap, 0, 0, 0);
+      const f32x4 c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[2], am, 0, 0, 0);
+      const f32x4 c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pn, kv[2], am, 0, 0, 0);
+      y[p + 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[3], c0, 0, 0, 0);
+      y[p + 2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pn, kv[3], c1, 0, 0, 0);
+      y[p + 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pn, kv[3], c2, 0, 0, 0);
+      y[p + 6] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[3], c3, 0, 0, 0);
+    }
+    if (have) {   // the previous tile's packing runs while this tile's rotation products do
+      finish16<B>(pend, out);
+      store_tile16<B>(out, lane, Ncap, planes, norms);
+    }
+    // a wave in its vector-heavy stretch issues ahead of waves running
+    // rotation products (measured 1-2% faster than equal priorities)
+    __builtin_amdgcn_s_setprio(1);
+    quant_sketch16<B>(y, nu2, ec, s_frag, lane, g, pos + n, valid, pend);
+    __builtin_amdgcn_s_setprio(0);
+    have = true;
+  }
+  if (have) {
+    finish16<B>(pend, out);
+    store_tile16<B>(out, lane, Ncap, planes, norms);
+  }
 }
 
 // ---- float32 keys (register loads, four waves per workgroup).
@@ -1331,13 +1706,14 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
   uint32_t* planes = static_cast<uint32_t*>(packed);
   uint32_t* norms = planes + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
   if (dtype == 1) {
-    const int64_t want = (ntiles + kEncBfWaves - 1) / kEncBfWaves;
-    const int grid = int(std::min<int64_t>(want, int64_t(num_cus())));
+    const int64_t ntiles16 = G * ((N + 15) / 16);
+    const int64_t want = (ntiles16 + kEnc16Waves - 1) / kEnc16Waves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 3));
     const uint16_t* kb = static_cast<const uint16_t*>(keys);
 #define TQ_ENCB(BB)                                                                              \
-  hipLaunchKernelGGL((encode128_bf16_kernel<BB, false>), dim3(grid), dim3(kEncBfThreads), 0, s, kb, G, N, \
-                     Ncap, pos, \
-                     planes, norms, cb.d_consts, cb.d_frag, cb.d_dpair)
+  hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB>), dim3(grid), dim3(kEnc16Threads), 0, s, kb, G, N, \
+                     Ncap, pos, planes, norms, cb.d_consts, cb.d_frag16,                       \
+                     reinterpret_cast<const uint4*>(cb.d_dm16))
     switch (cb.bits - 1) {
       case 1: TQ_ENCB(1); break;
       case 2: TQ_ENCB(2); break;
