@@ -237,7 +237,7 @@ uint16_t half_bits(double v) {
   return u;
 }
 
-// Lane layout of the d = 128 encoder (two lanes per key): after its butterfly,
+// Lane layout of the d = 128 float32-key encoder (two lanes per key): after its butterfly,
 // register r of the lane in wave half h holds rotated coordinate
 //   coord(h, r) = (r % 32) + 32 * (h + 2 * (r / 32)).
 // The matrix-core B operand takes K-slice [8h, 8h+8) of each 16-wide chunk kc
@@ -383,7 +383,6 @@ void release_device(tq::Codebook& cb) {
   if (cb.d_consts) (void)hipFree(cb.d_consts);
   if (cb.d_frag) (void)hipFree(cb.d_frag);
   if (cb.d_St) (void)hipFree(cb.d_St);
-  if (cb.d_dpair) (void)hipFree(cb.d_dpair);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
   if (cb.d_fragW) (void)hipFree(cb.d_fragW);
   if (cb.d_frag16) (void)hipFree(cb.d_frag16);
@@ -394,7 +393,6 @@ void release_device(tq::Codebook& cb) {
   cb.d_consts = nullptr;
   cb.d_frag = nullptr;
   cb.d_St = nullptr;
-  cb.d_dpair = nullptr;
   cb.d_flip_f32 = nullptr;
 }
 
@@ -427,20 +425,10 @@ int upload_device(tq::Codebook& cb) {
     std::vector<uint16_t> frag;
     build_fragments_128(cb.S_rot, frag);
     e = upload(&cb.d_frag, frag.data(), frag.size() * sizeof(uint16_t));
-    // D as bf16 sign bits in the order the rotation product reads the keys:
-    // [k-half kh][k-step ks][word j] covers coordinates 16 ks + 8 kh + 2 j, +1;
-    // for float32 keys sign-flip words for the lane holding [64h, 64h + 64).
-    std::vector<uint32_t> dp(64, 0), ff(128, 0);
-    for (int kh = 0; kh < 2; ++kh)
-      for (int ks = 0; ks < 8; ++ks)
-        for (int j = 0; j < 4; ++j) {
-          const int i0 = 16 * ks + 8 * kh + 2 * j;
-          dp[(kh * 8 + ks) * 4 + j] = (cb.delta[i0] < 0 ? 0x8000u : 0u) |
-                                      (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
-        }
+    // float32 keys: sign-flip words for the lane holding [64h, 64h + 64)
+    std::vector<uint32_t> ff(128, 0);
     for (int i = 0; i < 128; ++i)
       if (cb.delta[i] < 0) ff[(i >> 6) * 64 + (i & 63)] = 0x80000000u;
-    if (e == hipSuccess) e = upload(&cb.d_dpair, dp.data(), dp.size() * 4);
     if (e == hipSuccess) e = upload(&cb.d_flip_f32, ff.data(), ff.size() * 4);
     // 16-key encoder: [word w][k-step t][register j] covers coordinates
     // 32 w + 8 t + 2 j, +1 (low, high half)

@@ -85,7 +85,11 @@ int num_cus() {
 
 // ============================================================== encode, d = 128
 //
-// Lane layout: a wave encodes 32 keys at a time, two lanes per key.  Lane
+// Two kernels: bf16 keys and values run 16 keys per wave-tile on the matrix
+// cores (encode128_bf16_t16_kernel, below); float32 keys and values use the
+// two-lane layout described here.
+//
+// Two-lane layout: a wave encodes 32 keys at a time, two lanes per key.  Lane
 // L = 32h + kl holds coordinates [64h, 64h + 64) of key kl in x[0..63].
 // Six butterfly stages run inside the register file; the stage across the
 // two halves uses v_permlane32_swap on register pairs (r, r + 32), which
@@ -419,183 +423,9 @@ __device__ __forceinline__ void value_tail(const float (&x)[64], float nu2,
   out.valid = valid;
 }
 
-// ---- bf16 keys.  Eight waves per workgroup, one workgroup per CU.  Each
-// wave owns an 8 KB LDS buffer that the next tile's keys stream into
-// (global_load_lds, 16 B per lane, no registers held) while the current tile
-// is encoded.  The rotation u = H D k runs on the matrix cores: bf16 keys
-// times +-1 are exact products, so one bf16 product per 32 x 32 x 16 block
-// gives u with fp32 accumulation (32 products per 32-key tile), where the
-// butterfly would cost about 550 vector instructions per tile.
-//
-// Product layout.  B operand (keys, K = input coordinate): lane (kl, e) of
-// k-step ks holds coordinates 16 ks + 8 e + t (t = 0..7) of key kl, which is
-// exactly the 16-byte chunk 2 ks + e of the key: the DMA places chunk
-// 2 c + h of key kl at slot c * 64 + lane, so each k-step is one
-// conflict-free 16-byte LDS read, and D is one XOR of the bf16 sign bits.
-// A operand (Hadamard rows, M = output coordinate): output row
-// 32 mb + 8 g + 4 h + e' of block mb lands in accumulator 4 g + e' of lane
-// half h; it is assigned the coordinate that the butterfly would leave in
-// register r = 16 mb + 4 g + e' of that half, (r % 32) + 32 (h + 2 (r / 32)),
-// so everything after the rotation is shared with the float32 kernel.
-// For Sylvester's H the entry sign is the parity of (row & column); with the
-// bit fields above it splits into a per-lane pattern over t, a per-lane flip
-// tied to bit 1 of ks, and a flip that depends on (mb, ks) only, so four
-// register fragments (G0, G1 and their negations) serve all 32 products.
-constexpr int kEncBfThreads = 512;
-constexpr int kEncBfWaves = kEncBfThreads / 64;
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
-
-// Rows hold din <= 128 elements (din a multiple of 16); k-steps at or past
-// din / 16 are zero padding: they re-read step 0 (valid memory) and the
-// consumer replaces them by zeros.
-__device__ __forceinline__ void issue_tile_dma(const uint16_t* __restrict__ keys, uint32_t tile,
-                                               uint32_t tpg, int64_t N, uint32_t din, int lane,
-                                               uint4* buf) {
-  const int h = lane >> 5, kl = lane & 31;
-  const uint32_t gt = tile / tpg;
-  const int64_t g = gt;
-  const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
-  const int64_t nl = n < N ? n : N - 1;
-  const uint4* src = reinterpret_cast<const uint4*>(keys + (g * N + nl) * din) + h;
-  const uint32_t kval = din >> 4;
-  if (kval == 8) {   // full rows: constant offsets
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * c),
-                                       (lds_void*)(buf + c * 64), 16, 0, 0);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + 2 * (uint32_t(c) < kval ? c : 0)),
-                                       (lds_void*)(buf + c * 64), 16, 0, 0);
-  }
-}
-
-// Hadamard A fragments of this lane (row rho = lane % 32, k-half e = lane / 32):
-// g[0] = G0, g[1] = G1, g[2] = -G0, g[3] = -G1 (bf16 +-1, eight per fragment).
-__device__ __forceinline__ void hadamard_frags(int lane, u32x4 (&g)[4]) {
-  const int rho = lane & 31, e = lane >> 5;
-  const int e0 = rho & 1, e1 = (rho >> 1) & 1, hq = (rho >> 2) & 1;
-  const int g0 = (rho >> 3) & 1, g1 = (rho >> 4) & 1;
-  uint32_t w[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = 2 * j + u;
-      const int sgn = (e0 & t) ^ (e1 & (t >> 1)) ^ (g0 & (t >> 2)) ^ (g1 & e);
-      v |= (sgn ? 0xBF80u : 0x3F80u) << (16 * u);
-    }
-    w[j] = v;
-  }
-  const uint32_t f1 = hq ? 0x80008000u : 0u;
-  g[0] = u32x4{w[0], w[1], w[2], w[3]};
-  g[1] = u32x4{w[0] ^ f1, w[1] ^ f1, w[2] ^ f1, w[3] ^ f1};
-  g[2] = g[0] ^ 0x80008000u;
-  g[3] = g[1] ^ 0x80008000u;
-}
-
-// VAL: value records (B = value bits, no sketch; norms are uint16 halves).
-template <int B, bool VAL>
-__global__ __launch_bounds__(kEncBfThreads, 2) void encode128_bf16_kernel(
-    const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
-    uint32_t* __restrict__ planes,
-    void* __restrict__ norms_, const DevConsts* __restrict__ cst,
-    const uint4* __restrict__ frag, const uint32_t* __restrict__ dmask) {
-  __shared__ uint4 s_frag[VAL ? 1 : 2048];         // 32 KB: [kc 8][jb 4][lane 64]
-  __shared__ uint4 s_raw[kEncBfWaves][8 * 64];     // 64 KB: per-wave key tile
-  __shared__ uint4 s_dm[2][8];                     // D as bf16 sign bits, [k-half][k-step]
-
-  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, kl = lane & 31;
-  // wave-uniform tile bookkeeping lives in scalar registers (tiles < 2^31)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t tpg = uint32_t((N + 31) / 32);
-  const uint32_t ntiles = uint32_t(G) * tpg;
-  const uint32_t stride = gridDim.x * kEncBfWaves;
-  uint32_t tile = blockIdx.x * kEncBfWaves + wave;
-  uint4* buf = s_raw[wave];
-  const uint32_t din = cst->din, kval = din >> 4;   // k-steps that hold input coordinates
-  if (tile < ntiles) issue_tile_dma(keys, tile, tpg, N, din, lane, buf);
-  if constexpr (!VAL)
-    for (int i = tid; i < 2048; i += kEncBfThreads) s_frag[i] = frag[i];
-  if (tid < 16) reinterpret_cast<uint4*>(s_dm)[tid] = reinterpret_cast<const uint4*>(dmask)[tid];
-  EncConsts ec;
-  load_enc_consts(cst, ec);
-  u32x4 hf[4];
-  hadamard_frags(lane, hf);
-  __syncthreads();
-
-  // Each iteration: wait for this tile's keys (the DMA issued one iteration
-  // earlier, and the previous iteration's stores, are the only vector memory
-  // operations in flight), copy them to registers, start the next tile's DMA,
-  // write the previous tile's results, then encode this tile.  The compiler
-  // does not track the loop-carried DMA, hence the explicit wait.
-  using Out = std::conditional_t<VAL, ValOut, TileOut>;
-  auto store = [&](const Out& o) {
-    if constexpr (VAL)
-      store_vtile<B>(o, lane, Ncap, planes, static_cast<uint16_t*>(norms_));
-    else
-      store_tile<B>(o, lane, Ncap, planes, static_cast<uint32_t*>(norms_));
-  };
-  Out prev;
-  prev.valid = false;
-  for (; tile < ntiles; tile += stride) {
-    const uint32_t gt = tile / tpg;
-    const int64_t g = gt;
-    const int64_t n = int64_t(tile - gt * tpg) * 32 + kl;
-    const bool valid = n < N;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    u32x4 raw[8], dmv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v = buf[c * 64 + lane];
-      raw[c] = u32x4{v.x, v.y, v.z, v.w};
-      const uint4 dm = s_dm[h][c];
-      dmv[c] = u32x4{dm.x, dm.y, dm.z, dm.w};
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
-    if (kval < 8) {   // zero padding past din
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (uint32_t(c) >= kval) raw[c] = u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tile + stride < ntiles) issue_tile_dma(keys, tile + stride, tpg, N, din, lane, buf);
-    store(prev);
-
-    float nu2 = 0.f;
-    f32x16 y[4] = {};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 kv = raw[ks] ^ dmv[ks];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x2 p = __builtin_bit_cast(bf16x2, uint32_t(raw[ks][t]));
-        nu2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, nu2, false);
-      }
-      const bf16x8 bk = __builtin_bit_cast(bf16x8, kv);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int neg = ((mb & 1) & (ks & 1)) ^ ((mb >> 1) & (ks >> 2));
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, hf[((ks >> 1) & 1) + 2 * neg]);
-        y[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bk, y[mb], 0, 0, 0);
-      }
-    }
-    float x[64];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) x[16 * mb + a] = y[mb][a];
-    if constexpr (VAL)
-      value_tail<B>(x, nu2, cst, lane, g, pos + n, valid, prev);
-    else
-      encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, prev);
-  }
-  store(prev);
-}
 
 // ---- bf16 keys, 16 keys per wave-tile (16 x 16 x 32 matrix products).
 // Lane L = 16 w + n serves key n of the tile and owns the coordinates
@@ -713,7 +543,7 @@ __device__ __forceinline__ void quant_sketch16(const f32x4 (&y)[8], float nu2, c
                                                int64_t g, int64_t n, bool valid, Pending16& pd) {
   constexpr int K = 1 << (B - 1);      // levels on the positive half
   nu2 = key16_sum(nu2);
-  // hardware square root and reciprocal, as in the two-lane encoder
+  // hardware square root and reciprocal, as in the float32-key encoder
   const float nu = __builtin_amdgcn_sqrtf(nu2);
   const bool zero = !(nu >= 1e-10f);
   const float nsd = nu * ec.sqrt_d;                       // u = y * nu * sqrt(d)
@@ -867,13 +697,74 @@ __device__ __forceinline__ void finish16(const Pending16& pd, TileOut16& out) {
   out.valid = valid;
 }
 
-template <int B>
-__global__ __launch_bounds__(kEnc16Threads, 3) void encode128_bf16_t16_kernel(
+// Value records in the 16-key layout: each lane's 32 rotated coordinates
+// give word w of the b level-index planes (same bit rules as value_tail).
+template <int BV>
+__device__ __forceinline__ void store_vtile16(const TileOut16& o, int lane, int64_t Ncap,
+                                              uint32_t* __restrict__ planes,
+                                              uint16_t* __restrict__ norms) {
+  if (!o.valid) return;
+  const int w = lane >> 4;
+  uint32_t* pl = planes + (o.g * BV) * Ncap * 4;
+#pragma unroll
+  for (int p = 0; p < BV; ++p) pl[(p * Ncap + o.n) * 4 + w] = o.w[p];
+  if (w == 0) norms[o.g * Ncap + o.n] = uint16_t(o.norm);
+}
+
+template <int BV>
+__device__ __forceinline__ void value_tail16(const f32x4 (&y)[8], float nu2,
+                                             const DevConsts* __restrict__ cst, int64_t g,
+                                             int64_t n, bool valid, TileOut16& out) {
+  constexpr int KV = 1 << (BV - 1);    // levels on the positive half
+  nu2 = key16_sum(nu2);
+  const float nu = __builtin_amdgcn_sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * cst->sqrt_d;
+  float tu[KV > 1 ? KV - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < KV - 1; ++k) tu[k] = cst->vtpos[k] * nsd;
+  uint32_t wu = 0u;
+  uint32_t wd[KV > 1 ? KV - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < (KV > 1 ? KV - 1 : 1); ++k) wd[k] = 0u;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {   // coordinate 32 w + r is value r % 4 of block r / 4
+    const float u = y[r >> 2][r & 3];
+    const float a = fabsf(u);
+    wu = push_sign(wu, u);
+#pragma unroll
+    for (int k = 0; k < KV - 1; ++k) {
+      const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
+      uint64_t co;
+      asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(wd[k]), "=s"(co) : "v"(wd[k]), "s"(below));
+    }
+  }
+  const bool keep = valid && !zero;
+  // words were filled oldest-bit-first: bit r sits at 31 - r
+  const uint32_t sg = __builtin_bitreverse32(wu);       // 1 = negative
+  out.w[BV - 1] = keep ? ~sg : 0u;
+#pragma unroll
+  for (int j = 0; j < BV - 1; ++j) {
+    uint32_t e = 0u;   // XOR of the "below" bits (complements of d_k); odd count
+#pragma unroll
+    for (int k = 0; k < KV - 1; ++k)
+      if (((k + 1) & ((1 << j) - 1)) == 0) e ^= __builtin_bitreverse32(wd[k]);
+    out.w[j] = keep ? ~(e ^ sg) : 0u;
+  }
+  out.norm = keep ? uint32_t(f2h_bits(nu)) : 0u;
+  out.g = g;
+  out.n = n;
+  out.valid = valid;
+}
+
+// VAL: value records (B = value bits, no sketch; norms are uint16 halves).
+template <int B, bool VAL>
+__global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : 3) void encode128_bf16_t16_kernel(
     const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
-    uint32_t* __restrict__ planes, uint32_t* __restrict__ norms,
+    uint32_t* __restrict__ planes, void* __restrict__ norms_,
     const DevConsts* __restrict__ cst, const uint4* __restrict__ frag,
     const uint4* __restrict__ dmask) {
-  __shared__ uint4 s_frag[2048];                     // 32 KB: [t 4][b 8][lane 64]
+  __shared__ uint4 s_frag[VAL ? 1 : 2048];           // 32 KB: [t 4][b 8][lane 64]
   __shared__ uint4 s_raw[kEnc16Waves][4 * 64];       // 16 KB: per-wave key tile
   __shared__ uint4 s_dm[16];                         // D as bf16 sign bits, [word][k-step]
 
@@ -886,7 +777,8 @@ __global__ __launch_bounds__(kEnc16Threads, 3) void encode128_bf16_t16_kernel(
   uint4* buf = s_raw[wave];
   const uint32_t din = cst->din;
   if (tile < ntiles) issue_tile_dma16(keys, uint32_t(tile), tpg, N, din, lane, buf);
-  for (int i = tid; i < 2048; i += kEnc16Threads) s_frag[i] = frag[i];
+  if constexpr (!VAL)
+    for (int i = tid; i < 2048; i += kEnc16Threads) s_frag[i] = frag[i];
   if (tid < 16) s_dm[tid] = dmask[tid];
   EncConsts ec;
   load_enc_consts(cst, ec);
@@ -954,20 +846,32 @@ __global__ __launch_bounds__(kEnc16Threads, 3) void encode128_bf16_t16_kernel(
       y[p + 4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pn, kv[3], c2, 0, 0, 0);
       y[p + 6] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp, kv[3], c3, 0, 0, 0);
     }
-    if (have) {   // the previous tile's packing runs while this tile's rotation products do
-      finish16<B>(pend, out);
-      store_tile16<B>(out, lane, Ncap, planes, norms);
+    uint32_t* nk = static_cast<uint32_t*>(norms_);
+    uint16_t* nv = static_cast<uint16_t*>(norms_);
+    if constexpr (VAL) {
+      if (have) store_vtile16<B>(out, lane, Ncap, planes, nv);
+      value_tail16<B>(y, nu2, cst, g, pos + n, valid, out);
+      have = true;
+    } else {
+      if (have) {   // the previous tile's packing runs while this tile's rotation products do
+        finish16<B>(pend, out);
+        store_tile16<B>(out, lane, Ncap, planes, nk);
+      }
+      // a wave in its vector-heavy stretch issues ahead of waves running
+      // rotation products (measured 1-2% faster than equal priorities)
+      __builtin_amdgcn_s_setprio(1);
+      quant_sketch16<B>(y, nu2, ec, s_frag, lane, g, pos + n, valid, pend);
+      __builtin_amdgcn_s_setprio(0);
+      have = true;
     }
-    // a wave in its vector-heavy stretch issues ahead of waves running
-    // rotation products (measured 1-2% faster than equal priorities)
-    __builtin_amdgcn_s_setprio(1);
-    quant_sketch16<B>(y, nu2, ec, s_frag, lane, g, pos + n, valid, pend);
-    __builtin_amdgcn_s_setprio(0);
-    have = true;
   }
   if (have) {
-    finish16<B>(pend, out);
-    store_tile16<B>(out, lane, Ncap, planes, norms);
+    if constexpr (VAL) {
+      store_vtile16<B>(out, lane, Ncap, planes, static_cast<uint16_t*>(norms_));
+    } else {
+      finish16<B>(pend, out);
+      store_tile16<B>(out, lane, Ncap, planes, static_cast<uint32_t*>(norms_));
+    }
   }
 }
 
@@ -1711,7 +1615,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
     const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 3));
     const uint16_t* kb = static_cast<const uint16_t*>(keys);
 #define TQ_ENCB(BB)                                                                              \
-  hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB>), dim3(grid), dim3(kEnc16Threads), 0, s, kb, G, N, \
+  hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, false>), dim3(grid), dim3(kEnc16Threads), 0, s, kb, G, N, \
                      Ncap, pos, planes, norms, cb.d_consts, cb.d_frag16,                       \
                      reinterpret_cast<const uint4*>(cb.d_dm16))
     switch (cb.bits - 1) {
@@ -1744,12 +1648,14 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
   uint32_t* planes = static_cast<uint32_t*>(vpacked);
   uint16_t* norms = reinterpret_cast<uint16_t*>(planes + G * N * int64_t(cb.bits) * (cb.d / 32));
   if (dtype == 1) {
-    const int64_t want = (ntiles + kEncBfWaves - 1) / kEncBfWaves;
-    const int grid = int(std::min<int64_t>(want, int64_t(num_cus())));
+    const int64_t ntiles16 = G * ((N + 15) / 16);
+    const int64_t want = (ntiles16 + kEnc16Waves - 1) / kEnc16Waves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 4));
     const uint16_t* vb = static_cast<const uint16_t*>(values);
 #define TQ_VB(BB)                                                                                  \
-  hipLaunchKernelGGL((encode128_bf16_kernel<BB, true>), dim3(grid), dim3(kEncBfThreads), 0, s, vb, \
-                     G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag, cb.d_dpair)
+  hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, true>), dim3(grid), dim3(kEnc16Threads), 0, s, vb, \
+                     G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag16,                 \
+                     reinterpret_cast<const uint4*>(cb.d_dm16))
     switch (cb.bits) {
       case 2: TQ_VB(2); break;
       case 3: TQ_VB(3); break;

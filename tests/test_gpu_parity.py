@@ -75,7 +75,7 @@ def test_config0_full():
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("N", [1, 31, 33, 1000])
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 31, 33, 1000])   # 16- and 32-key tile edges
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_ragged_groups(bits, N, dt):
     rng = np.random.default_rng(1000 * bits + N + (7 if dt == "bf16" else 0))
