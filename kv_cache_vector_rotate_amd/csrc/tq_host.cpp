@@ -383,6 +383,7 @@ void release_device(tq::Codebook& cb) {
   if (cb.d_consts) (void)hipFree(cb.d_consts);
   if (cb.d_frag) (void)hipFree(cb.d_frag);
   if (cb.d_St) (void)hipFree(cb.d_St);
+  if (cb.d_Sh) (void)hipFree(cb.d_Sh);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
   if (cb.d_fragW) (void)hipFree(cb.d_fragW);
   if (cb.d_frag16) (void)hipFree(cb.d_frag16);
@@ -393,6 +394,7 @@ void release_device(tq::Codebook& cb) {
   cb.d_consts = nullptr;
   cb.d_frag = nullptr;
   cb.d_St = nullptr;
+  cb.d_Sh = nullptr;
   cb.d_flip_f32 = nullptr;
 }
 
@@ -443,6 +445,13 @@ int upload_device(tq::Codebook& cb) {
                                     (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
         }
     if (e == hipSuccess) e = upload(&cb.d_frag16, f16.data(), f16.size() * sizeof(uint16_t));
+    // scorer: S R^T columns 16 s .. 16 s + 15 of row j, contiguous per (s, j)
+    std::vector<uint16_t> sh(8 * 128 * 16);
+    for (int sg = 0; sg < 8; ++sg)
+      for (int j = 0; j < 128; ++j)
+        for (int m = 0; m < 16; ++m)
+          sh[(size_t(sg) * 128 + j) * 16 + m] = half_bits(cb.S_rot[size_t(j) * 128 + 16 * sg + m]);
+    if (e == hipSuccess) e = upload(&cb.d_Sh, sh.data(), sh.size() * sizeof(uint16_t));
     if (e == hipSuccess) e = upload(&cb.d_dm16, dm.data(), dm.size() * 4);
   }
   if (e != hipSuccess) {
@@ -562,7 +571,8 @@ int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
   if (G == 0 || N == 0) return TQ_OK;
   if (!keys || !packed || !aligned16(keys) || !aligned16(packed)) return TQ_ERR_ARG;
   if (!tq::encode_supported(*cb)) return TQ_ERR_UNSUPPORTED;
-  if (G * ((N + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;   // 32-key tiles < 2^31
+  // tile counts fit the kernels' 32-bit indices: 32-key tiles < 2^31, 16-key tiles < 2^32
+  if (G * ((N + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
   hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, N, N, 0, packed,

@@ -1030,7 +1030,7 @@ template <int B, bool QBF16>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
     int64_t N, int64_t Ncap, int Qg, int64_t chunk, float* __restrict__ logits,
-    const DevConsts* __restrict__ cst, const float* __restrict__ St) {
+    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
   constexpr int D = 2;   // key tiles in flight per wave (two measured 2-3% faster than three at b = 3)
@@ -1047,12 +1047,17 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const uint4* pg = planes + g * P * Ncap;
   const uint32_t* ng = norms + g * Ncap;
 
-  // ---- loads: S columns, the R q input, the first D key tiles
+  // ---- loads: sixteen S R^T columns (fp16, exact), the R q input, the
+  // first D key tiles.  S q = (S R^T)(R q): the scorer needs R q anyway, and
+  // the fp16 table is half the bytes every workgroup fetches at its start.
   const int seg = wave >> 1;
   const int jrow = 64 * (wave & 1) + lane;
-  float sv[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) sv[m] = St[(16 * seg + m) * 128 + jrow];
+  uint4 sh[2];   // (S R^T)[jrow][16 seg + m], m = 0..15
+  {
+    const uint4* sp = Sh + (size_t(seg) * 128 + jrow) * 2;
+    sh[0] = sp[0];
+    sh[1] = sp[1];
+  }
   // query rows hold din <= 128 elements; coordinates at or past din are zero
   // padding (the loads are clamped to the row and their values dropped)
   const int din = int(cst->din);
@@ -1095,34 +1100,6 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const float v0 = lane < din ? __uint_as_float(QBF16 ? u0 << 16 : u0) : 0.f;
   const float v1 = lane + 64 < din ? __uint_as_float(QBF16 ? u1 << 16 : u1) : 0.f;
 
-  // ---- S q partial sums over this wave's sixteen columns
-  {
-    float acc[4];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      const int qh = qc * 4 + qq;
-      const bool seg_in = 16 * seg < din;   // this wave's sixteen coordinates are input, not padding
-      const int64_t at = (g * Qg + std::min(qh, Qg - 1)) * din + (seg_in ? 16 * seg : 0);
-      float qv[16];
-      if constexpr (QBF16) {
-        const uint32_t* qp = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(q) + at);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const uint32_t pr = qp[m];
-          qv[2 * m] = __uint_as_float(pr << 16);
-          qv[2 * m + 1] = __uint_as_float(pr & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) qv[m] = static_cast<const float*>(q)[at + m];
-      }
-      float a = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) a = fmaf(sv[m], qv[m], a);
-      acc[qq] = qh < Qg && seg_in ? a : 0.f;
-    }
-    sm.part[seg][jrow] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-  }
   // ---- R q = H D q / sqrt(d)
   if (wave < 4) {
     const bool live = qc * 4 + wave < Qg;
@@ -1141,11 +1118,27 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = 2.0f * (y1 * cst->inv_sqrt_d);
   }
   __syncthreads();
+  // ---- 2 S q partial sums over this wave's sixteen coordinates of 2 R q
+  {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t hw[8] = {sh[0].x, sh[0].y, sh[0].z, sh[0].w, sh[1].x, sh[1].y, sh[1].z, sh[1].w};
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float sv = h2f_bits(hw[m >> 1] >> (16 * (m & 1)));
+      const f32x4 xv = sm.x[0][m & 7][2 * seg + (m >> 3)];   // coordinate 16 seg + m, 4 queries
+      acc[0] = fmaf(sv, xv[0], acc[0]);
+      acc[1] = fmaf(sv, xv[1], acc[1]);
+      acc[2] = fmaf(sv, xv[2], acc[2]);
+      acc[3] = fmaf(sv, xv[3], acc[3]);
+    }
+    sm.part[seg][jrow] = acc;
+  }
+  __syncthreads();
   if (tid < 128) {
     f32x4 t = sm.part[0][tid];
 #pragma unroll
     for (int k = 1; k < 8; ++k) t += sm.part[k][tid];
-    sm.x[1][tid & 7][tid >> 3] = 2.0f * t;
+    sm.x[1][tid & 7][tid >> 3] = t;
   }
   __syncthreads();
   // ---- tables: thread (pos, ty, hi) writes entries idx = 8 hi + j, j = 0..7
@@ -1749,7 +1742,7 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const bool bf = qdtype == 1;
 #define TQ_SC(BB, QB)                                                                   \
   hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_St)
+                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_Sh)
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
