@@ -417,7 +417,7 @@ int upload_device(tq::Codebook& cb) {
     build_fragments_wide(cb.S_rot, cb.d, frag);
     e = upload(&cb.d_fragW, frag.data(), frag.size() * sizeof(uint16_t));
   }
-  if (e == hipSuccess) {   // the scorer reads S column by column: store its transpose
+  if (e == hipSuccess && cb.d == 1024) {   // the d = 1024 query preparation reads S column by column
     std::vector<float> st(cb.S.size());
     for (int j = 0; j < cb.m; ++j)
       for (int c = 0; c < cb.d; ++c) st[size_t(c) * cb.m + j] = float(cb.S[size_t(j) * cb.d + c]);

@@ -46,7 +46,7 @@ struct Codebook {
   uint4* d_frag = nullptr;       // -S R^T as float16 (exact), matrix-core A-operand order
   uint4* d_frag16 = nullptr;     // the same for the 16-key bf16 encoder: [k-step 4][row block 8][lane 64]
   uint32_t* d_dm16 = nullptr;    // [word 4][k-step 4][4] D as bf16 sign bits for that encoder
-  float* d_St = nullptr;         // S transposed, float32 [d][m]
+  float* d_St = nullptr;         // S transposed, float32 [d][m] (d = 1024)
   uint4* d_Sh = nullptr;         // d = 128 scorer: S R^T as float16 (exact), [column segment 8][row 128][16]
   uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
   uint4* d_fragW = nullptr;         // S R^T for d = 1024: [row block 32][k-step 64][lane 64]
