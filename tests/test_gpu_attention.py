@@ -52,7 +52,7 @@ def _encode_values_checked(cb, cbo, v, dtype):
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [1, 33, 300])
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 33, 300])   # 16- and 32-key tile edges
 def test_value_encode(bits, dt, N):
     rng = np.random.default_rng(900 + 10 * bits + N + (5 if dt == "bf16" else 0))
     v = _rows(rng, 3, N)
