@@ -279,6 +279,77 @@ def test_qjl_estimator_unbiased_and_variance():
     assert abs(q @ r) > 20 * se
 
 
+def test_score_equals_estimator_on_packed_records():
+    """score() reads records from the packed buffer; for every (query, key) it
+    equals the Monte-Carlo-pinned estimator above, evaluated on the same
+    record's pieces: the MSE reconstruction, the stored half norm of the
+    residual, the codebook's S and the stored sign bits [Qiita explainer,
+    Stage 2: QJL, estimator equation].  This ties the function every GPU
+    logit test compares against to the unbiasedness pin."""
+    cb = O.make_codebook(128, 3, 128, 42)
+    rng = np.random.default_rng(91)
+    G, N, Qg = 2, 37, 3
+    k = rng.standard_normal((G, N, 128)) * np.exp(rng.normal(0, 0.7, 128))
+    k[1, 5] = 0.0                                  # a zero record among them
+    e = O.encode(cb, k.reshape(-1, 128))
+    buf = O.pack(cb, e.codes.reshape(G, N, 128), e.signs.reshape(G, N, 128),
+                 e.nu16.reshape(G, N), e.rho16.reshape(G, N))
+    q = rng.standard_normal((G, Qg, 128))
+    lg = O.score(cb, buf, G, N, q)
+    codes, signs, nu16, rho16 = O.unpack(cb, buf, G, N)
+    kmse = O.decode_mse(cb, buf, G, N)
+    for g in range(G):
+        for h in range(Qg):
+            ref = O.estimate_inner_product(q[g, h][None, :], kmse[g], rho16[g].astype(np.float64),
+                                           cb.S, signs[g])
+            assert np.allclose(lg[g, h], ref, rtol=0, atol=1e-12)
+    assert lg[1, :, 5].tolist() == [0.0] * Qg
+
+
+def test_qjl_unbiased_with_half_precision_sketch_draws():
+    """The sketch the library draws: S = S_rot R with S_rot's entries N(0,1)
+    draws rounded to float16.  Over 10^4 independent such sketches, scoring
+    a packed record with score() is unbiased for <q, k> (mean within 3
+    standard errors, plus the bias the half-precision residual norm can
+    carry, bounded below and far smaller) and its variance is the QJL
+    variance ((pi/2) ||q||^2 rho^2 - <q, r>^2) / m of a Gaussian sketch
+    within a chi-square interval [Qiita explainer, Stage 2: QJL; ai.spot.hk,
+    無偏內積估計].  The key's norm is 16 exactly so that the stored half norm
+    is exact."""
+    import dataclasses
+    d = m = 128
+    cb0 = O.make_codebook(d, 3, m, 42)
+    rng = np.random.default_rng(2024)
+    k = rng.standard_normal(d) * np.exp(rng.normal(0, 0.7, d))
+    k *= 16.0 / np.linalg.norm(k)
+    e0 = O.encode(cb0, k[None])
+    assert e0.nu16[0] == np.float16(16.0) and abs(e0.nu[0] - 16.0) < 1e-12
+    kmse = e0.nu[0] * (cb0.levels[e0.codes[0]] @ cb0.R)
+    r = k - kmse
+    rho = float(np.linalg.norm(r))
+    q = rng.standard_normal(d) + 3.0 * r / rho
+    T = 10000
+    est = np.empty(T)
+    for t in range(T):
+        S_rot = rng.standard_normal((m, d)).astype(np.float16).astype(np.float64)
+        cb = dataclasses.replace(cb0, S_rot=S_rot, S=S_rot @ cb0.R)
+        e = O.encode(cb, k[None])
+        assert np.array_equal(e.codes, e0.codes)
+        buf = O.pack(cb, e.codes[None], e.signs[None], e.nu16[None], e.rho16[None])
+        est[t] = O.score(cb, buf, 1, 1, q[None, None])[0, 0, 0]
+    truth = float(q @ k)
+    se = est.std(ddof=1) / math.sqrt(T)
+    # the stored residual norm rho~ = half(rho) scales the QJL term, whose
+    # mean is <q, r>, by rho~ / rho: a fixed bias of at most 2^-11 |<q, r>|
+    bias = abs(float(e0.rho16[0]) / rho - 1.0) * abs(float(q @ r))
+    assert bias < 0.2 * se
+    assert abs(est.mean() - truth) < 3 * se + bias
+    var = ((math.pi / 2) * (q @ q) * rho ** 2 - (q @ r) ** 2) / m
+    lo, hi = stats.chi2.ppf([0.0005, 0.9995], T - 1) / (T - 1)
+    assert lo < est.var(ddof=1) / var < hi
+    assert abs(q @ r) > 20 * se
+
+
 def test_large_m_estimate_converges():
     """With m = 65536 sketch rows the estimate is within 5 standard
     deviations (~1/sqrt(m)) of the exact inner product."""
