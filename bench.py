@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--bits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--preroll", type=float, default=1.0,
+                    help="seconds of untimed back-to-back steps before the counted warm-up "
+                         "(brings the GPU clock to its loaded steady state)")
     return ap.parse_args()
 
 
@@ -73,11 +76,14 @@ def cpu_baseline(wl, budget_s):
     workload: whole groups, encode + score, until ~budget_s of work."""
     import oracle as O
     from kv_cache_vector_rotate_amd import workloads as W
+    avail = len(os.sched_getaffinity(0))
+    blas = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(avail)
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
     cbo = O.make_codebook(wl.d, wl.bits, wl.m, 42)
     keys_done, t_work, groups = 0, 0.0, 0
     for g in range(wl.G):
@@ -92,9 +98,44 @@ def cpu_baseline(wl, budget_s):
         groups += 1
         if t_work >= budget_s:
             break
-    return {"value": keys_done / t_work, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+    return {"value": keys_done / t_work, "unit": "keys/s", "cores": int(blas or 1), "kind": "oracle",
             "sample": f"{groups} of {wl.G} groups ({keys_done} keys): fp64 encode + pack + score of "
-                      f"{wl.Qg} queries per group, {t_work:.1f} s"}
+                      f"{wl.Qg} queries per group, {t_work:.1f} s",
+            "blas_threads": blas, "affinity_cores": avail, "os_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
+            "note": "numpy fp64 oracle; its matrix products use the BLAS threads, the rest runs "
+                    "on one Python thread"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
+def clock_mhz(K, torch):
+    """Core clock seen by one wave over 40 us (constant 100 MHz reference)."""
+    t = K.clock_probe(4000)
+    torch.cuda.synchronize()
+    cyc, ticks = (int(v) for v in t.cpu().tolist())
+    return round(100.0 * cyc / max(ticks, 1), 1)
+
+
+def preroll(step, seconds, torch):
+    """Untimed back-to-back steps for `seconds` of wall time (GPU kept busy:
+    one synchronisation per 50 steps)."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return {"seconds": round(time.perf_counter() - t0, 3), "steps": n}
 
 
 def run_decode(args):
@@ -148,16 +189,20 @@ def run_decode(args):
         if evs is not None:
             evs[2].record()
 
+    clk_idle = clock_mhz(K, torch)
+    pre = preroll(step, args.preroll, torch)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    clk_before = clock_mhz(K, torch)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    clk_after = clock_mhz(K, torch)
     enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     sc_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
 
@@ -166,8 +211,9 @@ def run_decode(args):
     enc_alg = key_bytes + pbytes                               # read keys, write records
     q_bytes = q.numel() * q.element_size()
     sc_alg = pbytes + logit_bytes + q_bytes                    # read records + queries, write logits
-    enc_avg_s = enc_ms.mean() * 1e-3
-    sc_avg_s = sc_ms.mean() * 1e-3
+    # rates from the median launch time (the mean is reported beside it)
+    enc_avg_s = float(np.median(enc_ms)) * 1e-3
+    sc_avg_s = float(np.median(sc_ms)) * 1e-3
     enc_gbps = enc_alg / enc_avg_s / 1e9
     sc_gbps = sc_alg / sc_avg_s / 1e9
     dominant = "encode" if enc_avg_s >= sc_avg_s else "score"
@@ -181,7 +227,9 @@ def run_decode(args):
             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round((enc_gbps if dominant == "encode" else sc_gbps) / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(enc_alg if dominant == "encode" else sc_alg)}
+            "algorithmic_bytes_per_launch": int(enc_alg if dominant == "encode" else sc_alg),
+            "time": "median HIP-event duration of the kernel's launches on the library's stream"}
+    ceil = ceilings(K, cb, keys, packed, logits, G, Qg, N, nk, npk, nl)
     out = {
         "metric": METRIC,
         "value": round(keys_per_step / (ms_per_step * 1e-3), 1),
@@ -197,17 +245,25 @@ def run_decode(args):
                   "hbm_GBps": round(sc_gbps, 1), "frac_of_peak": round(sc_gbps / PEAK_HBM_GBPS, 4),
                   "packed_kv_GBps": round(pbytes / sc_avg_s / 1e9, 1),
                   "us_median": round(float(np.median(sc_ms)) * 1e3, 2),
+                  "us_mean": round(float(sc_ms.mean()) * 1e3, 2),
                   "us_p10": round(float(np.percentile(sc_ms, 10)) * 1e3, 2),
                   "us_p90": round(float(np.percentile(sc_ms, 90)) * 1e3, 2),
-                  "algorithmic_bytes": int(sc_alg)},
+                  "algorithmic_bytes": int(sc_alg),
+                  "frac_of_score_pattern_ceiling": round(sc_gbps / ceil["score_pattern_GBps"], 4)},
         "encode": {"keys_per_s": round(keys_per_step / enc_avg_s, 1),
                    "hbm_GBps": round(enc_gbps, 1), "frac_of_peak": round(enc_gbps / PEAK_HBM_GBPS, 4),
                    "packed_kv_GBps": round(pbytes / enc_avg_s / 1e9, 1),
                    "us_median": round(float(np.median(enc_ms)) * 1e3, 2),
+                   "us_mean": round(float(enc_ms.mean()) * 1e3, 2),
                    "us_p10": round(float(np.percentile(enc_ms, 10)) * 1e3, 2),
                    "us_p90": round(float(np.percentile(enc_ms, 90)) * 1e3, 2),
-                   "algorithmic_bytes": int(enc_alg)},
+                   "algorithmic_bytes": int(enc_alg),
+                   "frac_of_encode_mix_ceiling": round(enc_gbps / ceil["encode_mix_GBps"], 4)},
         "roofline": roof,
+        "ceilings": ceil,
+        "clock_MHz": {"idle": clk_idle, "before_timed": clk_before, "after_timed": clk_after,
+                      "how": "one wave counts core-clock cycles over 40 us of the 100 MHz reference"},
+        "preroll": dict(pre, note="untimed back-to-back steps before the counted warm-up"),
         "rotation": {"key_copies": nk, "packed_copies": npk, "logit_copies": nl},
     }
     out["append"] = run_append(K, cb, keys0, q, G, N, Qg)
@@ -215,6 +271,40 @@ def run_decode(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def ceilings(K, cb, keys, packed, logits, G, Qg, N, nk, npk, nl, reps=40):
+    """Measured streaming ceilings on the same buffers (rotating past the
+    Infinity Cache), median of `reps` launches each:
+      read_only:     the key cache read with 16-byte loads, nothing written;
+      copy:          key cache to key cache (equal read and write bytes);
+      encode_mix:    the encoder's bytes (bf16 keys read, records written);
+      score_mix:     the scorer's bytes (records read, logits written) by the
+                     generic stream kernel, four workgroups per CU;
+      score_pattern: the scorer's own grid, record loads and logit stores
+                     without its set-up and arithmetic."""
+    kb = keys[0].numel() * keys[0].element_size()
+    pb = K.packed_nbytes(cb, G, N)
+    lb = G * Qg * N * 4
+    flat = lambda t: t.view(-1).view(torch_u8())
+    out = {}
+    t = _event_times(lambda i: K.stream_probe(flat(keys[i % nk])), reps)
+    out["read_only_GBps"] = round(kb / (np.median(t) * 1e-3) / 1e9, 1)
+    t = _event_times(lambda i: K.stream_probe(flat(keys[i % nk]), flat(keys[(i + 1) % nk])), reps)
+    out["copy_GBps"] = round(2 * kb / (np.median(t) * 1e-3) / 1e9, 1)
+    t = _event_times(lambda i: K.stream_probe(flat(keys[i % nk]), packed[i % npk]), reps)
+    out["encode_mix_GBps"] = round((kb + pb) / (np.median(t) * 1e-3) / 1e9, 1)
+    t = _event_times(lambda i: K.stream_probe(packed[i % npk], flat(logits[i % nl])), reps)
+    out["score_mix_GBps"] = round((pb + lb) / (np.median(t) * 1e-3) / 1e9, 1)
+    t = _event_times(lambda i: K.score_stream_probe(cb, G, Qg, packed[i % npk], N, logits[i % nl]), reps)
+    out["score_pattern_GBps"] = round((pb + lb) / (np.median(t) * 1e-3) / 1e9, 1)
+    out["score_pattern_us_median"] = round(float(np.median(t)) * 1e3, 2)
+    return out
+
+
+def torch_u8():
+    import torch
+    return torch.uint8
 
 
 def run_append(K, cb, keys0, q, G, N, Qg, steps=64):
@@ -268,9 +358,10 @@ def run_attention(K, cb, keys0, q, G, N, Qg, packed, npk, steps):
                                                     ws=ws), steps)
     key_bytes = keys0.numel() * keys0.element_size()
     kbytes = K.packed_nbytes(cb, G, N)
-    # attention: read key and value records and the queries, write and read
-    # back the logits, write the outputs (the range partials stay in cache)
-    att_alg = kbytes + vbytes + q.numel() * q.element_size() + 2 * G * Qg * N * 4 + G * Qg * cb.d * 4
+    # attention, the method's own bytes: read key and value records and the
+    # queries, write the outputs (anything the kernels stage in between is
+    # not counted)
+    att_alg = kbytes + vbytes + q.numel() * q.element_size() + G * Qg * cb.d * 4
     return {"values_encode": _stats(enc, key_bytes + vbytes, G * N, "values"),
             "attention": _stats(att, att_alg, G * N, "keys"),
             "value_record_bytes": int(vbytes // (G * N)),

@@ -165,6 +165,13 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
  * (S r is evaluated as S_rot (R r) on the matrix cores: S_rot is exact in
  * float16, R r is split into float16 hi + lo, float32 accumulation), norms
  * stored as half.
+ * Passages: normalise, rotate with the randomized Hadamard transform and
+ * quantise every coordinate with one scalar codebook [ICLR 2026 paper digest,
+ * "Step 1: PolarQuant"; Qiita explainer, "Stage 1: PolarQuant" step 3];
+ * sign sketch of the residual with a Gaussian projection [Qiita explainer,
+ * "Stage 2: QJL"]; (b-1) + 1 bits [ai.spot.hk article, "無偏內積估計"];
+ * zero vectors and "0 counts as positive" [ICLR 2026 paper digest,
+ * "実装の擬似コード"].
  * keys and packed are device pointers owned by the caller; G*N == 0 is a
  * no-op.  d = 1024 runs in chunks of 65,536 keys through a temporary of
  * 256 MiB taken from the device's stream-ordered pool (hipMallocAsync /
@@ -294,8 +301,17 @@ int tq_score_topk(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t
 
 /*
  * MSE-only reconstruction of every packed key: out[g][n] = nu~ R^T c[code]
- * (the community API's MSE compressor) as TQ_F32 or TQ_BF16 [G][N][d].
- * Errors: TQ_ERR_ARG, TQ_ERR_HIP.
+ * as TQ_F32 or TQ_BF16 [G][N][d] (rows of the codebook's d elements; the
+ * zero-padded coordinates are dropped).  This is the Stage-1 dequantisation:
+ * the level of each code, the inverse rotation R^T = D H / sqrt(d) and the
+ * stored norm [ICLR 2026 paper digest, "Step 1: PolarQuant" (R orthogonal,
+ * norm kept on the side); Qiita explainer, API table (MSE-only compressor,
+ * "TurboQuantMSE")].  Computed in float32, rounded to nearest even for
+ * TQ_BF16.  d = 128 and d = 1024 (and the zero-padded d of those D).
+ * G*N == 0 is a no-op; nothing is allocated.
+ * Errors: TQ_ERR_ARG (null/misaligned pointer, negative size, bad dtype,
+ * codebook made on another device), TQ_ERR_UNSUPPORTED (a rotation dimension
+ * without device kernels), TQ_ERR_HIP.
  */
 int tq_decode_mse(const tq_codebook* cb, const void* packed, int64_t G, int64_t N,
                   void* out, int32_t out_dtype, void* stream);
@@ -309,6 +325,43 @@ int tq_decode_mse(const tq_codebook* cb, const void* packed, int64_t G, int64_t 
  */
 int tq_dense_logits_bf16(const void* q, const void* keys, int64_t G, int32_t Qg,
                          int64_t N, int32_t d, float* logits, void* stream);
+
+/*
+ * Measurement helpers, not part of the method: the ceilings and the clock
+ * the benchmark reports beside the kernels.
+ *
+ * tq_clock_probe: one wave reads the core-clock cycle counter and the
+ * constant-rate reference counter, spins until the reference counter has
+ * advanced by `ticks`, and writes out[0] = cycles elapsed, out[1] = reference
+ * ticks elapsed (device memory, 2 x uint64).  The core clock in MHz is
+ * out[0] / out[1] times the reference rate (100 MHz on gfx950).
+ * Errors: TQ_ERR_ARG (out NULL or misaligned, ticks <= 0), TQ_ERR_HIP.
+ */
+int tq_clock_probe(uint64_t* out, int32_t ticks, void* stream);
+
+/*
+ * tq_stream_probe: streams src_bytes from src with 16-byte non-temporal
+ * loads and writes dst_bytes to dst with 16-byte non-temporal stores, the
+ * writes spread evenly between the reads, over `grid` workgroups of 1024
+ * threads (grid <= 0: four per compute unit), each taking a contiguous share
+ * of both buffers.  dst_bytes == 0 gives a read-only stream (dst may then be
+ * NULL); src_bytes == dst_bytes a copy.  Sizes are multiples of 16; device
+ * pointers, 16-byte aligned.  Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED
+ * (grid > 2^20), TQ_ERR_HIP.
+ */
+int tq_stream_probe(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int32_t grid,
+                    void* stream);
+
+/*
+ * tq_score_stream_probe: the memory traffic of tq_score_logits at d = 128 in
+ * its own launch configuration (same grid, same record loads, same logit
+ * stores) without the query preparation and without the estimator's
+ * arithmetic: every logit is a fold of its key's record, so the output is
+ * meaningless.  The rate it reaches is the ceiling of the scorer's access
+ * pattern.  Errors as tq_score_cache.
+ */
+int tq_score_stream_probe(const tq_codebook* cb, int64_t G, int32_t Qg, const void* packed, int64_t N,
+                          float* logits, void* stream);
 
 /* Static description of a status code. */
 const char* tq_status_string(int status);

@@ -25,6 +25,7 @@ EXPORTED_SYMBOLS = (
     "tq_dense_logits_bf16", "tq_status_string", "tq_last_hip_error",
     "tq_value_packed_bytes", "tq_encode_values", "tq_attention_workspace_bytes",
     "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex", "tq_rotation_dim",
+    "tq_clock_probe", "tq_stream_probe", "tq_score_stream_probe",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -57,6 +58,9 @@ _SIGS = {
     "tq_attention_decode": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
                                            ctypes.c_float, _vp, _vp, _c_sz, _vp]),
     "tq_last_hip_error": (ctypes.c_int, []),
+    "tq_clock_probe": (ctypes.c_int, [_vp, _c_i32, _vp]),
+    "tq_stream_probe": (ctypes.c_int, [_vp, _c_sz, _vp, _c_sz, _c_i32, _vp]),
+    "tq_score_stream_probe": (ctypes.c_int, [_vp, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp]),
 }
 
 _lib = None
@@ -196,6 +200,19 @@ def _need_cuda(t, name):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
+def _need_bytes(t, nbytes: int, name: str):
+    """The C ABI takes raw pointers and cannot see allocation sizes: refuse a
+    buffer smaller than what the kernels will read or write."""
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def _need_rows(t, name: str, G: int, d: int):
+    if t.dim() != 3 or t.shape[0] != G or t.shape[2] != d:
+        raise ValueError(f"{name} must be [G={G}, n, d={d}], got {tuple(t.shape)}")
+
+
 def encode_keys(cb: Codebook, keys, out=None):
     """keys [G, N, d] (float32/bfloat16, device) -> packed uint8 [packed_nbytes]."""
     torch = _torch()
@@ -243,6 +260,9 @@ def score_cache(cb: Codebook, q, packed, Ncap: int, length: int, out=None):
     G, Qg, d = q.shape
     if d != cb.d:
         raise ValueError("query dimension does not match the codebook")
+    if not 0 <= length <= Ncap:
+        raise ValueError("length must lie in [0, Ncap]")
+    _need_bytes(packed, packed_nbytes(cb, G, Ncap), "packed cache (Ncap records per group)")
     if out is None:
         out = torch.empty((G, Qg, length), dtype=torch.float32, device=q.device)
     _need_out(out, G * Qg * length)
@@ -286,6 +306,8 @@ def attention_decode(cb: Codebook, q, kpacked, vpacked, N: int, scale=None, out=
     if d != cb.d:
         raise ValueError("query dimension does not match the codebook")
     scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    _need_bytes(kpacked, packed_nbytes(cb, G, N), "kpacked")
+    _need_bytes(vpacked, value_packed_nbytes(cb, G, N), "vpacked")
     if out is None:
         out = torch.empty((G, Qg, d), dtype=torch.float32, device=q.device)
     _need_out(out, G * Qg * d)
@@ -307,6 +329,7 @@ def score_logits(cb: Codebook, q, packed, N: int, out=None, ws=None):
     G, Qg, d = q.shape
     if d != cb.d:
         raise ValueError("query dimension does not match the codebook")
+    _need_bytes(packed, packed_nbytes(cb, G, N), "packed")
     if out is None:
         out = torch.empty((G, Qg, N), dtype=torch.float32, device=q.device)
     _need_out(out, G * Qg * N)
@@ -333,6 +356,7 @@ def score_topk(cb: Codebook, q, packed, N: int, k: int = 10, ws=None):
     G, Qg, d = q.shape
     if d != cb.d:
         raise ValueError("query dimension does not match the codebook")
+    _need_bytes(packed, packed_nbytes(cb, G, N), "packed")
     idx = torch.empty((G, Qg, k), dtype=torch.int32, device=q.device)
     scores = torch.empty((G, Qg, k), dtype=torch.float32, device=q.device)
     if ws is None:
@@ -348,9 +372,14 @@ def decode_mse(cb: Codebook, packed, G: int, N: int, dtype=None, out=None):
     """packed keys -> nu~ R^T c[code], [G, N, d] float32 (default) or bfloat16."""
     torch = _torch()
     _need_cuda(packed, "packed")
+    _need_bytes(packed, packed_nbytes(cb, G, N), "packed")
     dtype = torch.float32 if dtype is None else dtype
     if out is None:
         out = torch.empty((G, N, cb.d), dtype=dtype, device=packed.device)
+    _need_cuda(out, "out")
+    _dtype_code(out)
+    if out.numel() < G * N * cb.d:
+        raise ValueError(f"out must hold G*N*d = {G * N * cb.d} elements")
     _check(library().tq_decode_mse(cb.handle, _ptr(packed), G, N, _ptr(out), _dtype_code(out),
                                    _stream()), "tq_decode_mse")
     return out
@@ -362,9 +391,46 @@ def dense_logits_bf16(q, keys, out=None):
     _need_cuda(q, "q")
     _need_cuda(keys, "keys")
     G, Qg, d = q.shape
+    _need_rows(keys, "keys", G, d)
+    if q.dtype != torch.bfloat16 or keys.dtype != torch.bfloat16:
+        raise TypeError("q and keys must be bfloat16")
     N = keys.shape[1]
     if out is None:
         out = torch.empty((G, Qg, N), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * N)
     _check(library().tq_dense_logits_bf16(_ptr(q), _ptr(keys), G, Qg, N, d, _ptr(out), _stream()),
            "tq_dense_logits_bf16")
     return out
+
+
+# ---- measurement helpers (not part of the method)
+
+def clock_probe(ticks: int = 4000):
+    """(core-clock cycles, reference ticks) counted by one wave over `ticks`
+    reference ticks, as a device tensor of two int64 (read it after a sync)."""
+    torch = _torch()
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _check(library().tq_clock_probe(_ptr(out), ticks, _stream()), "tq_clock_probe")
+    return out
+
+
+def stream_probe(src, dst=None, src_bytes=None, dst_bytes=None, grid: int = 0):
+    """Stream src (read) and dst (write) device buffers: read-only when dst is
+    None, a copy when both are the same size."""
+    sb = src.numel() * src.element_size() if src_bytes is None else src_bytes
+    db = 0 if dst is None else (dst.numel() * dst.element_size() if dst_bytes is None else dst_bytes)
+    _need_cuda(src, "src")
+    _need_bytes(src, sb, "src")
+    if dst is not None:
+        _need_cuda(dst, "dst")
+        _need_bytes(dst, db, "dst")
+    _check(library().tq_stream_probe(_ptr(src), sb, _ptr(dst), db, grid, _stream()), "tq_stream_probe")
+
+
+def score_stream_probe(cb: Codebook, G: int, Qg: int, packed, N: int, out):
+    """The scorer's loads and stores without its arithmetic (a ceiling)."""
+    _need_cuda(packed, "packed")
+    _need_bytes(packed, packed_nbytes(cb, G, N), "packed")
+    _need_out(out, G * Qg * N)
+    _check(library().tq_score_stream_probe(cb.handle, G, Qg, _ptr(packed), N, _ptr(out), _stream()),
+           "tq_score_stream_probe")

@@ -714,7 +714,7 @@ int tq_decode_mse(const tq_codebook* cb, const void* packed, int64_t G, int64_t 
   if (!cb || G < 0 || N < 0 || (out_dtype != TQ_F32 && out_dtype != TQ_BF16)) return TQ_ERR_ARG;
   if (G == 0 || N == 0) return TQ_OK;
   if (!packed || !out || !aligned16(packed) || !aligned16(out)) return TQ_ERR_ARG;
-  if (cb->d != 128) return TQ_ERR_UNSUPPORTED;
+  if (!tq::encode_supported(*cb)) return TQ_ERR_UNSUPPORTED;
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
   hipError_t e = tq::launch_decode(*cb, packed, G, N, out, out_dtype,
@@ -731,6 +731,37 @@ int tq_dense_logits_bf16(const void* q, const void* keys, int64_t G, int32_t Qg,
     return TQ_ERR_ARG;
   hipError_t e = tq::launch_dense_bf16(q, keys, G, Qg, N, d, logits,
                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_clock_probe(uint64_t* out, int32_t ticks, void* stream) {
+  if (!out || ticks <= 0 || (reinterpret_cast<uintptr_t>(out) & 7u)) return TQ_ERR_ARG;
+  hipError_t e = tq::launch_clock_probe(out, uint32_t(ticks), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_stream_probe(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int32_t grid,
+                    void* stream) {
+  if ((src_bytes | dst_bytes) & 15u) return TQ_ERR_ARG;
+  if ((src_bytes && (!src || !aligned16(src))) || (dst_bytes && (!dst || !aligned16(dst))))
+    return TQ_ERR_ARG;
+  if (grid > (1 << 20)) return TQ_ERR_UNSUPPORTED;
+  if (src_bytes == 0 && dst_bytes == 0) return TQ_OK;
+  hipError_t e = tq::launch_stream_probe(src, src_bytes, dst, dst_bytes, grid,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_score_stream_probe(const tq_codebook* cb, int64_t G, int32_t Qg, const void* packed, int64_t N,
+                          float* logits, void* stream) {
+  if (!cb || G < 0 || N < 0 || Qg < 0) return TQ_ERR_ARG;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || N >= (int64_t(1) << 28)) return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || N == 0 || Qg == 0) return TQ_OK;
+  if (!packed || !logits || !aligned16(packed) || !aligned16(logits)) return TQ_ERR_ARG;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_score_stream_probe(*cb, G, Qg, packed, N, logits,
+                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 

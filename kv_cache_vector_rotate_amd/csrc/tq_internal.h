@@ -79,6 +79,8 @@ hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64
                             const void* kpacked, const void* vpacked, int64_t N, float scale,
                             float* out, void* ws, hipStream_t s);
 // d = 1024 (tq_wide.hip)
+hipError_t launch_decode_wide(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
+                              int odtype, hipStream_t s);
 hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                               void* packed, hipStream_t s);
 size_t score_wide_prep_bytes(int64_t G, int Qg);
@@ -88,6 +90,12 @@ hipError_t launch_score_wide(const Codebook& cb, const void* q, int qdtype, int6
 hipError_t launch_topk_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                             const void* packed, int64_t N, int K, int32_t* idx, float* scores,
                             void* ws, hipStream_t s);
+// measurement helpers (not part of the method)
+hipError_t launch_clock_probe(uint64_t* out, uint32_t ticks, hipStream_t s);
+hipError_t launch_stream_probe(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int grid,
+                               hipStream_t s);
+hipError_t launch_score_stream_probe(const Codebook& cb, int64_t G, int Qg, const void* packed, int64_t N,
+                                     float* logits, hipStream_t s);
 constexpr int kMaxTopKAbi = 16;
 bool encode_supported(const Codebook& cb);
 bool score_supported(const Codebook& cb);

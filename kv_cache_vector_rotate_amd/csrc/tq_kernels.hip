@@ -1295,8 +1295,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
 }
 
 // ============================================================== decode, d = 128
-// One wave per key: lane L reconstructs coordinates L and L + 64 of
-// nu~ D H c[code] / sqrt(d)  (= nu~ R^T c[code]).
+// One wave per key (grid-stride over keys): lane L reconstructs coordinates
+// L and L + 64 of nu~ D H c[code] / sqrt(d)  (= nu~ R^T c[code]).
 
 template <int B, bool BF16OUT>
 __global__ __launch_bounds__(256) void decode128_kernel(const uint32_t* __restrict__ planes,
@@ -1305,41 +1305,42 @@ __global__ __launch_bounds__(256) void decode128_kernel(const uint32_t* __restri
                                                          const DevConsts* __restrict__ cst) {
   constexpr int P = B + 1;
   const int lane = threadIdx.x & 63;
-  const int64_t key = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (key >= G * N) return;
-  const int64_t g = key / N, n = key - g * N;
-  const uint32_t* pk = planes + (g * P * N + n) * 4;
-  int c0 = 0, c1 = 0;
+  const int64_t stride = int64_t(gridDim.x) * 4;
+  for (int64_t key = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); key < G * N; key += stride) {
+    const int64_t g = key / N, n = key - g * N;
+    const uint32_t* pk = planes + (g * P * N + n) * 4;
+    int c0 = 0, c1 = 0;
 #pragma unroll
-  for (int p = 0; p < B; ++p) {
-    c0 |= int((pk[p * N * 4 + (lane >> 5)] >> (lane & 31)) & 1u) << p;
-    c1 |= int((pk[p * N * 4 + 2 + (lane >> 5)] >> (lane & 31)) & 1u) << p;
-  }
-  float a = cst->levels[c0], b = cst->levels[c1];
-  float y0 = a + b, y1 = a - b;
+    for (int p = 0; p < B; ++p) {
+      c0 |= int((pk[p * N * 4 + (lane >> 5)] >> (lane & 31)) & 1u) << p;
+      c1 |= int((pk[p * N * 4 + 2 + (lane >> 5)] >> (lane & 31)) & 1u) << p;
+    }
+    float a = cst->levels[c0], b = cst->levels[c1];
+    float y0 = a + b, y1 = a - b;
 #pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const float p0 = __shfl_xor(y0, s), p1 = __shfl_xor(y1, s);
-    const bool up = lane & s;
-    y0 = up ? p0 - y0 : y0 + p0;
-    y1 = up ? p1 - y1 : y1 + p1;
-  }
-  const float nu = h2f_bits(norms[g * N + n] & 0xffffu);
-  const float sc = nu * cst->inv_sqrt_d;
-  const uint32_t n0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
-  const uint32_t n1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
-  y0 = (n0 ? -y0 : y0) * sc;
-  y1 = (n1 ? -y1 : y1) * sc;
-  // rows of din elements: the coordinates a zero-padded input never had are dropped
-  const int din = int(cst->din);
-  if constexpr (BF16OUT) {
-    __bf16* o = static_cast<__bf16*>(out) + key * din;
-    if (lane < din) o[lane] = static_cast<__bf16>(y0);
-    if (lane + 64 < din) o[lane + 64] = static_cast<__bf16>(y1);
-  } else {
-    float* o = static_cast<float*>(out) + key * din;
-    if (lane < din) o[lane] = y0;
-    if (lane + 64 < din) o[lane + 64] = y1;
+    for (int s = 1; s < 64; s <<= 1) {
+      const float p0 = __shfl_xor(y0, s), p1 = __shfl_xor(y1, s);
+      const bool up = lane & s;
+      y0 = up ? p0 - y0 : y0 + p0;
+      y1 = up ? p1 - y1 : y1 + p1;
+    }
+    const float nu = h2f_bits(norms[g * N + n] & 0xffffu);
+    const float sc = nu * cst->inv_sqrt_d;
+    const uint32_t n0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
+    const uint32_t n1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
+    y0 = (n0 ? -y0 : y0) * sc;
+    y1 = (n1 ? -y1 : y1) * sc;
+    // rows of din elements: the coordinates a zero-padded input never had are dropped
+    const int din = int(cst->din);
+    if constexpr (BF16OUT) {
+      __bf16* o = static_cast<__bf16*>(out) + key * din;
+      if (lane < din) o[lane] = static_cast<__bf16>(y0);
+      if (lane + 64 < din) o[lane + 64] = static_cast<__bf16>(y1);
+    } else {
+      float* o = static_cast<float*>(out) + key * din;
+      if (lane < din) o[lane] = y0;
+      if (lane + 64 < din) o[lane + 64] = y1;
+    }
   }
 }
 
@@ -1585,6 +1586,100 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
   if (64 + lane < din) o[64 + lane] = (f1 ? -y1 : y1) * sc;
 }
 
+// ============================================================== measurement helpers
+// Not part of the method: ceilings and clocks the benchmark reports beside
+// the kernels above.
+
+// One wave reads the core-clock cycle counter and the constant-rate
+// reference counter, spins until the reference counter has advanced by
+// `ticks` (or a cap on iterations), and reads both again.
+__global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ out, uint32_t ticks) {
+  const uint64_t c0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t r1 = r0, c1 = c0;
+  for (uint32_t it = 0; it < (1u << 24); ++it) {
+    r1 = __builtin_amdgcn_s_memrealtime();
+    c1 = __builtin_amdgcn_s_memtime();
+    if (r1 - r0 >= ticks) break;
+  }
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r1 - r0;
+  }
+}
+
+// Streaming ceiling: workgroup w reads its contiguous share of src (16-byte
+// non-temporal loads, 1024 threads side by side) and writes its share of dst
+// in between, one write round after every read round that brings the reads
+// past the next write's proportional position.  The written value is a fold
+// of what was read; with no writes the fold is kept alive by a store that
+// only happens when it equals a constant.
+constexpr int kProbeThreads = 1024;
+__global__ __launch_bounds__(kProbeThreads) void stream_probe_kernel(const uint4* __restrict__ src,
+                                                                     uint64_t nsrc,
+                                                                     uint4* __restrict__ dst,
+                                                                     uint64_t ndst) {
+  const uint64_t wgs = gridDim.x, w = blockIdx.x;
+  const uint64_t r0 = nsrc * w / wgs, r1 = nsrc * (w + 1) / wgs;
+  const uint64_t w0 = ndst * w / wgs, w1 = ndst * (w + 1) / wgs;
+  const uint64_t nr = r1 - r0, nw = w1 - w0;
+  const uint32_t tid = threadIdx.x;
+  u32x4 fold = {0u, 0u, 0u, 0u};
+  const uint64_t rounds_r = (nr + kProbeThreads - 1) / kProbeThreads;
+  const uint64_t rounds_w = (nw + kProbeThreads - 1) / kProbeThreads;
+  uint64_t wr = 0;   // write rounds done
+  for (uint64_t k = 0; k < rounds_r || wr < rounds_w; ++k) {
+    if (k < rounds_r) {
+      const uint64_t i = k * kProbeThreads + tid;
+      if (i < nr) fold ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r0 + i));
+    }
+    const uint64_t due = rounds_r ? (k + 1 >= rounds_r ? rounds_w : (k + 1) * rounds_w / rounds_r) : rounds_w;
+    for (; wr < due; ++wr) {
+      const uint64_t j = wr * kProbeThreads + tid;
+      if (j < nw) __builtin_nontemporal_store(fold, reinterpret_cast<u32x4*>(dst + w0 + j));
+    }
+  }
+  if (ndst == 0 && dst != nullptr && fold[0] == 0x9E3779B9u && fold[1] == 0x7F4A7C15u)
+    dst[0] = make_uint4(fold[0], fold[1], fold[2], fold[3]);
+}
+
+// The loads and stores of score128_kernel (same grid, same 64-key tiles per
+// wave, same record reads and logit writes) without the query preparation
+// and without the table arithmetic: each logit is a fold of the record.
+template <int B>
+__global__ __launch_bounds__(kScoreThreads, 1) void score128_stream_kernel(
+    const uint4* __restrict__ planes, const uint32_t* __restrict__ norms, int64_t N, int Qg,
+    int64_t chunk, float* __restrict__ logits) {
+  constexpr int P = B + 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t g = blockIdx.x;
+  const int qc = blockIdx.y;
+  const int64_t n0 = int64_t(blockIdx.z) * chunk;
+  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
+  const uint4* pg = planes + g * P * N;
+  const uint32_t* ng = norms + g * N;
+  float* lrow[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
+  for (int64_t b = n0 + int64_t(wave) * 64; b < n1; b += kScoreThreads) {
+    const uint32_t n = uint32_t(std::min<int64_t>(b + lane, n1 - 1));
+    uint32_t f = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ng) + n * 4u));
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pg + p * N) + n * 16u));
+      f ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (b + lane < n1) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        if (qc * 4 + qq < Qg) __builtin_nontemporal_store(__uint_as_float(f + qq), lrow[qq] + b + lane);
+    }
+  }
+}
+
 }  // namespace
 
 bool encode_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
@@ -1722,20 +1817,26 @@ hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64
   return hipGetLastError();
 }
 
-hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
-                        const void* packed, int64_t N, int64_t Ncap, float* logits, void* ws,
-                        hipStream_t s) {
-  if (cb.d == 1024) return launch_score_wide(cb, q, qdtype, G, Qg, packed, N, logits, ws, s);
-  // enough workgroups for every CU: split each (group, query chunk) unit's
-  // keys into ranges of at least 512 keys, a multiple of 64 each
+// Grid of the d = 128 scorer: (group, chunk of 4 queries, key range), with
+// enough workgroups for every CU: each (group, query chunk) unit's keys are
+// split into ranges of at least 512 keys, a multiple of 64 each.
+static dim3 score_grid(int64_t G, int Qg, int64_t N, int64_t& chunk) {
   const int nqc = (Qg + 3) / 4;
   const int64_t units = G * nqc;
   const int64_t cus = num_cus();
   int64_t want = std::max<int64_t>(1, (cus + units - 1) / units);
   want = std::min<int64_t>(want, std::max<int64_t>(1, (N + 511) / 512));
-  const int64_t chunk = ((N + want - 1) / want + 63) / 64 * 64;
+  chunk = ((N + want - 1) / want + 63) / 64 * 64;
   const int64_t splits = (N + chunk - 1) / chunk;
-  const dim3 grid{unsigned(G), unsigned(nqc), unsigned(splits)};
+  return dim3{unsigned(G), unsigned(nqc), unsigned(splits)};
+}
+
+hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                        const void* packed, int64_t N, int64_t Ncap, float* logits, void* ws,
+                        hipStream_t s) {
+  if (cb.d == 1024) return launch_score_wide(cb, q, qdtype, G, Qg, packed, N, logits, ws, s);
+  int64_t chunk = 0;
+  const dim3 grid = score_grid(G, Qg, N, chunk);
   const uint4* planes = static_cast<const uint4*>(packed);
   const uint32_t* norms =
       static_cast<const uint32_t*>(packed) + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
@@ -1754,8 +1855,9 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
 
 hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
                          int odtype, hipStream_t s) {
+  if (cb.d == 1024) return launch_decode_wide(cb, packed, G, N, out, odtype, s);
   const int64_t keys = G * N;
-  const int grid = int((keys + 3) / 4);
+  const int grid = int(std::min<int64_t>((keys + 3) / 4, int64_t(num_cus()) * 64));
   const uint32_t* planes = static_cast<const uint32_t*>(packed);
   const uint32_t* norms = planes + keys * int64_t(cb.bits) * (cb.d / 32);
 #define TQ_DE(BB, BF)                                                                      \
@@ -1794,6 +1896,38 @@ hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg,
     default: TQ_DN(8); break;
   }
 #undef TQ_DN
+  return hipGetLastError();
+}
+
+hipError_t launch_clock_probe(uint64_t* out, uint32_t ticks, hipStream_t s) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, s, out, ticks);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_probe(const void* src, size_t src_bytes, void* dst, size_t dst_bytes, int grid,
+                               hipStream_t s) {
+  if (grid <= 0) grid = num_cus() * 4;
+  hipLaunchKernelGGL(stream_probe_kernel, dim3(unsigned(grid)), dim3(kProbeThreads), 0, s,
+                     static_cast<const uint4*>(src), uint64_t(src_bytes / 16), static_cast<uint4*>(dst),
+                     uint64_t(dst_bytes / 16));
+  return hipGetLastError();
+}
+
+hipError_t launch_score_stream_probe(const Codebook& cb, int64_t G, int Qg, const void* packed, int64_t N,
+                                     float* logits, hipStream_t s) {
+  int64_t chunk = 0;
+  const dim3 grid = score_grid(G, Qg, N, chunk);
+  const uint4* planes = static_cast<const uint4*>(packed);
+  const uint32_t* norms = static_cast<const uint32_t*>(packed) + G * N * int64_t(cb.bits) * (cb.d / 32);
+#define TQ_SP(BB)                                                                                   \
+  hipLaunchKernelGGL((score128_stream_kernel<BB>), grid, dim3(kScoreThreads), 0, s, planes, norms, N, Qg, \
+                     chunk, logits)
+  switch (cb.bits - 1) {
+    case 1: TQ_SP(1); break;
+    case 2: TQ_SP(2); break;
+    default: TQ_SP(3); break;
+  }
+#undef TQ_SP
   return hipGetLastError();
 }
 

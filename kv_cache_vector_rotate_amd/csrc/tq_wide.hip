@@ -224,6 +224,77 @@ __global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- decode
+// MSE-only reconstruction nu~ R^T c[code] = nu~ D H c[code] / sqrt(d), one key
+// per wave: lane L unpacks coordinates 16 L + t (bits 16 (L & 1) + t of plane
+// word L / 2), applies the same 1024-point butterfly as the rotation (H is
+// symmetric), then D and the scale; rows of din elements are written.
+template <int B, bool BF16OUT>
+__global__ __launch_bounds__(256) void decode1024_kernel(const uint32_t* __restrict__ planes,
+                                                         const uint32_t* __restrict__ norms,
+                                                         int64_t total, int64_t N,
+                                                         void* __restrict__ out,
+                                                         const DevConsts* __restrict__ cst) {
+  constexpr int P = B + 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t wstride = int64_t(gridDim.x) * 4;
+  const uint32_t dn = (cst->dneg[lane >> 1] >> (16 * (lane & 1))) & 0xffffu;
+  const int din = int(cst->din);
+  const bool lane_in = 16 * lane < din;
+  const float inv_sqrt_d = cst->inv_sqrt_d;
+  for (int64_t kk = wave0; kk < total; kk += wstride) {
+    const int64_t g = kk / N, n = kk - g * N;
+    uint32_t bits16[B];
+#pragma unroll
+    for (int p = 0; p < B; ++p)
+      bits16[p] = (planes[((g * P + p) * N + n) * 32 + (lane >> 1)] >> (16 * (lane & 1))) & 0xffffu;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      int c = 0;
+#pragma unroll
+      for (int p = 0; p < B; ++p) c |= int((bits16[p] >> t) & 1u) << p;
+      x[t] = cst->levels[c];
+    }
+#pragma unroll
+    for (int st = 1; st < 16; st <<= 1)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        if (t & st) continue;
+        const float a = x[t], b = x[t + st];
+        x[t] = a + b;
+        x[t + st] = a - b;
+      }
+    stage_lanes<1>(x, lane);
+    stage_lanes<2>(x, lane);
+    stage_lanes<4>(x, lane);
+    stage_lanes<8>(x, lane);
+    stage_lanes<16>(x, lane);
+    stage_lanes32(x, lane);
+    const uint32_t nb = norms[g * N + n] & 0xffffu;
+    const float sc = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(nb))) * inv_sqrt_d;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) x[t] = ((dn >> t) & 1u) ? -(x[t] * sc) : x[t] * sc;
+    if (!lane_in) continue;
+    if constexpr (BF16OUT) {
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 lo = static_cast<__bf16>(x[2 * i]), hi = static_cast<__bf16>(x[2 * i + 1]);
+        w[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
+      uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + kk * din + 16 * lane);
+      o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + kk * din + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- QJL projection
 // Workgroup tile: all 1024 sketch rows x 64 keys; wave w owns rows
 // [128 w, 128 w + 128) (four 32-row blocks) and both 32-key blocks.  The
@@ -1092,6 +1163,26 @@ hipError_t launch_topk_wide(const Codebook& cb, const void* q, int qdtype, int64
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, tk_s, tk_i,
                      int(ranges), K, idx, scores);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_decode_wide(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
+                              int odtype, hipStream_t s) {
+  const int64_t total = G * N;
+  const uint32_t* planes = static_cast<const uint32_t*>(packed);
+  const uint32_t* norms = planes + total * int64_t(cb.bits) * (kD / 32);
+  const int grid = int(std::min<int64_t>((total + 3) / 4, int64_t(std::max(1, cb.num_cus)) * 16));
+  const bool bf = odtype == 1;
+#define TQ_DW(BB, BF)                                                                             \
+  hipLaunchKernelGGL((decode1024_kernel<BB, BF>), dim3(grid), dim3(256), 0, s, planes, norms, total, N, \
+                     out, cb.d_consts)
+  switch (cb.bits - 1) {
+    case 1: if (bf) TQ_DW(1, true); else TQ_DW(1, false); break;
+    case 2: if (bf) TQ_DW(2, true); else TQ_DW(2, false); break;
+    default: if (bf) TQ_DW(3, true); else TQ_DW(3, false); break;
+  }
+#undef TQ_DW
   return hipGetLastError();
 }
 
