@@ -1609,29 +1609,39 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t* __restrict__ 
 }
 
 // Streaming ceiling: workgroup w reads its contiguous share of src (16-byte
-// non-temporal loads, 1024 threads side by side) and writes its share of dst
-// in between, one write round after every read round that brings the reads
-// past the next write's proportional position.  The written value is a fold
-// of what was read; with no writes the fold is kept alive by a store that
-// only happens when it equals a constant.
+// non-temporal loads, 1024 threads side by side, four loads in flight per
+// thread) and writes its share of dst in between: after each read round
+// (four loads per thread) the write rounds that bring the writes up to the
+// same fraction of their share.  The written value is a fold of what was
+// read; with no writes the fold is kept alive by a store that only happens
+// when it equals a constant.
 constexpr int kProbeThreads = 1024;
+constexpr int kProbeUnroll = 4;
 __global__ __launch_bounds__(kProbeThreads) void stream_probe_kernel(const uint4* __restrict__ src,
                                                                      uint64_t nsrc,
                                                                      uint4* __restrict__ dst,
                                                                      uint64_t ndst) {
+  constexpr uint64_t kRound = uint64_t(kProbeThreads) * kProbeUnroll;
   const uint64_t wgs = gridDim.x, w = blockIdx.x;
   const uint64_t r0 = nsrc * w / wgs, r1 = nsrc * (w + 1) / wgs;
   const uint64_t w0 = ndst * w / wgs, w1 = ndst * (w + 1) / wgs;
   const uint64_t nr = r1 - r0, nw = w1 - w0;
   const uint32_t tid = threadIdx.x;
   u32x4 fold = {0u, 0u, 0u, 0u};
-  const uint64_t rounds_r = (nr + kProbeThreads - 1) / kProbeThreads;
+  const uint64_t rounds_r = (nr + kRound - 1) / kRound;
   const uint64_t rounds_w = (nw + kProbeThreads - 1) / kProbeThreads;
-  uint64_t wr = 0;   // write rounds done
+  uint64_t wr = 0;   // write rounds done (1024 stores each)
   for (uint64_t k = 0; k < rounds_r || wr < rounds_w; ++k) {
     if (k < rounds_r) {
-      const uint64_t i = k * kProbeThreads + tid;
-      if (i < nr) fold ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r0 + i));
+      u32x4 v[kProbeUnroll];
+#pragma unroll
+      for (int u = 0; u < kProbeUnroll; ++u) {
+        const uint64_t i = k * kRound + uint64_t(u) * kProbeThreads + tid;
+        v[u] = i < nr ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + r0 + i))
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kProbeUnroll; ++u) fold ^= v[u];
     }
     const uint64_t due = rounds_r ? (k + 1 >= rounds_r ? rounds_w : (k + 1) * rounds_w / rounds_r) : rounds_w;
     for (; wr < due; ++wr) {
@@ -1644,13 +1654,16 @@ __global__ __launch_bounds__(kProbeThreads) void stream_probe_kernel(const uint4
 }
 
 // The loads and stores of score128_kernel (same grid, same 64-key tiles per
-// wave, same record reads and logit writes) without the query preparation
-// and without the table arithmetic: each logit is a fold of the record.
+// wave with two tiles in flight, same record reads and logit writes) without
+// the query preparation and without the table arithmetic: each logit is a
+// fold of the record.
 template <int B>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_stream_kernel(
     const uint4* __restrict__ planes, const uint32_t* __restrict__ norms, int64_t N, int Qg,
     int64_t chunk, float* __restrict__ logits) {
   constexpr int P = B + 1;
+  constexpr int D = 2;
+  constexpr int64_t kStride = kScoreThreads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t g = blockIdx.x;
@@ -1662,7 +1675,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_stream_kernel(
   float* lrow[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
-  for (int64_t b = n0 + int64_t(wave) * 64; b < n1; b += kScoreThreads) {
+  auto load_tile = [&](int64_t b) {
     const uint32_t n = uint32_t(std::min<int64_t>(b + lane, n1 - 1));
     uint32_t f = __builtin_nontemporal_load(
         reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ng) + n * 4u));
@@ -1672,10 +1685,23 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_stream_kernel(
           reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pg + p * N) + n * 16u));
       f ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
-    if (b + lane < n1) {
+    return f;
+  };
+  const int64_t first = n0 + int64_t(wave) * 64;
+  const int64_t ntiles = first < n1 ? (n1 - first + kStride - 1) / kStride : 0;
+  uint32_t f[D];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        if (qc * 4 + qq < Qg) __builtin_nontemporal_store(__uint_as_float(f + qq), lrow[qq] + b + lane);
+  for (int k = 0; k < D; ++k) f[k] = load_tile(first + k * kStride);
+  for (int64_t t0 = 0; t0 < ntiles; t0 += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+      const int64_t b = first + (t0 + k) * kStride;
+      if (t0 + k < ntiles && b + lane < n1) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (qc * 4 + qq < Qg) __builtin_nontemporal_store(__uint_as_float(f[k] + qq), lrow[qq] + b + lane);
+      }
+      f[k] = load_tile(first + (t0 + k + D) * kStride);
     }
   }
 }
