@@ -242,6 +242,27 @@ int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, i
                         int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
                         float scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * tq_attention_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same launches, same results as
+ * tq_attention_decode; the workspace lives in a static device array of
+ * tq_attention_noalloc_max_bytes() bytes (32 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  Nothing is allocated and no
+ * memory is cleared: every byte the launches read from the array is written
+ * by an earlier launch of the same call.  All calls on one GPU share the
+ * array, so calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ * Errors: as tq_attention_decode, and TQ_ERR_WORKSPACE when
+ * tq_attention_workspace_bytes(cb, G, Qg, N) exceeds the array.
+ */
+int tq_attention_decode_noalloc(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
+                                int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
+                                float scale, float* out, void* stream);
+
+/* Size in bytes of the static array tq_attention_decode_noalloc works in. */
+size_t tq_attention_noalloc_max_bytes(void);
+
 /* Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
  * d = 128 (each workgroup prepares its queries on chip; ws may be NULL);
  * G*Qg*(2*1024 + 4)*4 for d = 1024 (the prepared queries 2 R q, 2 S q and

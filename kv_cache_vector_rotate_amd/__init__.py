@@ -12,5 +12,6 @@ from ._binding import (  # noqa: F401
     score_cache, value_packed_nbytes, encode_values, attention_workspace_nbytes, attention_decode,
     score_topk, score_topk_workspace_nbytes, decode_mse, dense_logits_bf16, packed_nbytes,
     score_workspace_nbytes, rotation_dim, library, library_path, EXPORTED_SYMBOLS,
-    clock_probe, stream_probe, score_stream_probe,
+    clock_probe, stream_probe, score_stream_probe, attention_decode_noalloc,
+    attention_noalloc_max_nbytes,
 )

@@ -26,6 +26,7 @@ EXPORTED_SYMBOLS = (
     "tq_value_packed_bytes", "tq_encode_values", "tq_attention_workspace_bytes",
     "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex", "tq_rotation_dim",
     "tq_clock_probe", "tq_stream_probe", "tq_score_stream_probe",
+    "tq_attention_decode_noalloc", "tq_attention_noalloc_max_bytes",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -58,6 +59,9 @@ _SIGS = {
     "tq_attention_decode": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
                                            ctypes.c_float, _vp, _vp, _c_sz, _vp]),
     "tq_last_hip_error": (ctypes.c_int, []),
+    "tq_attention_decode_noalloc": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
+                                                   ctypes.c_float, _vp, _vp]),
+    "tq_attention_noalloc_max_bytes": (_c_sz, []),
     "tq_clock_probe": (ctypes.c_int, [_vp, _c_i32, _vp]),
     "tq_stream_probe": (ctypes.c_int, [_vp, _c_sz, _vp, _c_sz, _c_i32, _vp]),
     "tq_score_stream_probe": (ctypes.c_int, [_vp, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp]),
@@ -319,6 +323,32 @@ def attention_decode(cb: Codebook, q, kpacked, vpacked, N: int, scale=None, out=
                                          ws.numel() * ws.element_size(), _stream()),
            "tq_attention_decode")
     return out
+
+
+def attention_decode_noalloc(cb: Codebook, q, kpacked, vpacked, N: int, scale=None, out=None):
+    """attention_decode working in the library's static device scratch (no
+    workspace argument, nothing allocated by the library); out must be given
+    by callers that cannot allocate."""
+    torch = _torch()
+    for t, name in ((q, "q"), (kpacked, "kpacked"), (vpacked, "vpacked")):
+        _need_cuda(t, name)
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    _need_bytes(kpacked, packed_nbytes(cb, G, N), "kpacked")
+    _need_bytes(vpacked, value_packed_nbytes(cb, G, N), "vpacked")
+    if out is None:
+        out = torch.empty((G, Qg, d), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * d)
+    _check(library().tq_attention_decode_noalloc(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(kpacked),
+                                                 _ptr(vpacked), N, scale, _ptr(out), _stream()),
+           "tq_attention_decode_noalloc")
+    return out
+
+
+def attention_noalloc_max_nbytes() -> int:
+    return int(library().tq_attention_noalloc_max_bytes())
 
 
 def score_logits(cb: Codebook, q, packed, N: int, out=None, ws=None):

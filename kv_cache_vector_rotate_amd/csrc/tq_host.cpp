@@ -642,6 +642,32 @@ int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, i
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 
+int tq_attention_decode_noalloc(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
+                                int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
+                                float scale, float* out, void* stream) {
+  if (!cb || G < 0 || N < 0 || Qg < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return TQ_ERR_ARG;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || G * Qg > INT32_MAX ||
+      N >= (int64_t(1) << 28))
+    return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || Qg == 0) return TQ_OK;
+  if (N == 0) return TQ_ERR_ARG;
+  if (!q || !kpacked || !vpacked || !out || !aligned16(q) || !aligned16(kpacked) ||
+      !aligned16(vpacked) || !aligned16(out))
+    return TQ_ERR_ARG;
+  if (tq::attention_workspace_bytes(*cb, G, Qg, N) > tq::kScratchBytes) return TQ_ERR_WORKSPACE;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  void* ws = nullptr;
+  hipError_t e = tq::scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, N, scale, out, ws,
+                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+size_t tq_attention_noalloc_max_bytes(void) { return tq::kScratchBytes; }
+
 size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg) {
   if (!cb || G < 0 || Qg < 0) return 0;
   return tq::score_workspace_bytes(*cb, G, Qg);

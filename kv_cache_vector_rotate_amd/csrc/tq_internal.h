@@ -75,6 +75,10 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
 // Decode attention over packed keys and values (d = 128): logits into the
 // workspace, a value pass over key ranges, a combine with the rotation back.
 size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N);
+// Static device scratch of the no-allocation attention call: its size and the
+// current device's address of it (looked up once per device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_address(void** ptr);
 hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                             const void* kpacked, const void* vpacked, int64_t N, float scale,
                             float* out, void* ws, hipStream_t s);

@@ -1793,6 +1793,33 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
   return hipGetLastError();
 }
 
+// Device scratch for callers that cannot allocate (tq_attention_decode_noalloc):
+// a file-scope device array that every GPU the library runs on holds until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol): its device address is
+// looked up once per device with hipGetSymbolAddress and that pointer is used
+// everywhere.  Calls that overlap on one device share it and race.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 // Key ranges of the decode-attention value pass: multiples of 64 keys,
 // enough (group, query chunk, range) workgroups for four per compute unit.
 static void attn_split(int64_t G, int Qg, int64_t N, int64_t& chunk, int64_t& splits) {
