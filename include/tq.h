@@ -199,6 +199,46 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
                    int64_t T, void* packed, int64_t Ncap, int64_t pos, void* stream);
 
 /*
+ * Paged key cache: compression at the time the cache is written, as above,
+ * into fixed-size pages that a page table maps, so a serving loop grows each
+ * sequence's cache page by page and reuses freed pages (a ring or a sliding
+ * window is a page table whose entries the caller rotates).
+ *
+ * Pool: num_pages pages of page_size records; page i is laid out exactly as
+ * the packed buffer of one group of page_size keys (planes, then norms), so
+ * the pool is tq_packed_bytes(cb, num_pages, page_size) bytes.  page_table:
+ * device int32 [G][pages_per_group]; entry (g, p) is the pool page holding
+ * logical positions [p * page_size, (p + 1) * page_size) of group g.  The
+ * table, pos and lens live in device memory (the host does not read them):
+ * a record whose logical page is past pages_per_group, or whose table entry
+ * is outside [0, num_pages), is not written (append) and not scored (score).
+ * d = 128 only; page_size a multiple of 64 in [64, 2^20].
+ *
+ * tq_paged_append_keys: keys [G][T][d] (TQ_F32 or TQ_BF16); key t of group g
+ * is encoded exactly as tq_encode_keys would and written to logical position
+ * pos[g] + t (pos: device int32 [G]).  The G*T rows are encoded as one batch,
+ * so single new tokens of many groups share the encoder's 16-key tiles.
+ * G*T == 0 is a no-op; nothing is allocated.
+ * Errors: TQ_ERR_ARG (null/misaligned pointer: keys and pool 16-byte,
+ * table and pos 4-byte aligned; a size <= 0), TQ_ERR_UNSUPPORTED (d != 128,
+ * page_size, G*T >= 2^31, G*pages_per_group >= 2^31), TQ_ERR_HIP.
+ *
+ * tq_paged_score: logits[g][h][n] (float32 [G][Qg][Lmax]) for n < min(lens[g],
+ * Lmax, pages_per_group * page_size), the estimator of tq_score_logits on the
+ * record at logical position n of group g; other logits are left untouched.
+ * Errors: as tq_paged_append_keys (logits 16-byte aligned, lens 4-byte),
+ * TQ_ERR_UNSUPPORTED also for Qg > 256 or Lmax >= 2^28.
+ */
+int tq_paged_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, int64_t G,
+                         int64_t T, void* pool, int64_t num_pages, int32_t page_size,
+                         const int32_t* page_table, int32_t pages_per_group, const int32_t* pos,
+                         void* stream);
+int tq_paged_score(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                   const void* pool, int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                   int32_t pages_per_group, const int32_t* lens, int64_t Lmax, float* logits,
+                   void* stream);
+
+/*
  * Value records (MSE-only): the community implementation on the Qiita
  * explainer compresses values with the Stage-1 quantizer alone (API table:
  * value compressor = rotation + Lloyd-Max), and its byte table counts b-bit

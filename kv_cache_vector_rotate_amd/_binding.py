@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex", "tq_rotation_dim",
     "tq_clock_probe", "tq_stream_probe", "tq_score_stream_probe",
     "tq_attention_decode_noalloc", "tq_attention_noalloc_max_bytes",
+    "tq_paged_append_keys", "tq_paged_score",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -62,6 +63,10 @@ _SIGS = {
     "tq_attention_decode_noalloc": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
                                                    ctypes.c_float, _vp, _vp]),
     "tq_attention_noalloc_max_bytes": (_c_sz, []),
+    "tq_paged_append_keys": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _vp,
+                                            _c_i32, _vp, _vp]),
+    "tq_paged_score": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _c_i32, _vp, _c_i32,
+                                      _vp, _c_i64, _vp, _vp]),
     "tq_clock_probe": (ctypes.c_int, [_vp, _c_i32, _vp]),
     "tq_stream_probe": (ctypes.c_int, [_vp, _c_sz, _vp, _c_sz, _c_i32, _vp]),
     "tq_score_stream_probe": (ctypes.c_int, [_vp, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp]),
@@ -272,6 +277,63 @@ def score_cache(cb: Codebook, q, packed, Ncap: int, length: int, out=None):
     _need_out(out, G * Qg * length)
     _check(library().tq_score_cache(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(packed), Ncap,
                                     length, _ptr(out), _stream()), "tq_score_cache")
+    return out
+
+
+def _need_i32(t, n: int, name: str):
+    torch = _torch()
+    _need_cuda(t, name)
+    if t.dtype != torch.int32 or t.numel() < n:
+        raise ValueError(f"{name} must be a device int32 tensor of at least {n} elements")
+
+
+def paged_pool_nbytes(cb: Codebook, num_pages: int, page_size: int) -> int:
+    """Bytes of a pool of num_pages pages of page_size records."""
+    return packed_nbytes(cb, num_pages, page_size)
+
+
+def paged_append_keys(cb: Codebook, keys, pool, page_size: int, page_table, pos):
+    """Encode keys [G, T, d] into a paged pool: key t of group g goes to
+    logical position pos[g] + t through page_table [G, pages_per_group]
+    (device int32); pos is a device int32 [G].  In place."""
+    _need_cuda(keys, "keys")
+    _need_cuda(pool, "pool")
+    G, T, d = keys.shape
+    if d != cb.d:
+        raise ValueError("key dimension does not match the codebook")
+    per_page = packed_nbytes(cb, 1, page_size)
+    num_pages = (pool.numel() * pool.element_size()) // per_page if per_page else 0
+    if page_table.dim() != 2 or page_table.shape[0] != G:
+        raise ValueError("page_table must be [G, pages_per_group]")
+    _need_i32(page_table, G * page_table.shape[1], "page_table")
+    _need_i32(pos, G, "pos")
+    _check(library().tq_paged_append_keys(cb.handle, _ptr(keys), _dtype_code(keys), G, T, _ptr(pool),
+                                          num_pages, page_size, _ptr(page_table), page_table.shape[1],
+                                          _ptr(pos), _stream()), "tq_paged_append_keys")
+    return pool
+
+
+def paged_score(cb: Codebook, q, pool, page_size: int, page_table, lens, Lmax: int, out=None):
+    """q [G, Qg, d] against the first lens[g] records of each group of a
+    paged pool -> float32 [G, Qg, Lmax] (entries past lens[g] untouched)."""
+    torch = _torch()
+    _need_cuda(q, "q")
+    _need_cuda(pool, "pool")
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    per_page = packed_nbytes(cb, 1, page_size)
+    num_pages = (pool.numel() * pool.element_size()) // per_page if per_page else 0
+    if page_table.dim() != 2 or page_table.shape[0] != G:
+        raise ValueError("page_table must be [G, pages_per_group]")
+    _need_i32(page_table, G * page_table.shape[1], "page_table")
+    _need_i32(lens, G, "lens")
+    if out is None:
+        out = torch.zeros((G, Qg, Lmax), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * Lmax)
+    _check(library().tq_paged_score(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(pool), num_pages,
+                                    page_size, _ptr(page_table), page_table.shape[1], _ptr(lens), Lmax,
+                                    _ptr(out), _stream()), "tq_paged_score")
     return out
 
 

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtq.so")
 SOURCES = [os.path.join(HERE, "csrc", "tq_host.cpp"), os.path.join(HERE, "csrc", "tq_kernels.hip"),
-           os.path.join(HERE, "csrc", "tq_wide.hip")]
+           os.path.join(HERE, "csrc", "tq_wide.hip"), os.path.join(HERE, "csrc", "tq_wider.hip")]
 
 
 def hipcc_command(out=LIB):

@@ -212,7 +212,7 @@ void sketch_from_rotated(const double* S_rot, const int8_t* delta, int m, int d,
 // to D [ICLR 2026 paper digest, "実装のポイント": zero padding up to the
 // nearest power of two for the Hadamard transform]); 0 when unsupported.
 int rotation_dim(int d) {
-  if (d < 1 || d > 1024) return 0;
+  if (d < 1 || d > 4096) return 0;
   int D = 32;
   while (D < d) D <<= 1;
   return (D == d || d % 16 == 0) ? D : 0;
@@ -227,7 +227,7 @@ bool valid_params(int d, int bits, int m) {
 
 bool device_params(int d) {
   const int D = rotation_dim(d);
-  return D == 128 || D == 1024;
+  return D == 128 || D == 1024 || D == 2048 || D == 4096;
 }
 
 uint16_t half_bits(double v) {
@@ -386,6 +386,8 @@ void release_device(tq::Codebook& cb) {
   if (cb.d_Sh) (void)hipFree(cb.d_Sh);
   if (cb.d_flip_f32) (void)hipFree(cb.d_flip_f32);
   if (cb.d_fragW) (void)hipFree(cb.d_fragW);
+  if (cb.d_Scol) (void)hipFree(cb.d_Scol);
+  cb.d_Scol = nullptr;
   if (cb.d_frag16) (void)hipFree(cb.d_frag16);
   if (cb.d_dm16) (void)hipFree(cb.d_dm16);
   cb.d_fragW = nullptr;
@@ -412,16 +414,25 @@ int upload_device(tq::Codebook& cb) {
       cb.num_cus <= 0)
     cb.num_cus = 256;
   e = upload(&cb.d_consts, &cb.consts, sizeof(tq::DevConsts));
-  if (e == hipSuccess && cb.d == 1024) {
+  if (e == hipSuccess && cb.d >= 1024) {
     std::vector<uint16_t> frag;
     build_fragments_wide(cb.S_rot, cb.d, frag);
     e = upload(&cb.d_fragW, frag.data(), frag.size() * sizeof(uint16_t));
   }
-  if (e == hipSuccess && cb.d == 1024) {   // the d = 1024 query preparation reads S column by column
+  if (e == hipSuccess && cb.d >= 1024) {   // the wide query preparation reads S column by column
     std::vector<float> st(cb.S.size());
     for (int j = 0; j < cb.m; ++j)
       for (int c = 0; c < cb.d; ++c) st[size_t(c) * cb.m + j] = float(cb.S[size_t(j) * cb.d + c]);
     e = upload(&cb.d_St, st.data(), st.size() * sizeof(float));
+  }
+  if (e == hipSuccess && cb.d > 1024) {    // sum_j (S q)_j = (column sums of S) . q
+    std::vector<float> col(cb.d);
+    for (int c = 0; c < cb.d; ++c) {
+      double t = 0.0;
+      for (int j = 0; j < cb.m; ++j) t += cb.S[size_t(j) * cb.d + c];
+      col[c] = float(t);
+    }
+    e = upload(&cb.d_Scol, col.data(), col.size() * sizeof(float));
   }
   if (e == hipSuccess && cb.d == 128) {
     std::vector<uint16_t> frag;
@@ -593,6 +604,62 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
   if (rc != TQ_OK) return rc;
   hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, T, Ncap, pos, packed,
                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+namespace {
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shape of a paged pool the d = 128 kernels take: pages of a multiple of 64
+// records (each 64-key score tile lies in one page).
+int check_pool(const tq_codebook* cb, int64_t num_pages, int32_t page_size, int32_t ppg) {
+  if (num_pages <= 0 || page_size <= 0 || ppg <= 0) return TQ_ERR_ARG;
+  if (cb->d != 128 || page_size % 64 != 0 || page_size > (1 << 20) || num_pages > INT32_MAX)
+    return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+}  // namespace
+
+int tq_paged_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, int64_t G,
+                         int64_t T, void* pool, int64_t num_pages, int32_t page_size,
+                         const int32_t* page_table, int32_t pages_per_group, const int32_t* pos,
+                         void* stream) {
+  if (!cb || G < 0 || T < 0 || (key_dtype != TQ_F32 && key_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  int rc = check_pool(cb, num_pages, page_size, pages_per_group);
+  if (rc != TQ_OK) return rc;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (G * T >= (int64_t(1) << 31) || G * int64_t(pages_per_group) >= (int64_t(1) << 31))
+    return TQ_ERR_UNSUPPORTED;
+  if (!keys || !pool || !page_table || !pos || !aligned16(keys) || !aligned16(pool) ||
+      !aligned4(page_table) || !aligned4(pos))
+    return TQ_ERR_ARG;
+  rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_encode_paged(*cb, keys, key_dtype, G, T, pool, num_pages, page_size,
+                                         page_table, pages_per_group, pos,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_paged_score(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                   const void* pool, int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                   int32_t pages_per_group, const int32_t* lens, int64_t Lmax, float* logits,
+                   void* stream) {
+  if (!cb || G < 0 || Qg < 0 || Lmax < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  int rc = check_pool(cb, num_pages, page_size, pages_per_group);
+  if (rc != TQ_OK) return rc;
+  if (Qg > 256 || G > INT32_MAX || Lmax >= (int64_t(1) << 28) ||
+      G * int64_t(pages_per_group) >= (int64_t(1) << 31))
+    return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || Qg == 0 || Lmax == 0) return TQ_OK;
+  if (!q || !pool || !page_table || !lens || !logits || !aligned16(q) || !aligned16(pool) ||
+      !aligned4(page_table) || !aligned4(lens) || !aligned16(logits))
+    return TQ_ERR_ARG;
+  rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_score_paged(*cb, q, q_dtype, G, Qg, pool, num_pages, page_size, page_table,
+                                        pages_per_group, lens, Lmax, logits,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 

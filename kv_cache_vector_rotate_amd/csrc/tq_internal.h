@@ -22,7 +22,7 @@ struct DevConsts {
   float inv_sqrt_d;   // 1/sqrt(d)
   float qjl_scale;    // sqrt(pi/2) / m
   float alpha_sum;    // alpha[0] + ... + alpha[3]
-  uint32_t dneg[32];  // bit (i % 32) of word i/32 set where delta_i = -1 (d <= 1024)
+  uint32_t dneg[128]; // bit (i % 32) of word i/32 set where delta_i = -1 (d <= 4096)
   uint32_t din;       // length of input rows (and of decoded rows): d, or less when zero-padded to d
   uint32_t pad[3];
 };
@@ -49,7 +49,8 @@ struct Codebook {
   float* d_St = nullptr;         // S transposed, float32 [d][m] (d = 1024)
   uint4* d_Sh = nullptr;         // d = 128 scorer: S R^T as float16 (exact), [column segment 8][row 128][16]
   uint32_t* d_flip_f32 = nullptr;   // [2][d/2] sign-flip words for f32 (d = 128)
-  uint4* d_fragW = nullptr;         // S R^T for d = 1024: [row block 32][k-step 64][lane 64]
+  uint4* d_fragW = nullptr;         // S R^T for d >= 1024: [row block d/32][k-step d/16][lane 64]
+  float* d_Scol = nullptr;          // column sums of S, float32 [d] (d >= 2048)
   int num_cus = 0;                  // compute units of the device
 };
 
@@ -64,6 +65,15 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
 hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                         const void* packed, int64_t N, int64_t Ncap, float* logits, void* ws,
                         hipStream_t s);
+// Paged cache (d = 128): a pool of num_pages pages of page_size records
+// (each page laid out as one packed group), a page table [G][ppg] of pool
+// page indices, per-group first positions (append) or lengths (score).
+hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
+                               void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                               int ppg, const int32_t* pos, hipStream_t s);
+hipError_t launch_score_paged(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                              const void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                              int ppg, const int32_t* lens, int64_t Lmax, float* logits, hipStream_t s);
 hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
                          int odtype, hipStream_t s);
 hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg, int64_t N, int d,
@@ -88,6 +98,14 @@ hipError_t launch_decode_wide(const Codebook& cb, const void* packed, int64_t G,
 hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                               void* packed, hipStream_t s);
 size_t score_wide_prep_bytes(int64_t G, int Qg);
+// d = 2048 and 4096 (tq_wider.hip)
+hipError_t launch_encode_wider(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
+                               void* packed, hipStream_t s);
+size_t score_wider_prep_bytes(const Codebook& cb, int64_t G, int Qg);
+hipError_t launch_score_wider(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                              const void* packed, int64_t N, float* logits, void* ws, hipStream_t s);
+hipError_t launch_decode_wider(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
+                               int odtype, hipStream_t s);
 size_t topk_wide_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N, int K);
 hipError_t launch_score_wide(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
                              const void* packed, int64_t N, float* logits, void* ws, hipStream_t s);

@@ -507,6 +507,37 @@ struct TileOut16 {
   bool valid;
 };
 
+// Paged cache: a pool of pages, each laid out as one packed group of
+// page_size records; table[g * ppg + p] is the pool page that holds logical
+// page p of group g.  Appends take rows [G][T] and pos[g], the logical
+// position of group g's first new row; scoring takes lens[g], the number of
+// records of group g.
+struct PageMap {
+  const int32_t* table;
+  const int32_t* pos;
+  const int32_t* lens;
+  uint32_t T;
+  int32_t ppg;         // table entries per group
+  int32_t page_size;   // records per page (a multiple of 64)
+  int32_t num_pages;   // pages in the pool
+};
+
+// Pool page and slot of row r of a [G][T] append; false when the row's
+// logical page lies outside its group's table or the entry outside the pool
+// (the row is then not written).
+__device__ __forceinline__ bool page_dest(const PageMap& pm, int64_t r, int64_t& page, int64_t& slot) {
+  const uint32_t g = uint32_t(r) / pm.T, t = uint32_t(r) - g * pm.T;
+  const int64_t lp = int64_t(pm.pos[g]) + t;
+  if (lp < 0) return false;
+  const int64_t lpage = lp / pm.page_size;
+  if (lpage >= pm.ppg) return false;
+  const int32_t ph = pm.table[int64_t(g) * pm.ppg + lpage];
+  if (ph < 0 || ph >= pm.num_pages) return false;
+  page = ph;
+  slot = lp - lpage * pm.page_size;
+  return true;
+}
+
 template <int B>
 __device__ __forceinline__ void store_tile16(const TileOut16& o, int lane, int64_t Ncap,
                                              uint32_t* __restrict__ planes,
@@ -758,12 +789,17 @@ __device__ __forceinline__ void value_tail16(const f32x4 (&y)[8], float nu2,
 }
 
 // VAL: value records (B = value bits, no sketch; norms are uint16 halves).
-template <int B, bool VAL>
-__global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : 3) void encode128_bf16_t16_kernel(
+// PAGED: keys are the G = 1 x N rows of a [groups][T] append whose records go
+// to the pool pages the page map gives (Ncap = page size); a 16-key tile then
+// holds rows of up to 16 different groups.
+// Keys run three workgroups per CU (168 VGPRs) except at B = 3, whose extra
+// thresholds and code words need more registers: two workgroups per CU.
+template <int B, bool VAL, bool PAGED = false>
+__global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : (B == 3 ? 2 : 3)) void encode128_bf16_t16_kernel(
     const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
     uint32_t* __restrict__ planes, void* __restrict__ norms_,
     const DevConsts* __restrict__ cst, const uint4* __restrict__ frag,
-    const uint4* __restrict__ dmask) {
+    const uint4* __restrict__ dmask, PageMap pm) {
   __shared__ uint4 s_frag[VAL ? 1 : 2048];           // 32 KB: [t 4][b 8][lane 64]
   __shared__ uint4 s_raw[kEnc16Waves][4 * 64];       // 16 KB: per-wave key tile
   __shared__ uint4 s_dm[16];                         // D as bf16 sign bits, [word][k-step]
@@ -800,6 +836,10 @@ __global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : 3) void encode128_bf16_t16
     const int64_t g = gt;
     const int64_t n = int64_t(t32 - gt * tpg) * 16 + kl;
     const bool valid = n < N;
+    // paged rows: the page-map loads go out before the wait for the key tile
+    int64_t dg = g, dn = pos + n;
+    bool dv = valid;
+    if constexpr (PAGED) dv = valid && page_dest(pm, n, dg, dn);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     u32x4 raw[4], dmv[4];
 #pragma unroll
@@ -860,7 +900,7 @@ __global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : 3) void encode128_bf16_t16
       // a wave in its vector-heavy stretch issues ahead of waves running
       // rotation products (measured 1-2% faster than equal priorities)
       __builtin_amdgcn_s_setprio(1);
-      quant_sketch16<B>(y, nu2, ec, s_frag, lane, g, pos + n, valid, pend);
+      quant_sketch16<B>(y, nu2, ec, s_frag, lane, dg, dn, dv, pend);
       __builtin_amdgcn_s_setprio(0);
       have = true;
     }
@@ -879,12 +919,12 @@ __global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : 3) void encode128_bf16_t16
 constexpr int kEncThreads = 256;
 constexpr int kEncWaves = kEncThreads / 64;
 
-template <int B, bool VAL>
+template <int B, bool VAL, bool PAGED = false>
 __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     const float* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
     uint32_t* __restrict__ planes,
     void* __restrict__ norms_, const DevConsts* __restrict__ cst,
-    const uint4* __restrict__ frag, const uint32_t* __restrict__ flip) {
+    const uint4* __restrict__ frag, const uint32_t* __restrict__ flip, PageMap pm) {
   __shared__ uint4 s_frag[VAL ? 1 : 2048];       // [kc 8][jb 4][lane 64]
   __shared__ uint32_t s_flip[128];
 
@@ -955,7 +995,10 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
       store_vtile<B>(out, lane, Ncap, planes, static_cast<uint16_t*>(norms_));
     } else {
       TileOut out;
-      encode_tail<B>(x, nu2, ec, s_frag, lane, g, pos + n, valid, out);
+      int64_t dg = g, dn = pos + n;
+      bool dv = valid;
+      if constexpr (PAGED) dv = valid && page_dest(pm, n, dg, dn);
+      encode_tail<B>(x, nu2, ec, s_frag, lane, dg, dn, dv, out);
       store_tile<B>(out, lane, Ncap, planes, static_cast<uint32_t*>(norms_));
     }
   }
@@ -1026,11 +1069,15 @@ __device__ __forceinline__ float butterfly_lane32(float y, bool up) {
   return up ? r0 - r1 : r0 + r1;   // lanes < 32: (own, partner); lanes >= 32: (partner, own)
 }
 
-template <int B, bool QBF16>
+// PAGED: records of group g live in the pool pages of the page map
+// (planes/norms are the pool's), group g has lens[g] of them (at most
+// ppg * page_size), and N is the logit row length; each 64-key tile lies in
+// one page.
+template <int B, bool QBF16, bool PAGED = false>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
     int64_t N, int64_t Ncap, int Qg, int64_t chunk, float* __restrict__ logits,
-    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh) {
+    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh, PageMap pm) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
   constexpr int D = 2;   // key tiles in flight per wave (two measured 2-3% faster than three at b = 3)
@@ -1042,7 +1089,11 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const int64_t g = blockIdx.x;
   const int qc = blockIdx.y;
   const int64_t n0 = int64_t(blockIdx.z) * chunk;
-  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);   // n0 < n1: the host sizes the grid so
+  int64_t n1 = std::min<int64_t>(N, n0 + chunk);   // n0 < n1: the host sizes the grid so
+  if constexpr (PAGED) {   // group lengths live in device memory: ranges past them have no work
+    n1 = std::min<int64_t>(n1, std::min<int64_t>(pm.lens[g], int64_t(pm.ppg) * pm.page_size));
+    if (n1 <= n0) return;
+  }
   // keys [0, N) of a cache holding Ncap records per group; logits [G][Qg][N]
   const uint4* pg = planes + g * P * Ncap;
   const uint32_t* ng = norms + g * Ncap;
@@ -1077,23 +1128,39 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   uint32_t dn0 = cst->dneg[lane >> 5], dn1 = cst->dneg[2 + (lane >> 5)];
   // wave-uniform plane bases + 32-bit lane offsets (key index < 2^28): the
   // loads take the scalar-base form and need no 64-bit address arithmetic
-  auto load_tile = [&](int64_t b, uint4 (&wv)[P], uint32_t& nv) {
-    const uint32_t n = uint32_t(std::min<int64_t>(b + lane, n1 - 1));
+  auto load_tile = [&](int64_t b, uint4 (&wv)[P], uint32_t& nv, bool& ok) {
+    uint32_t n = uint32_t(std::min<int64_t>(b + lane, n1 - 1));
+    const uint4* pt = pg;
+    const uint32_t* nt = ng;
+    int64_t stride = Ncap;
+    ok = true;
+    if constexpr (PAGED) {
+      // the tile (or, past the range, the clamped last record) lies in one page
+      const int32_t lpage = int32_t(std::min<int64_t>(b, n1 - 1) / pm.page_size);
+      int32_t ph = __builtin_amdgcn_readfirstlane(pm.table[g * pm.ppg + lpage]);
+      ok = ph >= 0 && ph < pm.num_pages;
+      if (!ok) ph = 0;   // read a valid page, store nothing
+      pt = planes + int64_t(ph) * P * pm.page_size;
+      nt = norms + int64_t(ph) * pm.page_size;
+      n -= uint32_t(lpage) * uint32_t(pm.page_size);
+      stride = pm.page_size;
+    }
     const uint32_t off16 = n * 16u, off4 = n * 4u;   // byte offsets, < 2^32
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const u32x4 v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pg + p * Ncap) + off16));
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(pt + p * stride) + off16));
       wv[p] = make_uint4(v[0], v[1], v[2], v[3]);
     }
     nv = __builtin_nontemporal_load(
-        reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(ng) + off4));
+        reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(nt) + off4));
   };
   const int64_t first = n0 + int64_t(wave) * 64;
   uint4 w[D][P];
   uint32_t nr[D];
+  bool okt[D];
 #pragma unroll
-  for (int k = 0; k < D; ++k) load_tile(first + k * kStride, w[k], nr[k]);
+  for (int k = 0; k < D; ++k) load_tile(first + k * kStride, w[k], nr[k], okt[k]);
   // (an empty use outside the branch below keeps these loads ahead of the key
   // tiles: issued later, waiting for them would also wait for the tiles)
   asm volatile("" : "+v"(u0), "+v"(u1), "+v"(dn0), "+v"(dn1));
@@ -1239,7 +1306,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     }
   };
 
-  auto score_tile = [&](const uint4 (&wt)[P], uint32_t nrm, int64_t b) {
+  auto score_tile = [&](const uint4 (&wt)[P], uint32_t nrm, int64_t b, bool ok) {
     uint32_t rw[NW][4];
 #pragma unroll
     for (int p = 0; p < P; ++p) permute_words(wt[p], s2, s1, rw[p]);
@@ -1259,7 +1326,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     add_plane(rw[B], 1, acc[B]);
 
     const float nu = h2f_bits(nrm & 0xffffu), rs = h2f_bits(nrm >> 16) * qs;
-    const bool in_range = b + lane < n1;
+    const bool in_range = b + lane < n1 && ok;
     uint32_t off4 = (uint32_t(b) + uint32_t(lane)) * 4u;
     asm volatile("" : "+v"(off4));   // keep the offset 32-bit (scalar-base stores)
 #pragma unroll
@@ -1286,8 +1353,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   for (int64_t t0 = 0; t0 < ntiles; t0 += D) {
 #pragma unroll
     for (int k = 0; k < D; ++k) {
-      if (t0 + k < ntiles) score_tile(w[k], nr[k], first + (t0 + k) * kStride);
-      load_tile(first + (t0 + k + D) * kStride, w[k], nr[k]);
+      if (t0 + k < ntiles) score_tile(w[k], nr[k], first + (t0 + k) * kStride, okt[k]);
+      load_tile(first + (t0 + k + D) * kStride, w[k], nr[k], okt[k]);
     }
   }
   // the refills past the range are never used: let them land before the wave ends
@@ -1708,30 +1775,33 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_stream_kernel(
 
 }  // namespace
 
-bool encode_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
-bool score_supported(const Codebook& cb) { return cb.d == 128 || cb.d == 1024; }
+bool encode_supported(const Codebook& cb) {
+  return cb.d == 128 || cb.d == 1024 || cb.d == 2048 || cb.d == 4096;
+}
+bool score_supported(const Codebook& cb) { return encode_supported(cb); }
 
 // d = 128: each workgroup prepares its queries itself, no workspace; d = 1024:
 // the prepared queries (2 R q, 2 S q and their sums) for all groups.
 size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg) {
-  return cb.d == 1024 ? score_wide_prep_bytes(G, Qg) : 0;
+  return cb.d == 1024 ? score_wide_prep_bytes(G, Qg) : cb.d > 1024 ? score_wider_prep_bytes(cb, G, Qg) : 0;
 }
 
 hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                          int64_t Ncap, int64_t pos, void* packed, hipStream_t s) {
   if (cb.d == 1024) return launch_encode_wide(cb, keys, dtype, G, N, packed, s);
+  if (cb.d > 1024) return launch_encode_wider(cb, keys, dtype, G, N, packed, s);
   const int64_t ntiles = G * ((N + 31) / 32);
   uint32_t* planes = static_cast<uint32_t*>(packed);
   uint32_t* norms = planes + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
   if (dtype == 1) {
     const int64_t ntiles16 = G * ((N + 15) / 16);
     const int64_t want = (ntiles16 + kEnc16Waves - 1) / kEnc16Waves;
-    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 3));
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * (cb.bits == 4 ? 2 : 3)));
     const uint16_t* kb = static_cast<const uint16_t*>(keys);
 #define TQ_ENCB(BB)                                                                              \
   hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, false>), dim3(grid), dim3(kEnc16Threads), 0, s, kb, G, N, \
                      Ncap, pos, planes, norms, cb.d_consts, cb.d_frag16,                       \
-                     reinterpret_cast<const uint4*>(cb.d_dm16))
+                     reinterpret_cast<const uint4*>(cb.d_dm16), PageMap{})
     switch (cb.bits - 1) {
       case 1: TQ_ENCB(1); break;
       case 2: TQ_ENCB(2); break;
@@ -1745,7 +1815,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
 #define TQ_ENCF(BB)                                                                             \
   hipLaunchKernelGGL((encode128_f32_kernel<BB, false>), dim3(grid), dim3(kEncThreads), 0, s, kf, G, N, \
                      Ncap, pos, \
-                     planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32)
+                     planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32, PageMap{})
     switch (cb.bits - 1) {
       case 1: TQ_ENCF(1); break;
       case 2: TQ_ENCF(2); break;
@@ -1769,7 +1839,7 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
 #define TQ_VB(BB)                                                                                  \
   hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, true>), dim3(grid), dim3(kEnc16Threads), 0, s, vb, \
                      G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag16,                 \
-                     reinterpret_cast<const uint4*>(cb.d_dm16))
+                     reinterpret_cast<const uint4*>(cb.d_dm16), PageMap{})
     switch (cb.bits) {
       case 2: TQ_VB(2); break;
       case 3: TQ_VB(3); break;
@@ -1782,7 +1852,7 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
     const float* vf = static_cast<const float*>(values);
 #define TQ_VF(BB)                                                                                \
   hipLaunchKernelGGL((encode128_f32_kernel<BB, true>), dim3(grid), dim3(kEncThreads), 0, s, vf, \
-                     G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32)
+                     G, N, N, int64_t(0), planes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32, PageMap{})
     switch (cb.bits) {
       case 2: TQ_VF(2); break;
       case 3: TQ_VF(3); break;
@@ -1888,6 +1958,7 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
                         const void* packed, int64_t N, int64_t Ncap, float* logits, void* ws,
                         hipStream_t s) {
   if (cb.d == 1024) return launch_score_wide(cb, q, qdtype, G, Qg, packed, N, logits, ws, s);
+  if (cb.d > 1024) return launch_score_wider(cb, q, qdtype, G, Qg, packed, N, logits, ws, s);
   int64_t chunk = 0;
   const dim3 grid = score_grid(G, Qg, N, chunk);
   const uint4* planes = static_cast<const uint4*>(packed);
@@ -1896,7 +1967,7 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const bool bf = qdtype == 1;
 #define TQ_SC(BB, QB)                                                                   \
   hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_Sh)
+                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
@@ -1909,6 +1980,7 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
 hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
                          int odtype, hipStream_t s) {
   if (cb.d == 1024) return launch_decode_wide(cb, packed, G, N, out, odtype, s);
+  if (cb.d > 1024) return launch_decode_wider(cb, packed, G, N, out, odtype, s);
   const int64_t keys = G * N;
   const int grid = int(std::min<int64_t>((keys + 3) / 4, int64_t(num_cus()) * 64));
   const uint32_t* planes = static_cast<const uint32_t*>(packed);
@@ -1981,6 +2053,70 @@ hipError_t launch_score_stream_probe(const Codebook& cb, int64_t G, int Qg, cons
     default: TQ_SP(3); break;
   }
 #undef TQ_SP
+  return hipGetLastError();
+}
+
+// Paged cache: appends as one [1][G*T] batch of rows whose destinations come
+// from the page map (so a 16-key tile packs rows of 16 groups when T = 1);
+// scoring with the page map and per-group lengths.
+hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
+                               void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                               int ppg, const int32_t* pos, hipStream_t s) {
+  const int64_t rows = G * T;
+  uint32_t* planes = static_cast<uint32_t*>(pool);
+  uint32_t* norms = planes + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
+  const PageMap pm{table, pos, nullptr, uint32_t(T), ppg, page_size, int32_t(num_pages)};
+  if (dtype == 1) {
+    const int64_t want = ((rows + 15) / 16 + kEnc16Waves - 1) / kEnc16Waves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * (cb.bits == 4 ? 2 : 3)));
+    const uint16_t* kb = static_cast<const uint16_t*>(keys);
+#define TQ_ENCP(BB)                                                                              \
+  hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, false, true>), dim3(grid), dim3(kEnc16Threads), 0, s, \
+                     kb, int64_t(1), rows, int64_t(page_size), int64_t(0), planes, norms, cb.d_consts,     \
+                     cb.d_frag16, reinterpret_cast<const uint4*>(cb.d_dm16), pm)
+    switch (cb.bits - 1) {
+      case 1: TQ_ENCP(1); break;
+      case 2: TQ_ENCP(2); break;
+      default: TQ_ENCP(3); break;
+    }
+#undef TQ_ENCP
+  } else {
+    const int64_t want = ((rows + 31) / 32 + kEncWaves - 1) / kEncWaves;
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 2));
+    const float* kf = static_cast<const float*>(keys);
+#define TQ_ENCPF(BB)                                                                               \
+  hipLaunchKernelGGL((encode128_f32_kernel<BB, false, true>), dim3(grid), dim3(kEncThreads), 0, s, kf,   \
+                     int64_t(1), rows, int64_t(page_size), int64_t(0), planes, norms, cb.d_consts,       \
+                     cb.d_frag, cb.d_flip_f32, pm)
+    switch (cb.bits - 1) {
+      case 1: TQ_ENCPF(1); break;
+      case 2: TQ_ENCPF(2); break;
+      default: TQ_ENCPF(3); break;
+    }
+#undef TQ_ENCPF
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_paged(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                              const void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                              int ppg, const int32_t* lens, int64_t Lmax, float* logits, hipStream_t s) {
+  int64_t chunk = 0;
+  const dim3 grid = score_grid(G, Qg, Lmax, chunk);
+  const uint4* planes = static_cast<const uint4*>(pool);
+  const uint32_t* norms =
+      static_cast<const uint32_t*>(pool) + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
+  const PageMap pm{table, nullptr, lens, 1u, ppg, page_size, int32_t(num_pages)};
+  const bool bf = qdtype == 1;
+#define TQ_SCP(BB, QB)                                                                          \
+  hipLaunchKernelGGL((score128_kernel<BB, QB, true>), grid, dim3(kScoreThreads), 0, s, q, planes, \
+                     norms, Lmax, int64_t(page_size), Qg, chunk, logits, cb.d_consts, cb.d_Sh, pm)
+  switch (cb.bits - 1) {
+    case 1: if (bf) TQ_SCP(1, true); else TQ_SCP(1, false); break;
+    case 2: if (bf) TQ_SCP(2, true); else TQ_SCP(2, false); break;
+    default: if (bf) TQ_SCP(3, true); else TQ_SCP(3, false); break;
+  }
+#undef TQ_SCP
   return hipGetLastError();
 }
 

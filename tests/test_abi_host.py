@@ -44,7 +44,7 @@ def test_host_tables_match_oracle(d, bits, seed):
 
 def test_host_tables_reject_unsupported():
     lib = K.library()
-    for d, bits, m in ((100, 3, 100), (2048, 3, 2048), (128, 5, 128), (128, 1, 128), (128, 3, 64), (16, 3, 16)):
+    for d, bits, m in ((100, 3, 100), (8192, 3, 8192), (128, 5, 128), (128, 1, 128), (128, 3, 64), (16, 3, 16)):
         assert lib.tq_codebook_tables(d, bits, m, 1, None, None, None, None, None) == -2
 
 
@@ -99,10 +99,11 @@ def test_rotation_dim_and_padded_tables():
     oracle's (same seed)."""
     lib = K.library()
     for d, D in ((96, 128), (80, 128), (112, 128), (128, 128), (32, 32), (16, 32), (48, 64),
-                 (768, 1024), (1008, 1024), (1024, 1024), (100, 0), (1000, 0), (2048, 0), (0, 0)):
+                 (768, 1024), (1008, 1024), (1024, 1024), (100, 0), (1000, 0), (1040, 2048),
+                 (1536, 2048), (2048, 2048), (3072, 4096), (4096, 4096), (4100, 0), (8192, 0), (0, 0)):
         assert lib.tq_rotation_dim(d) == D, d
         assert K.rotation_dim(d) == D
-    for d in (96, 768):
+    for d in (96, 768, 1536):
         D = lib.tq_rotation_dim(d)
         t = K.codebook_tables(d, 4, D, 42)
         cb = O.make_codebook(d, 4, D, 42)
