@@ -215,10 +215,14 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
  * d = 128 only; page_size a multiple of 64 in [64, 2^20].
  *
  * tq_paged_append_keys: keys [G][T][d] (TQ_F32 or TQ_BF16); key t of group g
- * is encoded exactly as tq_encode_keys would and written to logical position
- * pos[g] + t (pos: device int32 [G]).  The G*T rows are encoded as one batch,
- * so single new tokens of many groups share the encoder's 16-key tiles.
- * G*T == 0 is a no-op; nothing is allocated.
+ * is encoded by the rules of tq_encode_keys and written to logical position
+ * pos[g] + t (pos: device int32 [G]).  The G*T rows are encoded as one batch:
+ * up to 2048 rows by a one-key-per-wave kernel for latency (float32
+ * rotation and projection: its records equal tq_encode_keys's except where a
+ * rotated coordinate lies within rounding of a threshold or a projection
+ * within rounding of zero, cases the method's parity rules leave open), more
+ * rows by the tile encoder of tq_encode_keys in paged form (identical
+ * records).  G*T == 0 is a no-op; nothing is allocated.
  * Errors: TQ_ERR_ARG (null/misaligned pointer: keys and pool 16-byte,
  * table and pos 4-byte aligned; a size <= 0), TQ_ERR_UNSUPPORTED (d != 128,
  * page_size, G*T >= 2^31, G*pages_per_group >= 2^31), TQ_ERR_HIP.

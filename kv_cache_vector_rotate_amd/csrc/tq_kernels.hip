@@ -1361,6 +1361,144 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ============================================================== append, few rows, d = 128
+// Latency path of the paged append: one key per wave.  Lane L holds
+// coordinates L and L + 64; the rotation is a float32 butterfly (stride 64
+// inside the lane with +0 so that no -0 survives, strides 1..32 across lanes);
+// every bit-plane word comes from a wave ballot (bit L of the ballot over
+// coordinate L or L + 64 is bit L % 32 of word L / 32 or 2 + L / 32, the
+// natural order); S r is formed in float32 from the exact float16 rows of
+// S R^T (lane L: sketch rows L and L + 64, loaded before anything else)
+// against the residual broadcast through LDS.  Same rules as the tile
+// encoders; the float32 sums differ from theirs only in rounding.
+constexpr int kAppendThreads = 256;
+
+template <int B, bool BF16>
+__global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
+    const void* __restrict__ keys, int64_t rows, uint32_t* __restrict__ planes,
+    uint32_t* __restrict__ norms, const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh,
+    PageMap pm) {
+  constexpr int K = 1 << (B - 1);   // levels on the positive half
+  constexpr int P = B + 1;
+  __shared__ f32x4 s_r[kAppendThreads / 64][32];   // per-wave residual, 128 floats
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = int64_t(blockIdx.x) * (kAppendThreads / 64) + wave;
+  if (r >= rows) return;   // wave-uniform; nothing below synchronises across waves
+  uint4 sh[2][8][2];       // S R^T[row][16 s + m], rows L and L + 64, as float16 pairs
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int sg = 0; sg < 8; ++sg) {
+      const uint4* sp = Sh + (size_t(sg) * 128 + lane + 64 * j) * 2;
+      sh[j][sg][0] = sp[0];
+      sh[j][sg][1] = sp[1];
+    }
+  int64_t dg = 0, dn = 0;
+  const bool ok = page_dest(pm, r, dg, dn);
+  const int din = int(cst->din);
+  float a, b;
+  if constexpr (BF16) {
+    const uint16_t* row = static_cast<const uint16_t*>(keys) + r * din;
+    a = lane < din ? __uint_as_float(uint32_t(row[lane]) << 16) : 0.f;
+    b = lane + 64 < din ? __uint_as_float(uint32_t(row[lane + 64]) << 16) : 0.f;
+  } else {
+    const float* row = static_cast<const float*>(keys) + r * din;
+    a = lane < din ? row[lane] : 0.f;
+    b = lane + 64 < din ? row[lane + 64] : 0.f;
+  }
+  float nu2 = fmaf(a, a, b * b);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) nu2 += __shfl_xor(nu2, o);
+  const float fa = ((cst->dneg[lane >> 5] >> (lane & 31)) & 1u) ? -a : a;
+  const float fb = ((cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -b : b;
+  float u0 = (fa + fb) + 0.0f, u1 = (fa - fb) + 0.0f;
+  u0 = butterfly_lane<1>(u0, lane & 1);   u1 = butterfly_lane<1>(u1, lane & 1);
+  u0 = butterfly_lane<2>(u0, lane & 2);   u1 = butterfly_lane<2>(u1, lane & 2);
+  u0 = butterfly_lane<4>(u0, lane & 4);   u1 = butterfly_lane<4>(u1, lane & 4);
+  u0 = butterfly_lane<8>(u0, lane & 8);   u1 = butterfly_lane<8>(u1, lane & 8);
+  u0 = butterfly_lane<16>(u0, lane & 16); u1 = butterfly_lane<16>(u1, lane & 16);
+  u0 = butterfly_lane32(u0, lane & 32);   u1 = butterfly_lane32(u1, lane & 32);
+
+  const float nu = __builtin_amdgcn_sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * cst->sqrt_d;                                    // u = y nu sqrt(d)
+  const float gsc = zero ? 0.f : kResidualScale * __builtin_amdgcn_rcpf(nsd);   // u -> 2^12 y
+  uint64_t neg[2], below[2][K > 1 ? K - 1 : 1];
+  float rho2 = 0.f;
+  float* sr = reinterpret_cast<float*>(s_r[wave]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float u = h ? u1 : u0, au = fabsf(u);
+    neg[h] = __builtin_amdgcn_ballot_w64(u < 0.f);
+    float mag = cst->cpos_s[0];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+      const bool bl = au < cst->tpos[k] * nsd;
+      below[h][k] = __builtin_amdgcn_ballot_w64(bl);
+      mag = bl ? mag : cst->cpos_s[k + 1];
+    }
+    const float e = zero ? 0.f : fmaf(u, gsc, -copysignf(mag, u));    // 2^12 (y - c[code])
+    rho2 = fmaf(e, e, rho2);
+    sr[lane + 64 * h] = e;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) rho2 += __shfl_xor(rho2, o);
+  const float rho = zero ? 0.f : __builtin_amdgcn_sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+  // p_j = (S R^T)_j . r_rot for rows j = L and L + 64 (sign only: any positive scale)
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int sg = 0; sg < 8; ++sg) {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const f32x4 rv = s_r[wave][4 * sg + c4];   // coordinates 16 sg + 4 c4 .. + 3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * c4 + i;
+        const uint4 w0 = sh[0][sg][m >> 3], w1 = sh[1][sg][m >> 3];
+        const uint32_t x0 = (m & 7) < 2 ? w0.x : (m & 7) < 4 ? w0.y : (m & 7) < 6 ? w0.z : w0.w;
+        const uint32_t x1 = (m & 7) < 2 ? w1.x : (m & 7) < 4 ? w1.y : (m & 7) < 6 ? w1.z : w1.w;
+        p0 = fmaf(h2f_bits(x0 >> (16 * (m & 1))), rv[i], p0);
+        p1 = fmaf(h2f_bits(x1 >> (16 * (m & 1))), rv[i], p1);
+      }
+    }
+  }
+  const uint64_t sg0 = __builtin_amdgcn_ballot_w64(p0 < 0.f), sg1 = __builtin_amdgcn_ballot_w64(p1 < 0.f);
+  if (!ok) return;
+  const bool keep = !zero, keep_s = keep && rho2 > 0.f;
+  // plane p: ~neg is the top code bit; lower bits XOR the "below" masks (as the tile encoders)
+  uint64_t pw[2][P - 1];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (B == 1) {
+      pw[h][0] = ~neg[h];
+    } else if constexpr (B == 2) {
+      pw[h][1] = ~neg[h];
+      pw[h][0] = ~(neg[h] ^ below[h][0]);
+    } else {
+      pw[h][2] = ~neg[h];
+      pw[h][1] = ~(neg[h] ^ below[h][1]);
+      pw[h][0] = ~(neg[h] ^ below[h][0] ^ below[h][1] ^ below[h][2]);
+    }
+  }
+  uint4* rec = reinterpret_cast<uint4*>(planes) + dg * P * int64_t(pm.page_size) + dn;
+  if (lane < P - 1) {
+    uint64_t lo = pw[0][0], hi = pw[1][0];
+#pragma unroll
+    for (int p = 1; p < P - 1; ++p)
+      if (lane == p) { lo = pw[0][p]; hi = pw[1][p]; }
+    rec[int64_t(lane) * pm.page_size] = keep ? make_uint4(uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi),
+                                                          uint32_t(hi >> 32))
+                                             : make_uint4(0u, 0u, 0u, 0u);
+  } else if (lane == P - 1) {
+    rec[int64_t(P - 1) * pm.page_size] =
+        keep_s ? make_uint4(uint32_t(sg0), uint32_t(sg0 >> 32), uint32_t(sg1), uint32_t(sg1 >> 32))
+               : make_uint4(0u, 0u, 0u, 0u);
+  } else if (lane == P) {
+    norms[dg * int64_t(pm.page_size) + dn] =
+        keep ? (uint32_t(f2h_bits(nu)) | (uint32_t(f2h_bits(rho)) << 16)) : 0u;
+  }
+}
+
 // ============================================================== decode, d = 128
 // One wave per key (grid-stride over keys): lane L reconstructs coordinates
 // L and L + 64 of nu~ D H c[code] / sqrt(d)  (= nu~ R^T c[code]).
@@ -2059,6 +2197,9 @@ hipError_t launch_score_stream_probe(const Codebook& cb, int64_t G, int Qg, cons
 // Paged cache: appends as one [1][G*T] batch of rows whose destinations come
 // from the page map (so a 16-key tile packs rows of 16 groups when T = 1);
 // scoring with the page map and per-group lengths.
+// Appends of at most this many rows take the one-key-per-wave kernel.
+constexpr int64_t kAppendRowsMax = 2048;
+
 hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
                                void* pool, int64_t num_pages, int page_size, const int32_t* table,
                                int ppg, const int32_t* pos, hipStream_t s) {
@@ -2066,6 +2207,18 @@ hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, 
   uint32_t* planes = static_cast<uint32_t*>(pool);
   uint32_t* norms = planes + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
   const PageMap pm{table, pos, nullptr, uint32_t(T), ppg, page_size, int32_t(num_pages)};
+  if (rows <= kAppendRowsMax) {   // latency path: one key per wave
+    const int grid = int((rows + kAppendThreads / 64 - 1) / (kAppendThreads / 64));
+    const bool bf = dtype == 1;
+#define TQ_APP(BB)                                                                                     if (bf) hipLaunchKernelGGL((append_rows128_kernel<BB, true>), dim3(grid), dim3(kAppendThreads), 0, s,                              keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm);                      else hipLaunchKernelGGL((append_rows128_kernel<BB, false>), dim3(grid), dim3(kAppendThreads), 0, s,                             keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm)
+    switch (cb.bits - 1) {
+      case 1: TQ_APP(1); break;
+      case 2: TQ_APP(2); break;
+      default: TQ_APP(3); break;
+    }
+#undef TQ_APP
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     const int64_t want = ((rows + 15) / 16 + kEnc16Waves - 1) / kEnc16Waves;
     const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * (cb.bits == 4 ? 2 : 3)));

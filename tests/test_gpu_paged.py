@@ -119,6 +119,34 @@ def test_paged_append_and_score(bits, dt, ps):
                      np.linalg.norm(keys[g:g + 1, :L].astype(np.float64), axis=-1))
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_paged_bulk_rows_take_the_tile_encoder(dt):
+    """A bulk append of more rows than the one-key-per-wave path takes (2048)
+    goes through the tile encoder in its paged form: records equal the
+    oracle's and the tile encoder's own records from tq_encode_keys."""
+    rng = np.random.default_rng(31 + (1 if dt == "bf16" else 0))
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    bits, ps, G, ppg, T = 3, 64, 8, 6, 300
+    num_pages = G * ppg
+    table = rng.permutation(num_pages).reshape(G, ppg).astype(np.int32)
+    cb = K.Codebook(D, bits)
+    cbo = O.make_codebook(D, bits, D, 42)
+    keys = _exact(_rows(rng, G, T), dtype)
+    pool = torch.full((K.paged_pool_nbytes(cb, num_pages, ps),), SENTINEL, dtype=torch.uint8, device="cuda")
+    print(f"[case] paged bulk dt={dt}", flush=True)
+    K.paged_append_keys(cb, _dev(keys, dtype), pool, ps, _i32(table), _i32(np.full(G, 5, np.int32)))
+    flat = K.encode_keys(cb, _dev(keys, dtype))
+    torch.cuda.synchronize()
+    buf = pool.cpu().numpy()
+    fc, fs, fn, fr = O.unpack(cbo, flat.cpu().numpy(), G, T)
+    for g in range(G):
+        c, s_, nu, rho = _gather(cbo, buf, num_pages, ps, table, g, np.arange(5, 5 + T))
+        assert np.array_equal(c, fc[g]) and np.array_equal(s_, fs[g])
+        assert np.array_equal(nu.view(np.uint16), fn[g].view(np.uint16))
+        assert np.array_equal(rho.view(np.uint16), fr[g].view(np.uint16))
+        check_encode(cbo, keys[g], c, s_, nu, rho)
+
+
 def test_paged_ring_wraps_and_scores_the_window():
     """Each group owns R pages; logical page p lives in physical page
     ring[g][p % R], so positions past R pages overwrite the oldest.  After three
