@@ -1069,15 +1069,196 @@ __device__ __forceinline__ float butterfly_lane32(float y, bool up) {
   return up ? r0 - r1 : r0 + r1;   // lanes < 32: (own, partner); lanes >= 32: (partner, own)
 }
 
+// Decode attention fused into the scorer (BV > 0 below): value records of the
+// same keys, the softmax scale and the per-range partial states.
+struct AttnArgs {
+  const uint4* vplanes;    // value planes [G][BV][N] (16 bytes per key and plane)
+  const uint16_t* vnorms;  // value half norms [G][N]
+  float* part;             // per (group, query chunk, range): m[4], Z[4], A[4][128]
+  float scale;
+};
+constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, query chunk, range)
+
+// LDS of the value phase, over the scorer's LDS once its tables are dead.
+struct AttnLds {
+  f32x4 lut[4096];            // levels of a coordinate quad by its plane nibbles (BV <= 3), or of a
+                              // coordinate pair by its plane bit pairs (BV = 4, float2 entries)
+  f32x4 w[16][64];            // per wave: weights of the tile's keys, four queries
+  uint4 pl[16][4][64];        // per wave: value plane words of the tile's keys
+  float m[16][4], z[16][4];   // per wave: logit maxima, normaliser parts
+  float M[4];                 // range maximum of scale * logit per query
+};
+static_assert(sizeof(AttnLds) <= sizeof(ScoreLds), "the value phase reuses the scorer's LDS");
+
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Value phase of the fused decode attention, after the range's logits of
+// queries qc*4 .. qc*4+3 are in `logits` (written by this wave for its own
+// tiles) and lmax holds this lane's largest logit per query.  The range's
+// maximum M is exact, so weights exp(scale l - M) need no rescaling.  Per
+// tile, each lane (= key) stages its weights (times the value's half norm)
+// and value plane words in the wave's LDS slot; then lane (h, cq) adds, for
+// the 32 keys of half h, weight x level of its coordinate quad cq (coordinates
+// 4 cq .. 4 cq + 3) for the four queries, the four levels coming from one
+// lookup indexed by the quad's nibble of every plane.  v_mse = nu~ R^T c_v,
+// so the sums stay in the rotated domain; the range's state goes to `part`
+// and attn_combine128_kernel rotates back.
+template <int BV>
+__device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lmax)[4], const AttnArgs& aa,
+                                                 const DevConsts* __restrict__ cst, const float* logits,
+                                                 int64_t g, int qc, int Qg, int64_t N, int64_t n1,
+                                                 int64_t first, int64_t ntiles, int64_t stride) {
+  AttnLds& sm = *reinterpret_cast<AttnLds*>(lds_raw);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const float m = wave_max64(lmax[qq]);
+    if (lane == 0) sm.m[wave][qq] = m;
+  }
+  __syncthreads();   // every wave is past its tables and its logit stores
+  if (tid < 4) {
+    float m = sm.m[0][tid];
+    for (int w = 1; w < 16; ++w) m = fmaxf(m, sm.m[w][tid]);
+    sm.M[tid] = qc * 4 + tid < Qg ? aa.scale * m : 0.f;
+  }
+  // level table
+  if constexpr (BV <= 3) {
+    constexpr int NE = 1 << (4 * BV);
+    for (int e = tid; e < NE; e += kScoreThreads) {
+      f32x4 v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        int code = 0;
+#pragma unroll
+        for (int p = 0; p < BV; ++p) code |= ((e >> (4 * p + c)) & 1) << p;
+        v[c] = cst->vlevels[code];
+      }
+      sm.lut[e] = v;
+    }
+  } else {
+    float2* lut2 = reinterpret_cast<float2*>(sm.lut);
+    for (int e = tid; e < 256; e += kScoreThreads) {
+      int ca = 0, cb = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        ca |= ((e >> (2 * p)) & 1) << p;
+        cb |= ((e >> (2 * p + 1)) & 1) << p;
+      }
+      lut2[e] = make_float2(cst->vlevels[ca], cst->vlevels[cb]);
+    }
+  }
+  __syncthreads();
+  float M[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) M[qq] = sm.M[qq];
+  const float* lrow[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
+  const uint4* vp = aa.vplanes + g * BV * N;
+  const uint16_t* vn = aa.vnorms + g * N;
+  const int h = lane >> 5, cq = lane & 31, wsel = cq >> 3, sh = 4 * (cq & 7);
+  float acc[4][4] = {};   // [coordinate of the quad][query]
+  float zp[4] = {0.f, 0.f, 0.f, 0.f};
+  const char* plb = reinterpret_cast<const char*>(sm.pl[wave]);
+  for (int64_t t = 0; t < ntiles; ++t) {
+    const int64_t b = first + t * stride;
+    const bool valid = b + lane < n1;
+    const int64_t n = valid ? b + lane : n1 - 1;
+    f32x4 wv;
+    const float nv = h2f_bits(vn[n]);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const float e = (valid && qc * 4 + qq < Qg) ? __expf(fmaf(aa.scale, lrow[qq][n], -M[qq])) : 0.f;
+      zp[qq] += e;
+      wv[qq] = e * nv;
+    }
+    sm.w[wave][lane] = wv;
+#pragma unroll
+    for (int p = 0; p < BV; ++p) sm.pl[wave][p][lane] = vp[p * N + n];
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int slot = 32 * h + k;
+      const f32x4 w = sm.w[wave][slot];
+      uint32_t x[BV];
+#pragma unroll
+      for (int p = 0; p < BV; ++p)
+        x[p] = *reinterpret_cast<const uint32_t*>(plb + (p * 64 + slot) * 16 + 4 * wsel);
+      float lv[4];
+      if constexpr (BV <= 3) {
+        uint32_t idx = __builtin_amdgcn_ubfe(x[0], sh, 4);
+#pragma unroll
+        for (int p = 1; p < BV; ++p) idx |= __builtin_amdgcn_ubfe(x[p], sh, 4) << (4 * p);
+        const f32x4 l4 = sm.lut[idx];
+        lv[0] = l4[0]; lv[1] = l4[1]; lv[2] = l4[2]; lv[3] = l4[3];
+      } else {
+        uint32_t i0 = 0, i1 = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          i0 |= __builtin_amdgcn_ubfe(x[p], sh, 2) << (2 * p);
+          i1 |= __builtin_amdgcn_ubfe(x[p], sh + 2, 2) << (2 * p);
+        }
+        const float2* lut2 = reinterpret_cast<const float2*>(sm.lut);
+        const float2 a = lut2[i0], c = lut2[i1];
+        lv[0] = a.x; lv[1] = a.y; lv[2] = c.x; lv[3] = c.y;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) acc[c][qq] = fmaf(w[qq], lv[c], acc[c][qq]);
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const float z = wave_sum64(zp[qq]);
+    if (lane == 0) sm.z[wave][qq] = z;
+  }
+  __syncthreads();   // every wave is done with the level table and its staging slot
+  float* red = reinterpret_cast<float*>(sm.pl);   // [wave][lane][16]: 64 KB
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) red[(wave * 64 + lane) * 16 + 4 * c + qq] = acc[c][qq];
+  __syncthreads();
+  float* out = aa.part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
+  if (tid < 512) {
+    const int qq = tid >> 7, i = tid & 127, quad = i >> 2, c = i & 3;
+    float a = 0.f;
+#pragma unroll 4
+    for (int w = 0; w < 16; ++w)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) a += red[(w * 64 + 32 * hh + quad) * 16 + 4 * c + qq];
+    out[8 + qq * 128 + i] = a;
+  } else if (tid < 516) {
+    const int qq = tid - 512;
+    float z = 0.f;
+    for (int w = 0; w < 16; ++w) z += sm.z[w][qq];
+    out[qq] = sm.M[qq];
+    out[4 + qq] = z;
+  }
+}
+
 // PAGED: records of group g live in the pool pages of the page map
 // (planes/norms are the pool's), group g has lens[g] of them (at most
 // ppg * page_size), and N is the logit row length; each 64-key tile lies in
 // one page.
-template <int B, bool QBF16, bool PAGED = false>
+// BV > 0: decode attention over value records of BV bits (see
+// attn_value_phase): logits go to `logits` through the caches and the
+// range's partial state to aa.part.
+template <int B, bool QBF16, bool PAGED = false, int BV = 0>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
     int64_t N, int64_t Ncap, int Qg, int64_t chunk, float* __restrict__ logits,
-    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh, PageMap pm) {
+    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh, PageMap pm, AttnArgs aa) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
   constexpr int D = 2;   // key tiles in flight per wave (two measured 2-3% faster than three at b = 3)
@@ -1306,6 +1487,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     }
   };
 
+  float lmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // BV > 0: largest logit per query
   auto score_tile = [&](const uint4 (&wt)[P], uint32_t nrm, int64_t b, bool ok) {
     uint32_t rw[NW][4];
 #pragma unroll
@@ -1341,9 +1523,16 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
               asum * sr[qq];
       }
       const int qh = qc * 4 + qq;
-      if (in_range && qh < Qg)   // streamed output: no reuse, written past the caches
-        __builtin_nontemporal_store(fmaf(nu, mse, rs * (ss[qq] - acc[B][qq])),
-                                    reinterpret_cast<float*>(reinterpret_cast<char*>(lrow[qq]) + off4));
+      const float v = fmaf(nu, mse, rs * (ss[qq] - acc[B][qq]));
+      float* dst = reinterpret_cast<float*>(reinterpret_cast<char*>(lrow[qq]) + off4);
+      if (in_range && qh < Qg) {
+        if constexpr (BV > 0) {   // read back by the value phase: kept in the caches
+          *dst = v;
+          lmax[qq] = fmaxf(lmax[qq], v);
+        } else {                  // streamed output: no reuse, written past the caches
+          __builtin_nontemporal_store(v, dst);
+        }
+      }
     }
   };
 
@@ -1359,6 +1548,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   }
   // the refills past the range are never used: let them land before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (BV > 0)
+    attn_value_phase<BV>(&sm, lmax, aa, cst, logits, g, qc, Qg, N, n1, first, ntiles, kStride);
 }
 
 // ============================================================== append, few rows, d = 128
@@ -1607,149 +1798,9 @@ __global__ __launch_bounds__(256) void dense128_kernel(const uint16_t* __restric
 // values v_mse = nu~ R^T c_v[code] (value records: b-bit Lloyd-Max codes and
 // a half norm).  R^T is linear, so the weighted sum is formed in the rotated
 // domain, A = sum_n w_n nu~_n c_v[code_n], and rotated back once per query.
-// Split over key ranges (flash-decoding style): each range keeps its own
-// maximum m_s, normaliser Z_s = sum exp(scale l - m_s) and A_s; a combine step
-// rescales by exp(m_s - M).
-constexpr int kAttnThreads = 256;
-constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, query chunk, range)
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Grid (G, query chunks of 4, key ranges).  Thread t: while weighting, key
-// t % 64 of a 64-key block for query t / 64; while accumulating, the four
-// adjacent coordinates 4 (t % 32) .. 4 (t % 32) + 3 of every eighth key of the
-// block, starting at key t / 32.  A 2^(2 BV)-entry table maps the BV plane
-// bits of two adjacent coordinates to their two levels, so each pair costs one
-// 8-byte LDS read after BV two-bit field extractions.
-template <int BV>
-__global__ __launch_bounds__(kAttnThreads) void attn_values128_kernel(
-    const float* __restrict__ logits, const uint4* __restrict__ vplanes,
-    const uint16_t* __restrict__ vnorms, int64_t N, int Qg, int64_t chunk, float scale,
-    const DevConsts* __restrict__ cst, float* __restrict__ part) {
-  constexpr int NL = 1 << (2 * BV);
-  __shared__ f32x4 s_w[2][64];              // weights of a block's keys, 4 queries (double-buffered)
-  __shared__ uint32_t s_pl[2][BV][64][4];   // value plane words of a block's keys
-  __shared__ float2 s_lut[NL];              // pair of levels by plane-major 2-bit fields
-  __shared__ float s_red[8][32][17];        // [key lane][coordinate quad][4 coords x 4 queries]
-  __shared__ float s_m[2][4];
-  __shared__ float s_f[2][4];               // rescale of the accumulators per block and query
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t g = blockIdx.x;
-  const int qc = blockIdx.y;
-  const int64_t n0 = int64_t(blockIdx.z) * chunk;
-  const int64_t n1 = std::min<int64_t>(N, n0 + chunk);
-  for (int j = tid; j < NL; j += kAttnThreads) {
-    int ca = 0, cb = 0;
-#pragma unroll
-    for (int p = 0; p < BV; ++p) {
-      ca |= ((j >> (2 * p)) & 1) << p;
-      cb |= ((j >> (2 * p + 1)) & 1) << p;
-    }
-    s_lut[j] = make_float2(cst->vlevels[ca], cst->vlevels[cb]);
-  }
-
-  // Online softmax: wave q keeps query q's running maximum mx (the same in
-  // every lane) and normaliser; when a block raises the maximum, every
-  // accumulator of that query is rescaled by exp(old - new) before the block
-  // is added.
-  const int qh = qc * 4 + wave;
-  const bool qlive = qh < Qg;
-  const float* lrow = logits + (g * Qg + (qlive ? qh : 0)) * N;
-  float mx = -INFINITY;
-  float zs = 0.f;                    // this thread's part of Z for query `wave`
-  float acc[4][4] = {};              // [coordinate][query]
-  const int cq = tid & 31, kq = tid >> 5;
-  const int wsel = cq >> 3, sh = 4 * (cq & 7);   // word and bit of the coordinate quad
-  const char* lut = reinterpret_cast<const char*>(s_lut);
-  // the next block's logit, norm and plane words are loaded into registers
-  // while the current block is accumulated (one barrier per block: a buffer
-  // is rewritten only after every thread has passed the next barrier)
-  float lg_n = 0.f;
-  uint32_t nv_n = 0;
-  uint4 pl_n = make_uint4(0, 0, 0, 0);
-  auto load_block = [&](int64_t nb) {
-    const int64_t nc = std::min<int64_t>(nb + lane, n1 - 1);
-    lg_n = lrow[nc];
-    nv_n = vnorms[g * N + nc];
-    if (wave < BV) pl_n = vplanes[(g * BV + wave) * N + nc];
-  };
-  load_block(n0);
-  int buf = 0;
-  for (int64_t nb = n0; nb < n1; nb += 64, buf ^= 1) {
-    {
-      const bool in = nb + lane < n1 && qlive;
-      const float z = scale * lg_n;
-      const float mnew = fmaxf(mx, wave_max(in ? z : -INFINITY));
-      const float f = qlive ? __expf(mx - mnew) : 1.f;     // exp(-inf) = 0 on the first block
-      mx = qlive ? mnew : 0.f;
-      float w = 0.f;
-      zs *= f;
-      if (in) {
-        const float e = __expf(z - mx);
-        zs += e;
-        w = e * h2f_bits(nv_n);
-      }
-      reinterpret_cast<float*>(&s_w[buf][lane])[wave] = w;
-      if (lane == 0) s_f[buf][wave] = f;
-      if (wave < BV) *reinterpret_cast<uint4*>(s_pl[buf][wave][lane]) = pl_n;
-    }
-    __syncthreads();
-    {
-      const float f0 = s_f[buf][0], f1 = s_f[buf][1], f2 = s_f[buf][2], f3 = s_f[buf][3];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[c][0] *= f0; acc[c][1] *= f1; acc[c][2] *= f2; acc[c][3] *= f3;
-      }
-    }
-    if (nb + 64 < n1) load_block(nb + 64);
-#pragma unroll 4
-    for (int j = 0; j < 8; ++j) {
-      const int kk = kq + 8 * j;
-      const f32x4 wv = s_w[buf][kk];
-      uint32_t a0 = 0, a1 = 0;   // byte offsets of the two level pairs
-#pragma unroll
-      for (int p = 0; p < BV; ++p) {
-        const uint32_t x = s_pl[buf][p][kk][wsel];
-        a0 |= __builtin_amdgcn_ubfe(x, sh, 2) << (2 * p + 3);
-        a1 |= __builtin_amdgcn_ubfe(x, sh + 2, 2) << (2 * p + 3);
-      }
-      const float2 l01 = *reinterpret_cast<const float2*>(lut + a0);
-      const float2 l23 = *reinterpret_cast<const float2*>(lut + a1);
-      const float lv[4] = {l01.x, l01.y, l23.x, l23.y};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[c][q] = fmaf(wv[q], lv[c], acc[c][q]);
-    }
-  }
-
-  // ---- reduce over the eight key lanes, write the range's partial state
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s_red[kq][cq][4 * c + q] = acc[c][q];
-  zs = wave_sum(zs);
-  if (lane == 0) { s_m[0][wave] = mx; s_m[1][wave] = zs; }
-  __syncthreads();
-  float* out = part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
-  if (tid < 8) out[tid] = s_m[tid >> 2][tid & 3];
-  for (int e = tid; e < 512; e += kAttnThreads) {
-    const int q = e >> 7, i = e & 127, quad = i >> 2, c = i & 3;
-    float a = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) a += s_red[k][quad][4 * c + q];
-    out[8 + e] = a;                 // A[q][i]
-  }
-}
+// The scorer (score128_kernel with BV > 0) computes each key range's logits,
+// maximum m, normaliser Z = sum exp(scale l - m) and A; the combine below
+// merges the ranges (flash-decoding rescale by exp(m_s - M)).
 
 // One wave per (group, query): merge the ranges, divide by Z, rotate back
 // with R^T = D H / sqrt(d).  Lane L holds coordinates L and L + 64.
@@ -2028,56 +2079,6 @@ hipError_t scratch_address(void** ptr) {
   return hipSuccess;
 }
 
-// Key ranges of the decode-attention value pass: multiples of 64 keys,
-// enough (group, query chunk, range) workgroups for four per compute unit.
-static void attn_split(int64_t G, int Qg, int64_t N, int64_t& chunk, int64_t& splits) {
-  const int64_t units = G * ((Qg + 3) / 4);
-  const int64_t want_wg = int64_t(num_cus()) * 4;
-  int64_t want = std::max<int64_t>(1, (want_wg + units - 1) / units);
-  want = std::min<int64_t>(want, std::max<int64_t>(1, (N + 255) / 256));
-  chunk = ((N + want - 1) / want + 63) / 64 * 64;
-  splits = (N + chunk - 1) / chunk;
-}
-
-size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N) {
-  (void)cb;
-  int64_t chunk, splits;
-  attn_split(G, Qg, N, chunk, splits);
-  const size_t lg = (size_t(G) * Qg * N * 4 + 255) / 256 * 256;
-  return lg + size_t(G) * ((Qg + 3) / 4) * splits * kAttnPart * 4;
-}
-
-hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
-                            const void* kpacked, const void* vpacked, int64_t N, float scale,
-                            float* out, void* ws, hipStream_t s) {
-  int64_t chunk, splits;
-  attn_split(G, Qg, N, chunk, splits);
-  float* logits = static_cast<float*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                         (size_t(G) * Qg * N * 4 + 255) / 256 * 256);
-  hipError_t e = launch_score(cb, q, qdtype, G, Qg, kpacked, N, N, logits, nullptr, s);
-  if (e != hipSuccess) return e;
-  const int nqc = (Qg + 3) / 4;
-  const uint4* vpl = static_cast<const uint4*>(vpacked);
-  const uint16_t* vn = reinterpret_cast<const uint16_t*>(static_cast<const uint32_t*>(vpacked) +
-                                                         G * N * int64_t(cb.bits) * (cb.d / 32));
-  const dim3 grid{unsigned(G), unsigned(nqc), unsigned(splits)};
-#define TQ_AV(BB)                                                                                 \
-  hipLaunchKernelGGL((attn_values128_kernel<BB>), grid, dim3(kAttnThreads), 0, s, logits, vpl, vn, \
-                     N, Qg, chunk, scale, cb.d_consts, part)
-  switch (cb.bits) {
-    case 2: TQ_AV(2); break;
-    case 3: TQ_AV(3); break;
-    default: TQ_AV(4); break;
-  }
-#undef TQ_AV
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine128_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, part, Qg, nqc,
-                     int(splits), cb.d_consts, out);
-  return hipGetLastError();
-}
-
 // Grid of the d = 128 scorer: (group, chunk of 4 queries, key range), with
 // enough workgroups for every CU: each (group, query chunk) unit's keys are
 // split into ranges of at least 512 keys, a multiple of 64 each.
@@ -2105,13 +2106,56 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const bool bf = qdtype == 1;
 #define TQ_SC(BB, QB)                                                                   \
   hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{})
+                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, AttnArgs{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
     default: if (bf) TQ_SC(3, true); else TQ_SC(3, false); break;
   }
 #undef TQ_SC
+  return hipGetLastError();
+}
+
+size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t N) {
+  (void)cb;
+  int64_t chunk = 0;
+  const dim3 grid = score_grid(G, Qg, N, chunk);
+  const size_t lg = (size_t(G) * Qg * N * 4 + 255) / 256 * 256;
+  return lg + size_t(grid.x) * grid.y * grid.z * kAttnPart * 4;
+}
+
+// Decode attention: the scorer with the value phase (one launch over the
+// scorer's grid; logits pass through the caches in the workspace, each key
+// range leaves its partial state), then the combine of the ranges.
+hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                            const void* kpacked, const void* vpacked, int64_t N, float scale,
+                            float* out, void* ws, hipStream_t s) {
+  int64_t chunk = 0;
+  const dim3 grid = score_grid(G, Qg, N, chunk);
+  float* logits = static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         (size_t(G) * Qg * N * 4 + 255) / 256 * 256);
+  const uint4* planes = static_cast<const uint4*>(kpacked);
+  const uint32_t* norms =
+      static_cast<const uint32_t*>(kpacked) + G * N * int64_t(cb.bits) * (cb.d / 32);
+  const uint4* vpl = static_cast<const uint4*>(vpacked);
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(static_cast<const uint32_t*>(vpacked) +
+                                                         G * N * int64_t(cb.bits) * (cb.d / 32));
+  const AttnArgs aa{vpl, vn, part, scale};
+  const bool bf = qdtype == 1;
+#define TQ_AT(BB, QB, BVV)                                                                       \
+  hipLaunchKernelGGL((score128_kernel<BB, QB, false, BVV>), grid, dim3(kScoreThreads), 0, s, q, planes, \
+                     norms, N, N, Qg, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, aa)
+  switch (cb.bits) {
+    case 2: if (bf) TQ_AT(1, true, 2); else TQ_AT(1, false, 2); break;
+    case 3: if (bf) TQ_AT(2, true, 3); else TQ_AT(2, false, 3); break;
+    default: if (bf) TQ_AT(3, true, 4); else TQ_AT(3, false, 4); break;
+  }
+#undef TQ_AT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine128_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, part, Qg,
+                     int(grid.y), int(grid.z), cb.d_consts, out);
   return hipGetLastError();
 }
 
@@ -2263,7 +2307,7 @@ hipError_t launch_score_paged(const Codebook& cb, const void* q, int qdtype, int
   const bool bf = qdtype == 1;
 #define TQ_SCP(BB, QB)                                                                          \
   hipLaunchKernelGGL((score128_kernel<BB, QB, true>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, Lmax, int64_t(page_size), Qg, chunk, logits, cb.d_consts, cb.d_Sh, pm)
+                     norms, Lmax, int64_t(page_size), Qg, chunk, logits, cb.d_consts, cb.d_Sh, pm, AttnArgs{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SCP(1, true); else TQ_SCP(1, false); break;
     case 2: if (bf) TQ_SCP(2, true); else TQ_SCP(2, false); break;
