@@ -37,8 +37,8 @@
  * N(0, 1/D), and records are D-dimensional.  Keys, values and queries are
  * passed as rows of d elements and decoded vectors come back as rows of d
  * elements; the kernels read the missing coordinates as zeros.  Where a call
- * below is limited to "d = 128" or "d = 1024", that names D: a zero-padded
- * codebook follows the rules of its D.
+ * below is limited to some d (128, 1024, 2048, 4096), that names D: a
+ * zero-padded codebook follows the rules of its D.
  *
  * Status: every entry point returns TQ_OK (0) or a negative TQ_ERR_* code.
  * No C++ exception crosses this boundary.  Launches are asynchronous on the
@@ -81,9 +81,10 @@ enum { TQ_CODEBOOK_GAUSSIAN = 0, TQ_CODEBOOK_BETA = 1 };
 typedef struct tq_codebook tq_codebook;
 
 /* The power of two D the method runs in for vectors of d elements: d when d
- * is a power of two in [32, 1024]; otherwise the next power of two >= 32
- * when d is a multiple of 16 below 1024 (zero padding, see above); 0 when d
- * is unsupported.  Pure host function. */
+ * is a power of two in [32, 4096]; otherwise the next power of two >= 32
+ * when d is a multiple of 16 below 4096 (zero padding, see above); 0 when d
+ * is unsupported.  Pure host function.  (The host tables exist for every such
+ * D; the device kernels for D in {128, 1024, 2048, 4096}.) */
 int32_t tq_rotation_dim(int32_t d);
 
 /*
@@ -125,9 +126,10 @@ int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int
  * cores, Walsh coefficients of the levels for the scorer).  The handle owns
  * its device memory (hipMalloc) and is immutable afterwards, so it may be
  * shared by streams and threads; it is valid on the device that was current
- * here.  Supported: tq_rotation_dim(d) in {128, 1024}, i.e. d = 128 or 1024,
- * or d in {80, 96, 112} or a multiple of 16 in [528, 1008] (zero-padded),
- * bits in {2, 3, 4}, m == tq_rotation_dim(d).
+ * here.  Supported: tq_rotation_dim(d) in {128, 1024, 2048, 4096}, i.e.
+ * d = 128, 1024, 2048 or 4096, or a zero-padded d: 80, 96, 112, or a multiple
+ * of 16 in [528, 1008], [1040, 2032] or [2064, 4080]; bits in {2, 3, 4};
+ * m == tq_rotation_dim(d).
  * Errors: TQ_ERR_ARG (out NULL), TQ_ERR_UNSUPPORTED, TQ_ERR_ALLOC, TQ_ERR_HIP.
  */
 int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out);
@@ -173,9 +175,10 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
  * zero vectors and "0 counts as positive" [ICLR 2026 paper digest,
  * "実装の擬似コード"].
  * keys and packed are device pointers owned by the caller; G*N == 0 is a
- * no-op.  d = 1024 runs in chunks of 65,536 keys through a temporary of
- * 256 MiB taken from the device's stream-ordered pool (hipMallocAsync /
- * hipFreeAsync on the given stream); d = 128 allocates nothing.
+ * no-op.  d = 1024 runs in chunks of 65,536 keys, d = 2048 and 4096 in
+ * chunks of 2^26 / d keys, each through a float32 temporary of 256 MiB taken
+ * from the device's stream-ordered pool (hipMallocAsync / hipFreeAsync on
+ * the given stream); d = 128 allocates nothing.
  * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP (also when that
  * temporary cannot be allocated).
  */
@@ -309,8 +312,8 @@ size_t tq_attention_noalloc_max_bytes(void);
 
 /* Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
  * d = 128 (each workgroup prepares its queries on chip; ws may be NULL);
- * G*Qg*(2*1024 + 4)*4 for d = 1024 (the prepared queries 2 R q, 2 S q and
- * their sums). */
+ * G*Qg*(2*d + 4)*4 for d = 1024, 2048 and 4096 (the prepared queries 2 R q,
+ * 2 S q and their sums). */
 size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
 
 /*
@@ -322,8 +325,10 @@ size_t tq_score_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg);
  * (R q via a Hadamard butterfly, S q, their sums) and then streams the packed
  * keys of its range.  All buffers are caller-owned device memory; ws must hold
  * tq_score_workspace_bytes(cb, G, Qg) bytes (may be NULL when that is 0).
- * G*N*Qg == 0 is a no-op.  d = 1024 runs a query-preparation kernel into ws
- * first, then scores with nibble subset-sum tables (same estimator).
+ * G*N*Qg == 0 is a no-op.  d = 1024, 2048 and 4096 run a query-preparation
+ * kernel into ws first, then score with nibble subset-sum tables (same
+ * estimator; at 2048 and 4096 in 1024-coordinate slices whose partial logits
+ * accumulate in the logits array).
  * Errors: TQ_ERR_ARG, TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (Qg > 256, G > 2^31 - 1,
  * or N >= 2^28 at d = 128: records and logits of a group are addressed with
  * 32-bit byte offsets), TQ_ERR_HIP.
@@ -372,7 +377,7 @@ int tq_score_topk(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t
  * stored norm [ICLR 2026 paper digest, "Step 1: PolarQuant" (R orthogonal,
  * norm kept on the side); Qiita explainer, API table (MSE-only compressor,
  * "TurboQuantMSE")].  Computed in float32, rounded to nearest even for
- * TQ_BF16.  d = 128 and d = 1024 (and the zero-padded d of those D).
+ * TQ_BF16.  d = 128, 1024, 2048 and 4096 (and the zero-padded d of those D).
  * G*N == 0 is a no-op; nothing is allocated.
  * Errors: TQ_ERR_ARG (null/misaligned pointer, negative size, bad dtype,
  * codebook made on another device), TQ_ERR_UNSUPPORTED (a rotation dimension

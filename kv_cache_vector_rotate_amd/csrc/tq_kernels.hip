@@ -1081,14 +1081,17 @@ constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, qu
 
 // LDS of the value phase, over the scorer's LDS once its tables are dead.
 struct AttnLds {
-  f32x4 lut[4096];            // levels of a coordinate quad by its plane nibbles (BV <= 3), or of a
-                              // coordinate pair by its plane bit pairs (BV = 4, float2 entries)
+  float2 lut[256];            // levels of a coordinate pair by its interleaved plane bit pairs
   f32x4 w[16][64];            // per wave: weights of the tile's keys, four queries
   uint4 pl[16][4][64];        // per wave: value plane words of the tile's keys
   float m[16][4], z[16][4];   // per wave: logit maxima, normaliser parts
   float M[4];                 // range maximum of scale * logit per query
 };
 static_assert(sizeof(AttnLds) <= sizeof(ScoreLds), "the value phase reuses the scorer's LDS");
+// the per-wave normaliser parts are written while other waves still read the
+// level table and their own staging slots
+static_assert(offsetof(AttnLds, z) >= offsetof(AttnLds, pl) + sizeof(AttnLds::pl),
+              "z lies past every array read in the value loop");
 
 __device__ __forceinline__ float wave_max64(float v) {
 #pragma unroll
@@ -1108,8 +1111,11 @@ __device__ __forceinline__ float wave_sum64(float v) {
 // tile, each lane (= key) stages its weights (times the value's half norm)
 // and value plane words in the wave's LDS slot; then lane (h, cq) adds, for
 // the 32 keys of half h, weight x level of its coordinate quad cq (coordinates
-// 4 cq .. 4 cq + 3) for the four queries, the four levels coming from one
-// lookup indexed by the quad's nibble of every plane.  v_mse = nu~ R^T c_v,
+// 4 cq .. 4 cq + 3) for the four queries, the four levels coming from two
+// lookups, one per coordinate pair, indexed by the pair's bits of every plane
+// (a table of 2^(2 BV) float2 entries; measured 2-5% faster than one lookup
+// per quad, whose 2^(4 BV)-entry table costs more to build and conflicts more
+// in LDS).  v_mse = nu~ R^T c_v,
 // so the sums stay in the rotated domain; the range's state goes to `part`
 // and attn_combine128_kernel rotates back.
 template <int BV>
@@ -1120,37 +1126,30 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   AttnLds& sm = *reinterpret_cast<AttnLds*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float mw[4];
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    const float m = wave_max64(lmax[qq]);
-    if (lane == 0) sm.m[wave][qq] = m;
+  for (int qq = 0; qq < 4; ++qq) mw[qq] = wave_max64(lmax[qq]);
+  // this LDS overlays the scorer's tables: nothing is written before every
+  // wave is past them (and past its logit stores)
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) sm.m[wave][qq] = mw[qq];
   }
-  __syncthreads();   // every wave is past its tables and its logit stores
+  __syncthreads();
   if (tid < 4) {
     float m = sm.m[0][tid];
     for (int w = 1; w < 16; ++w) m = fmaxf(m, sm.m[w][tid]);
     sm.M[tid] = qc * 4 + tid < Qg ? aa.scale * m : 0.f;
   }
-  // level table
-  if constexpr (BV <= 3) {
-    constexpr int NE = 1 << (4 * BV);
-    for (int e = tid; e < NE; e += kScoreThreads) {
-      f32x4 v;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        int code = 0;
-#pragma unroll
-        for (int p = 0; p < BV; ++p) code |= ((e >> (4 * p + c)) & 1) << p;
-        v[c] = cst->vlevels[code];
-      }
-      sm.lut[e] = v;
-    }
-  } else {
-    float2* lut2 = reinterpret_cast<float2*>(sm.lut);
-    for (int e = tid; e < 256; e += kScoreThreads) {
+  // level table of coordinate pairs: entry e holds the levels of the two
+  // codes whose plane bits interleave in e (bit 2p: first code, 2p + 1: second)
+  {
+    float2* lut2 = sm.lut;
+    for (int e = tid; e < (1 << (2 * BV)); e += kScoreThreads) {
       int ca = 0, cb = 0;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int p = 0; p < BV; ++p) {
         ca |= ((e >> (2 * p)) & 1) << p;
         cb |= ((e >> (2 * p + 1)) & 1) << p;
       }
@@ -1193,24 +1192,15 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
 #pragma unroll
       for (int p = 0; p < BV; ++p)
         x[p] = *reinterpret_cast<const uint32_t*>(plb + (p * 64 + slot) * 16 + 4 * wsel);
-      float lv[4];
-      if constexpr (BV <= 3) {
-        uint32_t idx = __builtin_amdgcn_ubfe(x[0], sh, 4);
+      uint32_t i0 = 0, i1 = 0;
 #pragma unroll
-        for (int p = 1; p < BV; ++p) idx |= __builtin_amdgcn_ubfe(x[p], sh, 4) << (4 * p);
-        const f32x4 l4 = sm.lut[idx];
-        lv[0] = l4[0]; lv[1] = l4[1]; lv[2] = l4[2]; lv[3] = l4[3];
-      } else {
-        uint32_t i0 = 0, i1 = 0;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          i0 |= __builtin_amdgcn_ubfe(x[p], sh, 2) << (2 * p);
-          i1 |= __builtin_amdgcn_ubfe(x[p], sh + 2, 2) << (2 * p);
-        }
-        const float2* lut2 = reinterpret_cast<const float2*>(sm.lut);
-        const float2 a = lut2[i0], c = lut2[i1];
-        lv[0] = a.x; lv[1] = a.y; lv[2] = c.x; lv[3] = c.y;
+      for (int p = 0; p < BV; ++p) {
+        i0 |= __builtin_amdgcn_ubfe(x[p], sh, 2) << (2 * p);
+        i1 |= __builtin_amdgcn_ubfe(x[p], sh + 2, 2) << (2 * p);
       }
+      const float2* lut2 = sm.lut;
+      const float2 la = lut2[i0], lc = lut2[i1];
+      const float lv[4] = {la.x, la.y, lc.x, lc.y};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -1257,7 +1247,7 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
 template <int B, bool QBF16, bool PAGED = false, int BV = 0>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
-    int64_t N, int64_t Ncap, int Qg, int64_t chunk, float* __restrict__ logits,
+    int64_t N, int64_t Ncap, int Qg, int din, int64_t chunk, float* __restrict__ logits,
     const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh, PageMap pm, AttnArgs aa) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
@@ -1280,7 +1270,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const uint32_t* ng = norms + g * Ncap;
 
   // ---- loads: sixteen S R^T columns (fp16, exact), the R q input, the
-  // first D key tiles.  S q = (S R^T)(R q): the scorer needs R q anyway, and
+  // first key tile.  S q = (S R^T)(R q): the scorer needs R q anyway, and
   // the fp16 table is half the bytes every workgroup fetches at its start.
   const int seg = wave >> 1;
   const int jrow = 64 * (wave & 1) + lane;
@@ -1290,12 +1280,16 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     sh[0] = sp[0];
     sh[1] = sp[1];
   }
-  // query rows hold din <= 128 elements; coordinates at or past din are zero
-  // padding (the loads are clamped to the row and their values dropped)
-  const int din = int(cst->din);
-  uint32_t u0, u1;   // raw bits of the R q input (converted after the pin below)
-  {
-    const int qr = std::min(qc * 4 + (wave & 3), Qg - 1);
+  // query rows hold din <= 128 elements (an argument: read from the constant
+  // block, it would put an L2 round trip before the query loads); coordinates
+  // at or past din are zero padding (the loads are clamped to the row and
+  // their values dropped)
+  // (waves 0..3 rotate query wave; the others load nothing they would wait for
+  // before the first barrier)
+  uint32_t u0 = 0, u1 = 0;   // raw bits of the R q input
+  uint32_t dn0 = 0, dn1 = 0;
+  if (wave < 4) {
+    const int qr = std::min(qc * 4 + wave, Qg - 1);
     const int64_t at = (g * Qg + qr) * din;
     const int i0 = std::min(lane, din - 1), i1 = std::min(lane + 64, din - 1);
     if constexpr (QBF16) {
@@ -1305,8 +1299,13 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
       u0 = static_cast<const uint32_t*>(q)[at + i0];
       u1 = static_cast<const uint32_t*>(q)[at + i1];
     }
+    dn0 = cst->dneg[lane >> 5];
+    dn1 = cst->dneg[2 + (lane >> 5)];
   }
-  uint32_t dn0 = cst->dneg[lane >> 5], dn1 = cst->dneg[2 + (lane >> 5)];
+  // codebook scalars, read with the setup loads: read where they are used,
+  // after the key tiles, they wait behind the whole chip's tile traffic in L2
+  float isd = cst->inv_sqrt_d, qs = cst->qjl_scale, asum = cst->alpha_sum;
+  float a0 = cst->alpha[0], a1 = cst->alpha[1], a2 = cst->alpha[2], a3 = cst->alpha[3];
   // wave-uniform plane bases + 32-bit lane offsets (key index < 2^28): the
   // loads take the scalar-base form and need no 64-bit address arithmetic
   auto load_tile = [&](int64_t b, uint4 (&wv)[P], uint32_t& nv, bool& ok) {
@@ -1340,16 +1339,24 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   uint4 w[D][P];
   uint32_t nr[D];
   bool okt[D];
-#pragma unroll
-  for (int k = 0; k < D; ++k) load_tile(first + k * kStride, w[k], nr[k], okt[k]);
-  // (an empty use outside the branch below keeps these loads ahead of the key
-  // tiles: issued later, waiting for them would also wait for the tiles)
-  asm volatile("" : "+v"(u0), "+v"(u1), "+v"(dn0), "+v"(dn1));
-  const float v0 = lane < din ? __uint_as_float(QBF16 ? u0 << 16 : u0) : 0.f;
-  const float v1 = lane + 64 < din ? __uint_as_float(QBF16 ? u1 << 16 : u1) : 0.f;
+  // Every wave issues the loads above before any wave issues a key tile, and
+  // only one tile goes out before the setup (the second after the S q sums).
+  // A CU takes only so many loads in flight: past that, a wave stalls where
+  // it issues the next one until earlier data comes back, and the setup's
+  // barriers wait for the slowest wave (measured at this scorer's launch on
+  // the Llama-3.1-8B decode shape: two tiles per wave up front left the
+  // tables ready after ~13,000 cycles, one after ~8,000).  A bare barrier,
+  // with no wait for the loads themselves.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  load_tile(first, w[0], nr[0], okt[0]);
 
   // ---- R q = H D q / sqrt(d)
   if (wave < 4) {
+    asm volatile("" : "+v"(u0), "+v"(u1), "+v"(dn0), "+v"(dn1), "+s"(isd));
+    const float v0 = lane < din ? __uint_as_float(QBF16 ? u0 << 16 : u0) : 0.f;
+    const float v1 = lane + 64 < din ? __uint_as_float(QBF16 ? u1 << 16 : u1) : 0.f;
     const bool live = qc * 4 + wave < Qg;
     const uint32_t f0 = (dn0 >> (lane & 31)) & 1u;
     const uint32_t f1 = (dn1 >> (lane & 31)) & 1u;
@@ -1362,10 +1369,11 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     y0 = butterfly_lane<16>(y0, lane & 16); y1 = butterfly_lane<16>(y1, lane & 16);
     y0 = butterfly_lane32(y0, lane & 32);   y1 = butterfly_lane32(y1, lane & 32);
     float* xf = reinterpret_cast<float*>(&sm.x[0][0][0]);
-    xf[((lane & 7) * 16 + (lane >> 3)) * 4 + wave] = 2.0f * (y0 * cst->inv_sqrt_d);
-    xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = 2.0f * (y1 * cst->inv_sqrt_d);
+    xf[((lane & 7) * 16 + (lane >> 3)) * 4 + wave] = 2.0f * (y0 * isd);
+    xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = 2.0f * (y1 * isd);
   }
   __syncthreads();
+  asm volatile("" : "+s"(qs), "+s"(asum), "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3));
   // ---- 2 S q partial sums over this wave's sixteen coordinates of 2 R q
   {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1382,6 +1390,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     sm.part[seg][jrow] = acc;
   }
   __syncthreads();
+  static_assert(D == 2, "the prologue loads one tile, this the second");
+  load_tile(first + kStride, w[1], nr[1], okt[1]);
   if (tid < 128) {
     f32x4 t = sm.part[0][tid];
 #pragma unroll
@@ -1443,8 +1453,6 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
       ss[qq] = 0.5f * __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(b)));
     }
   }
-  const float a0 = cst->alpha[0], a1 = cst->alpha[1], a2 = cst->alpha[2], a3 = cst->alpha[3];
-  const float asum = cst->alpha_sum, qs = cst->qjl_scale;
   float* lrow[4];   // logit rows of the chunk's queries (wave-uniform)
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
@@ -2106,7 +2114,7 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const bool bf = qdtype == 1;
 #define TQ_SC(BB, QB)                                                                   \
   hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, Ncap, Qg, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, AttnArgs{})
+                     norms, N, Ncap, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, AttnArgs{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
@@ -2145,7 +2153,7 @@ hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64
   const bool bf = qdtype == 1;
 #define TQ_AT(BB, QB, BVV)                                                                       \
   hipLaunchKernelGGL((score128_kernel<BB, QB, false, BVV>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, N, Qg, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, aa)
+                     norms, N, N, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, aa)
   switch (cb.bits) {
     case 2: if (bf) TQ_AT(1, true, 2); else TQ_AT(1, false, 2); break;
     case 3: if (bf) TQ_AT(2, true, 3); else TQ_AT(2, false, 3); break;
@@ -2307,7 +2315,7 @@ hipError_t launch_score_paged(const Codebook& cb, const void* q, int qdtype, int
   const bool bf = qdtype == 1;
 #define TQ_SCP(BB, QB)                                                                          \
   hipLaunchKernelGGL((score128_kernel<BB, QB, true>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, Lmax, int64_t(page_size), Qg, chunk, logits, cb.d_consts, cb.d_Sh, pm, AttnArgs{})
+                     norms, Lmax, int64_t(page_size), Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_Sh, pm, AttnArgs{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SCP(1, true); else TQ_SCP(1, false); break;
     case 2: if (bf) TQ_SCP(2, true); else TQ_SCP(2, false); break;
