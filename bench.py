@@ -369,7 +369,8 @@ def burst_us(K, torch, calls, filler, n_fill=40):
 def run_paged(K, cb, keys0, q, G, N, Qg, steps, ps=256):
     """The same decode loop on a paged cache: pages of 256 records assigned to
     the groups in a shuffled order, the N keys appended as one batch, then per
-    step one new key per group (the G single rows share 16-key encoder tiles)
+    step one new key per group (the G single rows take the latency kernel,
+    one key per workgroup)
     and the paged score of every group's records."""
     import torch
     dev = keys0.device
@@ -405,8 +406,12 @@ def run_paged(K, cb, keys0, q, G, N, Qg, steps, ps=256):
                                                          out=lg[:G * Qg * L].view(G, Qg, L)))
     app_us, app_ok = burst_us(K, torch, app, filler)
     step_us, step_ok = burst_us(K, torch, step_calls, filler)
+    # the same measure for a minimal launch (one workgroup reading 4 KB)
+    tiny = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    floor_us, _ = burst_us(K, torch, [lambda: K.stream_probe(tiny, grid=1)] * steps, filler)
     return {"page_size": ps, "pages": num_pages, "keys_per_append": G,
             "append_gpu_us": round(app_us, 2), "decode_step_gpu_us": round(2 * step_us, 2),
+            "launch_floor_gpu_us": round(floor_us, 2),
             "back_to_back": bool(app_ok and step_ok),
             "append_us_median": round(float(np.median(ap)) * 1e3, 2),
             "append_us_p90": round(float(np.percentile(ap, 90)) * 1e3, 2),
@@ -421,8 +426,8 @@ def run_attention(K, cb, keys0, q, G, N, Qg, packed, npk, steps):
     """Value path on the same shapes: value records for the cache (values drawn
     like the keys: the key rows in reverse order), then decode attention of the
     step's queries over packed keys and values, with both caches rotating past
-    the Infinity Cache.  Reports the value encoder and the three attention
-    launches (score, value pass, combine) by HIP events."""
+    the Infinity Cache.  Reports the value encoder and the attention call (the
+    scorer with its value phase, then the combine) by HIP events."""
     import torch
     vals = keys0.flip(1).contiguous()
     vbytes = K.value_packed_nbytes(cb, G, N)
@@ -443,7 +448,8 @@ def run_attention(K, cb, keys0, q, G, N, Qg, packed, npk, steps):
     return {"values_encode": _stats(enc, key_bytes + vbytes, G * N, "values"),
             "attention": _stats(att, att_alg, G * N, "keys"),
             "value_record_bytes": int(vbytes // (G * N)),
-            "note": "attention = score kernel (logits to workspace) + value pass + combine"}
+            "note": "attention = scorer with its value phase (logits through the caches, "
+                    "per-range softmax state) + combine (ranges merged, rotated back)"}
 
 
 def _event_times(fn, reps, warm=2):

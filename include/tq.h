@@ -220,7 +220,7 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
  * tq_paged_append_keys: keys [G][T][d] (TQ_F32 or TQ_BF16); key t of group g
  * is encoded by the rules of tq_encode_keys and written to logical position
  * pos[g] + t (pos: device int32 [G]).  The G*T rows are encoded as one batch:
- * up to 2048 rows by a one-key-per-wave kernel for latency (float32
+ * up to 2048 rows by a latency kernel, one key per workgroup (float32
  * rotation and projection: its records equal tq_encode_keys's except where a
  * rotated coordinate lies within rounding of a threshold or a projection
  * within rounding of zero, cases the method's parity rules leave open), more

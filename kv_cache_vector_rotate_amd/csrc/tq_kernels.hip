@@ -491,6 +491,7 @@ __device__ __forceinline__ void issue_tile_dma16(const uint16_t* __restrict__ ke
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + t), (lds_void*)(buf + t * 64),
                                        16, 0, 0);
   } else {
+    asm volatile("");   // a real branch: if-converted, every tile would pay the selects
     const uint4* row = src - 4 * w;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -851,6 +852,8 @@ __global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : (B == 3 ? 2 : 3)) void enc
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // buffer free again
     if (din < 128) {   // zero padding past din
+      // (a real branch: if-converted, the selects would run on every tile)
+      asm volatile("");
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         if (uint32_t(32 * w + 8 * t) >= din) raw[t] = u32x4{0u, 0u, 0u, 0u};
@@ -1561,16 +1564,30 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
 }
 
 // ============================================================== append, few rows, d = 128
-// Latency path of the paged append: one key per wave.  Lane L holds
-// coordinates L and L + 64; the rotation is a float32 butterfly (stride 64
-// inside the lane with +0 so that no -0 survives, strides 1..32 across lanes);
-// every bit-plane word comes from a wave ballot (bit L of the ballot over
-// coordinate L or L + 64 is bit L % 32 of word L / 32 or 2 + L / 32, the
-// natural order); S r is formed in float32 from the exact float16 rows of
-// S R^T (lane L: sketch rows L and L + 64, loaded before anything else)
-// against the residual broadcast through LDS.  Same rules as the tile
-// encoders; the float32 sums differ from theirs only in rounding.
+// Latency path of the paged append: one key per workgroup of four waves.
+// Every wave rotates and quantises the whole key (lane L: coordinates L and
+// L + 64; a float32 butterfly, stride 64 inside the lane with +0 so that no
+// -0 survives, strides 1..32 across lanes; every bit-plane word comes from a
+// wave ballot: bit L of the ballot over coordinate L or L + 64 is bit L % 32
+// of word L / 32 or 2 + L / 32, the natural order), then forms the sketch
+// sums S r of rows L and L + 64 over its own quarter of the coordinates in
+// float32 from the exact float16 rows of S R^T; wave 0 adds the four
+// quarters in a fixed order and stores the record.  A key's chain is the
+// load, the butterfly and 64 products per lane (one wave would take 256).
+// Same rules as the tile encoders; the float32 sums differ from theirs only
+// in rounding.
 constexpr int kAppendThreads = 256;
+constexpr int kAppendWaves = kAppendThreads / 64;
+
+// sum over the 64 lanes (DPP, swizzle and a half swap: no LDS round trips)
+__device__ __forceinline__ float wave_sum64_fast(float v) {
+  v += lane_xor<1>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<16>(v);
+  return xor32_sum(v);
+}
 
 template <int B, bool BF16>
 __global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
@@ -1579,21 +1596,25 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
     PageMap pm) {
   constexpr int K = 1 << (B - 1);   // levels on the positive half
   constexpr int P = B + 1;
-  __shared__ f32x4 s_r[kAppendThreads / 64][32];   // per-wave residual, 128 floats
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = int64_t(blockIdx.x) * (kAppendThreads / 64) + wave;
-  if (r >= rows) return;   // wave-uniform; nothing below synchronises across waves
-  uint4 sh[2][8][2];       // S R^T[row][16 s + m], rows L and L + 64, as float16 pairs
+  __shared__ float s_e[kAppendWaves][128];   // per-wave residual, coordinate order
+  __shared__ float2 s_p[kAppendWaves][64];   // per-wave partial sketch sums (rows L, L + 64)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r = blockIdx.x;   // one key per workgroup (the grid has exactly `rows` of them)
+  // S R^T[row][16 s + m], rows L and L + 64, segments s = 2 wave, 2 wave + 1
+  // (coordinates [32 wave, 32 wave + 32)), as float16 pairs
+  uint4 sh[2][2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int sg = 0; sg < 8; ++sg) {
-      const uint4* sp = Sh + (size_t(sg) * 128 + lane + 64 * j) * 2;
+    for (int sg = 0; sg < 2; ++sg) {
+      const uint4* sp = Sh + (size_t(2 * wave + sg) * 128 + lane + 64 * j) * 2;
       sh[j][sg][0] = sp[0];
       sh[j][sg][1] = sp[1];
     }
   int64_t dg = 0, dn = 0;
-  const bool ok = page_dest(pm, r, dg, dn);
+  bool ok = false;
+  if (wave == 0) ok = page_dest(pm, r, dg, dn);
   const int din = int(cst->din);
   float a, b;
   if constexpr (BF16) {
@@ -1605,9 +1626,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
     a = lane < din ? row[lane] : 0.f;
     b = lane + 64 < din ? row[lane + 64] : 0.f;
   }
-  float nu2 = fmaf(a, a, b * b);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) nu2 += __shfl_xor(nu2, o);
+  const float nu2 = wave_sum64_fast(fmaf(a, a, b * b));
   const float fa = ((cst->dneg[lane >> 5] >> (lane & 31)) & 1u) ? -a : a;
   const float fb = ((cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -b : b;
   float u0 = (fa + fb) + 0.0f, u1 = (fa - fb) + 0.0f;
@@ -1624,7 +1643,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
   const float gsc = zero ? 0.f : kResidualScale * __builtin_amdgcn_rcpf(nsd);   // u -> 2^12 y
   uint64_t neg[2], below[2][K > 1 ? K - 1 : 1];
   float rho2 = 0.f;
-  float* sr = reinterpret_cast<float*>(s_r[wave]);
+  float* sr = s_e[wave];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const float u = h ? u1 : u0, au = fabsf(u);
@@ -1640,27 +1659,43 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
     rho2 = fmaf(e, e, rho2);
     sr[lane + 64 * h] = e;
   }
+  rho2 = wave_sum64_fast(rho2);
+  // partial p_j = sum over this wave's 32 coordinates of (S R^T)_j,c r_c for
+  // rows j = L and L + 64, two chains per row (sign only: any positive scale)
+  float p0a = 0.f, p0b = 0.f, p1a = 0.f, p1b = 0.f;
+  const f32x4* sr4 = reinterpret_cast<const f32x4*>(sr) + 8 * wave;   // coordinates 32 wave ..
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) rho2 += __shfl_xor(rho2, o);
-  const float rho = zero ? 0.f : __builtin_amdgcn_sqrtf(rho2) * (nu * (1.0f / kResidualScale));
-  // p_j = (S R^T)_j . r_rot for rows j = L and L + 64 (sign only: any positive scale)
-  float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-  for (int sg = 0; sg < 8; ++sg) {
+  for (int sg = 0; sg < 2; ++sg) {
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
-      const f32x4 rv = s_r[wave][4 * sg + c4];   // coordinates 16 sg + 4 c4 .. + 3
+      const f32x4 rv = sr4[4 * sg + c4];   // coordinates 32 wave + 16 sg + 4 c4 .. + 3
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * c4 + i;
         const uint4 w0 = sh[0][sg][m >> 3], w1 = sh[1][sg][m >> 3];
         const uint32_t x0 = (m & 7) < 2 ? w0.x : (m & 7) < 4 ? w0.y : (m & 7) < 6 ? w0.z : w0.w;
         const uint32_t x1 = (m & 7) < 2 ? w1.x : (m & 7) < 4 ? w1.y : (m & 7) < 6 ? w1.z : w1.w;
-        p0 = fmaf(h2f_bits(x0 >> (16 * (m & 1))), rv[i], p0);
-        p1 = fmaf(h2f_bits(x1 >> (16 * (m & 1))), rv[i], p1);
+        if (i & 1) {
+          p0b = fmaf(h2f_bits(x0 >> (16 * (m & 1))), rv[i], p0b);
+          p1b = fmaf(h2f_bits(x1 >> (16 * (m & 1))), rv[i], p1b);
+        } else {
+          p0a = fmaf(h2f_bits(x0 >> (16 * (m & 1))), rv[i], p0a);
+          p1a = fmaf(h2f_bits(x1 >> (16 * (m & 1))), rv[i], p1a);
+        }
       }
     }
   }
+  s_p[wave][lane] = make_float2(p0a + p0b, p1a + p1b);
+  __syncthreads();
+  if (wave != 0) return;   // no barrier follows
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < kAppendWaves; ++q) {
+    const float2 pq = s_p[q][lane];
+    p0 += pq.x;
+    p1 += pq.y;
+  }
+  const float rho = zero ? 0.f : __builtin_amdgcn_sqrtf(rho2) * (nu * (1.0f / kResidualScale));
   const uint64_t sg0 = __builtin_amdgcn_ballot_w64(p0 < 0.f), sg1 = __builtin_amdgcn_ballot_w64(p1 < 0.f);
   if (!ok) return;
   const bool keep = !zero, keep_s = keep && rho2 > 0.f;
@@ -2259,8 +2294,8 @@ hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, 
   uint32_t* planes = static_cast<uint32_t*>(pool);
   uint32_t* norms = planes + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
   const PageMap pm{table, pos, nullptr, uint32_t(T), ppg, page_size, int32_t(num_pages)};
-  if (rows <= kAppendRowsMax) {   // latency path: one key per wave
-    const int grid = int((rows + kAppendThreads / 64 - 1) / (kAppendThreads / 64));
+  if (rows <= kAppendRowsMax) {   // latency path: one key per workgroup
+    const int grid = int(rows);   // one key per workgroup (rows <= kAppendRowsMax)
     const bool bf = dtype == 1;
 #define TQ_APP(BB)                                                                                     if (bf) hipLaunchKernelGGL((append_rows128_kernel<BB, true>), dim3(grid), dim3(kAppendThreads), 0, s,                              keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm);                      else hipLaunchKernelGGL((append_rows128_kernel<BB, false>), dim3(grid), dim3(kAppendThreads), 0, s,                             keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm)
     switch (cb.bits - 1) {

@@ -121,7 +121,7 @@ def test_paged_append_and_score(bits, dt, ps):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_paged_bulk_rows_take_the_tile_encoder(dt):
-    """A bulk append of more rows than the one-key-per-wave path takes (2048)
+    """A bulk append of more rows than the latency path takes (2048)
     goes through the tile encoder in its paged form: records equal the
     oracle's and the tile encoder's own records from tq_encode_keys."""
     rng = np.random.default_rng(31 + (1 if dt == "bf16" else 0))
