@@ -225,6 +225,45 @@ def test_paged_invalid_entries_are_skipped():
     assert np.all(lg[2] != -3.0) and np.all(lg[0, :, :ps] != -3.0)
 
 
+@pytest.mark.parametrize("rows,dt", [(1, "bf16"), (700, "f32")])
+def test_paged_zero_padded_d(rows, dt):
+    """d = 96 runs in D = 128 on the paged path too: three single rows take the
+    latency kernel, three groups of 700 rows (2100 > 2048) the tile encoder in
+    paged form; records and paged scores against the oracle's padded codebook."""
+    rng = np.random.default_rng(900 + rows)
+    din, bits, ps, G, Qg = 96, 3, 64, 3, 4
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    ppg = -(-(rows + 5) // ps)
+    num_pages = G * ppg
+    table = rng.permutation(num_pages).reshape(G, ppg).astype(np.int32)
+    cb = K.Codebook(din, bits)
+    cbo = O.make_codebook(din, bits, D, 42)
+    assert cb.D == D
+    pool = torch.full((K.paged_pool_nbytes(cb, num_pages, ps),), SENTINEL, dtype=torch.uint8, device="cuda")
+    x = rng.standard_normal((G, rows, din)) * np.exp(rng.normal(0, math.sqrt(0.5), din))
+    x = _exact(x.astype(np.float32), dtype)
+    x[0, 0] = 0.0                                        # zero record
+    start = np.array([0, 5, 3], dtype=np.int64)
+    print(f"[case] paged d=96 rows={rows} dt={dt}", flush=True)
+    K.paged_append_keys(cb, _dev(x, dtype), pool, ps, _i32(table), _i32(start))
+    torch.cuda.synchronize()
+    buf = pool.cpu().numpy()
+    for g in range(G):
+        c, s, nu, rho = _gather(cbo, buf, num_pages, ps, table, g, np.arange(start[g], start[g] + rows))
+        check_encode(cbo, x[g], c, s, nu, rho)
+    q = _exact(rng.standard_normal((G, Qg, din)).astype(np.float32), dtype)
+    lens = np.array([rows, 0, 0], dtype=np.int32)       # group 0 starts at 0
+    out = torch.full((G, Qg, rows), -5.0, device="cuda")
+    K.paged_score(cb, _dev(q, dtype), pool, ps, _i32(table), _i32(lens), rows, out=out)
+    torch.cuda.synchronize()
+    lg = out.cpu().numpy()
+    assert np.all(lg[1:] == -5.0)
+    c, s, nu, rho = _gather(cbo, buf, num_pages, ps, table, 0, np.arange(rows))
+    one = O.pack(cbo, c[None], s[None], nu[None], rho[None])
+    check_logits(lg[:1], O.score(cbo, one, 1, rows, q[:1]), q[:1],
+                 np.linalg.norm(x[:1].astype(np.float64), axis=-1))
+
+
 def test_paged_argument_errors():
     cb = K.Codebook(D, 3)
     lib = K.library()
