@@ -1034,7 +1034,7 @@ constexpr int kScoreThreads = 1024;
 struct ScoreLds {
   f32x4 tab[2 * 256 * 16];   // 128 KB, first: its byte offsets are the table addresses
   f32x4 x[2][8][16];         // [ty][t][pos] = 2 X_ty[8 pos + t]
-  f32x4 part[8][128];        // S q partial sums, [column segment][row]
+  uint4 bq[4][64];           // 2 R q as fp16 hi + lo: the B operand of the S q products [step][lane]
   f32x4 sum[2];              // sum over all coordinates of 2 X_ty
 };
 
@@ -1251,7 +1251,7 @@ template <int B, bool QBF16, bool PAGED = false, int BV = 0>
 __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     const void* __restrict__ q, const uint4* __restrict__ planes, const uint32_t* __restrict__ norms,
     int64_t N, int64_t Ncap, int Qg, int din, int64_t chunk, float* __restrict__ logits,
-    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sh, PageMap pm, AttnArgs aa) {
+    const DevConsts* __restrict__ cst, const uint4* __restrict__ Sfrag, PageMap pm, AttnArgs aa) {
   constexpr int P = B + 1;
   constexpr int NW = B == 3 ? P + 1 : P;   // plane words scored per key (B = 3: + parity)
   constexpr int D = 2;   // key tiles in flight per wave (two measured 2-3% faster than three at b = 3)
@@ -1272,16 +1272,17 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   const uint4* pg = planes + g * P * Ncap;
   const uint32_t* ng = norms + g * Ncap;
 
-  // ---- loads: sixteen S R^T columns (fp16, exact), the R q input, the
-  // first key tile.  S q = (S R^T)(R q): the scorer needs R q anyway, and
-  // the fp16 table is half the bytes every workgroup fetches at its start.
-  const int seg = wave >> 1;
-  const int jrow = 64 * (wave & 1) + lane;
-  uint4 sh[2];   // (S R^T)[jrow][16 seg + m], m = 0..15
-  {
-    const uint4* sp = Sh + (size_t(seg) * 128 + jrow) * 2;
-    sh[0] = sp[0];
-    sh[1] = sp[1];
+  // ---- loads: the S q products' A operands, the R q input, the first key
+  // tile.  S q = (S R^T)(R q): the scorer needs R q anyway.  Waves 0..7 form
+  // the sixteen sketch rows of block `wave` on the matrix cores from -S R^T
+  // in fp16 (exact), in the key encoder's operand order: step t's A operand
+  // of row block b at [t][b][lane], matrix row m of block b = sketch row
+  // 32 (m / 4) + 4 b + m % 4, K index k of step t = coordinate
+  // 32 (k / 8) + 8 t + k % 8.
+  uint4 sa[4];
+  if (wave < 8) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sa[t] = Sfrag[(t * 8 + wave) * 64 + lane];
   }
   // query rows hold din <= 128 elements (an argument: read from the constant
   // block, it would put an L2 round trip before the query loads); coordinates
@@ -1354,6 +1355,11 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   load_tile(first, w[0], nr[0], okt[0]);
+  // B operand columns 8..15 of the S q products carry no query: zeros
+  if (tid >= 256 && tid < 384) {
+    const int i = tid - 256, t = i >> 5, kg = (i >> 3) & 3, c = 8 + (i & 7);
+    sm.bq[t][16 * kg + c] = make_uint4(0u, 0u, 0u, 0u);
+  }
 
   // ---- R q = H D q / sqrt(d)
   if (wave < 4) {
@@ -1372,42 +1378,71 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     y0 = butterfly_lane<16>(y0, lane & 16); y1 = butterfly_lane<16>(y1, lane & 16);
     y0 = butterfly_lane32(y0, lane & 32);   y1 = butterfly_lane32(y1, lane & 32);
     float* xf = reinterpret_cast<float*>(&sm.x[0][0][0]);
-    xf[((lane & 7) * 16 + (lane >> 3)) * 4 + wave] = 2.0f * (y0 * isd);
-    xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = 2.0f * (y1 * isd);
+    const float x0 = 2.0f * (y0 * isd), x1 = 2.0f * (y1 * isd);   // coordinates lane, lane + 64
+    xf[((lane & 7) * 16 + (lane >> 3)) * 4 + wave] = x0;
+    xf[((lane & 7) * 16 + 8 + (lane >> 3)) * 4 + wave] = x1;
+    // B operand of the S q products: column 2 q + h of K row k holds query
+    // q's coordinate 32 (k / 8) + 8 t + k % 8 as fp16 hi (h = 0) and
+    // 2^11 x (x - hi) (h = 1, exact in float32 before its rounding)
+    uint16_t* bq16 = reinterpret_cast<uint16_t*>(&sm.bq[0][0]);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const float x = h2 ? x1 : x0;
+      const int c = lane + 64 * h2;
+      const _Float16 hi = static_cast<_Float16>(x);
+      const _Float16 lo = static_cast<_Float16>((x - static_cast<float>(hi)) * 2048.0f);
+      const int base = (((c >> 3) & 3) * 64 + 16 * (c >> 5) + 2 * wave) * 8 + (c & 7);
+      bq16[base] = __builtin_bit_cast(uint16_t, hi);
+      bq16[base + 8] = __builtin_bit_cast(uint16_t, lo);
+    }
   }
   __syncthreads();
   asm volatile("" : "+s"(qs), "+s"(asum), "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3));
-  // ---- 2 S q partial sums over this wave's sixteen coordinates of 2 R q
-  {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint32_t hw[8] = {sh[0].x, sh[0].y, sh[0].z, sh[0].w, sh[1].x, sh[1].y, sh[1].z, sh[1].w};
+  // ---- byte subset-sum tables T[ty][idx][pos] = sum over the set bits t of
+  // idx of 2 X_ty[8 pos + t].  Waves 8..15 build the R q tables (ty = 0,
+  // eight entries per thread) while waves 0..7 form 2 S q on the matrix
+  // cores; then all sixteen waves build the S q tables (four entries each).
+  // The full-byte entries (idx 255) of every position give the sums.
+  auto byte_sums = [&](const f32x4& full, int at) {
+    f32x4 t = full;   // lanes 48..63 of wave 15 hold idx 255 of positions 0..15
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float sv = h2f_bits(hw[m >> 1] >> (16 * (m & 1)));
-      const f32x4 xv = sm.x[0][m & 7][2 * seg + (m >> 3)];   // coordinate 16 seg + m, 4 queries
-      acc[0] = fmaf(sv, xv[0], acc[0]);
-      acc[1] = fmaf(sv, xv[1], acc[1]);
-      acc[2] = fmaf(sv, xv[2], acc[2]);
-      acc[3] = fmaf(sv, xv[3], acc[3]);
+    for (int c = 0; c < 4; ++c) {
+      t[c] += lane_xor<1>(t[c]);
+      t[c] += lane_xor<2>(t[c]);
+      t[c] += lane_xor<4>(t[c]);
+      t[c] += lane_xor<8>(t[c]);
     }
-    sm.part[seg][jrow] = acc;
-  }
-  __syncthreads();
-  static_assert(D == 2, "the prologue loads one tile, this the second");
-  load_tile(first + kStride, w[1], nr[1], okt[1]);
-  if (tid < 128) {
-    f32x4 t = sm.part[0][tid];
+    if (lane == 48) sm.sum[at] = t;
+  };
+  if (wave < 8) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 1; k < 8; ++k) t += sm.part[k][tid];
-    sm.x[1][tid & 7][tid >> 3] = t;
-  }
-  __syncthreads();
-  // ---- tables: thread (pos, ty, hi) writes entries idx = 8 hi + j, j = 0..7
-  {
-    const int pos = tid & 15, ty = (tid >> 4) & 1, hi = tid >> 5;
+    for (int t = 0; t < 4; ++t) {
+      const uint4 bv = sm.bq[t][lane];
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, sa[t]),
+                                                   __builtin_bit_cast(half8, bv), acc, 0, 0, 0);
+    }
+    // D[m][col] (m = 4 (lane / 16) + i, col = lane % 16) = -(2 S q) of sketch
+    // row 32 (lane / 16) + 4 wave + i for query col / 2, hi (even col) or
+    // 2^11 x lo part (odd col, the next lane's)
+    float lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lo[i] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc[i]), 0x101, 0xF, 0xF, false));
+    if ((lane & 1) == 0 && (lane & 15) < 8) {
+      float* xf1 = reinterpret_cast<float*>(&sm.x[1][0][0]);
+      const int qq = (lane & 15) >> 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 32 * (lane >> 4) + 4 * wave + i;
+        xf1[((j & 7) * 16 + (j >> 3)) * 4 + qq] = -fmaf(lo[i], 1.0f / 2048.0f, acc[i]);
+      }
+    }
+  } else {
+    const int tt = tid - 512, pos = tt & 15, hi = tt >> 4;   // entries idx = 8 hi + j
     f32x4 xv[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) xv[t] = sm.x[ty][t][pos];
+    for (int t = 0; t < 8; ++t) xv[t] = sm.x[0][t][pos];
     f32x4 bs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 3; t < 8; ++t) {
@@ -1427,19 +1462,34 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
     e[6] = e[4] + xv[1];
     e[7] = e[6] + xv[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sm.tab[(ty * 256 + hi * 8 + j) * 16 + pos] = e[j];
-    if (wave == 15) {   // lanes 32..63 hold the full-byte sums (idx 255) of every position
-      f32x4 t = e[7];
+    for (int j = 0; j < 8; ++j) sm.tab[(hi * 8 + j) * 16 + pos] = e[j];
+    if (wave == 15) byte_sums(e[7], 0);
+  }
+  __syncthreads();
+  static_assert(D == 2, "the prologue loads one tile, this the second");
+  load_tile(first + kStride, w[1], nr[1], okt[1]);
+  {
+    const int pos = tid & 15, h = tid >> 4;   // entries idx = 4 h + j of the S q tables
+    f32x4 xv[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        t[c] += lane_xor<1>(t[c]);
-        t[c] += lane_xor<2>(t[c]);
-        t[c] += lane_xor<4>(t[c]);
-        t[c] += lane_xor<8>(t[c]);
-      }
-      if (lane == 32) sm.sum[0] = t;
-      if (lane == 48) sm.sum[1] = t;
+    for (int t = 0; t < 8; ++t) xv[t] = sm.x[1][t][pos];
+    f32x4 bs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 2; t < 8; ++t) {
+      const float on = float((h >> (t - 2)) & 1);
+      bs[0] = fmaf(on, xv[t][0], bs[0]);
+      bs[1] = fmaf(on, xv[t][1], bs[1]);
+      bs[2] = fmaf(on, xv[t][2], bs[2]);
+      bs[3] = fmaf(on, xv[t][3], bs[3]);
     }
+    f32x4 e[4];
+    e[0] = bs;
+    e[1] = bs + xv[0];
+    e[2] = bs + xv[1];
+    e[3] = e[2] + xv[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.tab[(256 + h * 4 + j) * 16 + pos] = e[j];
+    if (wave == 15) byte_sums(e[3], 1);
   }
   __syncthreads();
 
@@ -2149,7 +2199,7 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
   const bool bf = qdtype == 1;
 #define TQ_SC(BB, QB)                                                                   \
   hipLaunchKernelGGL((score128_kernel<BB, QB>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, Ncap, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, AttnArgs{})
+                     norms, N, Ncap, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_frag16, PageMap{}, AttnArgs{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SC(1, true); else TQ_SC(1, false); break;
     case 2: if (bf) TQ_SC(2, true); else TQ_SC(2, false); break;
@@ -2188,7 +2238,7 @@ hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64
   const bool bf = qdtype == 1;
 #define TQ_AT(BB, QB, BVV)                                                                       \
   hipLaunchKernelGGL((score128_kernel<BB, QB, false, BVV>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, N, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_Sh, PageMap{}, aa)
+                     norms, N, N, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_frag16, PageMap{}, aa)
   switch (cb.bits) {
     case 2: if (bf) TQ_AT(1, true, 2); else TQ_AT(1, false, 2); break;
     case 3: if (bf) TQ_AT(2, true, 3); else TQ_AT(2, false, 3); break;
@@ -2350,7 +2400,7 @@ hipError_t launch_score_paged(const Codebook& cb, const void* q, int qdtype, int
   const bool bf = qdtype == 1;
 #define TQ_SCP(BB, QB)                                                                          \
   hipLaunchKernelGGL((score128_kernel<BB, QB, true>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, Lmax, int64_t(page_size), Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_Sh, pm, AttnArgs{})
+                     norms, Lmax, int64_t(page_size), Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_frag16, pm, AttnArgs{})
   switch (cb.bits - 1) {
     case 1: if (bf) TQ_SCP(1, true); else TQ_SCP(1, false); break;
     case 2: if (bf) TQ_SCP(2, true); else TQ_SCP(2, false); break;
