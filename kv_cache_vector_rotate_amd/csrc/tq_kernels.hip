@@ -1399,20 +1399,42 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   __syncthreads();
   asm volatile("" : "+s"(qs), "+s"(asum), "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3));
   // ---- byte subset-sum tables T[ty][idx][pos] = sum over the set bits t of
-  // idx of 2 X_ty[8 pos + t].  Waves 8..15 build the R q tables (ty = 0,
-  // eight entries per thread) while waves 0..7 form 2 S q on the matrix
-  // cores; then all sixteen waves build the S q tables (four entries each).
-  // The full-byte entries (idx 255) of every position give the sums.
-  auto byte_sums = [&](const f32x4& full, int at) {
-    f32x4 t = full;   // lanes 48..63 of wave 15 hold idx 255 of positions 0..15
+  // idx of 2 X_ty[8 pos + t], thread (pos, h) writing entries idx = 4 h + j,
+  // j = 0..3.  Waves 0..7 first form 2 S q on the matrix cores, then join the
+  // other waves on the R q tables; then all build the S q tables.  The
+  // full-byte entries (idx 255) of every position give the sums.
+  auto build_tables = [&](int ty) {
+    const int pos = tid & 15, h = tid >> 4;
+    f32x4 xv[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      t[c] += lane_xor<1>(t[c]);
-      t[c] += lane_xor<2>(t[c]);
-      t[c] += lane_xor<4>(t[c]);
-      t[c] += lane_xor<8>(t[c]);
+    for (int t = 0; t < 8; ++t) xv[t] = sm.x[ty][t][pos];
+    f32x4 bs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 2; t < 8; ++t) {
+      const float on = float((h >> (t - 2)) & 1);
+      bs[0] = fmaf(on, xv[t][0], bs[0]);
+      bs[1] = fmaf(on, xv[t][1], bs[1]);
+      bs[2] = fmaf(on, xv[t][2], bs[2]);
+      bs[3] = fmaf(on, xv[t][3], bs[3]);
     }
-    if (lane == 48) sm.sum[at] = t;
+    f32x4 e[4];
+    e[0] = bs;
+    e[1] = bs + xv[0];
+    e[2] = bs + xv[1];
+    e[3] = e[2] + xv[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sm.tab[(ty * 256 + h * 4 + j) * 16 + pos] = e[j];
+    if (wave == 15) {   // lanes 48..63 hold idx 255 of positions 0..15
+      f32x4 t = e[3];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t[c] += lane_xor<1>(t[c]);
+        t[c] += lane_xor<2>(t[c]);
+        t[c] += lane_xor<4>(t[c]);
+        t[c] += lane_xor<8>(t[c]);
+      }
+      if (lane == 48) sm.sum[ty] = t;
+    }
   };
   if (wave < 8) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1438,33 +1460,8 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
         xf1[((j & 7) * 16 + (j >> 3)) * 4 + qq] = -fmaf(lo[i], 1.0f / 2048.0f, acc[i]);
       }
     }
-  } else {
-    const int tt = tid - 512, pos = tt & 15, hi = tt >> 4;   // entries idx = 8 hi + j
-    f32x4 xv[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) xv[t] = sm.x[0][t][pos];
-    f32x4 bs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 3; t < 8; ++t) {
-      const float on = float((hi >> (t - 3)) & 1);
-      bs[0] = fmaf(on, xv[t][0], bs[0]);
-      bs[1] = fmaf(on, xv[t][1], bs[1]);
-      bs[2] = fmaf(on, xv[t][2], bs[2]);
-      bs[3] = fmaf(on, xv[t][3], bs[3]);
-    }
-    f32x4 e[8];
-    e[0] = bs;
-    e[1] = bs + xv[0];
-    e[2] = bs + xv[1];
-    e[3] = e[2] + xv[0];
-    e[4] = bs + xv[2];
-    e[5] = e[4] + xv[0];
-    e[6] = e[4] + xv[1];
-    e[7] = e[6] + xv[0];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sm.tab[(hi * 8 + j) * 16 + pos] = e[j];
-    if (wave == 15) byte_sums(e[7], 0);
   }
+  build_tables(0);
   __syncthreads();
   // The second tile of each wave: at b = 2 here, at b = 3 and 4 after the
   // tables (measured on the Llama-3.1-8B decode shape: 15.6 against 16.0 us
@@ -1472,29 +1469,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   // that issues it here stalls until the first tiles free their slots)
   static_assert(D == 2, "the prologue loads one tile, this the second");
   if constexpr (B == 1) load_tile(first + kStride, w[1], nr[1], okt[1]);
-  {
-    const int pos = tid & 15, h = tid >> 4;   // entries idx = 4 h + j of the S q tables
-    f32x4 xv[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) xv[t] = sm.x[1][t][pos];
-    f32x4 bs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 2; t < 8; ++t) {
-      const float on = float((h >> (t - 2)) & 1);
-      bs[0] = fmaf(on, xv[t][0], bs[0]);
-      bs[1] = fmaf(on, xv[t][1], bs[1]);
-      bs[2] = fmaf(on, xv[t][2], bs[2]);
-      bs[3] = fmaf(on, xv[t][3], bs[3]);
-    }
-    f32x4 e[4];
-    e[0] = bs;
-    e[1] = bs + xv[0];
-    e[2] = bs + xv[1];
-    e[3] = e[2] + xv[0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm.tab[(256 + h * 4 + j) * 16 + pos] = e[j];
-    if (wave == 15) byte_sums(e[3], 1);
-  }
+  build_tables(1);
   __syncthreads();
   if constexpr (B != 1) load_tile(first + kStride, w[1], nr[1], okt[1]);
 
