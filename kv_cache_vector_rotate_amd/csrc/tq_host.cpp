@@ -456,7 +456,7 @@ int upload_device(tq::Codebook& cb) {
                                     (cb.delta[i0 + 1] < 0 ? 0x80000000u : 0u);
         }
     if (e == hipSuccess) e = upload(&cb.d_frag16, f16.data(), f16.size() * sizeof(uint16_t));
-    // scorer: S R^T columns 16 s .. 16 s + 15 of row j, contiguous per (s, j)
+    // paged append (latency path): S R^T columns 16 s .. 16 s + 15 of row j, contiguous per (s, j)
     std::vector<uint16_t> sh(8 * 128 * 16);
     for (int sg = 0; sg < 8; ++sg)
       for (int j = 0; j < 128; ++j)

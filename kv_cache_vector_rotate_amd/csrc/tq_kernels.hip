@@ -2327,7 +2327,13 @@ hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, 
   if (rows <= kAppendRowsMax) {   // latency path: one key per workgroup
     const int grid = int(rows);   // one key per workgroup (rows <= kAppendRowsMax)
     const bool bf = dtype == 1;
-#define TQ_APP(BB)                                                                                     if (bf) hipLaunchKernelGGL((append_rows128_kernel<BB, true>), dim3(grid), dim3(kAppendThreads), 0, s,                              keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm);                      else hipLaunchKernelGGL((append_rows128_kernel<BB, false>), dim3(grid), dim3(kAppendThreads), 0, s,                             keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm)
+#define TQ_APP(BB)                                                                            \
+  if (bf)                                                                                     \
+    hipLaunchKernelGGL((append_rows128_kernel<BB, true>), dim3(grid), dim3(kAppendThreads), 0, s, \
+                       keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm);                  \
+  else                                                                                        \
+    hipLaunchKernelGGL((append_rows128_kernel<BB, false>), dim3(grid), dim3(kAppendThreads), 0, s, \
+                       keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm)
     switch (cb.bits - 1) {
       case 1: TQ_APP(1); break;
       case 2: TQ_APP(2); break;
