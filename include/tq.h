@@ -112,7 +112,10 @@ int tq_codebook_tables(int32_t d, int32_t bits, int32_t m, uint64_t seed,
                        double* levels, double* thresholds, int8_t* delta,
                        double* S, double* S_rot);
 
-/* tq_codebook_tables for a chosen coordinate law (TQ_CODEBOOK_*); kind
+/* tq_codebook_tables for a chosen coordinate law (TQ_CODEBOOK_*) [ai.spot.hk
+ * article, "隨機旋轉與Beta分佈": a rotated coordinate follows a Beta law;
+ * ICLR 2026 paper digest, "Step 1: PolarQuant": that law, then N(0, 1/d) for
+ * large d]; kind
  * TQ_CODEBOOK_GAUSSIAN is tq_codebook_tables.  Errors as above, plus
  * TQ_ERR_ARG for an unknown kind. */
 int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32_t kind,
@@ -134,29 +137,32 @@ int tq_codebook_tables_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int
  */
 int tq_make_codebook(int32_t d, int32_t bits, int32_t m, uint64_t seed, tq_codebook** out);
 
-/* tq_make_codebook for a chosen coordinate law (TQ_CODEBOOK_*): every
- * entry point then encodes, scores and decodes with those levels and
- * thresholds (keys: bits-1 bit codes, values: bits bit codes).  Errors as
- * above, plus TQ_ERR_ARG for an unknown kind. */
+/* tq_make_codebook for a chosen coordinate law (TQ_CODEBOOK_*; passages as
+ * tq_codebook_tables_ex): every entry point then encodes, scores and
+ * decodes with those levels and thresholds (keys: bits-1 bit codes, values:
+ * bits bit codes).  Errors as above, plus TQ_ERR_ARG for an unknown kind. */
 int tq_make_codebook_ex(int32_t d, int32_t bits, int32_t m, uint64_t seed, int32_t kind,
                         tq_codebook** out);
 
 /* Release a codebook (NULL is a no-op).  The caller must ensure no launch
- * that uses it is still in flight. */
+ * that uses it is still in flight.  (Library bookkeeping: defines no step of
+ * the method.) */
 void tq_free_codebook(tq_codebook* cb);
 
-/* Host copies of a codebook's tables (same meaning and sizes as
+/* (Library bookkeeping.)  Host copies of a codebook's tables (same meaning and sizes as
  * tq_codebook_tables: delta has tq_rotation_dim(d) entries; any pointer may
  * be NULL).  Errors: TQ_ERR_ARG (cb NULL). */
 int tq_codebook_export(const tq_codebook* cb, double* levels, double* thresholds,
                        int8_t* delta, double* S, double* S_rot);
 
-/* (d, bits, m, seed) of a codebook as passed to tq_make_codebook (d is the
+/* (Library bookkeeping.)  (d, bits, m, seed) of a codebook as passed to tq_make_codebook (d is the
  * caller's vector length, before any zero padding); any pointer may be NULL. */
 int tq_codebook_info(const tq_codebook* cb, int32_t* d, int32_t* bits, int32_t* m,
                      uint64_t* seed);
 
-/* Bytes of a packed buffer for G groups of N keys; 0 on bad arguments. */
+/* Bytes of a packed buffer for G groups of N keys [ICLR 2026 paper digest,
+ * implementation notes: the norm kept beside each vector, sign bits eight per
+ * byte; Qiita explainer, byte table: bytes per key at each width]; 0 on bad arguments. */
 size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
 
 /*
@@ -267,7 +273,7 @@ size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
 int tq_encode_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G,
                      int64_t N, void* vpacked, void* stream);
 
-/* Workspace bytes of tq_attention_decode (the logits plus per-range partial
+/* (Library bookkeeping.)  Workspace bytes of tq_attention_decode (the logits plus per-range partial
  * sums); 0 on bad arguments or d != 128. */
 size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N);
 
@@ -307,10 +313,11 @@ int tq_attention_decode_noalloc(const tq_codebook* cb, const void* q, int32_t q_
                                 int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
                                 float scale, float* out, void* stream);
 
-/* Size in bytes of the static array tq_attention_decode_noalloc works in. */
+/* Size in bytes of the static array tq_attention_decode_noalloc works in
+ * (library bookkeeping, for the callers that entry point is for). */
 size_t tq_attention_noalloc_max_bytes(void);
 
-/* Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
+/* (Library bookkeeping.)  Workspace bytes tq_score_logits needs for G groups of Qg queries: 0 for
  * d = 128 (each workgroup prepares its queries on chip; ws may be NULL);
  * G*Qg*(2*d + 4)*4 for d = 1024, 2048 and 4096 (the prepared queries 2 R q,
  * 2 S q and their sums). */
@@ -410,6 +417,7 @@ int tq_dense_logits_bf16(const void* q, const void* keys, int64_t G, int32_t Qg,
 int tq_clock_probe(uint64_t* out, int32_t ticks, void* stream);
 
 /*
+ * (A measurement helper, as tq_clock_probe.)
  * tq_stream_probe: streams src_bytes from src with 16-byte non-temporal
  * loads and writes dst_bytes to dst with 16-byte non-temporal stores, the
  * writes spread evenly between the reads, over `grid` workgroups of 1024
@@ -433,10 +441,11 @@ int tq_stream_probe(const void* src, size_t src_bytes, void* dst, size_t dst_byt
 int tq_score_stream_probe(const tq_codebook* cb, int64_t G, int32_t Qg, const void* packed, int64_t N,
                           float* logits, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (library bookkeeping). */
 const char* tq_status_string(int status);
 
-/* hipError_t of the last failing HIP call on this thread (0 if none). */
+/* hipError_t of the last failing HIP call on this thread (0 if none;
+ * library bookkeeping). */
 int tq_last_hip_error(void);
 
 #ifdef __cplusplus
