@@ -51,6 +51,7 @@ __all__ = [
     "exact_logits", "top_k", "fp16_midpoint_flag", "ZERO_NORM",
     "FLAG_BAND", "kv_bytes_per_vector",
     "lloyd_max_beta", "haar_rotation", "rotation_dim", "value_quantizer", "ValueEncodeResult", "encode_values", "value_packed_nbytes",
+    "value_group_size", "value_slot_coordinate",
     "pack_values", "unpack_values", "decode_values", "attention_from_logits", "attention",
 ]
 
@@ -621,36 +622,74 @@ def encode_values(cb: Codebook, values: np.ndarray) -> ValueEncodeResult:
                              nu16_flag=fp16_midpoint_flag(nu_st) & ~zero)
 
 
-# Packed value layout: planes uint32 [G][bits][N][d/32] (bit p of the level
-# index, LSB first; bit j of word w is coordinate 32 w + j), then norms
-# uint16 [G][N] = half(nu).
+# Packed value layout (a storage format of this library; the pages fix only
+# its size, b-bit codes and one half norm per value).  Values are grouped in
+# tiles of 16 consecutive values of a group, T = ceil(N / 16) tiles per group:
+#   codes: uint32 [G][T][bits * d / 2]: tile t holds values 16 t .. 16 t + 15
+#          (values past N have code 0); its 16 * bits * d bits (bit k is bit
+#          k % 32 of word k // 32) are d slots of 16 * bits bits, slot s holding
+#          coordinate value_slot_coordinate(s).  A slot is a row of groups of
+#          K = value_group_size(bits) values: group q holds values K q .. K q +
+#          K - 1 in K * bits bits, bit K p + i of the group being bit p of the
+#          code of value K q + i.
+#   norms: uint16 [G][N] = half(nu).
+# So one slot group is the level index of a table of K levels at once.
+
+def value_group_size(bits: int) -> int:
+    """Values per slot group: 4 up to 3 bits, 2 from 4 bits (a group spans at
+    most 12 bits)."""
+    return 4 if bits <= 3 else 2
+
+
+def value_slot_coordinate(s: np.ndarray) -> np.ndarray:
+    """Coordinate held by slot s of a value tile: 32 (s // 32) + 16 (s % 2) +
+    (s % 32) // 2."""
+    s = np.asarray(s)
+    return 32 * (s // 32) + 16 * (s % 2) + (s % 32) // 2
+
 
 def value_packed_nbytes(cb: Codebook, G: int, N: int) -> int:
-    return G * N * (cb.bits * cb.d // 8 + 2)
+    T = (N + 15) // 16
+    return G * (T * 16 * cb.bits * cb.d // 8 + 2 * N)
+
+
+def _value_tile_bits(cb: Codebook, codes: np.ndarray) -> np.ndarray:
+    """codes [G, T*16, d] -> bits [G, T, 16 * bits * d] in stream order."""
+    G, NP, d = codes.shape
+    b, K = cb.bits, value_group_size(cb.bits)
+    T = NP // 16
+    planes = (codes[..., None] >> np.arange(b, dtype=np.uint8)) & 1          # [G, NP, d, b]
+    planes = planes[:, :, value_slot_coordinate(np.arange(d)), :]           # coordinate -> slot
+    t = planes.reshape(G, T, 16 // K, K, d, b)                             # [G, T, q, i, slot, p]
+    return t.transpose(0, 1, 4, 2, 5, 3).reshape(G, T, 16 * b * d)        # [slot][q][p][i]
 
 
 def pack_values(cb: Codebook, codes, nu16) -> np.ndarray:
     codes = np.asarray(codes, dtype=np.uint8)
     G, N, d = codes.shape
-    planes = np.empty((G, cb.bits, N, d // 32), dtype=np.uint32)
-    for p in range(cb.bits):
-        planes[:, p] = _bits_to_words((codes >> p) & 1)
+    T = (N + 15) // 16
+    padded = np.zeros((G, T * 16, d), np.uint8)
+    padded[:, :N] = codes
+    words = _bits_to_words(_value_tile_bits(cb, padded))
     norms = np.asarray(nu16, dtype=np.float16).reshape(G, N).view(np.uint16)
-    return np.concatenate([planes.reshape(-1).view(np.uint8), norms.reshape(-1).view(np.uint8)])
+    return np.concatenate([words.reshape(-1).view(np.uint8), norms.reshape(-1).view(np.uint8)])
 
 
 def unpack_values(cb: Codebook, buf: np.ndarray, G: int, N: int):
     """Inverse of :func:`pack_values`: (codes [G, N, d], nu16 [G, N])."""
     buf = np.ascontiguousarray(np.asarray(buf).reshape(-1).view(np.uint8))
     assert buf.size == value_packed_nbytes(cb, G, N)
-    d = cb.d
-    nplane = G * cb.bits * N * (d // 32)
-    planes = buf[: nplane * 4].view(np.uint32).reshape(G, cb.bits, N, d // 32)
-    nu16 = buf[nplane * 4:].view(np.float16).reshape(G, N)
-    codes = np.zeros((G, N, d), dtype=np.uint8)
-    for p in range(cb.bits):
-        codes |= (_words_to_bits(planes[:, p]) << p).astype(np.uint8)
-    return codes, nu16
+    d, b, K = cb.d, cb.bits, value_group_size(cb.bits)
+    T = (N + 15) // 16
+    nword = G * T * 16 * b * d // 32
+    bits = _words_to_bits(buf[: nword * 4].view(np.uint32).reshape(G, T, 16 * b * d // 32))
+    t = bits.reshape(G, T, d, 16 // K, b, K).transpose(0, 1, 3, 5, 2, 4)    # [G, T, q, i, slot, p]
+    planes = t.reshape(G, T * 16, d, b)
+    codes_slot = (planes.astype(np.uint8) << np.arange(b, dtype=np.uint8)).sum(axis=-1).astype(np.uint8)
+    codes = np.empty_like(codes_slot)
+    codes[:, :, value_slot_coordinate(np.arange(d))] = codes_slot
+    nu16 = buf[nword * 4:].view(np.float16).reshape(G, N)
+    return codes[:, :N], nu16
 
 
 def decode_values(cb: Codebook, buf: np.ndarray, G: int, N: int) -> np.ndarray:

@@ -57,23 +57,70 @@ def test_value_distortion_matches_max_table(bits):
 
 
 def test_value_record_layout_by_hand():
+    """d = 64, 3 bits (groups of 4 values, 12 bits), N = 2: one tile of 16
+    values, 64 slots of 48 bits = 96 words, then the two half norms.
+    Coordinate 33 sits in slot 34 (32 * 1 + 16 * 0 + 2 // 2 = 33) and
+    coordinate 0 in slot 0.  Code 5 of value 1 at coordinate 33: planes 0
+    and 2 of value 1 = bits 4 * 0 + 1 and 4 * 2 + 1 of slot 34, stream bits
+    1633 and 1641 = bits 1 and 9 of word 51.  Code 2 of value 0 at
+    coordinate 0: plane 1 = bit 4 of slot 0 = bit 4 of word 0."""
     d, bits = 64, 3
     cb = O.make_codebook(d, bits, d, 1)
+    assert O.value_group_size(bits) == 4 and O.value_group_size(4) == 2
+    assert O.value_slot_coordinate(34) == 33 and O.value_slot_coordinate(0) == 0
+    assert sorted(O.value_slot_coordinate(np.arange(d)).tolist()) == list(range(d))
     codes = np.zeros((1, 2, d), np.uint8)
-    codes[0, 1, 33] = 5            # 0b101: planes 0 and 2 of key 1, word 1, bit 1
-    codes[0, 0, 0] = 2             # 0b010: plane 1 of key 0, word 0, bit 0
+    codes[0, 1, 33] = 5
+    codes[0, 0, 0] = 2
     nu16 = np.array([[1.5, -0.0]], np.float16)
     buf = O.pack_values(cb, codes, nu16)
-    assert buf.size == O.value_packed_nbytes(cb, 1, 2) == 2 * O.kv_bytes_per_vector(d, bits)[1]
-    w = buf[: 1 * bits * 2 * 2 * 4].view(np.uint32).reshape(bits, 2, 2)   # [plane][key][word]
-    expect = np.zeros((bits, 2, 2), np.uint32)
-    expect[0, 1, 1] = 2
-    expect[2, 1, 1] = 2
-    expect[1, 0, 0] = 1
+    assert buf.size == O.value_packed_nbytes(cb, 1, 2) == 96 * 4 + 2 * 2
+    w = buf[: 96 * 4].view(np.uint32)
+    expect = np.zeros(96, np.uint32)
+    expect[51] = (1 << 1) | (1 << 9)
+    expect[0] = 1 << 4
     assert np.array_equal(w, expect)
     assert buf[-4:].view(np.uint16).tolist() == [0x3E00, 0x8000]
     c2, n2 = O.unpack_values(cb, buf, 1, 2)
     assert np.array_equal(c2, codes) and np.array_equal(n2.view(np.uint16), nu16.view(np.uint16))
+
+
+def test_value_record_layout_four_bits_by_hand():
+    """4 bits: groups of 2 values (8 bits).  Code 9 (0b1001) of value 3 at
+    coordinate 17 (slot 3: 32 * 0 + 16 * 1 + 2 // 2): value 3 is i = 1 of
+    group 1, planes 0 and 3 = bits 8 + 2 * 0 + 1 and 8 + 2 * 3 + 1 of the
+    64-bit slot 3, stream bits 201 and 207 = bits 9 and 15 of word 6."""
+    d, bits = 32, 4
+    cb = O.make_codebook(d, bits, d, 1)
+    codes = np.zeros((1, 5, d), np.uint8)
+    codes[0, 3, 17] = 9
+    buf = O.pack_values(cb, codes, np.zeros((1, 5), np.float16))
+    assert buf.size == 16 * 4 * 32 // 8 + 2 * 5
+    w = buf[: 16 * 4 * 32 // 8].view(np.uint32)
+    expect = np.zeros(64, np.uint32)
+    expect[6] = (1 << 9) | (1 << 15)
+    assert np.array_equal(w, expect)
+
+
+def test_value_records_round_trip_ragged():
+    """Random codes for N = 1, 15, 16, 17, 40 values: unpack(pack) is the
+    identity, and the words equal those of the tiles padded with code-0
+    values."""
+    rng = np.random.default_rng(8)
+    for bits in (2, 3, 4):
+        cb = O.make_codebook(128, bits, 128, 3)
+        for N in (1, 15, 16, 17, 40):
+            codes = rng.integers(0, 1 << bits, size=(2, N, 128), dtype=np.uint8)
+            nu16 = rng.standard_normal((2, N)).astype(np.float16)
+            buf = O.pack_values(cb, codes, nu16)
+            c2, n2 = O.unpack_values(cb, buf, 2, N)
+            assert np.array_equal(c2, codes) and np.array_equal(n2.view(np.uint16), nu16.view(np.uint16))
+            NP = ((N + 15) // 16) * 16
+            padded = np.zeros((2, NP, 128), np.uint8)
+            padded[:, :N] = codes
+            full = O.pack_values(cb, padded, np.zeros((2, NP), np.float16))
+            nw = buf.size - 2 * 2 * N
+            assert nw == full.size - 2 * 2 * NP and np.array_equal(buf[:nw], full[:nw])
 
 
 def test_value_bytes_reproduce_the_compression_table():
