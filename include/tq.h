@@ -257,12 +257,20 @@ int tq_paged_score(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_
  * value compressor = rotation + Lloyd-Max), and its byte table counts b-bit
  * value codes plus one half norm per value.  A value record uses all `bits`
  * bits of the codebook for a Lloyd-Max code of N(0, 1/d) (2^bits levels),
- * with the same rotation R; no sketch bit.  Layout for G groups x N values:
- *   planes: uint32 [G][bits][N][D/32], bit p of the level index, LSB first,
- *           bit j of word w = coordinate 32*w + j;
+ * with the same rotation R; no sketch bit.  Layout for G groups x N values,
+ * in tiles of 16 consecutive values of a group (T = ceil(N/16) per group):
+ *   codes:  uint32 [G][T][bits*D/2]: tile t holds values 16t .. 16t+15
+ *           (values past N have code 0); its 16*bits*D bits (bit k = bit
+ *           k%32 of word k/32) are D slots of 16*bits bits, slot s holding
+ *           coordinate 32*(s/32) + 16*(s%2) + (s%32)/2 of the 16 values, as
+ *           8 groups of 2*bits bits: bit 2p+i of group q = bit p of the
+ *           level index of value 2q+i;
  *   norms:  uint16 [G][N] = half(||v||) (RNE); zero record if ||v|| < 1e-10.
- *   Total:  G*N*(bits*D/8 + 2) bytes.
- * d = 128 only.
+ *   Total:  G*(16*T*bits*D/8 + 2*N) bytes (bits*D/8 + 2 per value when N is
+ *           a multiple of 16).
+ * A slot group is the index of a table of level pairs: the decode attention
+ * forms its weighted sums on the matrix cores from it (this bit order is the
+ * library's, not the pages').  d = 128 only.
  */
 size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
 
@@ -283,10 +291,11 @@ size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg
  * logit = the estimator of tq_score_logits, v_mse = nu~ R^T c_v[code]
  * (scale = 1/sqrt(d) for scaled dot-product attention).  q [G][Qg][d]
  * (TQ_F32/TQ_BF16), kpacked: key records for N keys per group, vpacked: value
- * records for N values per group, out float32 [G][Qg][d].  Three launches on
- * the stream: the score kernel into ws, a value pass over key ranges that keeps
- * each range's maximum, normaliser and weighted code sum (in the rotated
- * domain), and a combine that merges the ranges and rotates back with R^T.
+ * records for N values per group, out float32 [G][Qg][d].  Two launches on
+ * the stream: the score kernel with a value pass over its key range (logits
+ * into ws; each range keeps its maximum, normaliser and weighted level sums
+ * in the rotated domain, float16 hi/lo operands on the matrix cores), and a
+ * combine that merges the ranges and rotates back with R^T.
  * ws: tq_attention_workspace_bytes(cb, G, Qg, N) bytes of device memory.
  * Errors: TQ_ERR_ARG (also N == 0 with G*Qg > 0, scale not finite and > 0),
  * TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (d != 128, Qg > 256, N >= 2^28), TQ_ERR_HIP.

@@ -665,7 +665,8 @@ int tq_paged_score(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_
 
 size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N) {
   if (!cb || G < 0 || N < 0) return 0;
-  return size_t(G) * size_t(N) * size_t(cb->bits * cb->d / 8 + 2);
+  // codes in tiles of 16 values (bits * d / 8 bytes per value), then one half norm per value
+  return size_t(G) * (size_t((N + 15) / 16) * 16 * size_t(cb->bits * cb->d / 8) + 2 * size_t(N));
 }
 
 int tq_encode_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G, int64_t N,

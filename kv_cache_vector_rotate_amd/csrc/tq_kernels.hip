@@ -346,29 +346,75 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
 // index is the XOR of d_k over k with (k + 1) divisible by 2^j, and the
 // stored bit j is that XOR the sign (negative levels mirror the positive
 // ones); the top bit is the complement of the sign.
-struct ValOut {
-  uint2 w[4];        // words (2h, 2h+1) of planes 0..BV-1
-  uint32_t norm;     // half(nu) in the low 16 bits
-  int64_t g, n;
-  bool valid;
-};
+//
+// Records are stored per tile of 16 values: slot s of a tile holds
+// coordinate 32 (s / 32) + 16 (s % 2) + (s % 32) / 2 for all 16 values, as
+// eight groups of two values, bit 2 p + i of group q being bit p of the code
+// of value 2 q + i.  The decode attention reads one group as the index of a
+// table of level pairs.
 
+constexpr int value_group(int) { return 2; }
+
+// Tile packing, for all 64 lanes of a wave: wp[p] of lane 16 w + n holds bit
+// p of the codes of value n of the tile at coordinates 32 w .. 32 w + 31 (bit
+// r: coordinate 32 w + r); out receives the lane's BV words of the tile,
+// slots 2 (16 w + n) and 2 (16 w + n) + 1.  First a bit transpose inside each
+// row of 16 lanes: four exchanges, exchange i trading lane bit i for word bit
+// i with lane n ^ 2^i, leave in word bit k + 16 h value k at coordinate
+// 32 w + 16 h + n; then each slot's bits are regrouped value group by value
+// group.
 template <int BV>
-__device__ __forceinline__ void store_vtile(const ValOut& o, int lane, int64_t Ncap,
-                                            uint32_t* __restrict__ planes,
-                                            uint16_t* __restrict__ norms) {
-  if (!o.valid) return;
-  const int h = lane >> 5;
-  uint32_t* pl = planes + (o.g * BV) * Ncap * 4;
+__device__ __forceinline__ void vtile_pack(uint32_t (&wp)[BV], int lane, uint32_t (&out)[BV]) {
+  constexpr int K = value_group(BV);
+  const int n = lane & 15;
 #pragma unroll
-  for (int p = 0; p < BV; ++p) *reinterpret_cast<uint2*>(pl + (p * Ncap + o.n) * 4 + 2 * h) = o.w[p];
-  if (h == 0) norms[o.g * Ncap + o.n] = uint16_t(o.norm);
+  for (int i = 0; i < 4; ++i) {
+    const int s = 1 << i;
+    const uint32_t m = i == 0 ? 0x55555555u : i == 1 ? 0x33333333u : i == 2 ? 0x0F0F0F0Fu : 0x00FF00FFu;
+    const bool low = ((n >> i) & 1) == 0;
+    const uint32_t own = low ? m : ~m;                  // bits this lane keeps
+    const uint32_t rot = low ? uint32_t(32 - s) : uint32_t(s);   // partner's bits move up / down
+#pragma unroll
+    for (int p = 0; p < BV; ++p) {
+      int y;
+      if (i == 0) y = __builtin_amdgcn_mov_dpp(int(wp[p]), 0xB1, 0xF, 0xF, false);       // lane ^ 1
+      else if (i == 1) y = __builtin_amdgcn_mov_dpp(int(wp[p]), 0x4E, 0xF, 0xF, false);  // lane ^ 2
+      else if (i == 2) y = __builtin_amdgcn_ds_swizzle(int(wp[p]), 0x101F);             // lane ^ 4
+      else y = __builtin_amdgcn_ds_swizzle(int(wp[p]), 0x201F);                         // lane ^ 8
+      const uint32_t z = __builtin_amdgcn_alignbit(uint32_t(y), uint32_t(y), rot);
+      wp[p] = (wp[p] & own) | (z & ~own);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < BV; ++j) out[j] = 0u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 16 / K; ++q)
+#pragma unroll
+      for (int p = 0; p < BV; ++p) {
+        const int pos = 16 * BV * h + K * BV * q + K * p;
+        out[pos >> 5] |= __builtin_amdgcn_ubfe(wp[p], 16 * h + K * q, K) << (pos & 31);
+      }
 }
 
+// The tile's words: lane L writes words BV L .. BV L + BV - 1 of tile t of
+// group g (tpg tiles per group).
 template <int BV>
-__device__ __forceinline__ void value_tail(const float (&x)[64], float nu2,
-                                           const DevConsts* __restrict__ cst, int lane, int64_t g,
-                                           int64_t n, bool valid, ValOut& out) {
+__device__ __forceinline__ void store_vwords(const uint32_t (&ow)[BV], int lane, int64_t g, int64_t tpg,
+                                             int64_t t, uint32_t* __restrict__ planes) {
+  uint32_t* dst = planes + ((g * tpg + t) * 64 + lane) * BV;
+#pragma unroll
+  for (int p = 0; p < BV; ++p) dst[p] = ow[p];
+}
+
+// float32 values (two-lane layout, 32 values per wave): each lane leaves its
+// key's plane words h and 2 + h in the wave's LDS area st ([plane][value][word]),
+// and returns half(nu), or 0 for a value below the zero-norm rule.
+template <int BV>
+__device__ __forceinline__ uint32_t value_tail(const float (&x)[64], float nu2,
+                                               const DevConsts* __restrict__ cst, int lane, bool valid,
+                                               uint32_t* st) {
   constexpr int KV = 1 << (BV - 1);    // levels on the positive half
   nu2 = xor32_sum(nu2);
   const float nu = __builtin_amdgcn_sqrtf(nu2);
@@ -378,49 +424,47 @@ __device__ __forceinline__ void value_tail(const float (&x)[64], float nu2,
 #pragma unroll
   for (int k = 0; k < KV - 1; ++k) tu[k] = cst->vtpos[k] * nsd;
   uint32_t wu[2] = {0u, 0u};
-  uint32_t wd[KV > 1 ? KV - 1 : 1][2];
+  uint32_t wb[BV - 1][2];   // pushed magnitude index bits, complemented (see value_tail16)
 #pragma unroll
-  for (int k = 0; k < (KV > 1 ? KV - 1 : 1); ++k) wd[k][0] = wd[k][1] = 0u;
+  for (int j = 0; j < BV - 1; ++j) wb[j][0] = wb[j][1] = 0u;
 #pragma unroll
   for (int r = 0; r < 64; ++r) {
     const int ws = r >> 5;
     const float u = x[r];
     const float a = fabsf(u);
     wu[ws] = push_sign(wu[ws], u);
+    uint64_t bx[BV - 1];
+#pragma unroll
+    for (int j = 0; j < BV - 1; ++j) bx[j] = 0u;
 #pragma unroll
     for (int k = 0; k < KV - 1; ++k) {
       const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
+#pragma unroll
+      for (int j = 0; j < BV - 1; ++j)
+        if (((k + 1) & ((1 << j) - 1)) == 0) bx[j] ^= below;
+    }
+#pragma unroll
+    for (int j = 0; j < BV - 1; ++j) {
       uint64_t co;
       asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3"
-          : "=v"(wd[k][ws]), "=s"(co) : "v"(wd[k][ws]), "s"(below));
+          : "=v"(wb[j][ws]), "=s"(co) : "v"(wb[j][ws]), "s"(bx[j]));
     }
   }
   const bool keep = valid && !zero;
-  uint32_t pw[BV][2];
+  const int h = lane >> 5, kl = lane & 31;
 #pragma unroll
   for (int ws = 0; ws < 2; ++ws) {
     // words were filled oldest-bit-first: bit (r % 32) sits at 31 - r % 32
     const uint32_t sg = __builtin_bitreverse32(wu[ws]);       // 1 = negative
-    pw[BV - 1][ws] = ~sg;
+    uint32_t pw[BV];
+    pw[BV - 1] = ~sg;
 #pragma unroll
-    for (int j = 0; j < BV - 1; ++j) {
-      uint32_t e = 0u;   // XOR of the "below" bits (complements of d_k); odd count
+    for (int j = 0; j < BV - 1; ++j) pw[j] = ~(__builtin_bitreverse32(wb[j][ws]) ^ sg);
+    // x[r] for r < 32 is coordinate 32 h + r (word h), for r >= 32 word 2 + h
 #pragma unroll
-      for (int k = 0; k < KV - 1; ++k)
-        if (((k + 1) & ((1 << j) - 1)) == 0) e ^= __builtin_bitreverse32(wd[k][ws]);
-      pw[j][ws] = ~(e ^ sg);
-    }
+    for (int p = 0; p < BV; ++p) st[(p * 32 + kl) * 4 + 2 * ws + h] = keep ? pw[p] : 0u;
   }
-#pragma unroll
-  for (int p = 0; p < BV; ++p) {
-    // (word h, word 2+h) of each lane -> (words 2h, 2h+1): swap across halves
-    auto pr = __builtin_amdgcn_permlane32_swap(pw[p][0], pw[p][1], false, false);
-    out.w[p] = make_uint2(keep ? uint32_t(pr[0]) : 0u, keep ? uint32_t(pr[1]) : 0u);
-  }
-  out.norm = keep ? uint32_t(f2h_bits(nu)) : 0u;
-  out.g = g;
-  out.n = n;
-  out.valid = valid;
+  return keep ? uint32_t(f2h_bits(nu)) : 0u;
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -729,23 +773,23 @@ __device__ __forceinline__ void finish16(const Pending16& pd, TileOut16& out) {
   out.valid = valid;
 }
 
-// Value records in the 16-key layout: each lane's 32 rotated coordinates
-// give word w of the b level-index planes (same bit rules as value_tail).
+// Value records of a 16-value tile: every lane writes its words of the tile
+// (the tile's values past N are zero), the lanes of the first quarter the
+// half norms of their values.
 template <int BV>
 __device__ __forceinline__ void store_vtile16(const TileOut16& o, int lane, int64_t Ncap,
                                               uint32_t* __restrict__ planes,
                                               uint16_t* __restrict__ norms) {
-  if (!o.valid) return;
-  const int w = lane >> 4;
-  uint32_t* pl = planes + (o.g * BV) * Ncap * 4;
+  uint32_t ow[BV];
 #pragma unroll
-  for (int p = 0; p < BV; ++p) pl[(p * Ncap + o.n) * 4 + w] = o.w[p];
-  if (w == 0) norms[o.g * Ncap + o.n] = uint16_t(o.norm);
+  for (int p = 0; p < BV; ++p) ow[p] = o.w[p];
+  store_vwords<BV>(ow, lane, o.g, (Ncap + 15) / 16, o.n >> 4, planes);
+  if (o.valid && (lane >> 4) == 0) norms[o.g * Ncap + o.n] = uint16_t(o.norm);
 }
 
 template <int BV>
 __device__ __forceinline__ void value_tail16(const f32x4 (&y)[8], float nu2,
-                                             const DevConsts* __restrict__ cst, int64_t g,
+                                             const DevConsts* __restrict__ cst, int lane, int64_t g,
                                              int64_t n, bool valid, TileOut16& out) {
   constexpr int KV = 1 << (BV - 1);    // levels on the positive half
   nu2 = key16_sum(nu2);
@@ -756,33 +800,43 @@ __device__ __forceinline__ void value_tail16(const f32x4 (&y)[8], float nu2,
 #pragma unroll
   for (int k = 0; k < KV - 1; ++k) tu[k] = cst->vtpos[k] * nsd;
   uint32_t wu = 0u;
-  uint32_t wd[KV > 1 ? KV - 1 : 1];
+  uint32_t wb[BV - 1];
 #pragma unroll
-  for (int k = 0; k < (KV > 1 ? KV - 1 : 1); ++k) wd[k] = 0u;
+  for (int j = 0; j < BV - 1; ++j) wb[j] = 0u;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {   // coordinate 32 w + r is value r % 4 of block r / 4
     const float u = y[r >> 2][r & 3];
     const float a = fabsf(u);
     wu = push_sign(wu, u);
+    // bit j of the magnitude index, complemented: the XOR of the "below"
+    // lane masks over k with (k + 1) divisible by 2^j (an odd count), formed
+    // on the scalar unit; one push per bit
+    uint64_t bx[BV - 1];
+#pragma unroll
+    for (int j = 0; j < BV - 1; ++j) bx[j] = 0u;
 #pragma unroll
     for (int k = 0; k < KV - 1; ++k) {
       const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
+#pragma unroll
+      for (int j = 0; j < BV - 1; ++j)
+        if (((k + 1) & ((1 << j) - 1)) == 0) bx[j] ^= below;
+    }
+#pragma unroll
+    for (int j = 0; j < BV - 1; ++j) {
       uint64_t co;
-      asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(wd[k]), "=s"(co) : "v"(wd[k]), "s"(below));
+      asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(wb[j]), "=s"(co) : "v"(wb[j]), "s"(bx[j]));
     }
   }
   const bool keep = valid && !zero;
   // words were filled oldest-bit-first: bit r sits at 31 - r
   const uint32_t sg = __builtin_bitreverse32(wu);       // 1 = negative
-  out.w[BV - 1] = keep ? ~sg : 0u;
+  uint32_t wp[BV], ow[BV];
+  wp[BV - 1] = keep ? ~sg : 0u;
 #pragma unroll
-  for (int j = 0; j < BV - 1; ++j) {
-    uint32_t e = 0u;   // XOR of the "below" bits (complements of d_k); odd count
+  for (int j = 0; j < BV - 1; ++j) wp[j] = keep ? ~(__builtin_bitreverse32(wb[j]) ^ sg) : 0u;
+  vtile_pack<BV>(wp, lane, ow);
 #pragma unroll
-    for (int k = 0; k < KV - 1; ++k)
-      if (((k + 1) & ((1 << j) - 1)) == 0) e ^= __builtin_bitreverse32(wd[k]);
-    out.w[j] = keep ? ~(e ^ sg) : 0u;
-  }
+  for (int j = 0; j < BV; ++j) out.w[j] = ow[j];
   out.norm = keep ? uint32_t(f2h_bits(nu)) : 0u;
   out.g = g;
   out.n = n;
@@ -893,7 +947,7 @@ __global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : (B == 3 ? 2 : 3)) void enc
     uint16_t* nv = static_cast<uint16_t*>(norms_);
     if constexpr (VAL) {
       if (have) store_vtile16<B>(out, lane, Ncap, planes, nv);
-      value_tail16<B>(y, nu2, cst, g, pos + n, valid, out);
+      value_tail16<B>(y, nu2, cst, lane, g, pos + n, valid, out);
       have = true;
     } else {
       if (have) {   // the previous tile's packing runs while this tile's rotation products do
@@ -930,6 +984,7 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     const uint4* __restrict__ frag, const uint32_t* __restrict__ flip, PageMap pm) {
   __shared__ uint4 s_frag[VAL ? 1 : 2048];       // [kc 8][jb 4][lane 64]
   __shared__ uint32_t s_flip[128];
+  __shared__ uint32_t s_vt[VAL ? kEncWaves * 4 * 32 * 4 : 1];   // values: [wave][plane][value][word]
 
   const int tid = threadIdx.x;
   if constexpr (!VAL)
@@ -993,9 +1048,25 @@ __global__ __launch_bounds__(kEncThreads, 2) void encode128_f32_kernel(
     }
     butterfly_rest(x, 2);
     if constexpr (VAL) {
-      ValOut out;
-      value_tail<B>(x, nu2, cst, lane, g, pos + n, valid, out);
-      store_vtile<B>(out, lane, Ncap, planes, static_cast<uint16_t*>(norms_));
+      // the wave's 32 values go out as two tiles of 16 (the second only when
+      // it holds a value): plane words through LDS into the 16-lane order of
+      // the tile packing
+      uint32_t* st = s_vt + wave * (4 * 32 * 4);
+      const uint32_t nh = value_tail<B>(x, nu2, cst, lane, valid, st);
+      if (valid && h == 0) static_cast<uint16_t*>(norms_)[g * Ncap + pos + n] = uint16_t(nh);
+      asm volatile("" ::: "memory");
+      const int64_t n0 = int64_t(tile - gt * tpg) * 32;   // first value of the 32
+      const int64_t tpg16 = (Ncap + 15) / 16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (n0 + 16 * u >= N) break;
+        uint32_t wp[B], ow[B];
+#pragma unroll
+        for (int p = 0; p < B; ++p) wp[p] = st[(p * 32 + 16 * u + (lane & 15)) * 4 + (lane >> 4)];
+        vtile_pack<B>(wp, lane, ow);
+        store_vwords<B>(ow, lane, g, tpg16, (pos + n0) / 16 + u, planes);
+      }
+      asm volatile("" ::: "memory");
     } else {
       TileOut out;
       int64_t dg = g, dn = pos + n;
@@ -1075,7 +1146,7 @@ __device__ __forceinline__ float butterfly_lane32(float y, bool up) {
 // Decode attention fused into the scorer (BV > 0 below): value records of the
 // same keys, the softmax scale and the per-range partial states.
 struct AttnArgs {
-  const uint4* vplanes;    // value planes [G][BV][N] (16 bytes per key and plane)
+  const uint4* vplanes;    // value codes: [G][ceil(N / 16)] tiles of 16 BV 16-byte units
   const uint16_t* vnorms;  // value half norms [G][N]
   float* part;             // per (group, query chunk, range): m[4], Z[4], A[4][128]
   float scale;
@@ -1083,18 +1154,35 @@ struct AttnArgs {
 constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, query chunk, range)
 
 // LDS of the value phase, over the scorer's LDS once its tables are dead.
+template <int BV>
 struct AttnLds {
-  float2 lut[256];            // levels of a coordinate pair by its interleaved plane bit pairs
-  f32x4 w[16][64];            // per wave: weights of the tile's keys, four queries
-  uint4 pl[16][4][64];        // per wave: value plane words of the tile's keys
-  float m[16][4], z[16][4];   // per wave: logit maxima, normaliser parts
+  // level table: entry e (a value pair's 2 BV code bits) holds the halves
+  // hi[2], lo[2] of the two levels, in kCopies copies side by side, lane L
+  // reading copy L % kCopies: the 8-byte reads of 32 lanes hit 64 different
+  // banks whatever the codes are (16 copies at 4 bits: 32 KB)
+  static constexpr int kLutEntries = 1 << (2 * BV);
+  static constexpr int kCopies = BV == 4 ? 16 : 32;
+  static constexpr int kStage = BV * 256 + 8;   // words per wave: 4 of padding, a 64-key tile's codes, 4
+  uint2 lut[kLutEntries * kCopies];
+  uint32_t stage[16][kStage];
+  uint16_t wt[16][8][64];     // per wave: scaled weights of the tile's keys, half hi (row q), lo (row 4 + q)
+  float m[16][4], z[16][4];
   float M[4];                 // range maximum of scale * logit per query
+  float lv[16];               // value levels
 };
-static_assert(sizeof(AttnLds) <= sizeof(ScoreLds), "the value phase reuses the scorer's LDS");
-// the per-wave normaliser parts are written while other waves still read the
-// level table and their own staging slots
-static_assert(offsetof(AttnLds, z) >= offsetof(AttnLds, pl) + sizeof(AttnLds::pl),
-              "z lies past every array read in the value loop");
+
+// Largest float exponent field of the wave's non-negative values (DPP
+// maxima inside each row of 16 lanes, then the four rows), wave-uniform.
+__device__ __forceinline__ uint32_t wave_max_exponent(float v) {
+  uint32_t m = __float_as_uint(v) >> 23;
+  m = std::max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0xB1, 0xF, 0xF, false)));    // lane ^ 1
+  m = std::max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x4E, 0xF, 0xF, false)));    // lane ^ 2
+  m = std::max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x141, 0xF, 0xF, false)));   // 7 - lane in 8
+  m = std::max(m, uint32_t(__builtin_amdgcn_mov_dpp(int(m), 0x140, 0xF, 0xF, false)));   // 15 - lane in 16
+  const uint32_t a = __builtin_amdgcn_readlane(m, 0), b = __builtin_amdgcn_readlane(m, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(m, 32), d = __builtin_amdgcn_readlane(m, 48);
+  return std::max(std::max(a, b), std::max(c, d));
+}
 
 __device__ __forceinline__ float wave_max64(float v) {
 #pragma unroll
@@ -1107,28 +1195,56 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return v;
 }
 
+// Loads of one 64-key tile of the value phase (keys from b): the lane's
+// logits and value norm (clamped to the range), the tile's value codes
+// (BV 16-byte units per lane, clamped to the group's last tile).
+template <int BV>
+__device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, const float* const (&lrow)[4],
+                                           const uint16_t* vn, const uint4* vq, int64_t vlast,
+                                           u32x4 (&cv)[BV], float (&lg)[4], uint32_t& nvb) {
+  const int64_t kn = std::min<int64_t>(b + lane, n1 - 1);
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) lg[qq] = lrow[qq][kn];
+  nvb = vn[kn];
+#pragma unroll
+  for (int j = 0; j < BV; ++j) {
+    const uint4 v = vq[std::min<int64_t>((b >> 4) * 16 * BV + j * 64 + lane, vlast)];
+    cv[j] = u32x4{v.x, v.y, v.z, v.w};
+  }
+}
+
 // Value phase of the fused decode attention, after the range's logits of
 // queries qc*4 .. qc*4+3 are in `logits` (written by this wave for its own
 // tiles) and lmax holds this lane's largest logit per query.  The range's
-// maximum M is exact, so weights exp(scale l - M) need no rescaling.  Per
-// tile, each lane (= key) stages its weights (times the value's half norm)
-// and value plane words in the wave's LDS slot; then lane (h, cq) adds, for
-// the 32 keys of half h, weight x level of its coordinate quad cq (coordinates
-// 4 cq .. 4 cq + 3) for the four queries, the four levels coming from two
-// lookups, one per coordinate pair, indexed by the pair's bits of every plane
-// (a table of 2^(2 BV) float2 entries; measured 2-5% faster than one lookup
-// per quad, whose 2^(4 BV)-entry table costs more to build and conflicts more
-// in LDS).  v_mse = nu~ R^T c_v,
-// so the sums stay in the rotated domain; the range's state goes to `part`
-// and attn_combine128_kernel rotates back.
+// maximum M is exact, so weights exp(scale l - M) need no rescaling.
+// v_mse = nu~ R^T c_v, so the weighted sums stay in the rotated domain: per
+// query and coordinate, sum over keys of w nu~ c_v[code].  They run on the
+// matrix cores, one 16 x 16 x 32 product per 16-value tile and 16 slots: the
+// B operand of lane (values 4 kg .. 4 kg + 3, slot 16 cb + n) is two entries
+// of a table of level pairs indexed by the lane's two value groups in that
+// slot (the levels as half hi[2], lo[2]); the A operand's rows 0..3 hold the weights' halves
+// hi twice (against hi and lo), rows 4..7 their lo once (against hi): float16
+// operands, about 22 bits of every product kept.  The weights w nu~ are
+// scaled by a power of 2 that keeps them under 2^14 (from the largest value
+// norm the wave has seen; its sums are rescaled when that grows), so that
+// the halves lose nothing to the float16 range.  The range's state goes to
+// `part` and attn_combine128_kernel rotates back.
 template <int BV>
 __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lmax)[4], const AttnArgs& aa,
                                                  const DevConsts* __restrict__ cst, const float* logits,
                                                  int64_t g, int qc, int Qg, int64_t N, int64_t n1,
                                                  int64_t first, int64_t ntiles, int64_t stride) {
-  AttnLds& sm = *reinterpret_cast<AttnLds*>(lds_raw);
+  using Lds = AttnLds<BV>;
+  static_assert(sizeof(Lds) <= sizeof(ScoreLds), "the value phase reuses the scorer's LDS");
+  // the per-wave normaliser parts are written while other waves still read
+  // the level table, their staging and their weights
+  static_assert(offsetof(Lds, z) >= offsetof(Lds, wt) + sizeof(Lds::wt), "z lies past the loop's arrays");
+  static_assert(offsetof(Lds, m) >= 16 * 8 * 4 * 16 * 4, "the final sums overlay only table and staging");
+  Lds& sm = *reinterpret_cast<Lds*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint16_t* vn = aa.vnorms + g * N;
+  const float lvg = tid < (1 << BV) ? cst->vlevels[tid] : 0.f;
   float mw[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) mw[qq] = wave_max64(lmax[qq]);
@@ -1139,75 +1255,167 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) sm.m[wave][qq] = mw[qq];
   }
+  if (tid < (1 << BV)) sm.lv[tid] = lvg;
   __syncthreads();
   if (tid < 4) {
-    float m = sm.m[0][tid];
-    for (int w = 1; w < 16; ++w) m = fmaxf(m, sm.m[w][tid]);
-    sm.M[tid] = qc * 4 + tid < Qg ? aa.scale * m : 0.f;
+    float mm = sm.m[0][tid];
+    for (int w = 1; w < 16; ++w) mm = fmaxf(mm, sm.m[w][tid]);
+    sm.M[tid] = qc * 4 + tid < Qg ? aa.scale * mm : 0.f;
   }
-  // level table of coordinate pairs: entry e holds the levels of the two
-  // codes whose plane bits interleave in e (bit 2p: first code, 2p + 1: second)
-  {
-    float2* lut2 = sm.lut;
-    for (int e = tid; e < (1 << (2 * BV)); e += kScoreThreads) {
-      int ca = 0, cb = 0;
+  // level table: value i of entry e has code bit p at bit 2 p + i of e
+  for (int x = tid; x < Lds::kLutEntries * Lds::kCopies; x += kScoreThreads) {
+    const int e = x / Lds::kCopies;
+    float a[2];
 #pragma unroll
-      for (int p = 0; p < BV; ++p) {
-        ca |= ((e >> (2 * p)) & 1) << p;
-        cb |= ((e >> (2 * p + 1)) & 1) << p;
-      }
-      lut2[e] = make_float2(cst->vlevels[ca], cst->vlevels[cb]);
+    for (int i = 0; i < 2; ++i) {
+      int c = 0;
+#pragma unroll
+      for (int p = 0; p < BV; ++p) c |= ((e >> (2 * p + i)) & 1) << p;
+      a[i] = sm.lv[c];
     }
+    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
+    const half2v l = {static_cast<_Float16>(a[0] - static_cast<float>(h[0])),
+                      static_cast<_Float16>(a[1] - static_cast<float>(h[1]))};
+    sm.lut[x] = make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l));
   }
   __syncthreads();
   float M[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) M[qq] = sm.M[qq];
+  // the weights w nu~ are scaled by 2^(140 - E), E the largest exponent
+  // field of the value norms seen so far by this wave: a norm below 2^(E - 126)
+  // times a weight of at most 1 stays under 2^14; when a tile raises E, the
+  // sums so far are scaled down by the same power of 2 (exact)
+  uint32_t erun = 103;   // the smallest non-zero half, 2^-24, has field 103
   const float* lrow[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
-  const uint4* vp = aa.vplanes + g * BV * N;
-  const uint16_t* vn = aa.vnorms + g * N;
-  const int h = lane >> 5, cq = lane & 31, wsel = cq >> 3, sh = 4 * (cq & 7);
-  float acc[4][4] = {};   // [coordinate of the quad][query]
+  const int64_t tpg16 = (N + 15) / 16;
+  const uint4* vq = aa.vplanes + g * tpg16 * 16 * BV;   // the group's codes, 16 BV units per tile
+  const int64_t vlast = tpg16 * 16 * BV - 1;
+  uint32_t* stw = sm.stage[wave];
+  const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds_raw);
+  uint16_t* wtw = &sm.wt[wave][0][0];
+  const int n = lane & 15, kg = lane >> 4;   // B: slot column n, values 4 kg .. 4 kg + 3; A: row n
+  // The lane's values 4 kg .. 4 kg + 3 in slot 16 cb + n are the two groups
+  // 2 kg, 2 kg + 1: 4 BV bits from bit 64 BV cb + 16 BV n + 4 BV kg of a tile.
+  // BV = 3: read 8 bits up in the 32 bits (word rd, word rd + 1) >> sh, so
+  // that each 6-bit index masked in place (bits 8..13) or after a shift is
+  // an entry's byte offset; a field in the low 8 bits of a word takes the
+  // word before it as the low half (the padding covers the first).
+  int rd = 0, sh = 0;
+  if constexpr (BV == 3) {
+    const int bp = 48 * n + 12 * kg, d0 = bp >> 5, o = bp & 31;
+    rd = o < 8 ? d0 - 1 : d0;
+    sh = o < 8 ? o + 24 : o - 8;
+  }
+  constexpr int kEntryShift = BV == 4 ? 7 : 8;   // entry stride: kCopies x 8 bytes
+  const uint32_t cofs = uint32_t(lane % Lds::kCopies) * 8u;
+  const bool row_hi = n < 4, row_any = n < 8;   // A rows: 0..3 hi (twice), 4..7 lo, 8..15 zero
+  f32x4 acc[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float zp[4] = {0.f, 0.f, 0.f, 0.f};
-  const char* plb = reinterpret_cast<const char*>(sm.pl[wave]);
+  // loads of tile t: the key's logits and value norm, the 64 keys' codes
+  u32x4 cv[BV];
+  float lg[4];
+  uint32_t nvb = 0;
+  if (ntiles > 0) attn_fetch<BV>(first, lane, n1, lrow, vn, vq, vlast, cv, lg, nvb);
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t b = first + t * stride;
     const bool valid = b + lane < n1;
-    const int64_t n = valid ? b + lane : n1 - 1;
-    f32x4 wv;
-    const float nv = h2f_bits(vn[n]);
+    const float nvr = h2f_bits(nvb);
+    const uint32_t et = wave_max_exponent(nvr);
+    if (et > erun) {
+      const float down = __uint_as_float((127u - (et - erun)) << 23);
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) acc[cb] *= down;
+      erun = et;
+    }
+    const float nv = nvr * __uint_as_float((267u - erun) << 23);
+    float wq[4];
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      const float e = (valid && qc * 4 + qq < Qg) ? __expf(fmaf(aa.scale, lrow[qq][n], -M[qq])) : 0.f;
+      const float e = (valid && qc * 4 + qq < Qg) ? __expf(fmaf(aa.scale, lg[qq], -M[qq])) : 0.f;
       zp[qq] += e;
-      wv[qq] = e * nv;
+      wq[qq] = e * nv;
     }
-    sm.w[wave][lane] = wv;
+    const half2v h0 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(wq[0], wq[1]));
+    const half2v h1 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(wq[2], wq[3]));
+    const _Float16 wh[4] = {h0[0], h0[1], h1[0], h1[1]};
 #pragma unroll
-    for (int p = 0; p < BV; ++p) sm.pl[wave][p][lane] = vp[p * N + n];
-#pragma unroll 4
-    for (int k = 0; k < 32; ++k) {
-      const int slot = 32 * h + k;
-      const f32x4 w = sm.w[wave][slot];
-      uint32_t x[BV];
+    for (int qq = 0; qq < 4; ++qq) {
+      wtw[qq * 64 + lane] = __builtin_bit_cast(uint16_t, wh[qq]);
+      wtw[(4 + qq) * 64 + lane] =
+          __builtin_bit_cast(uint16_t, static_cast<_Float16>(wq[qq] - static_cast<float>(wh[qq])));
+    }
 #pragma unroll
-      for (int p = 0; p < BV; ++p)
-        x[p] = *reinterpret_cast<const uint32_t*>(plb + (p * 64 + slot) * 16 + 4 * wsel);
-      uint32_t i0 = 0, i1 = 0;
+    for (int j = 0; j < BV; ++j) reinterpret_cast<u32x4*>(stw + 4)[j * 64 + lane] = cv[j];
+    // the next tile's loads fly over this tile's products
+    attn_fetch<BV>(first + std::min<int64_t>(t + 1, ntiles - 1) * stride, lane, n1, lrow, vn, vq, vlast,
+                   cv, lg, nvb);
+    // in steps of four products (16-value tile u = k / 2, slots 16 cb + n for
+    // cb = 4 (k % 2) .. + 3): the four groups' fields, their table entries,
+    // then the products; the next step's fields are requested before this
+    // step's products, so the two LDS round trips of a step overlap the
+    // previous step's products
+    uint32_t fw[4][2];   // BV = 3: the word pair holding the lane's group; else the group itself
+    auto read_fields = [&](int k) __attribute__((always_inline)) {
+      const int u = k >> 1;
+      // BV = 3: one address register per step, the slot blocks at immediate offsets
+      // (an index from the start of the LDS, signed: the slot offsets fold into the reads)
+      int fi = int(stw - l32) + 4 + u * 192 + 96 * (k & 1) + rd;
+      if constexpr (BV == 3) asm volatile("" : "+v"(fi));
 #pragma unroll
-      for (int p = 0; p < BV; ++p) {
-        i0 |= __builtin_amdgcn_ubfe(x[p], sh, 2) << (2 * p);
-        i1 |= __builtin_amdgcn_ubfe(x[p], sh + 2, 2) << (2 * p);
+      for (int c = 0; c < 4; ++c) {
+        const int cb = 4 * (k & 1) + c;
+        if constexpr (BV == 3) {
+          fw[c][0] = l32[fi + 24 * c];
+          fw[c][1] = l32[fi + 24 * c + 1];
+        } else if constexpr (BV == 2) {
+          fw[c][0] = reinterpret_cast<const uint8_t*>(stw + 4)[u * 512 + 4 * (16 * cb + n) + kg];
+        } else {
+          fw[c][0] = reinterpret_cast<const uint16_t*>(stw + 4)[u * 512 + 4 * (16 * cb + n) + kg];
+        }
       }
-      const float2* lut2 = sm.lut;
-      const float2 la = lut2[i0], lc = lut2[i1];
-      const float lv[4] = {la.x, la.y, lc.x, lc.y};
+    };
+    read_fields(0);
+    half8 A;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+    for (int k = 0; k < 8; ++k) {
+      const int u = k >> 1;
+      u32x4 bv[4];
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) acc[c][qq] = fmaf(w[qq], lv[c], acc[c][qq]);
+      for (int c = 0; c < 4; ++c) {
+        uint32_t o0, o1;   // byte offsets of the two pairs' entries
+        if constexpr (BV == 3) {
+          const uint32_t v = __builtin_amdgcn_alignbit(fw[c][1], fw[c][0], sh);
+          o0 = (v & 0x3F00u) | cofs;
+          o1 = ((v >> 6) & 0x3F00u) | cofs;
+        } else if constexpr (BV == 2) {
+          o0 = ((fw[c][0] & 0xFu) << kEntryShift) | cofs;
+          o1 = ((fw[c][0] >> 4) << kEntryShift) | cofs;
+        } else {
+          o0 = ((fw[c][0] & 0xFFu) << kEntryShift) | cofs;
+          o1 = ((fw[c][0] >> 8) << kEntryShift) | cofs;
+        }
+        const char* lb = reinterpret_cast<const char*>(sm.lut);
+        const uint2 e0 = *reinterpret_cast<const uint2*>(lb + o0);
+        const uint2 e1 = *reinterpret_cast<const uint2*>(lb + o1);
+        bv[c] = u32x4{e0.x, e0.y, e1.x, e1.y};
+      }
+      if ((k & 1) == 0) {
+        const uint2 x = *reinterpret_cast<const uint2*>(wtw + (n & 7) * 64 + 16 * u + 4 * kg);
+        const u32x4 av = {row_any ? x.x : 0u, row_hi ? x.x : 0u, row_any ? x.y : 0u, row_hi ? x.y : 0u};
+        A = __builtin_bit_cast(half8, av);
+      }
+      if (k < 7) read_fields(k + 1);
+      __builtin_amdgcn_sched_barrier(0);   // the reads above go out before the products
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int cb = 4 * (k & 1) + c;
+        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8, bv[c]), acc[cb], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -1215,22 +1423,33 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
     const float z = wave_sum64(zp[qq]);
     if (lane == 0) sm.z[wave][qq] = z;
   }
-  __syncthreads();   // every wave is done with the level table and its staging slot
-  float* red = reinterpret_cast<float*>(sm.pl);   // [wave][lane][16]: 64 KB
+  // rows 0..3 (lanes 0..15) and 4..7 (lanes 16..31) of every block: the sums
+  // against the weights' hi and lo halves
+  const float unscale = __uint_as_float((erun - 13u) << 23);   // 2^(E - 140)
+  float tot[8][4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) red[(wave * 64 + lane) * 16 + 4 * c + qq] = acc[c][qq];
+    for (int i = 0; i < 4; ++i)
+      tot[cb][i] = unscale * (acc[cb][i] +
+                              __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(acc[cb][i]), 0x401F)));
+  __syncthreads();   // every wave is done with the level table and its staging
+  float* red = reinterpret_cast<float*>(lds_raw);   // [wave][cb][query][column]: 32 KB
+  if (lane < 16) {
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[((wave * 8 + cb) * 4 + i) * 16 + lane] = tot[cb][i];
+  }
   __syncthreads();
   float* out = aa.part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
   if (tid < 512) {
-    const int qq = tid >> 7, i = tid & 127, quad = i >> 2, c = i & 3;
+    const int qq = tid >> 7, s = tid & 127, cb = s >> 4, col = s & 15;
     float a = 0.f;
 #pragma unroll 4
-    for (int w = 0; w < 16; ++w)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) a += red[(w * 64 + 32 * hh + quad) * 16 + 4 * c + qq];
-    out[8 + qq * 128 + i] = a;
+    for (int w = 0; w < 16; ++w) a += red[((w * 8 + cb) * 4 + qq) * 16 + col];
+    const int c = 32 * (s >> 5) + 16 * (s & 1) + ((s & 31) >> 1);   // the coordinate of slot s
+    out[8 + qq * 128 + c] = a;
   } else if (tid < 516) {
     const int qq = tid - 512;
     float z = 0.f;
@@ -1886,17 +2105,44 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
   const int64_t g = gh / Qg;
   const int h = int(gh - g * Qg), qc = h >> 2, q = h & 3;
   const float* base = part + (g * nqc + qc) * int64_t(splits) * kAttnPart;
-  float M = -INFINITY;
+  // the codebook scalars are requested with the ranges' states
+  const float sc = cst->inv_sqrt_d;
+  const uint32_t dn0 = cst->dneg[lane >> 5], dn1 = cst->dneg[2 + (lane >> 5)];
+  const int din = int(cst->din);   // output rows keep the input coordinates only
+  float M = -INFINITY, Z = 0.f, a0 = 0.f, a1 = 0.f;
+  if (splits <= 8) {   // one pass: every range's state in registers
+    float mv[8], zv[8], x0[8], x1[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s < splits) {
+        const float* ps = base + s * kAttnPart;
+        mv[s] = ps[q];
+        zv[s] = ps[4 + q];
+        x0[s] = ps[8 + q * 128 + lane];
+        x1[s] = ps[8 + q * 128 + 64 + lane];
+        M = fmaxf(M, mv[s]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s < splits) {
+        const float f = __expf(mv[s] - M);
+        Z = fmaf(f, zv[s], Z);
+        a0 = fmaf(f, x0[s], a0);
+        a1 = fmaf(f, x1[s], a1);
+      }
+    }
+  } else {
 #pragma unroll 8
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * kAttnPart + q]);
-  float Z = 0.f, a0 = 0.f, a1 = 0.f;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * kAttnPart + q]);
 #pragma unroll 8
-  for (int s = 0; s < splits; ++s) {
-    const float* ps = base + s * kAttnPart;
-    const float f = __expf(ps[q] - M);
-    Z = fmaf(f, ps[4 + q], Z);
-    a0 = fmaf(f, ps[8 + q * 128 + lane], a0);
-    a1 = fmaf(f, ps[8 + q * 128 + 64 + lane], a1);
+    for (int s = 0; s < splits; ++s) {
+      const float* ps = base + s * kAttnPart;
+      const float f = __expf(ps[q] - M);
+      Z = fmaf(f, ps[4 + q], Z);
+      a0 = fmaf(f, ps[8 + q * 128 + lane], a0);
+      a1 = fmaf(f, ps[8 + q * 128 + 64 + lane], a1);
+    }
   }
   const float inv = 1.0f / Z;
   float y0 = a0 * inv + a1 * inv, y1 = a0 * inv - a1 * inv;
@@ -1906,10 +2152,8 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
   y0 = butterfly_lane<8>(y0, lane & 8);   y1 = butterfly_lane<8>(y1, lane & 8);
   y0 = butterfly_lane<16>(y0, lane & 16); y1 = butterfly_lane<16>(y1, lane & 16);
   y0 = butterfly_lane32(y0, lane & 32);   y1 = butterfly_lane32(y1, lane & 32);
-  const float sc = cst->inv_sqrt_d;
-  const uint32_t f0 = (cst->dneg[lane >> 5] >> (lane & 31)) & 1u;
-  const uint32_t f1 = (cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u;
-  const int din = int(cst->din);   // output rows keep the input coordinates only
+  const uint32_t f0 = (dn0 >> (lane & 31)) & 1u;
+  const uint32_t f1 = (dn1 >> (lane & 31)) & 1u;
   float* o = out + gh * din;
   if (lane < din) o[lane] = (f0 ? -y0 : y0) * sc;
   if (64 + lane < din) o[64 + lane] = (f1 ? -y1 : y1) * sc;
@@ -2092,7 +2336,9 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
                                 int64_t N, void* vpacked, hipStream_t s) {
   const int64_t ntiles = G * ((N + 31) / 32);
   uint32_t* planes = static_cast<uint32_t*>(vpacked);
-  uint16_t* norms = reinterpret_cast<uint16_t*>(planes + G * N * int64_t(cb.bits) * (cb.d / 32));
+  // codes: 16-value tiles of 16 * bits * d / 32 words, then the half norms
+  uint16_t* norms = reinterpret_cast<uint16_t*>(planes + G * ((N + 15) / 16) * 16 * int64_t(cb.bits) *
+                                                             (cb.d / 32));
   if (dtype == 1) {
     const int64_t ntiles16 = G * ((N + 15) / 16);
     const int64_t want = (ntiles16 + kEnc16Waves - 1) / kEnc16Waves;
@@ -2212,8 +2458,8 @@ hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64
   const uint32_t* norms =
       static_cast<const uint32_t*>(kpacked) + G * N * int64_t(cb.bits) * (cb.d / 32);
   const uint4* vpl = static_cast<const uint4*>(vpacked);
-  const uint16_t* vn = reinterpret_cast<const uint16_t*>(static_cast<const uint32_t*>(vpacked) +
-                                                         G * N * int64_t(cb.bits) * (cb.d / 32));
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(
+      static_cast<const uint32_t*>(vpacked) + G * ((N + 15) / 16) * 16 * int64_t(cb.bits) * (cb.d / 32));
   const AttnArgs aa{vpl, vn, part, scale};
   const bool bf = qdtype == 1;
 #define TQ_AT(BB, QB, BVV)                                                                       \

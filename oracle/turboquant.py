@@ -628,17 +628,16 @@ def encode_values(cb: Codebook, values: np.ndarray) -> ValueEncodeResult:
 #   codes: uint32 [G][T][bits * d / 2]: tile t holds values 16 t .. 16 t + 15
 #          (values past N have code 0); its 16 * bits * d bits (bit k is bit
 #          k % 32 of word k // 32) are d slots of 16 * bits bits, slot s holding
-#          coordinate value_slot_coordinate(s).  A slot is a row of groups of
-#          K = value_group_size(bits) values: group q holds values K q .. K q +
-#          K - 1 in K * bits bits, bit K p + i of the group being bit p of the
-#          code of value K q + i.
+#          coordinate value_slot_coordinate(s).  A slot is a row of 8 groups
+#          of K = value_group_size(bits) = 2 values: group q holds values 2 q
+#          and 2 q + 1 in 2 * bits bits, bit 2 p + i of the group being bit p
+#          of the code of value 2 q + i.
 #   norms: uint16 [G][N] = half(nu).
-# So one slot group is the level index of a table of K levels at once.
+# So one slot group is the index of a table of value pairs.
 
 def value_group_size(bits: int) -> int:
-    """Values per slot group: 4 up to 3 bits, 2 from 4 bits (a group spans at
-    most 12 bits)."""
-    return 4 if bits <= 3 else 2
+    """Values per slot group (2: a group is a 2 * bits-bit table index)."""
+    return 2
 
 
 def value_slot_coordinate(s: np.ndarray) -> np.ndarray:

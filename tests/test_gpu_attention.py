@@ -132,6 +132,43 @@ def test_attention_ragged(bits, N, Qg):
     _attention_case(bits, 2, N, Qg, "f32", 1000 + 7 * bits + N + Qg)
 
 
+def test_attention_value_norm_range():
+    """Value norms from 2^-20 to 2^14 (rising and falling along the keys,
+    all tiny, all large): the weights' power-of-2 scale follows the largest
+    norm a wave has seen, and its sums are rescaled when a later tile raises
+    it.  260 groups of 1100 keys put two key tiles on some waves of every
+    range."""
+    rng = np.random.default_rng(77)
+    G, N, Qg = 260, 1100, 4
+    k = _rows(rng, G, N)
+    v = _rows(rng, G, N, outliers=False)
+    v /= np.linalg.norm(v, axis=-1, keepdims=True)
+    ramp = np.linspace(-20.0, 12.0, N)
+    prof = np.empty((G, N))
+    prof[0::4] = ramp
+    prof[1::4] = ramp[::-1]
+    prof[2::4] = -20.0
+    prof[3::4] = 14.0
+    v = (v * np.exp2(prof)[..., None]).astype(np.float32)
+    q = rng.standard_normal((G, Qg, 128)).astype(np.float32)
+    cb = K.Codebook(128, 3)
+    cbo = O.make_codebook(128, 3, 128, 42)
+    print(f"[case] attention value norm range G={G} N={N}", flush=True)
+    kb = K.encode_keys(cb, _dev(k, torch.float32))
+    vb = K.encode_values(cb, _dev(v, torch.float32))
+    qd = _dev(q, torch.float32)
+    out = K.attention_decode(cb, qd, kb, vb, N)
+    lg = K.score_logits(cb, qd, kb, N)
+    torch.cuda.synchronize()
+    vbuf = vb.cpu().numpy()
+    out, lg = out.cpu().numpy().astype(np.float64), lg.cpu().numpy().astype(np.float64)
+    vhat = O.decode_values(cbo, vbuf, G, N)
+    ref = O.attention_from_logits(cbo, lg, vbuf, G, N)
+    tol = attention_tolerance(vhat)
+    err = np.abs(out - ref)
+    assert np.all(err <= tol), f"worst |delta|/tol = {np.max(err / tol):.3g}"
+
+
 def test_attention_bf16_long():
     _attention_case(3, 3, 5000, 4, "bf16", 4242)
 

@@ -57,16 +57,17 @@ def test_value_distortion_matches_max_table(bits):
 
 
 def test_value_record_layout_by_hand():
-    """d = 64, 3 bits (groups of 4 values, 12 bits), N = 2: one tile of 16
+    """d = 64, 3 bits (groups of 2 values, 6 bits), N = 2: one tile of 16
     values, 64 slots of 48 bits = 96 words, then the two half norms.
     Coordinate 33 sits in slot 34 (32 * 1 + 16 * 0 + 2 // 2 = 33) and
-    coordinate 0 in slot 0.  Code 5 of value 1 at coordinate 33: planes 0
-    and 2 of value 1 = bits 4 * 0 + 1 and 4 * 2 + 1 of slot 34, stream bits
-    1633 and 1641 = bits 1 and 9 of word 51.  Code 2 of value 0 at
-    coordinate 0: plane 1 = bit 4 of slot 0 = bit 4 of word 0."""
+    coordinate 0 in slot 0.  Code 5 of value 1 at coordinate 33: value 1 is
+    i = 1 of group 0, planes 0 and 2 = bits 2 * 0 + 1 and 2 * 2 + 1 of slot
+    34, stream bits 48 * 34 + 1 = 1633 and 1637 = bits 1 and 5 of word 51.
+    Code 2 of value 0 at coordinate 0: plane 1 = bit 2 of slot 0 = bit 2 of
+    word 0."""
     d, bits = 64, 3
     cb = O.make_codebook(d, bits, d, 1)
-    assert O.value_group_size(bits) == 4 and O.value_group_size(4) == 2
+    assert O.value_group_size(bits) == 2 and O.value_group_size(4) == 2
     assert O.value_slot_coordinate(34) == 33 and O.value_slot_coordinate(0) == 0
     assert sorted(O.value_slot_coordinate(np.arange(d)).tolist()) == list(range(d))
     codes = np.zeros((1, 2, d), np.uint8)
@@ -77,8 +78,8 @@ def test_value_record_layout_by_hand():
     assert buf.size == O.value_packed_nbytes(cb, 1, 2) == 96 * 4 + 2 * 2
     w = buf[: 96 * 4].view(np.uint32)
     expect = np.zeros(96, np.uint32)
-    expect[51] = (1 << 1) | (1 << 9)
-    expect[0] = 1 << 4
+    expect[51] = (1 << 1) | (1 << 5)
+    expect[0] = 1 << 2
     assert np.array_equal(w, expect)
     assert buf[-4:].view(np.uint16).tolist() == [0x3E00, 0x8000]
     c2, n2 = O.unpack_values(cb, buf, 1, 2)
