@@ -1245,6 +1245,18 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* vn = aa.vnorms + g * N;
   const float lvg = tid < (1 << BV) ? cst->vlevels[tid] : 0.f;
+  const float* lrow[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
+  const int64_t tpg16 = (N + 15) / 16;
+  const uint4* vq = aa.vplanes + g * tpg16 * 16 * BV;   // the group's codes, 16 BV units per tile
+  const int64_t vlast = tpg16 * 16 * BV - 1;
+  // loads of tile t: the key's logits and value norm, the 64 keys' codes;
+  // the first tile's go out now, over the barriers below
+  u32x4 cv[BV];
+  float lg[4];
+  uint32_t nvb = 0;
+  if (ntiles > 0) attn_fetch<BV>(first, lane, n1, lrow, vn, vq, vlast, cv, lg, nvb);
   float mw[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) mw[qq] = wave_max64(lmax[qq]);
@@ -1287,12 +1299,6 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   // times a weight of at most 1 stays under 2^14; when a tile raises E, the
   // sums so far are scaled down by the same power of 2 (exact)
   uint32_t erun = 103;   // the smallest non-zero half, 2^-24, has field 103
-  const float* lrow[4];
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
-  const int64_t tpg16 = (N + 15) / 16;
-  const uint4* vq = aa.vplanes + g * tpg16 * 16 * BV;   // the group's codes, 16 BV units per tile
-  const int64_t vlast = tpg16 * 16 * BV - 1;
   uint32_t* stw = sm.stage[wave];
   const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds_raw);
   uint16_t* wtw = &sm.wt[wave][0][0];
@@ -1316,11 +1322,6 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float zp[4] = {0.f, 0.f, 0.f, 0.f};
-  // loads of tile t: the key's logits and value norm, the 64 keys' codes
-  u32x4 cv[BV];
-  float lg[4];
-  uint32_t nvb = 0;
-  if (ntiles > 0) attn_fetch<BV>(first, lane, n1, lrow, vn, vq, vlast, cv, lg, nvb);
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t b = first + t * stride;
     const bool valid = b + lane < n1;
