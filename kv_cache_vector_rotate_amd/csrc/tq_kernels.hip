@@ -385,17 +385,44 @@ __device__ __forceinline__ void vtile_pack(uint32_t (&wp)[BV], int lane, uint32_
       wp[p] = (wp[p] & own) | (z & ~own);
     }
   }
+  // regrouping: byte j of a word holds the 2-bit units (value pairs) 4 (j % 2)
+  // .. + 3 of slot j / 2; two shift-and-mask steps move a byte's four units
+  // to stride 2 BV bits, and the planes are ORed in at 2 p: block j (8 BV
+  // bits) is then four groups of the slot
+  static_assert(K == 2, "value groups of two");
+  uint32_t blk[4];
 #pragma unroll
-  for (int j = 0; j < BV; ++j) out[j] = 0u;
+  for (int j = 0; j < 4; ++j) {
+    uint32_t acc = 0u;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int q = 0; q < 16 / K; ++q)
-#pragma unroll
-      for (int p = 0; p < BV; ++p) {
-        const int pos = 16 * BV * h + K * BV * q + K * p;
-        out[pos >> 5] |= __builtin_amdgcn_ubfe(wp[p], 16 * h + K * q, K) << (pos & 31);
+    for (int p = 0; p < BV; ++p) {
+      uint32_t x = __builtin_amdgcn_ubfe(wp[p], 8 * j, 8);
+      if constexpr (BV == 2) {
+        x = (x | (x << 4)) & 0x0F0Fu;
+        x = (x | (x << 2)) & 0x3333u;
+      } else if constexpr (BV == 3) {
+        x = (x | (x << 8)) & 0xF00Fu;
+        x = (x | (x << 4)) & 0xC30C3u;
+      } else {
+        x = (x | (x << 12)) & 0x000F000Fu;
+        x = (x | (x << 6)) & 0x03030303u;
       }
+      acc |= x << (2 * p);
+    }
+    blk[j] = acc;
+  }
+  // block j sits at bit 8 BV j of the lane's 32 BV bits
+  if constexpr (BV == 2) {
+    out[0] = blk[0] | (blk[1] << 16);
+    out[1] = blk[2] | (blk[3] << 16);
+  } else if constexpr (BV == 3) {
+    out[0] = blk[0] | (blk[1] << 24);
+    out[1] = (blk[1] >> 8) | (blk[2] << 16);
+    out[2] = (blk[2] >> 16) | (blk[3] << 8);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = blk[j];
+  }
 }
 
 // The tile's words: lane L writes words BV L .. BV L + BV - 1 of tile t of
