@@ -1193,9 +1193,7 @@ struct AttnLds {
   uint2 lut[kLutEntries * kCopies];
   uint32_t stage[16][kStage];
   uint16_t wt[16][8][64];     // per wave: scaled weights of the tile's keys, half hi (row q), lo (row 4 + q)
-  float m[16][4], z[16][4];
-  float M[4];                 // range maximum of scale * logit per query
-  float lv[16];               // value levels
+  float m[16][4], z[16][4];   // per wave: maximum of scale * logit, normaliser
 };
 
 // Largest float exponent field of the wave's non-negative values (DPP
@@ -1211,15 +1209,28 @@ __device__ __forceinline__ uint32_t wave_max_exponent(float v) {
   return std::max(std::max(a, b), std::max(c, d));
 }
 
+// Wave-wide maximum and sum, wave-uniform: DPP inside each row of 16 lanes
+// (lane ^ 1, lane ^ 2, 7 - lane in 8, 15 - lane in 16), then the four rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_lane(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
 __device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
 }
 __device__ __forceinline__ float wave_sum64(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
 }
 
 // Loads of one 64-key tile of the value phase (keys from b): the lane's
@@ -1242,8 +1253,10 @@ __device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, cons
 
 // Value phase of the fused decode attention, after the range's logits of
 // queries qc*4 .. qc*4+3 are in `logits` (written by this wave for its own
-// tiles) and lmax holds this lane's largest logit per query.  The range's
-// maximum M is exact, so weights exp(scale l - M) need no rescaling.
+// tiles) and lmax holds this lane's largest logit per query.  Each wave
+// weighs its keys with exp(scale l - M_w), M_w its own exact maximum (no
+// wait for the other waves), and the workgroup merges the waves' states
+// with exp(M_w - M) at the end.
 // v_mse = nu~ R^T c_v, so the weighted sums stay in the rotated domain: per
 // query and coordinate, sum over keys of w nu~ c_v[code].  They run on the
 // matrix cores, one 16 x 16 x 32 product per 16-value tile and 16 slots: the
@@ -1271,7 +1284,6 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* vn = aa.vnorms + g * N;
-  const float lvg = tid < (1 << BV) ? cst->vlevels[tid] : 0.f;
   const float* lrow[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
@@ -1284,43 +1296,44 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   float lg[4];
   uint32_t nvb = 0;
   if (ntiles > 0) attn_fetch<BV>(first, lane, n1, lrow, vn, vq, vlast, cv, lg, nvb);
-  float mw[4];
+  // the wave's own maximum of scale * logit per query: its weights
+  // exp(scale l - M) are at most 1, and the workgroup's sums merge the
+  // waves' states with exp(M_w - M) at the end
+  float M[4];
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) mw[qq] = wave_max64(lmax[qq]);
-  // this LDS overlays the scorer's tables: nothing is written before every
-  // wave is past them (and past its logit stores)
-  __syncthreads();
-  if (lane == 0) {
+  for (int qq = 0; qq < 4; ++qq) {
+    const float mw = wave_max64(lmax[qq]);
+    M[qq] = qc * 4 + qq < Qg ? aa.scale * mw : 0.f;
+  }
+  // level table: value i of entry e has code bit p at bit 2 p + i of e; the
+  // levels are read now, the entries written once the scorer's LDS is free
+  constexpr int kLutPer = (Lds::kLutEntries * Lds::kCopies + kScoreThreads - 1) / kScoreThreads;
+  float la[kLutPer][2];
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) sm.m[wave][qq] = mw[qq];
-  }
-  if (tid < (1 << BV)) sm.lv[tid] = lvg;
-  __syncthreads();
-  if (tid < 4) {
-    float mm = sm.m[0][tid];
-    for (int w = 1; w < 16; ++w) mm = fmaxf(mm, sm.m[w][tid]);
-    sm.M[tid] = qc * 4 + tid < Qg ? aa.scale * mm : 0.f;
-  }
-  // level table: value i of entry e has code bit p at bit 2 p + i of e
-  for (int x = tid; x < Lds::kLutEntries * Lds::kCopies; x += kScoreThreads) {
-    const int e = x / Lds::kCopies;
-    float a[2];
+  for (int j = 0; j < kLutPer; ++j) {
+    const int e = (tid + j * kScoreThreads) / Lds::kCopies;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int c = 0;
 #pragma unroll
       for (int p = 0; p < BV; ++p) c |= ((e >> (2 * p + i)) & 1) << p;
-      a[i] = sm.lv[c];
+      la[j][i] = e < Lds::kLutEntries ? cst->vlevels[c] : 0.f;
     }
-    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
-    const half2v l = {static_cast<_Float16>(a[0] - static_cast<float>(h[0])),
-                      static_cast<_Float16>(a[1] - static_cast<float>(h[1]))};
-    sm.lut[x] = make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l));
+  }
+  // this LDS overlays the scorer's tables: nothing is written before every
+  // wave is past them (and past its logit stores)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kLutPer; ++j) {
+    const int x = tid + j * kScoreThreads;
+    if (x < Lds::kLutEntries * Lds::kCopies) {
+      const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(la[j][0], la[j][1]));
+      const half2v l = {static_cast<_Float16>(la[j][0] - static_cast<float>(h[0])),
+                        static_cast<_Float16>(la[j][1] - static_cast<float>(h[1]))};
+      sm.lut[x] = make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l));
+    }
   }
   __syncthreads();
-  float M[4];
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) M[qq] = sm.M[qq];
   // the weights w nu~ are scaled by 2^(140 - E), E the largest exponent
   // field of the value norms seen so far by this wave: a norm below 2^(E - 126)
   // times a weight of at most 1 stays under 2^14; when a tile raises E, the
@@ -1449,7 +1462,10 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const float z = wave_sum64(zp[qq]);
-    if (lane == 0) sm.z[wave][qq] = z;
+    if (lane == 0) {
+      sm.z[wave][qq] = z;
+      sm.m[wave][qq] = M[qq];
+    }
   }
   // rows 0..3 (lanes 0..15) and 4..7 (lanes 16..31) of every block: the sums
   // against the weights' hi and lo halves
@@ -1471,19 +1487,24 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   }
   __syncthreads();
   float* out = aa.part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
-  if (tid < 512) {
-    const int qq = tid >> 7, s = tid & 127, cb = s >> 4, col = s & 15;
-    float a = 0.f;
-#pragma unroll 4
-    for (int w = 0; w < 16; ++w) a += red[((w * 8 + cb) * 4 + qq) * 16 + col];
-    const int c = 32 * (s >> 5) + 16 * (s & 1) + ((s & 31) >> 1);   // the coordinate of slot s
-    out[8 + qq * 128 + c] = a;
-  } else if (tid < 516) {
-    const int qq = tid - 512;
-    float z = 0.f;
-    for (int w = 0; w < 16; ++w) z += sm.z[w][qq];
-    out[qq] = sm.M[qq];
-    out[4 + qq] = z;
+  if (tid < 516) {
+    const int qq = tid < 512 ? tid >> 7 : tid - 512;
+    float mm = sm.m[0][qq];
+    for (int w = 1; w < 16; ++w) mm = fmaxf(mm, sm.m[w][qq]);
+    // waves without keys hold M = -inf and no sums
+    auto f = [&](int w) { const float mw = sm.m[w][qq]; return mw == -INFINITY ? 0.f : __expf(mw - mm); };
+    if (tid < 512) {
+      const int s = tid & 127, cb = s >> 4, col = s & 15;
+      float a = 0.f;
+      for (int w = 0; w < 16; ++w) a = fmaf(f(w), red[((w * 8 + cb) * 4 + qq) * 16 + col], a);
+      const int c = 32 * (s >> 5) + 16 * (s & 1) + ((s & 31) >> 1);   // the coordinate of slot s
+      out[8 + qq * 128 + c] = a;
+    } else {
+      float z = 0.f;
+      for (int w = 0; w < 16; ++w) z = fmaf(f(w), sm.z[w][qq], z);
+      out[qq] = mm;
+      out[4 + qq] = z;
+    }
   }
 }
 
