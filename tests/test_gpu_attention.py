@@ -47,6 +47,9 @@ def _encode_values_checked(cb, cbo, v, dtype):
     buf = vb.cpu().numpy()
     codes, nu16 = O.unpack_values(cbo, buf, G, N)
     check_values(cbo, v.reshape(-1, d), codes.reshape(-1, d), nu16.reshape(-1))
+    # the layout itself, padding of the last tile included: the buffer is the
+    # oracle's packing of the codes and norms it holds, byte for byte
+    assert np.array_equal(buf.view(np.uint8), O.pack_values(cbo, codes, nu16))
     return vb, buf
 
 
