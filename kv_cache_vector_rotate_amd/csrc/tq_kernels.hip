@@ -353,8 +353,6 @@ __device__ __forceinline__ void encode_tail(const float (&x)[64], float nu2, con
 // of value 2 q + i.  The decode attention reads one group as the index of a
 // table of level pairs.
 
-constexpr int value_group(int) { return 2; }
-
 // Tile packing, for all 64 lanes of a wave: wp[p] of lane 16 w + n holds bit
 // p of the codes of value n of the tile at coordinates 32 w .. 32 w + 31 (bit
 // r: coordinate 32 w + r); out receives the lane's BV words of the tile,
@@ -365,7 +363,6 @@ constexpr int value_group(int) { return 2; }
 // group.
 template <int BV>
 __device__ __forceinline__ void vtile_pack(uint32_t (&wp)[BV], int lane, uint32_t (&out)[BV]) {
-  constexpr int K = value_group(BV);
   const int n = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -389,7 +386,6 @@ __device__ __forceinline__ void vtile_pack(uint32_t (&wp)[BV], int lane, uint32_
   // .. + 3 of slot j / 2; two shift-and-mask steps move a byte's four units
   // to stride 2 BV bits, and the planes are ORed in at 2 p: block j (8 BV
   // bits) is then four groups of the slot
-  static_assert(K == 2, "value groups of two");
   uint32_t blk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
