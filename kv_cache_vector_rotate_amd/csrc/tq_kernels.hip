@@ -630,7 +630,7 @@ __device__ __forceinline__ float key16_sum(float v) {
 // issued, so no wave waits for its own matrix products to drain.
 struct Pending16 {
   f32x4 acc[8];
-  uint32_t wu, wd[3];
+  uint32_t wu, wd[2];   // sign word; magnitude index bits (complemented), pushed
   float rho2, nu;
   bool zero, valid;
   int64_t g, n;
@@ -656,10 +656,11 @@ __device__ __forceinline__ void quant_sketch16(const f32x4 (&y)[8], float nu2, c
   int fl_off = lane;
   asm volatile("" : "+v"(fl_off));
   const half8* fh = reinterpret_cast<const half8*>(s_frag) + fl_off;
+  constexpr int NB = B - 1;   // magnitude index bits
   uint32_t wu = 0u;
-  uint32_t wd[K > 1 ? K - 1 : 1];
+  uint32_t wd[NB > 0 ? NB : 1];
 #pragma unroll
-  for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k] = 0u;
+  for (int j = 0; j < (NB > 0 ? NB : 1); ++j) wd[j] = 0u;
   f32x4 acc[8] = {};
   float rho2 = 0.f;
   float mone = -1.0f;
@@ -678,15 +679,26 @@ __device__ __forceinline__ void quant_sketch16(const f32x4 (&y)[8], float nu2, c
         const float a = fabsf(u);
         wu = push_sign(wu, u);
         float mag = ec.cpos[0];
+        // one compare per positive threshold: its lane mask selects the
+        // level; bit j of the magnitude index (complemented) is the XOR of
+        // the masks over k with (k + 1) divisible by 2^j, formed on the
+        // scalar unit and pushed by the carry-in of a doubling add
+        uint64_t bx[NB > 0 ? NB : 1];
+#pragma unroll
+        for (int j = 0; j < (NB > 0 ? NB : 1); ++j) bx[j] = 0u;
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) {
-          // the lane mask of one compare is the carry-in of a doubling add
-          // (pushes the bit) and the select of the level
           const uint64_t below = __builtin_amdgcn_ballot_w64(a < tu[k]);
-          uint64_t co;
           const float up = ec.cpos[k + 1];
-          asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(wd[k]), "=s"(co) : "v"(wd[k]), "s"(below));
           asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(mag) : "v"(up), "v"(mag), "s"(below));
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            if (((k + 1) & ((1 << j) - 1)) == 0) bx[j] ^= below;
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          uint64_t co;
+          asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(wd[j]), "=s"(co) : "v"(wd[j]), "s"(bx[j]));
         }
         const float yh = copysignf(mag, u);
         // negated residual 2^12 (c[code] - y); the table holds -S R^T
@@ -697,8 +709,8 @@ __device__ __forceinline__ void quant_sketch16(const f32x4 (&y)[8], float nu2, c
     }
   };
   auto pin_words = [&]() {
-    if constexpr (K > 2) {
-      asm volatile("" : "+v"(wu), "+v"(wd[0]), "+v"(wd[1]), "+v"(wd[2]));
+    if constexpr (NB > 1) {
+      asm volatile("" : "+v"(wu), "+v"(wd[0]), "+v"(wd[1]));
     } else {
       asm volatile("" : "+v"(wu), "+v"(wd[0]));
     }
@@ -741,7 +753,7 @@ __device__ __forceinline__ void quant_sketch16(const f32x4 (&y)[8], float nu2, c
   for (int b = 0; b < 8; ++b) pd.acc[b] = acc[b];
   pd.wu = wu;
 #pragma unroll
-  for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) pd.wd[k] = wd[k];
+  for (int j = 0; j < NB; ++j) pd.wd[j] = wd[j];
   pd.rho2 = rho2;
   pd.nu = nu;
   pd.zero = zero;
@@ -765,19 +777,11 @@ __device__ __forceinline__ void finish16(const Pending16& pd, TileOut16& out) {
   const bool keep = valid && !zero;
   const uint32_t u_ = __builtin_bitreverse32(wu);
   uint32_t pw[P - 1];
-  if constexpr (B == 1) {
-    pw[0] = ~u_;
-  } else if constexpr (B == 2) {
-    pw[1] = ~u_;
-    pw[0] = ~(u_ ^ __builtin_bitreverse32(wd[0]));
-  } else {
-    const uint32_t d0 = __builtin_bitreverse32(wd[0]);
-    const uint32_t d1 = __builtin_bitreverse32(wd[1]);
-    const uint32_t d2 = __builtin_bitreverse32(wd[2]);
-    pw[2] = ~u_;
-    pw[1] = ~(u_ ^ d1);
-    pw[0] = ~(u_ ^ d0 ^ d1 ^ d2);
-  }
+  // stored bit j = magnitude index bit j XOR the sign; the top plane is the
+  // complement of the sign (the pushed bits are complemented, odd counts)
+  pw[P - 2] = ~u_;
+#pragma unroll
+  for (int j = 0; j < P - 2; ++j) pw[j] = ~(u_ ^ __builtin_bitreverse32(wd[j]));
 #pragma unroll
   for (int p = 0; p < P - 1; ++p) out.w[p] = keep ? pw[p] : 0u;
 
@@ -870,10 +874,10 @@ __device__ __forceinline__ void value_tail16(const f32x4 (&y)[8], float nu2,
 // PAGED: keys are the G = 1 x N rows of a [groups][T] append whose records go
 // to the pool pages the page map gives (Ncap = page size); a 16-key tile then
 // holds rows of up to 16 different groups.
-// Keys run three workgroups per CU (168 VGPRs) except at B = 3, whose extra
-// thresholds and code words need more registers: two workgroups per CU.
+// Keys run three workgroups per CU (at most 168 VGPRs); the paged form at
+// B = 3 (page-map registers beside the extra thresholds) runs two.
 template <int B, bool VAL, bool PAGED = false>
-__global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : (B == 3 ? 2 : 3)) void encode128_bf16_t16_kernel(
+__global__ __launch_bounds__(kEnc16Threads, VAL ? 4 : (PAGED && B == 3 ? 2 : 3)) void encode128_bf16_t16_kernel(
     const uint16_t* __restrict__ keys, int64_t G, int64_t N, int64_t Ncap, int64_t pos,
     uint32_t* __restrict__ planes, void* __restrict__ norms_,
     const DevConsts* __restrict__ cst, const uint4* __restrict__ frag,
@@ -2347,7 +2351,7 @@ hipError_t launch_encode(const Codebook& cb, const void* keys, int dtype, int64_
   if (dtype == 1) {
     const int64_t ntiles16 = G * ((N + 15) / 16);
     const int64_t want = (ntiles16 + kEnc16Waves - 1) / kEnc16Waves;
-    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * (cb.bits == 4 ? 2 : 3)));
+    const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 3));
     const uint16_t* kb = static_cast<const uint16_t*>(keys);
 #define TQ_ENCB(BB)                                                                              \
   hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, false>), dim3(grid), dim3(kEnc16Threads), 0, s, kb, G, N, \
