@@ -1262,9 +1262,9 @@ __device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, cons
 // matrix cores, one 16 x 16 x 32 product per 16-value tile and 16 slots: the
 // B operand of lane (values 4 kg .. 4 kg + 3, slot 16 cb + n) is two entries
 // of a table of level pairs indexed by the lane's two value groups in that
-// slot (the levels as half hi[2], lo[2]); the A operand's rows 0..3 hold the weights' halves
-// hi twice (against hi and lo), rows 4..7 their lo once (against hi): float16
-// operands, about 22 bits of every product kept.  The weights w nu~ are
+// slot (the levels as half hi[2], lo[2]); the A operand's rows 0..3 hold the
+// weights' halves hi twice (against hi and lo), rows 4..7 their lo once
+// (against hi): float16 operands, about 22 bits of every product kept.  The weights w nu~ are
 // scaled by a power of 2 that keeps them under 2^14 (from the largest value
 // norm the wave has seen; its sums are rescaled when that grows), so that
 // the halves lose nothing to the float16 range.  The range's state goes to
@@ -1443,10 +1443,14 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
         const char* lb = reinterpret_cast<const char*>(sm.lut);
         const uint2 e0 = *reinterpret_cast<const uint2*>(lb + o0);
         const uint2 e1 = *reinterpret_cast<const uint2*>(lb + o1);
+        // K order of the lane's 8 products: hi(v0) hi(v1) lo(v0) lo(v1) hi(v2)
+        // hi(v3) lo(v2) lo(v3) for its values v0..v3 = 4 kg .. 4 kg + 3
         bv[c] = u32x4{e0.x, e0.y, e1.x, e1.y};
       }
       if ((k & 1) == 0) {
         const uint2 x = *reinterpret_cast<const uint2*>(wtw + (n & 7) * 64 + 16 * u + 4 * kg);
+        // the same K order: row q < 4 holds w_hi(v0, v1) twice, then w_hi(v2, v3)
+        // twice; row 4 + q w_lo(v0, v1), 0, w_lo(v2, v3), 0 (hi levels only)
         const u32x4 av = {row_any ? x.x : 0u, row_hi ? x.x : 0u, row_any ? x.y : 0u, row_hi ? x.y : 0u};
         A = __builtin_bit_cast(half8, av);
       }
