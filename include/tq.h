@@ -281,6 +281,32 @@ size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
 int tq_encode_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G,
                      int64_t N, void* vpacked, void* stream);
 
+/*
+ * Append new values to a value cache at write time, the value side of
+ * tq_append_keys (the Qiita explainer's API table lists an MSE compressor for
+ * value vectors beside the key compressor; the ICLR 2026 paper digest,
+ * "実装のポイント", has compression happen when the cache is written).
+ * values: [G][T][d] device rows (TQ_F32 or TQ_BF16).  vpacked: a value cache
+ * laid out as above for G groups of Ncap records
+ * (tq_value_packed_bytes(cb, G, Ncap)).  Value t of group g is coded by the
+ * rules of tq_encode_values and written to record pos + t of group g (its
+ * level indices into its tile, its half norm); no other record is touched,
+ * also not the other values of a tile it shares.  Whole tiles (pos and T
+ * multiples of 16) are written by the tile encoder of tq_encode_values
+ * (identical records); other shapes by a latency kernel, one value per wave
+ * (float32 rotation; its level indices equal tq_encode_values's except where
+ * a rotated coordinate lies within rounding of a threshold) that sets the
+ * value's bits with atomic OR / AND.  Records pos .. pos+T-1 of one call may
+ * share tiles with records another call on another stream writes at the same
+ * time: the bit updates do not race, but the caller orders appends before the
+ * attention that reads them.  Requires 0 <= pos and pos + T <= Ncap.
+ * G*T == 0 is a no-op; nothing is allocated.  d = 128 only.
+ * Errors: TQ_ERR_ARG (also pos + T > Ncap), TQ_ERR_UNSUPPORTED (d != 128,
+ * G*T >= 2^33), TQ_ERR_HIP.
+ */
+int tq_append_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G, int64_t T,
+                     void* vpacked, int64_t Ncap, int64_t pos, void* stream);
+
 /* (Library bookkeeping.)  Workspace bytes of tq_attention_decode (the logits plus per-range partial
  * sums); 0 on bad arguments or d != 128. */
 size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N);
@@ -303,6 +329,23 @@ size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg
 int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G,
                         int32_t Qg, const void* kpacked, const void* vpacked, int64_t N,
                         float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tq_attention_decode over the first len records of each group of a key
+ * cache and a value cache that hold Ncap records per group (the layouts
+ * tq_append_keys and tq_append_values write into): the decode step of a
+ * serving loop that compresses each token as it is cached [ICLR 2026 paper
+ * digest, "実装のポイント"].  Same launches and same results as
+ * tq_attention_decode on a buffer of len records; records past len are not
+ * weighed (their codes may hold anything, their norms are not read).
+ * ws: tq_attention_workspace_bytes(cb, G, Qg, len) bytes.  Requires
+ * 1 <= len <= Ncap when G*Qg > 0.
+ * Errors: TQ_ERR_ARG (also len == 0 or len > Ncap), TQ_ERR_WORKSPACE,
+ * TQ_ERR_UNSUPPORTED (d != 128, Qg > 256, Ncap >= 2^28), TQ_ERR_HIP.
+ */
+int tq_attention_cache(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                       const void* kpacked, const void* vpacked, int64_t Ncap, int64_t len, float scale,
+                       float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tq_attention_decode without a workspace argument, for callers that cannot

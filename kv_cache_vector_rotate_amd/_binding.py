@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = (
     "tq_attention_decode", "tq_codebook_tables_ex", "tq_make_codebook_ex", "tq_rotation_dim",
     "tq_clock_probe", "tq_stream_probe", "tq_score_stream_probe",
     "tq_attention_decode_noalloc", "tq_attention_noalloc_max_bytes",
-    "tq_paged_append_keys", "tq_paged_score",
+    "tq_paged_append_keys", "tq_paged_score", "tq_append_values", "tq_attention_cache",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -59,6 +59,9 @@ _SIGS = {
     "tq_attention_workspace_bytes": (_c_sz, [_vp, _c_i64, _c_i32, _c_i64]),
     "tq_attention_decode": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
                                            ctypes.c_float, _vp, _vp, _c_sz, _vp]),
+    "tq_append_values": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp]),
+    "tq_attention_cache": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64, _c_i64,
+                                          ctypes.c_float, _vp, _vp, _c_sz, _vp]),
     "tq_last_hip_error": (ctypes.c_int, []),
     "tq_attention_decode_noalloc": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64,
                                                    ctypes.c_float, _vp, _vp]),
@@ -358,6 +361,20 @@ def encode_values(cb: Codebook, values, out=None):
     return out
 
 
+def append_values(cb: Codebook, values, vpacked, Ncap: int, pos: int):
+    """Encode values [G, T, d] into records pos .. pos+T-1 of each group of a
+    value cache holding Ncap records per group (in place)."""
+    _need_cuda(values, "values")
+    _need_cuda(vpacked, "vpacked")
+    G, T, d = values.shape
+    if d != cb.d:
+        raise ValueError("value dimension does not match the codebook")
+    _need_bytes(vpacked, value_packed_nbytes(cb, G, Ncap), "vpacked (Ncap records per group)")
+    _check(library().tq_append_values(cb.handle, _ptr(values), _dtype_code(values), G, T, _ptr(vpacked),
+                                      Ncap, pos, _stream()), "tq_append_values")
+    return vpacked
+
+
 def attention_workspace_nbytes(cb: Codebook, G: int, Qg: int, N: int) -> int:
     return int(library().tq_attention_workspace_bytes(cb.handle, G, Qg, N))
 
@@ -384,6 +401,34 @@ def attention_decode(cb: Codebook, q, kpacked, vpacked, N: int, scale=None, out=
                                          _ptr(vpacked), N, scale, _ptr(out), _ptr(ws),
                                          ws.numel() * ws.element_size(), _stream()),
            "tq_attention_decode")
+    return out
+
+
+def attention_cache(cb: Codebook, q, kpacked, vpacked, Ncap: int, length: int, scale=None, out=None,
+                    ws=None):
+    """attention_decode over the first `length` records of a key cache and a
+    value cache of Ncap records per group each -> float32 [G, Qg, d]."""
+    torch = _torch()
+    for t, name in ((q, "q"), (kpacked, "kpacked"), (vpacked, "vpacked")):
+        _need_cuda(t, name)
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    if not 0 < length <= Ncap:
+        raise ValueError("length must lie in [1, Ncap]")
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    _need_bytes(kpacked, packed_nbytes(cb, G, Ncap), "kpacked (Ncap records per group)")
+    _need_bytes(vpacked, value_packed_nbytes(cb, G, Ncap), "vpacked (Ncap records per group)")
+    if out is None:
+        out = torch.empty((G, Qg, d), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * d)
+    wsb = attention_workspace_nbytes(cb, G, Qg, length)
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check(library().tq_attention_cache(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(kpacked),
+                                        _ptr(vpacked), Ncap, length, scale, _ptr(out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream()),
+           "tq_attention_cache")
     return out
 
 

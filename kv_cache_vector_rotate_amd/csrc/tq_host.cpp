@@ -683,6 +683,22 @@ int tq_encode_values(const tq_codebook* cb, const void* values, int32_t dtype, i
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 
+int tq_append_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G, int64_t T,
+                     void* vpacked, int64_t Ncap, int64_t pos, void* stream) {
+  if (!cb || G < 0 || T < 0 || Ncap < 0 || pos < 0 || (dtype != TQ_F32 && dtype != TQ_BF16))
+    return TQ_ERR_ARG;
+  if (pos > Ncap || T > Ncap - pos) return TQ_ERR_ARG;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (!values || !vpacked || !aligned16(values) || !aligned16(vpacked)) return TQ_ERR_ARG;
+  if (cb->d != 128) return TQ_ERR_UNSUPPORTED;
+  if (G * ((T + 31) / 32) >= (int64_t(1) << 31) || G * T >= (int64_t(1) << 33)) return TQ_ERR_UNSUPPORTED;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_append_values(*cb, values, dtype, G, T, vpacked, Ncap, pos,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
 size_t tq_attention_workspace_bytes(const tq_codebook* cb, int64_t G, int32_t Qg, int64_t N) {
   if (!cb || G <= 0 || Qg <= 0 || N <= 0 || cb->d != 128) return 0;
   return tq::attention_workspace_bytes(*cb, G, Qg, N);
@@ -705,8 +721,32 @@ int tq_attention_decode(const tq_codebook* cb, const void* q, int32_t q_dtype, i
   if (!ws || !aligned16(ws) || ws_bytes < need) return TQ_ERR_WORKSPACE;
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
-  hipError_t e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, N, scale, out, ws,
+  hipError_t e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, N, N, scale, out, ws,
                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_attention_cache(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                       const void* kpacked, const void* vpacked, int64_t Ncap, int64_t len, float scale,
+                       float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!cb || G < 0 || Qg < 0 || Ncap < 0 || len < 0 || len > Ncap ||
+      (q_dtype != TQ_F32 && q_dtype != TQ_BF16))
+    return TQ_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return TQ_ERR_ARG;
+  if (cb->d != 128 || Qg > 256 || G > INT32_MAX || G * Qg > INT32_MAX ||
+      Ncap >= (int64_t(1) << 28))
+    return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || Qg == 0) return TQ_OK;
+  if (len == 0) return TQ_ERR_ARG;   // softmax over no keys
+  if (!q || !kpacked || !vpacked || !out || !aligned16(q) || !aligned16(kpacked) ||
+      !aligned16(vpacked) || !aligned16(out))
+    return TQ_ERR_ARG;
+  const size_t need = tq::attention_workspace_bytes(*cb, G, Qg, len);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  int rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, len, Ncap, scale, out,
+                                      ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 
@@ -729,7 +769,7 @@ int tq_attention_decode_noalloc(const tq_codebook* cb, const void* q, int32_t q_
   void* ws = nullptr;
   hipError_t e = tq::scratch_address(&ws);
   if (e != hipSuccess) return hip_fail(e);
-  e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, N, scale, out, ws,
+  e = tq::launch_attention(*cb, q, q_dtype, G, Qg, kpacked, vpacked, N, N, scale, out, ws,
                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }

@@ -79,7 +79,8 @@ hipError_t launch_decode(const Codebook& cb, const void* packed, int64_t G, int6
 hipError_t launch_dense_bf16(const void* q, const void* keys, int64_t G, int Qg, int64_t N, int d,
                              float* logits, hipStream_t s);
 size_t score_workspace_bytes(const Codebook& cb, int64_t G, int Qg);
-// Value records (d = 128): planes uint32 [G][bits][N][4], then uint16 half norms [G][N].
+// Value records (d = 128): codes in 16-value tiles [G][ceil(N/16)][bits*64] uint32, then uint16
+// half norms [G][N].
 hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtype, int64_t G,
                                 int64_t N, void* vpacked, hipStream_t s);
 // Decode attention over packed keys and values (d = 128): logits into the
@@ -90,8 +91,12 @@ size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t 
 constexpr size_t kScratchBytes = size_t(32) << 20;
 hipError_t scratch_address(void** ptr);
 hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
-                            const void* kpacked, const void* vpacked, int64_t N, float scale,
-                            float* out, void* ws, hipStream_t s);
+                            const void* kpacked, const void* vpacked, int64_t N, int64_t Ncap,
+                            float scale, float* out, void* ws, hipStream_t s);
+// Write-time value append (d = 128): T values per group into records pos ..
+// pos + T - 1 of a value cache of Ncap records per group.
+hipError_t launch_append_values(const Codebook& cb, const void* values, int dtype, int64_t G, int64_t T,
+                                void* vpacked, int64_t Ncap, int64_t pos, hipStream_t s);
 // d = 1024 (tq_wide.hip)
 hipError_t launch_decode_wide(const Codebook& cb, const void* packed, int64_t G, int64_t N, void* out,
                               int odtype, hipStream_t s);

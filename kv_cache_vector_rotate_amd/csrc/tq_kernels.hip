@@ -1173,10 +1173,11 @@ __device__ __forceinline__ float butterfly_lane32(float y, bool up) {
 // Decode attention fused into the scorer (BV > 0 below): value records of the
 // same keys, the softmax scale and the per-range partial states.
 struct AttnArgs {
-  const uint4* vplanes;    // value codes: [G][ceil(N / 16)] tiles of 16 BV 16-byte units
-  const uint16_t* vnorms;  // value half norms [G][N]
+  const uint4* vplanes;    // value codes: [G][ceil(vcap / 16)] tiles of 16 BV 16-byte units
+  const uint16_t* vnorms;  // value half norms [G][vcap]
   float* part;             // per (group, query chunk, range): m[4], Z[4], A[4][128]
   float scale;
+  int64_t vcap;            // value records per group (N, or a cache's capacity)
 };
 constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, query chunk, range)
 
@@ -1283,11 +1284,11 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   Lds& sm = *reinterpret_cast<Lds*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint16_t* vn = aa.vnorms + g * N;
+  const uint16_t* vn = aa.vnorms + g * aa.vcap;
   const float* lrow[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
-  const int64_t tpg16 = (N + 15) / 16;
+  const int64_t tpg16 = (aa.vcap + 15) / 16;
   const uint4* vq = aa.vplanes + g * tpg16 * 16 * BV;   // the group's codes, 16 BV units per tile
   const int64_t vlast = tpg16 * 16 * BV - 1;
   // loads of tile t: the key's logits and value norm, the 64 keys' codes;
@@ -2212,6 +2213,83 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
   if (64 + lane < din) o[64 + lane] = (f1 ? -y1 : y1) * sc;
 }
 
+// ============================================================== value append, d = 128
+// Latency path of the write-time value append: one value per wave.  The wave
+// rotates the value (the float32 butterfly of the key append: lane L holds
+// coordinates L and L + 64), forms each coordinate's level index by the
+// value encoders' rules (compares of |u| against t nu sqrt(d), stored bit j =
+// bit j of the magnitude index XOR the sign, the top bit the complement of
+// the sign) and writes it into the value's 16-value tile bit by bit with
+// atomic OR / AND: the tile's other values are not touched.
+template <int BV, bool BF16>
+__device__ __forceinline__ void append_value128(const void* __restrict__ values, int64_t r, int64_t T,
+                                                int64_t Ncap, int64_t pos, int lane,
+                                                uint32_t* __restrict__ codes, uint16_t* __restrict__ norms,
+                                                const DevConsts* __restrict__ cst) {
+  constexpr int KV = 1 << (BV - 1);   // levels on the positive half
+  const int64_t g = r / T;
+  const int64_t n = pos + (r - g * T);
+  const int din = int(cst->din);
+  float a, b;
+  if constexpr (BF16) {
+    const uint16_t* row = static_cast<const uint16_t*>(values) + r * din;
+    a = lane < din ? __uint_as_float(uint32_t(row[lane]) << 16) : 0.f;
+    b = lane + 64 < din ? __uint_as_float(uint32_t(row[lane + 64]) << 16) : 0.f;
+  } else {
+    const float* row = static_cast<const float*>(values) + r * din;
+    a = lane < din ? row[lane] : 0.f;
+    b = lane + 64 < din ? row[lane + 64] : 0.f;
+  }
+  const float nu2 = wave_sum64_fast(fmaf(a, a, b * b));
+  const float fa = ((cst->dneg[lane >> 5] >> (lane & 31)) & 1u) ? -a : a;
+  const float fb = ((cst->dneg[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -b : b;
+  // the first stage adds +0: no -0 survives, so u < 0 is the sign bit
+  float u0 = (fa + fb) + 0.0f, u1 = (fa - fb) + 0.0f;
+  u0 = butterfly_lane<1>(u0, lane & 1);   u1 = butterfly_lane<1>(u1, lane & 1);
+  u0 = butterfly_lane<2>(u0, lane & 2);   u1 = butterfly_lane<2>(u1, lane & 2);
+  u0 = butterfly_lane<4>(u0, lane & 4);   u1 = butterfly_lane<4>(u1, lane & 4);
+  u0 = butterfly_lane<8>(u0, lane & 8);   u1 = butterfly_lane<8>(u1, lane & 8);
+  u0 = butterfly_lane<16>(u0, lane & 16); u1 = butterfly_lane<16>(u1, lane & 16);
+  u0 = butterfly_lane32(u0, lane & 32);   u1 = butterfly_lane32(u1, lane & 32);
+  const float nu = __builtin_amdgcn_sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * cst->sqrt_d;
+  // the value's tile; value v of the tile is i = v % 2 of group q = v / 2
+  uint32_t* tw = codes + ((g * ((Ncap + 15) / 16) + (n >> 4)) * 64) * BV;
+  const int v = int(n & 15), q = v >> 1, i = v & 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = lane + 64 * h;
+    const float u = h ? u1 : u0, au = fabsf(u);
+    int m = 0;   // magnitude index: thresholds at or below |u|
+#pragma unroll
+    for (int k = 0; k < KV - 1; ++k) m += au < cst->vtpos[k] * nsd ? 0 : 1;
+    const bool neg = u < 0.f;
+    const int code = zero ? 0 : (((m ^ (neg ? KV - 1 : 0)) & (KV - 1)) | (neg ? 0 : KV));
+    const int slot = 32 * (c >> 5) + 2 * (c & 15) + ((c >> 4) & 1);   // slot of coordinate c
+    const int bit0 = 16 * BV * slot + 2 * BV * q + i;                   // plane p at bit0 + 2 p
+#pragma unroll
+    for (int p = 0; p < BV; ++p) {
+      const int bit = bit0 + 2 * p;
+      uint32_t* w = tw + (bit >> 5);
+      const uint32_t mask = 1u << (bit & 31);
+      if ((code >> p) & 1) atomicOr(w, mask);
+      else atomicAnd(w, ~mask);
+    }
+  }
+  if (lane == 0) norms[g * Ncap + n] = zero ? uint16_t(0) : f2h_bits(nu);
+}
+
+template <int BV, bool BF16>
+__global__ __launch_bounds__(256) void append_values128_kernel(
+    const void* __restrict__ values, int64_t G, int64_t T, int64_t Ncap, int64_t pos,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ norms, const DevConsts* __restrict__ cst) {
+  const int lane = threadIdx.x & 63;
+  // wave-uniform grid-stride loop over the G T values (no barriers)
+  for (int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); r < G * T; r += int64_t(gridDim.x) * 4)
+    append_value128<BV, BF16>(values, r, T, Ncap, pos, lane, codes, norms, cst);
+}
+
 // ============================================================== measurement helpers
 // Not part of the method: ceilings and clocks the benchmark reports beside
 // the kernels above.
@@ -2424,6 +2502,58 @@ hipError_t launch_encode_values(const Codebook& cb, const void* values, int dtyp
   return hipGetLastError();
 }
 
+// Value append: whole 16-value tiles (pos and pos + T multiples of 16) take
+// the tile encoders, which write only those tiles; other shapes the latency
+// kernel above.
+hipError_t launch_append_values(const Codebook& cb, const void* values, int dtype, int64_t G, int64_t T,
+                                void* vpacked, int64_t Ncap, int64_t pos, hipStream_t s) {
+  uint32_t* codes = static_cast<uint32_t*>(vpacked);
+  uint16_t* norms = reinterpret_cast<uint16_t*>(codes + G * ((Ncap + 15) / 16) * 16 * int64_t(cb.bits) *
+                                                              (cb.d / 32));
+  if (pos % 16 == 0 && T % 16 == 0) {
+    if (dtype == 1) {
+      const int64_t want = (G * (T / 16) + kEnc16Waves - 1) / kEnc16Waves;
+      const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 4));
+      const uint16_t* vb = static_cast<const uint16_t*>(values);
+#define TQ_VB(BB)                                                                                  \
+  hipLaunchKernelGGL((encode128_bf16_t16_kernel<BB, true>), dim3(grid), dim3(kEnc16Threads), 0, s, vb, \
+                     G, T, Ncap, pos, codes, norms, cb.d_consts, cb.d_frag16,                       \
+                     reinterpret_cast<const uint4*>(cb.d_dm16), PageMap{})
+      switch (cb.bits) {
+        case 2: TQ_VB(2); break;
+        case 3: TQ_VB(3); break;
+        default: TQ_VB(4); break;
+      }
+#undef TQ_VB
+    } else {
+      const int64_t want = (G * ((T + 31) / 32) + kEncWaves - 1) / kEncWaves;
+      const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * 2));
+      const float* vf = static_cast<const float*>(values);
+#define TQ_VF(BB)                                                                                \
+  hipLaunchKernelGGL((encode128_f32_kernel<BB, true>), dim3(grid), dim3(kEncThreads), 0, s, vf, \
+                     G, T, Ncap, pos, codes, norms, cb.d_consts, cb.d_frag, cb.d_flip_f32, PageMap{})
+      switch (cb.bits) {
+        case 2: TQ_VF(2); break;
+        case 3: TQ_VF(3); break;
+        default: TQ_VF(4); break;
+      }
+#undef TQ_VF
+    }
+    return hipGetLastError();
+  }
+  const unsigned grid = unsigned(std::min<int64_t>((G * T + 3) / 4, int64_t(num_cus()) * 8));
+#define TQ_AV(BB, BF)                                                                              \
+  hipLaunchKernelGGL((append_values128_kernel<BB, BF>), dim3(grid), dim3(256), 0, s, values, G, T, Ncap, \
+                     pos, codes, norms, cb.d_consts)
+  switch (cb.bits) {
+    case 2: if (dtype == 1) TQ_AV(2, true); else TQ_AV(2, false); break;
+    case 3: if (dtype == 1) TQ_AV(3, true); else TQ_AV(3, false); break;
+    default: if (dtype == 1) TQ_AV(4, true); else TQ_AV(4, false); break;
+  }
+#undef TQ_AV
+  return hipGetLastError();
+}
+
 // Device scratch for callers that cannot allocate (tq_attention_decode_noalloc):
 // a file-scope device array that every GPU the library runs on holds until
 // the process ends.  Host code never passes the array's name to a kernel (on
@@ -2500,8 +2630,8 @@ size_t attention_workspace_bytes(const Codebook& cb, int64_t G, int Qg, int64_t 
 // scorer's grid; logits pass through the caches in the workspace, each key
 // range leaves its partial state), then the combine of the ranges.
 hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
-                            const void* kpacked, const void* vpacked, int64_t N, float scale,
-                            float* out, void* ws, hipStream_t s) {
+                            const void* kpacked, const void* vpacked, int64_t N, int64_t Ncap,
+                            float scale, float* out, void* ws, hipStream_t s) {
   int64_t chunk = 0;
   const dim3 grid = score_grid(G, Qg, N, chunk);
   float* logits = static_cast<float*>(ws);
@@ -2509,15 +2639,15 @@ hipError_t launch_attention(const Codebook& cb, const void* q, int qdtype, int64
                                          (size_t(G) * Qg * N * 4 + 255) / 256 * 256);
   const uint4* planes = static_cast<const uint4*>(kpacked);
   const uint32_t* norms =
-      static_cast<const uint32_t*>(kpacked) + G * N * int64_t(cb.bits) * (cb.d / 32);
+      static_cast<const uint32_t*>(kpacked) + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
   const uint4* vpl = static_cast<const uint4*>(vpacked);
   const uint16_t* vn = reinterpret_cast<const uint16_t*>(
-      static_cast<const uint32_t*>(vpacked) + G * ((N + 15) / 16) * 16 * int64_t(cb.bits) * (cb.d / 32));
-  const AttnArgs aa{vpl, vn, part, scale};
+      static_cast<const uint32_t*>(vpacked) + G * ((Ncap + 15) / 16) * 16 * int64_t(cb.bits) * (cb.d / 32));
+  const AttnArgs aa{vpl, vn, part, scale, Ncap};
   const bool bf = qdtype == 1;
 #define TQ_AT(BB, QB, BVV)                                                                       \
   hipLaunchKernelGGL((score128_kernel<BB, QB, false, BVV>), grid, dim3(kScoreThreads), 0, s, q, planes, \
-                     norms, N, N, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_frag16, PageMap{}, aa)
+                     norms, N, Ncap, Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_frag16, PageMap{}, aa)
   switch (cb.bits) {
     case 2: if (bf) TQ_AT(1, true, 2); else TQ_AT(1, false, 2); break;
     case 3: if (bf) TQ_AT(2, true, 3); else TQ_AT(2, false, 3); break;

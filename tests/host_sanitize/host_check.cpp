@@ -122,6 +122,16 @@ int main() {
   EXPECT(tq_attention_decode(cb, p, TQ_F32, 1, 4, p, p, 0, 0.1f, f, p, 1 << 16, nullptr) == TQ_ERR_ARG);
   EXPECT(tq_attention_decode(cb, p, TQ_F32, 1, 4, p, p, 10, -1.f, f, p, 1 << 16, nullptr) == TQ_ERR_ARG);
   EXPECT(tq_attention_decode(cb, p, TQ_F32, 1, 4, p, p, 10, 0.1f, f, nullptr, 0, nullptr) == TQ_ERR_WORKSPACE);
+  EXPECT(tq_append_values(cb, p, TQ_BF16, 1, 4, p, 3, 0, nullptr) == TQ_ERR_ARG);
+  EXPECT(tq_append_values(cb, p, TQ_BF16, 1, 2, p, 3, 2, nullptr) == TQ_ERR_ARG);
+  EXPECT(tq_append_values(cb, mis, TQ_BF16, 1, 1, p, 3, 0, nullptr) == TQ_ERR_ARG);
+  EXPECT(tq_append_values(cw, p, TQ_BF16, 1, 1, p, 3, 0, nullptr) == TQ_ERR_UNSUPPORTED);
+  EXPECT(tq_append_values(cb, p, TQ_BF16, 1, 1, p, 3, 2, nullptr) == TQ_ERR_HIP);
+  EXPECT(tq_attention_cache(cb, p, TQ_F32, 1, 4, p, p, 10, 11, 0.1f, f, p, 1 << 16, nullptr) == TQ_ERR_ARG);
+  EXPECT(tq_attention_cache(cb, p, TQ_F32, 1, 4, p, p, 10, 0, 0.1f, f, p, 1 << 16, nullptr) == TQ_ERR_ARG);
+  EXPECT(tq_attention_cache(cb, p, TQ_F32, 1, 4, p, p, 10, 5, 0.1f, f, nullptr, 0, nullptr) ==
+         TQ_ERR_WORKSPACE);
+  EXPECT(tq_attention_cache(cb, p, TQ_F32, 1, 4, p, p, 10, 5, 0.1f, f, p, 1 << 16, nullptr) == TQ_ERR_HIP);
   EXPECT(tq_attention_decode_noalloc(cb, p, TQ_F32, 1, 4, p, p, 10, NAN, f, nullptr) == TQ_ERR_ARG);
   EXPECT(tq_attention_decode_noalloc(cb, p, TQ_F32, 128, 4, p, p, 20000, 0.1f, f, nullptr) ==
          TQ_ERR_WORKSPACE);
