@@ -449,7 +449,47 @@ def run_attention(K, cb, keys0, q, G, N, Qg, packed, npk, steps):
             "attention": _stats(att, att_alg, G * N, "keys"),
             "value_record_bytes": int(vbytes // (G * N)),
             "note": "attention = scorer with its value phase (logits through the caches, "
-                    "per-range softmax state) + combine (ranges merged, rotated back)"}
+                    "per-range softmax state) + combine (ranges merged, rotated back)",
+            "cache_step": run_cache_step(K, cb, keys0, vals, q, G, N, Qg)}
+
+
+def run_cache_step(K, cb, keys0, vals, q, G, N, Qg, steps=64):
+    """The decode step of a serving loop on the same shapes: key and value
+    caches of N + steps records per group, prefilled with the N keys and
+    values; per step one new key and one new value per group appended
+    (tq_append_keys, tq_append_values, T = 1) and attention over the filled
+    prefix (tq_attention_cache).  Back-to-back GPU times per call and per
+    step; the caches fit the Infinity Cache here."""
+    import torch
+    Ncap = N + steps
+    kc = torch.empty(K.packed_nbytes(cb, G, Ncap), dtype=torch.uint8, device=keys0.device)
+    vc = torch.empty(K.value_packed_nbytes(cb, G, Ncap), dtype=torch.uint8, device=keys0.device)
+    K.append_keys(cb, keys0, kc, Ncap, 0)
+    K.append_values(cb, vals, vc, Ncap, 0)
+    newk = [keys0[:, i:i + 1].contiguous() for i in range(steps)]   # stand-in new tokens
+    newv = [vals[:, i:i + 1].contiguous() for i in range(steps)]
+    ws = torch.empty(max(16, K.attention_workspace_nbytes(cb, G, Qg, Ncap)), dtype=torch.uint8,
+                     device=keys0.device)
+    out = torch.empty((G, Qg, cb.d), dtype=torch.float32, device=keys0.device)
+    torch.cuda.synchronize()
+    filler = lambda: K.stream_probe(keys0.view(-1).view(torch.uint8))
+    app_us, app_ok = burst_us(K, torch, [(lambda i=i: K.append_values(cb, newv[i], vc, Ncap, N + i))
+                                         for i in range(steps)], filler)
+    att = _event_times(lambda i: K.attention_cache(cb, q, kc, vc, Ncap, N + steps, out=out, ws=ws), 20)
+    calls = []
+    for i in range(steps):
+        L = N + i + 1
+        calls.append(lambda i=i, L=L: K.append_keys(cb, newk[i], kc, Ncap, L - 1))
+        calls.append(lambda i=i, L=L: K.append_values(cb, newv[i], vc, Ncap, L - 1))
+        calls.append(lambda L=L: K.attention_cache(cb, q, kc, vc, Ncap, L, out=out, ws=ws))
+    step_us, step_ok = burst_us(K, torch, calls, filler, n_fill=150)
+    return {"values_per_append": G,
+            "append_values_gpu_us": round(app_us, 2),
+            "attention_cache_us_median": round(float(np.median(att)) * 1e3, 2),
+            "decode_step_gpu_us": round(3 * step_us, 2),
+            "back_to_back": bool(app_ok and step_ok),
+            "note": "decode step = append key + append value + attention over the prefix, "
+                    "GPU time back to back"}
 
 
 def _event_times(fn, reps, warm=2):

@@ -198,8 +198,14 @@ int tq_encode_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype,
  * keys: [G][T][d] device rows (TQ_F32 or TQ_BF16), typically T = 1 new
  * token per (batch, KV head) per decode step.  packed: a device buffer laid
  * out as above for G groups of Ncap records (tq_packed_bytes(cb, G, Ncap)).
- * Key t of group g is encoded exactly as tq_encode_keys would encode it and
- * written to record pos + t of group g; no other record is touched.
+ * Key t of group g is encoded by the rules of tq_encode_keys and written to
+ * record pos + t of group g; no other record is touched.  Up to 2048 keys
+ * (G*T) are encoded by the latency kernel of tq_paged_append_keys, one key
+ * per workgroup (float32 rotation and projection: records equal
+ * tq_encode_keys's except where a rotated coordinate lies within rounding of
+ * a threshold or a projection within rounding of zero, cases the method's
+ * parity rules leave open); more keys by the tile encoder of tq_encode_keys
+ * (identical records).
  * Requires 0 <= pos and pos + T <= Ncap.  G*T == 0 is a no-op.  d = 128 only.
  * Allocates nothing.  Errors: TQ_ERR_ARG (also pos + T > Ncap),
  * TQ_ERR_UNSUPPORTED (d != 128), TQ_ERR_HIP.

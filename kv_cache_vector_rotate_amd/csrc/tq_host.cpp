@@ -602,8 +602,8 @@ int tq_append_keys(const tq_codebook* cb, const void* keys, int32_t key_dtype, i
   if (G * ((T + 31) / 32) >= (int64_t(1) << 31)) return TQ_ERR_UNSUPPORTED;
   int rc = check_device(*cb);
   if (rc != TQ_OK) return rc;
-  hipError_t e = tq::launch_encode(*cb, keys, key_dtype, G, T, Ncap, pos, packed,
-                                   static_cast<hipStream_t>(stream));
+  hipError_t e = tq::launch_append_keys(*cb, keys, key_dtype, G, T, Ncap, pos, packed,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 

@@ -68,6 +68,9 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
 // Paged cache (d = 128): a pool of num_pages pages of page_size records
 // (each page laid out as one packed group), a page table [G][ppg] of pool
 // page indices, per-group first positions (append) or lengths (score).
+// Write-time key append into a contiguous cache of Ncap records per group.
+hipError_t launch_append_keys(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
+                              int64_t Ncap, int64_t pos, void* packed, hipStream_t s);
 hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
                                void* pool, int64_t num_pages, int page_size, const int32_t* table,
                                int ppg, const int32_t* pos, hipStream_t s);

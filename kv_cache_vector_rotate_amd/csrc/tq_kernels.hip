@@ -588,6 +588,10 @@ struct PageMap {
   int32_t ppg;         // table entries per group
   int32_t page_size;   // records per page (a multiple of 64)
   int32_t num_pages;   // pages in the pool
+  // append latency kernel only: table == nullptr maps row r of a [G][T]
+  // append to page r / T (the group) at slot base + r % T, a contiguous cache
+  // of page_size records per group
+  int64_t base;
 };
 
 // Pool page and slot of row r of a [G][T] append; false when the row's
@@ -1917,7 +1921,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_rows128_kernel(
     }
   int64_t dg = 0, dn = 0;
   bool ok = false;
-  if (wave == 0) ok = page_dest(pm, r, dg, dn);
+  if (wave == 0) {
+    if (pm.table) {
+      ok = page_dest(pm, r, dg, dn);
+    } else {
+      dg = r / pm.T;
+      dn = pm.base + (r - dg * pm.T);
+      ok = true;
+    }
+  }
   const int din = int(cst->din);
   float a, b;
   if constexpr (BF16) {
@@ -2746,16 +2758,12 @@ hipError_t launch_score_stream_probe(const Codebook& cb, int64_t G, int Qg, cons
 // Appends of at most this many rows take the one-key-per-wave kernel.
 constexpr int64_t kAppendRowsMax = 2048;
 
-hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
-                               void* pool, int64_t num_pages, int page_size, const int32_t* table,
-                               int ppg, const int32_t* pos, hipStream_t s) {
-  const int64_t rows = G * T;
-  uint32_t* planes = static_cast<uint32_t*>(pool);
-  uint32_t* norms = planes + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
-  const PageMap pm{table, pos, nullptr, uint32_t(T), ppg, page_size, int32_t(num_pages)};
-  if (rows <= kAppendRowsMax) {   // latency path: one key per workgroup
-    const int grid = int(rows);   // one key per workgroup (rows <= kAppendRowsMax)
-    const bool bf = dtype == 1;
+// The append latency kernel over `rows` keys (rows <= kAppendRowsMax), one
+// key per workgroup, destinations from pm.
+hipError_t launch_append_rows(const Codebook& cb, const void* keys, int dtype, int64_t rows,
+                              uint32_t* planes, uint32_t* norms, const PageMap& pm, hipStream_t s) {
+  const int grid = int(rows);
+  const bool bf = dtype == 1;
 #define TQ_APP(BB)                                                                            \
   if (bf)                                                                                     \
     hipLaunchKernelGGL((append_rows128_kernel<BB, true>), dim3(grid), dim3(kAppendThreads), 0, s, \
@@ -2763,14 +2771,39 @@ hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, 
   else                                                                                        \
     hipLaunchKernelGGL((append_rows128_kernel<BB, false>), dim3(grid), dim3(kAppendThreads), 0, s, \
                        keys, rows, planes, norms, cb.d_consts, cb.d_Sh, pm)
-    switch (cb.bits - 1) {
-      case 1: TQ_APP(1); break;
-      case 2: TQ_APP(2); break;
-      default: TQ_APP(3); break;
-    }
-#undef TQ_APP
-    return hipGetLastError();
+  switch (cb.bits - 1) {
+    case 1: TQ_APP(1); break;
+    case 2: TQ_APP(2); break;
+    default: TQ_APP(3); break;
   }
+#undef TQ_APP
+  return hipGetLastError();
+}
+
+// Write-time append into a contiguous cache of Ncap records per group: such
+// a cache is a pool whose page g is group g, Ncap records a page, so up to
+// kAppendRowsMax keys take the latency kernel with the contiguous map; larger
+// batches the tile encoders.
+hipError_t launch_append_keys(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
+                              int64_t Ncap, int64_t pos, void* packed, hipStream_t s) {
+  const int64_t rows = G * T;
+  if (cb.d != 128 || rows > kAppendRowsMax || Ncap > INT32_MAX)
+    return launch_encode(cb, keys, dtype, G, T, Ncap, pos, packed, s);
+  uint32_t* planes = static_cast<uint32_t*>(packed);
+  uint32_t* norms = planes + G * Ncap * int64_t(cb.bits) * (cb.d / 32);
+  const PageMap pm{nullptr, nullptr, nullptr, uint32_t(T), 1, int32_t(Ncap), int32_t(G), pos};
+  return launch_append_rows(cb, keys, dtype, rows, planes, norms, pm, s);
+}
+
+hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
+                               void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                               int ppg, const int32_t* pos, hipStream_t s) {
+  const int64_t rows = G * T;
+  uint32_t* planes = static_cast<uint32_t*>(pool);
+  uint32_t* norms = planes + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
+  const PageMap pm{table, pos, nullptr, uint32_t(T), ppg, page_size, int32_t(num_pages), 0};
+  if (rows <= kAppendRowsMax)   // latency path: one key per workgroup
+    return launch_append_rows(cb, keys, dtype, rows, planes, norms, pm, s);
   if (dtype == 1) {
     const int64_t want = ((rows + 15) / 16 + kEnc16Waves - 1) / kEnc16Waves;
     const int grid = int(std::min<int64_t>(want, int64_t(num_cus()) * (cb.bits == 4 ? 2 : 3)));

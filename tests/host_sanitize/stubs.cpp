@@ -66,6 +66,8 @@ hipError_t launch_encode_values(const Codebook&, const void*, int, int64_t, int6
 }
 hipError_t launch_attention(const Codebook&, const void*, int, int64_t, int, const void*, const void*,
                             int64_t, int64_t, float, float*, void*, hipStream_t) { return kNo; }
+hipError_t launch_append_keys(const Codebook&, const void*, int, int64_t, int64_t, int64_t, int64_t, void*,
+                              hipStream_t) { return kNo; }
 hipError_t launch_append_values(const Codebook&, const void*, int, int64_t, int64_t, void*, int64_t, int64_t,
                                 hipStream_t) { return kNo; }
 hipError_t launch_topk_wide(const Codebook&, const void*, int, int64_t, int, const void*, int64_t, int,

@@ -1,10 +1,12 @@
 """GPU tests of the write-time cache calls: tq_append_keys and tq_score_cache.
 
 A cache of Ncap records per group is filled in pieces (a prefill chunk, then
-one token per decode step); every appended record must be byte-identical to
-what tq_encode_keys writes for the same keys, must pass the oracle's parity
-rules, and no other record may change.  Scoring a prefix of the cache must
-equal the oracle's estimator on that prefix.
+one token per decode step).  Appends of up to 2048 keys take the latency
+kernel (float32 rotation and projection): its records must pass the oracle's
+parity rules and differ from tq_encode_keys's only where those rules flag a
+coordinate.  Larger appends take the tile encoder: its records must be
+byte-identical to tq_encode_keys's.  No other record may change.  Scoring a
+prefix of the cache must equal the oracle's estimator on that prefix.
 """
 
 import ctypes
@@ -73,11 +75,39 @@ def test_append_pieces_match_encode(bits, dt):
     buf = cache.cpu().numpy()
     pc, nc = _records(cbo, buf, G, Ncap)
     pr, nr = _records(cbo, ref, G, N)
-    assert np.array_equal(pc[:, :, :N], pr) and np.array_equal(nc[:, :N], nr)
     assert np.all(pc[:, :, N:].view(np.uint8) == FILL) and np.all(nc[:, N:].view(np.uint8) == FILL)
     codes, signs, nu16, rho16 = O.unpack(cbo, buf, G, Ncap)
     check_encode(cbo, keys.reshape(-1, 128), codes[:, :N].reshape(-1, 128),
                  signs[:, :N].reshape(-1, 128), nu16[:, :N].reshape(-1), rho16[:, :N].reshape(-1))
+    # the latency kernel against the tile encoder: the same records but for
+    # the few the parity rules leave open
+    same = np.all(pc[:, :, :N] == pr, axis=(1, 3)) & (nc[:, :N] == nr)
+    assert int((~same).sum()) <= 3, f"{int((~same).sum())} of {G * N} records differ from tq_encode_keys"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_append_bulk_rows_take_the_tile_encoder(dt):
+    """An append of more than 2048 keys (3 groups x 700) goes through the tile
+    encoder: byte-identical records to tq_encode_keys, at an offset."""
+    rng = np.random.default_rng(510 + (1 if dt == "bf16" else 0))
+    G, T, Ncap, pos = 3, 700, 750, 33
+    keys = _keys(rng, G, T)
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    if dt == "bf16":
+        keys = W.bf16_bits_to_f32(W.f32_to_bf16_bits(keys))
+    cb = K.Codebook(128, 3)
+    cbo = O.make_codebook(128, 3, 128, 42)
+    kd = _dev(keys, dtype)
+    print(f"[case] append bulk dtype={dt}", flush=True)
+    cache = torch.full((K.packed_nbytes(cb, G, Ncap),), FILL, dtype=torch.uint8, device="cuda")
+    K.append_keys(cb, kd, cache, Ncap, pos)
+    ref = K.encode_keys(cb, kd).cpu().numpy()
+    torch.cuda.synchronize()
+    pc, nc = _records(cbo, cache.cpu().numpy(), G, Ncap)
+    pr, nr = _records(cbo, ref, G, T)
+    assert np.array_equal(pc[:, :, pos:pos + T], pr) and np.array_equal(nc[:, pos:pos + T], nr)
+    assert np.all(pc[:, :, :pos].view(np.uint8) == FILL) and np.all(pc[:, :, pos + T:].view(np.uint8) == FILL)
+    assert np.all(nc[:, :pos].view(np.uint8) == FILL) and np.all(nc[:, pos + T:].view(np.uint8) == FILL)
 
 
 def test_decode_loop_score_cache():

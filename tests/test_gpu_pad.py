@@ -101,14 +101,23 @@ def test_padded_append_and_cache(dt):
     for t in range(30, 50):
         K.append_keys(cb, kd[:, t:t + 1].contiguous(), cache, Ncap, t)
     lc = K.score_cache(cb, _dev(q, dtype), cache, Ncap, 50)
-    lr = K.score_logits(cb, _dev(q, dtype), ref, 50)
     torch.cuda.synchronize()
-    assert torch.equal(lc, lr)
+    # the appends (latency kernel, float32 rotation) against the oracle, and
+    # against tq_encode_keys's records but for the few the parity rules leave open
     cbo = O.make_codebook(din, 3, D, 42)
-    c1 = O.unpack(cbo, cache.cpu().numpy(), G, Ncap)
+    c1 = [np.ascontiguousarray(np.asarray(a)[:, :50]) for a in O.unpack(cbo, cache.cpu().numpy(), G, Ncap)]
     c2 = O.unpack(cbo, ref.cpu().numpy(), G, 50)
+    codes, signs, nu16, rho16 = c1
+    check_encode(cbo, k.reshape(-1, din), codes.reshape(-1, D), signs.reshape(-1, D),
+                 nu16.reshape(-1), rho16.reshape(-1))
+    differ = np.zeros((G, 50), bool)
     for a, b in zip(c1, c2):
-        assert np.array_equal(np.asarray(a)[:, :50].view(np.uint8), np.asarray(b).view(np.uint8))
+        a8, b8 = a.view(np.uint8).reshape(G, 50, -1), np.asarray(b).view(np.uint8).reshape(G, 50, -1)
+        differ |= np.any(a8 != b8, axis=-1)
+    assert int(differ.sum()) <= 2
+    knorm = np.linalg.norm(k.astype(np.float64), axis=-1)
+    compact = O.pack(cbo, codes, signs, nu16, rho16)
+    check_logits(lc.cpu().numpy(), O.score(cbo, compact, G, 50, q), q, knorm)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
