@@ -1189,15 +1189,19 @@ constexpr int kAttnPart = 8 + 4 * 128;   // m[4], Z[4], A[4][128] per (group, qu
 template <int BV>
 struct AttnLds {
   // level table: entry e (a value pair's 2 BV code bits) holds the halves
-  // hi[2], lo[2] of the two levels, in kCopies copies side by side, lane L
-  // reading copy L % kCopies: the 8-byte reads of 32 lanes hit 64 different
-  // banks whatever the codes are (16 copies at 4 bits: 32 KB)
+  // hi, lo of the first level, then hi, lo of the second, in kCopies copies
+  // side by side, lane L reading copy L % kCopies: the 8-byte reads of 32
+  // lanes hit 64 different banks whatever the codes are (16 copies at 4
+  // bits: 32 KB)
   static constexpr int kLutEntries = 1 << (2 * BV);
   static constexpr int kCopies = BV == 4 ? 16 : 32;
   static constexpr int kStage = BV * 256 + 8;   // words per wave: 4 of padding, a 64-key tile's codes, 4
   uint2 lut[kLutEntries * kCopies];
   uint32_t stage[16][kStage];
-  uint16_t wt[16][8][64];     // per wave: scaled weights of the tile's keys, half hi (row q), lo (row 4 + q)
+  // per wave: the scaled weights of the tile's keys as matrix-core A rows,
+  // one word per key: row q the half hi twice, row 4 + q the half lo and 0
+  uint32_t wt[16][8][64];
+  uint32_t wz[64];            // zeros: the A rows 8..15
   float m[16][4], z[16][4];   // per wave: maximum of scale * logit, normaliser
 };
 
@@ -1240,18 +1244,23 @@ __device__ __forceinline__ float wave_sum64(float v) {
 
 // Loads of one 64-key tile of the value phase (keys from b): the lane's
 // logits and value norm (clamped to the range), the tile's value codes
-// (BV 16-byte units per lane, clamped to the group's last tile).
+// (BV 16-byte units per lane, clamped to the group's last tile).  The bases
+// are wave-uniform and the per-lane offsets 32-bit (a scalar base and one
+// vector offset per load, no 64-bit address arithmetic per lane).
 template <int BV>
 __device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, const float* const (&lrow)[4],
                                            const uint16_t* vn, const uint4* vq, int64_t vlast,
                                            u32x4 (&cv)[BV], float (&lg)[4], uint32_t& nvb) {
-  const int64_t kn = std::min<int64_t>(b + lane, n1 - 1);
+  const uint32_t kn = std::min(uint32_t(lane), uint32_t(std::min<int64_t>(n1 - 1 - b, 63)));
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) lg[qq] = lrow[qq][kn];
-  nvb = vn[kn];
+  for (int qq = 0; qq < 4; ++qq) lg[qq] = (lrow[qq] + b)[kn];
+  nvb = (vn + b)[kn];
+  const int64_t u0 = (b >> 4) * (16 * BV);   // the tile's first 16-byte unit
+  const uint4* vt = vq + u0;
+  const uint32_t ul = uint32_t(std::min<int64_t>(vlast - u0, 64 * BV - 1));
 #pragma unroll
   for (int j = 0; j < BV; ++j) {
-    const uint4 v = vq[std::min<int64_t>((b >> 4) * 16 * BV + j * 64 + lane, vlast)];
+    const uint4 v = vt[std::min(uint32_t(j * 64 + lane), ul)];
     cv[j] = u32x4{v.x, v.y, v.z, v.w};
   }
 }
@@ -1267,9 +1276,10 @@ __device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, cons
 // matrix cores, one 16 x 16 x 32 product per 16-value tile and 16 slots: the
 // B operand of lane (values 4 kg .. 4 kg + 3, slot 16 cb + n) is two entries
 // of a table of level pairs indexed by the lane's two value groups in that
-// slot (the levels as half hi[2], lo[2]); the A operand's rows 0..3 hold the
+// slot (each level as half hi, lo); the A operand's rows 0..3 hold the
 // weights' halves hi twice (against hi and lo), rows 4..7 their lo once
-// (against hi): float16 operands, about 22 bits of every product kept.  The weights w nu~ are
+// (against hi), both as written to LDS per key, rows 8..15 zeros: float16
+// operands, about 22 bits of every product kept.  The weights w nu~ are
 // scaled by a power of 2 that keeps them under 2^14 (from the largest value
 // norm the wave has seen; its sums are rescaled when that grows), so that
 // the halves lose nothing to the float16 range.  The range's state goes to
@@ -1333,11 +1343,12 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
     const int x = tid + j * kScoreThreads;
     if (x < Lds::kLutEntries * Lds::kCopies) {
       const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(la[j][0], la[j][1]));
-      const half2v l = {static_cast<_Float16>(la[j][0] - static_cast<float>(h[0])),
-                        static_cast<_Float16>(la[j][1] - static_cast<float>(h[1]))};
-      sm.lut[x] = make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l));
+      const half2v e0 = {h[0], static_cast<_Float16>(la[j][0] - static_cast<float>(h[0]))};
+      const half2v e1 = {h[1], static_cast<_Float16>(la[j][1] - static_cast<float>(h[1]))};
+      sm.lut[x] = make_uint2(__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1));
     }
   }
+  if (tid < 64) sm.wz[tid] = 0u;
   __syncthreads();
   // the weights w nu~ are scaled by 2^(140 - E), E the largest exponent
   // field of the value norms seen so far by this wave: a norm below 2^(E - 126)
@@ -1346,7 +1357,7 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   uint32_t erun = 103;   // the smallest non-zero half, 2^-24, has field 103
   uint32_t* stw = sm.stage[wave];
   const uint32_t* l32 = reinterpret_cast<const uint32_t*>(lds_raw);
-  uint16_t* wtw = &sm.wt[wave][0][0];
+  uint32_t* wtw = &sm.wt[wave][0][0];
   const int n = lane & 15, kg = lane >> 4;   // B: slot column n, values 4 kg .. 4 kg + 3; A: row n
   // The lane's values 4 kg .. 4 kg + 3 in slot 16 cb + n are the two groups
   // 2 kg, 2 kg + 1: 4 BV bits from bit 64 BV cb + 16 BV n + 4 BV kg of a tile.
@@ -1362,14 +1373,14 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   }
   constexpr int kEntryShift = BV == 4 ? 7 : 8;   // entry stride: kCopies x 8 bytes
   const uint32_t cofs = uint32_t(lane % Lds::kCopies) * 8u;
-  const bool row_hi = n < 4, row_any = n < 8;   // A rows: 0..3 hi (twice), 4..7 lo, 8..15 zero
+  const uint32_t* arow = n < 8 ? wtw + n * 64 : sm.wz;   // A rows: 0..3 hi (twice), 4..7 lo, 8..15 zero
   f32x4 acc[8];
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float zp[4] = {0.f, 0.f, 0.f, 0.f};
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t b = first + t * stride;
-    const bool valid = b + lane < n1;
+    const bool valid = uint32_t(lane) < uint32_t(std::min<int64_t>(n1 - b, 64));
     const float nvr = h2f_bits(nvb);
     const uint32_t et = wave_max_exponent(nvr);
     if (et > erun) {
@@ -1386,14 +1397,12 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
       zp[qq] += e;
       wq[qq] = e * nv;
     }
-    const half2v h0 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(wq[0], wq[1]));
-    const half2v h1 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(wq[2], wq[3]));
-    const _Float16 wh[4] = {h0[0], h0[1], h1[0], h1[1]};
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
-      wtw[qq * 64 + lane] = __builtin_bit_cast(uint16_t, wh[qq]);
+      const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(wq[qq], wq[qq]));
+      wtw[qq * 64 + lane] = __builtin_bit_cast(uint32_t, hh);
       wtw[(4 + qq) * 64 + lane] =
-          __builtin_bit_cast(uint16_t, static_cast<_Float16>(wq[qq] - static_cast<float>(wh[qq])));
+          uint32_t(__builtin_bit_cast(uint16_t, static_cast<_Float16>(wq[qq] - static_cast<float>(hh[0]))));
     }
 #pragma unroll
     for (int j = 0; j < BV; ++j) reinterpret_cast<u32x4*>(stw + 4)[j * 64 + lane] = cv[j];
@@ -1448,15 +1457,14 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
         const char* lb = reinterpret_cast<const char*>(sm.lut);
         const uint2 e0 = *reinterpret_cast<const uint2*>(lb + o0);
         const uint2 e1 = *reinterpret_cast<const uint2*>(lb + o1);
-        // K order of the lane's 8 products: hi(v0) hi(v1) lo(v0) lo(v1) hi(v2)
-        // hi(v3) lo(v2) lo(v3) for its values v0..v3 = 4 kg .. 4 kg + 3
+        // K order of the lane's 8 products: hi(v0) lo(v0) hi(v1) lo(v1) hi(v2)
+        // lo(v2) hi(v3) lo(v3) for its values v0..v3 = 4 kg .. 4 kg + 3
         bv[c] = u32x4{e0.x, e0.y, e1.x, e1.y};
       }
       if ((k & 1) == 0) {
-        const uint2 x = *reinterpret_cast<const uint2*>(wtw + (n & 7) * 64 + 16 * u + 4 * kg);
-        // the same K order: row q < 4 holds w_hi(v0, v1) twice, then w_hi(v2, v3)
-        // twice; row 4 + q w_lo(v0, v1), 0, w_lo(v2, v3), 0 (hi levels only)
-        const u32x4 av = {row_any ? x.x : 0u, row_hi ? x.x : 0u, row_any ? x.y : 0u, row_hi ? x.y : 0u};
+        // the same K order: row q < 4 holds w_hi(v) twice per value (against
+        // the level's hi and lo), row 4 + q w_lo(v) and 0 (hi levels only)
+        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + 16 * u + 4 * kg);
         A = __builtin_bit_cast(half8, av);
       }
       if (k < 7) read_fields(k + 1);
