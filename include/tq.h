@@ -258,6 +258,50 @@ int tq_paged_score(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_
                    void* stream);
 
 /*
+ * Paged value pool and decode attention over paged caches: the value side of
+ * the paged key cache above, for a serving loop whose KV-cache wrapper keeps
+ * every token compressed from the moment it is cached [Qiita explainer, API
+ * table: the KV-cache wrapper beside the key and value compressors; ICLR
+ * 2026 paper digest, "実装のポイント": compression at write time].
+ *
+ * Value pool: num_pages pages of page_size value records, laid out as the
+ * value records (tq_value_packed_bytes layout) of num_pages groups of
+ * page_size values, so tq_value_packed_bytes(cb, num_pages, page_size)
+ * bytes.  It shares the key pool's page table: entry (g, p) names the page
+ * of logical positions [p * page_size, (p + 1) * page_size) of group g in
+ * both pools.  page_size as for the key pool (a multiple of 64).
+ *
+ * tq_paged_append_values: values [G][T][d] (TQ_F32 or TQ_BF16); value t of
+ * group g is coded by the rules of tq_encode_values and written to logical
+ * position pos[g] + t (pos: device int32 [G]) by the value append latency
+ * kernel (one value per wave, float32 rotation: level indices equal
+ * tq_encode_values's except where a rotated coordinate lies within rounding
+ * of a threshold), which sets the value's bits in its 16-value tile with
+ * atomic OR / AND, so the values of one tile may arrive in any calls.  A
+ * position whose page is invalid is not written.  G*T == 0 is a no-op;
+ * nothing is allocated.  Errors: as tq_paged_append_keys.
+ *
+ * tq_paged_attention: out[g][h] (float32 [G][Qg][d]) = sum over the
+ * positions n < min(lens[g], Lmax, pages_per_group * page_size) whose page
+ * entry is valid of softmax_n(scale * logit) * v_mse, with the estimator and
+ * the value decode of tq_attention_decode; a group without such positions
+ * gets zeros.  kpool: the key pool (its size in pages is num_pages for both
+ * pools), vpool: the value pool.  Two launches (the paged scorer with the
+ * value phase, then the combine); ws: tq_attention_workspace_bytes(cb, G,
+ * Qg, Lmax) bytes of device memory.
+ * Errors: TQ_ERR_ARG (as tq_paged_score; also Lmax == 0 with G*Qg > 0, scale
+ * not finite and > 0), TQ_ERR_WORKSPACE, TQ_ERR_UNSUPPORTED (as
+ * tq_paged_score), TQ_ERR_HIP.
+ */
+int tq_paged_append_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G, int64_t T,
+                           void* pool, int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                           int32_t pages_per_group, const int32_t* pos, void* stream);
+int tq_paged_attention(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                       const void* kpool, const void* vpool, int64_t num_pages, int32_t page_size,
+                       const int32_t* page_table, int32_t pages_per_group, const int32_t* lens, int64_t Lmax,
+                       float scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Value records (MSE-only): the community implementation on the Qiita
  * explainer compresses values with the Stage-1 quantizer alone (API table:
  * value compressor = rotation + Lloyd-Max), and its byte table counts b-bit

@@ -14,5 +14,5 @@ from ._binding import (  # noqa: F401
     score_workspace_nbytes, rotation_dim, library, library_path, EXPORTED_SYMBOLS,
     clock_probe, stream_probe, score_stream_probe, attention_decode_noalloc,
     attention_noalloc_max_nbytes, paged_pool_nbytes, paged_append_keys, paged_score,
-    append_values, attention_cache,
+    append_values, attention_cache, paged_value_pool_nbytes, paged_append_values, paged_attention,
 )

@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "tq_clock_probe", "tq_stream_probe", "tq_score_stream_probe",
     "tq_attention_decode_noalloc", "tq_attention_noalloc_max_bytes",
     "tq_paged_append_keys", "tq_paged_score", "tq_append_values", "tq_attention_cache",
+    "tq_paged_append_values", "tq_paged_attention",
 )
 
 _c_i32, _c_i64, _c_u64, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
@@ -70,6 +71,10 @@ _SIGS = {
                                             _c_i32, _vp, _vp]),
     "tq_paged_score": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _c_i64, _c_i32, _vp, _c_i32,
                                       _vp, _c_i64, _vp, _vp]),
+    "tq_paged_append_values": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _vp,
+                                              _c_i32, _vp, _vp]),
+    "tq_paged_attention": (ctypes.c_int, [_vp, _vp, _c_i32, _c_i64, _c_i32, _vp, _vp, _c_i64, _c_i32, _vp,
+                                          _c_i32, _vp, _c_i64, ctypes.c_float, _vp, _vp, _c_sz, _vp]),
     "tq_clock_probe": (ctypes.c_int, [_vp, _c_i32, _vp]),
     "tq_stream_probe": (ctypes.c_int, [_vp, _c_sz, _vp, _c_sz, _c_i32, _vp]),
     "tq_score_stream_probe": (ctypes.c_int, [_vp, _c_i64, _c_i32, _vp, _c_i64, _vp, _vp]),
@@ -342,6 +347,67 @@ def paged_score(cb: Codebook, q, pool, page_size: int, page_table, lens, Lmax: i
 
 def value_packed_nbytes(cb: Codebook, G: int, N: int) -> int:
     return int(library().tq_value_packed_bytes(cb.handle, G, N))
+
+
+def paged_value_pool_nbytes(cb: Codebook, num_pages: int, page_size: int) -> int:
+    """Bytes of a value pool of num_pages pages of page_size value records."""
+    return value_packed_nbytes(cb, num_pages, page_size)
+
+
+def _pages(nbytes_of_one, t, page_size):
+    per_page = nbytes_of_one(page_size)
+    return (t.numel() * t.element_size()) // per_page if per_page else 0
+
+
+def paged_append_values(cb: Codebook, values, pool, page_size: int, page_table, pos):
+    """Encode values [G, T, d] into a paged value pool: value t of group g
+    goes to logical position pos[g] + t through page_table [G,
+    pages_per_group] (device int32); pos is a device int32 [G].  In place."""
+    _need_cuda(values, "values")
+    _need_cuda(pool, "pool")
+    G, T, d = values.shape
+    if d != cb.d:
+        raise ValueError("value dimension does not match the codebook")
+    num_pages = _pages(lambda ps: value_packed_nbytes(cb, 1, ps), pool, page_size)
+    if page_table.dim() != 2 or page_table.shape[0] != G:
+        raise ValueError("page_table must be [G, pages_per_group]")
+    _need_i32(page_table, G * page_table.shape[1], "page_table")
+    _need_i32(pos, G, "pos")
+    _check(library().tq_paged_append_values(cb.handle, _ptr(values), _dtype_code(values), G, T, _ptr(pool),
+                                            num_pages, page_size, _ptr(page_table), page_table.shape[1],
+                                            _ptr(pos), _stream()), "tq_paged_append_values")
+    return pool
+
+
+def paged_attention(cb: Codebook, q, kpool, vpool, page_size: int, page_table, lens, Lmax: int, scale=None,
+                    out=None, ws=None):
+    """Decode attention of q [G, Qg, d] over the first lens[g] (at most Lmax)
+    positions of each group of a paged key pool and value pool that share
+    page_table -> float32 [G, Qg, d] (zeros for a group without keys)."""
+    torch = _torch()
+    for t, name in ((q, "q"), (kpool, "kpool"), (vpool, "vpool")):
+        _need_cuda(t, name)
+    G, Qg, d = q.shape
+    if d != cb.d:
+        raise ValueError("query dimension does not match the codebook")
+    scale = 1.0 / d ** 0.5 if scale is None else float(scale)
+    num_pages = _pages(lambda ps: packed_nbytes(cb, 1, ps), kpool, page_size)
+    _need_bytes(vpool, paged_value_pool_nbytes(cb, num_pages, page_size), "vpool (as many pages as kpool)")
+    if page_table.dim() != 2 or page_table.shape[0] != G:
+        raise ValueError("page_table must be [G, pages_per_group]")
+    _need_i32(page_table, G * page_table.shape[1], "page_table")
+    _need_i32(lens, G, "lens")
+    if out is None:
+        out = torch.empty((G, Qg, d), dtype=torch.float32, device=q.device)
+    _need_out(out, G * Qg * d)
+    wsb = attention_workspace_nbytes(cb, G, Qg, Lmax)
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check(library().tq_paged_attention(cb.handle, _ptr(q), _dtype_code(q), G, Qg, _ptr(kpool), _ptr(vpool),
+                                        num_pages, page_size, _ptr(page_table), page_table.shape[1],
+                                        _ptr(lens), Lmax, scale, _ptr(out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream()), "tq_paged_attention")
+    return out
 
 
 def encode_values(cb: Codebook, values, out=None):

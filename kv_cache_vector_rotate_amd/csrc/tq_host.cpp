@@ -663,6 +663,52 @@ int tq_paged_score(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_
   return e == hipSuccess ? TQ_OK : hip_fail(e);
 }
 
+int tq_paged_append_values(const tq_codebook* cb, const void* values, int32_t dtype, int64_t G, int64_t T,
+                           void* pool, int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                           int32_t pages_per_group, const int32_t* pos, void* stream) {
+  if (!cb || G < 0 || T < 0 || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_ARG;
+  int rc = check_pool(cb, num_pages, page_size, pages_per_group);
+  if (rc != TQ_OK) return rc;
+  if (G == 0 || T == 0) return TQ_OK;
+  if (G * T >= (int64_t(1) << 31) || G * int64_t(pages_per_group) >= (int64_t(1) << 31))
+    return TQ_ERR_UNSUPPORTED;
+  if (!values || !pool || !page_table || !pos || !aligned16(values) || !aligned16(pool) ||
+      !aligned4(page_table) || !aligned4(pos))
+    return TQ_ERR_ARG;
+  rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_append_values_paged(*cb, values, dtype, G, T, pool, num_pages, page_size,
+                                                page_table, pages_per_group, pos,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
+int tq_paged_attention(const tq_codebook* cb, const void* q, int32_t q_dtype, int64_t G, int32_t Qg,
+                       const void* kpool, const void* vpool, int64_t num_pages, int32_t page_size,
+                       const int32_t* page_table, int32_t pages_per_group, const int32_t* lens, int64_t Lmax,
+                       float scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!cb || G < 0 || Qg < 0 || Lmax < 0 || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_ERR_ARG;
+  if (!(scale > 0.f) || !(scale < INFINITY)) return TQ_ERR_ARG;
+  int rc = check_pool(cb, num_pages, page_size, pages_per_group);
+  if (rc != TQ_OK) return rc;
+  if (Qg > 256 || G > INT32_MAX || G * Qg > INT32_MAX || Lmax >= (int64_t(1) << 28) ||
+      G * int64_t(pages_per_group) >= (int64_t(1) << 31))
+    return TQ_ERR_UNSUPPORTED;
+  if (G == 0 || Qg == 0) return TQ_OK;
+  if (Lmax == 0) return TQ_ERR_ARG;
+  if (!q || !kpool || !vpool || !page_table || !lens || !out || !aligned16(q) || !aligned16(kpool) ||
+      !aligned16(vpool) || !aligned4(page_table) || !aligned4(lens) || !aligned16(out))
+    return TQ_ERR_ARG;
+  const size_t need = tq::attention_workspace_bytes(*cb, G, Qg, Lmax);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return TQ_ERR_WORKSPACE;
+  rc = check_device(*cb);
+  if (rc != TQ_OK) return rc;
+  hipError_t e = tq::launch_attention_paged(*cb, q, q_dtype, G, Qg, kpool, vpool, num_pages, page_size,
+                                            page_table, pages_per_group, lens, Lmax, scale, out, ws,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TQ_OK : hip_fail(e);
+}
+
 size_t tq_value_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N) {
   if (!cb || G < 0 || N < 0) return 0;
   // codes in tiles of 16 values (bits * d / 8 bytes per value), then one half norm per value

@@ -71,6 +71,16 @@ hipError_t launch_score(const Codebook& cb, const void* q, int qdtype, int64_t G
 // Write-time key append into a contiguous cache of Ncap records per group.
 hipError_t launch_append_keys(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
                               int64_t Ncap, int64_t pos, void* packed, hipStream_t s);
+// Paged value pool (num_pages pages of page_size value records, the layout
+// of a value buffer of num_pages groups) and decode attention over a paged
+// key pool and value pool sharing one page table.
+hipError_t launch_append_values_paged(const Codebook& cb, const void* values, int dtype, int64_t G, int64_t T,
+                                      void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                                      int ppg, const int32_t* pos, hipStream_t s);
+hipError_t launch_attention_paged(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                                  const void* kpool, const void* vpool, int64_t num_pages, int page_size,
+                                  const int32_t* table, int ppg, const int32_t* lens, int64_t Lmax,
+                                  float scale, float* out, void* ws, hipStream_t s);
 hipError_t launch_encode_paged(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t T,
                                void* pool, int64_t num_pages, int page_size, const int32_t* table,
                                int ppg, const int32_t* pos, hipStream_t s);

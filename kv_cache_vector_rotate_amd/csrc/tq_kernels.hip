@@ -1242,26 +1242,55 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
 }
 
-// Loads of one 64-key tile of the value phase (keys from b): the lane's
-// logits and value norm (clamped to the range), the tile's value codes
-// (BV 16-byte units per lane, clamped to the group's last tile).  The bases
-// are wave-uniform and the per-lane offsets 32-bit (a scalar base and one
-// vector offset per load, no 64-bit address arithmetic per lane).
+// Loads of one 64-key tile of the value phase (keys from position b, their
+// value records from record bv of vn / vq): the lane's logits and value
+// norm (clamped to the range), the tile's value codes (BV 16-byte units per
+// lane, clamped to the last tile of vq).  The bases are wave-uniform and the
+// per-lane offsets 32-bit (a scalar base and one vector offset per load, no
+// 64-bit address arithmetic per lane).
 template <int BV>
-__device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, const float* const (&lrow)[4],
-                                           const uint16_t* vn, const uint4* vq, int64_t vlast,
-                                           u32x4 (&cv)[BV], float (&lg)[4], uint32_t& nvb) {
+__device__ __forceinline__ void attn_fetch(int64_t b, int64_t bv, int lane, int64_t n1,
+                                           const float* const (&lrow)[4], const uint16_t* vn,
+                                           const uint4* vq, int64_t vlast, u32x4 (&cv)[BV], float (&lg)[4],
+                                           uint32_t& nvb) {
   const uint32_t kn = std::min(uint32_t(lane), uint32_t(std::min<int64_t>(n1 - 1 - b, 63)));
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lg[qq] = (lrow[qq] + b)[kn];
-  nvb = (vn + b)[kn];
-  const int64_t u0 = (b >> 4) * (16 * BV);   // the tile's first 16-byte unit
+  nvb = (vn + bv)[kn];
+  const int64_t u0 = (bv >> 4) * (16 * BV);   // the tile's first 16-byte unit
   const uint4* vt = vq + u0;
   const uint32_t ul = uint32_t(std::min<int64_t>(vlast - u0, 64 * BV - 1));
 #pragma unroll
   for (int j = 0; j < BV; ++j) {
     const uint4 v = vt[std::min(uint32_t(j * 64 + lane), ul)];
     cv[j] = u32x4{v.x, v.y, v.z, v.w};
+  }
+}
+
+// The value records of the 64-key tile at position b (b < n1): the group's
+// own (a cache of aa.vcap records per group), or, paged, those of the pool
+// page the page map gives for b (pages of aa.vcap = page_size records).  ok:
+// the tile has records; a tile in an invalid page reads page 0 and is
+// weighed with nothing (its logits were not written either).
+template <int BV, bool PAGED>
+__device__ __forceinline__ void attn_fetch_tile(int64_t b, int lane, int64_t n1, int64_t g,
+                                                const float* const (&lrow)[4], const AttnArgs& aa,
+                                                const PageMap& pm, u32x4 (&cv)[BV], float (&lg)[4],
+                                                uint32_t& nvb, bool& ok) {
+  const int64_t tpg16 = (aa.vcap + 15) / 16;
+  const int64_t vlast = tpg16 * 16 * BV - 1;
+  if constexpr (PAGED) {
+    const int32_t lpage = int32_t(b / pm.page_size);
+    int32_t ph = __builtin_amdgcn_readfirstlane(pm.table[g * pm.ppg + lpage]);
+    ok = ph >= 0 && ph < pm.num_pages;
+    if (!ok) ph = 0;
+    attn_fetch<BV>(b, b - int64_t(lpage) * pm.page_size, lane, n1, lrow, aa.vnorms + int64_t(ph) * aa.vcap,
+                   aa.vplanes + int64_t(ph) * tpg16 * 16 * BV, vlast, cv, lg, nvb);
+    if (!ok) nvb = 0u;
+  } else {
+    ok = true;
+    attn_fetch<BV>(b, b, lane, n1, lrow, aa.vnorms + g * aa.vcap, aa.vplanes + g * tpg16 * 16 * BV, vlast,
+                   cv, lg, nvb);
   }
 }
 
@@ -1284,11 +1313,12 @@ __device__ __forceinline__ void attn_fetch(int64_t b, int lane, int64_t n1, cons
 // norm the wave has seen; its sums are rescaled when that grows), so that
 // the halves lose nothing to the float16 range.  The range's state goes to
 // `part` and attn_combine128_kernel rotates back.
-template <int BV>
+template <int BV, bool PAGED>
 __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lmax)[4], const AttnArgs& aa,
                                                  const DevConsts* __restrict__ cst, const float* logits,
                                                  int64_t g, int qc, int Qg, int64_t N, int64_t n1,
-                                                 int64_t first, int64_t ntiles, int64_t stride) {
+                                                 int64_t first, int64_t ntiles, int64_t stride,
+                                                 const PageMap& pm) {
   using Lds = AttnLds<BV>;
   static_assert(sizeof(Lds) <= sizeof(ScoreLds), "the value phase reuses the scorer's LDS");
   // the per-wave normaliser parts are written while other waves still read
@@ -1298,19 +1328,16 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   Lds& sm = *reinterpret_cast<Lds*>(lds_raw);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint16_t* vn = aa.vnorms + g * aa.vcap;
   const float* lrow[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) lrow[qq] = logits + (g * Qg + std::min(qc * 4 + qq, Qg - 1)) * N;
-  const int64_t tpg16 = (aa.vcap + 15) / 16;
-  const uint4* vq = aa.vplanes + g * tpg16 * 16 * BV;   // the group's codes, 16 BV units per tile
-  const int64_t vlast = tpg16 * 16 * BV - 1;
   // loads of tile t: the key's logits and value norm, the 64 keys' codes;
   // the first tile's go out now, over the barriers below
   u32x4 cv[BV];
   float lg[4];
   uint32_t nvb = 0;
-  if (ntiles > 0) attn_fetch<BV>(first, lane, n1, lrow, vn, vq, vlast, cv, lg, nvb);
+  bool okn = false;
+  if (ntiles > 0) attn_fetch_tile<BV, PAGED>(first, lane, n1, g, lrow, aa, pm, cv, lg, nvb, okn);
   // the wave's own maximum of scale * logit per query: its weights
   // exp(scale l - M) are at most 1, and the workgroup's sums merge the
   // waves' states with exp(M_w - M) at the end
@@ -1380,7 +1407,7 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
   float zp[4] = {0.f, 0.f, 0.f, 0.f};
   for (int64_t t = 0; t < ntiles; ++t) {
     const int64_t b = first + t * stride;
-    const bool valid = uint32_t(lane) < uint32_t(std::min<int64_t>(n1 - b, 64));
+    const bool valid = okn && uint32_t(lane) < uint32_t(std::min<int64_t>(n1 - b, 64));
     const float nvr = h2f_bits(nvb);
     const uint32_t et = wave_max_exponent(nvr);
     if (et > erun) {
@@ -1407,8 +1434,8 @@ __device__ __forceinline__ void attn_value_phase(void* lds_raw, const float (&lm
 #pragma unroll
     for (int j = 0; j < BV; ++j) reinterpret_cast<u32x4*>(stw + 4)[j * 64 + lane] = cv[j];
     // the next tile's loads fly over this tile's products
-    attn_fetch<BV>(first + std::min<int64_t>(t + 1, ntiles - 1) * stride, lane, n1, lrow, vn, vq, vlast,
-                   cv, lg, nvb);
+    attn_fetch_tile<BV, PAGED>(first + std::min<int64_t>(t + 1, ntiles - 1) * stride, lane, n1, g, lrow, aa,
+                               pm, cv, lg, nvb, okn);
     // in steps of four products (16-value tile u = k / 2, slots 16 cb + n for
     // cb = 4 (k % 2) .. + 3): the four groups' fields, their table entries,
     // then the products; the next step's fields are requested before this
@@ -1551,7 +1578,13 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   int64_t n1 = std::min<int64_t>(N, n0 + chunk);   // n0 < n1: the host sizes the grid so
   if constexpr (PAGED) {   // group lengths live in device memory: ranges past them have no work
     n1 = std::min<int64_t>(n1, std::min<int64_t>(pm.lens[g], int64_t(pm.ppg) * pm.page_size));
-    if (n1 <= n0) return;
+    if (n1 <= n0) {
+      if constexpr (BV > 0) {   // attention: the range's state is empty (maximum -inf, no sums)
+        float* st = aa.part + ((g * gridDim.y + qc) * gridDim.z + blockIdx.z) * kAttnPart;
+        if (tid < kAttnPart) st[tid] = tid < 4 ? -INFINITY : 0.f;
+      }
+      return;
+    }
   }
   // keys [0, N) of a cache holding Ncap records per group; logits [G][Qg][N]
   const uint4* pg = planes + g * P * Ncap;
@@ -1875,7 +1908,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void score128_kernel(
   // the refills past the range are never used: let them land before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (BV > 0)
-    attn_value_phase<BV>(&sm, lmax, aa, cst, logits, g, qc, Qg, N, n1, first, ntiles, kStride);
+    attn_value_phase<BV, PAGED>(&sm, lmax, aa, cst, logits, g, qc, Qg, N, n1, first, ntiles, kStride, pm);
 }
 
 // ============================================================== append, few rows, d = 128
@@ -2200,7 +2233,7 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       if (s < splits) {
-        const float f = __expf(mv[s] - M);
+        const float f = mv[s] == -INFINITY ? 0.f : __expf(mv[s] - M);   // a range without keys
         Z = fmaf(f, zv[s], Z);
         a0 = fmaf(f, x0[s], a0);
         a1 = fmaf(f, x1[s], a1);
@@ -2212,13 +2245,13 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
 #pragma unroll 8
     for (int s = 0; s < splits; ++s) {
       const float* ps = base + s * kAttnPart;
-      const float f = __expf(ps[q] - M);
+      const float f = ps[q] == -INFINITY ? 0.f : __expf(ps[q] - M);
       Z = fmaf(f, ps[4 + q], Z);
       a0 = fmaf(f, ps[8 + q * 128 + lane], a0);
       a1 = fmaf(f, ps[8 + q * 128 + 64 + lane], a1);
     }
   }
-  const float inv = 1.0f / Z;
+  const float inv = Z > 0.f ? 1.0f / Z : 0.f;   // no keys at all (a paged group of length 0): zeros
   float y0 = a0 * inv + a1 * inv, y1 = a0 * inv - a1 * inv;
   y0 = butterfly_lane<1>(y0, lane & 1);   y1 = butterfly_lane<1>(y1, lane & 1);
   y0 = butterfly_lane<2>(y0, lane & 2);   y1 = butterfly_lane<2>(y1, lane & 2);
@@ -2240,15 +2273,15 @@ __global__ __launch_bounds__(64) void attn_combine128_kernel(const float* __rest
 // value encoders' rules (compares of |u| against t nu sqrt(d), stored bit j =
 // bit j of the magnitude index XOR the sign, the top bit the complement of
 // the sign) and writes it into the value's 16-value tile bit by bit with
-// atomic OR / AND: the tile's other values are not touched.
+// atomic OR / AND: the tile's other values are not touched.  Input row r
+// goes to record n of group (or pool page) g of a buffer of Ncap records per
+// group.
 template <int BV, bool BF16>
-__device__ __forceinline__ void append_value128(const void* __restrict__ values, int64_t r, int64_t T,
-                                                int64_t Ncap, int64_t pos, int lane,
+__device__ __forceinline__ void append_value128(const void* __restrict__ values, int64_t r, int64_t g,
+                                                int64_t n, int64_t Ncap, int lane,
                                                 uint32_t* __restrict__ codes, uint16_t* __restrict__ norms,
                                                 const DevConsts* __restrict__ cst) {
   constexpr int KV = 1 << (BV - 1);   // levels on the positive half
-  const int64_t g = r / T;
-  const int64_t n = pos + (r - g * T);
   const int din = int(cst->din);
   float a, b;
   if constexpr (BF16) {
@@ -2300,14 +2333,28 @@ __device__ __forceinline__ void append_value128(const void* __restrict__ values,
   if (lane == 0) norms[g * Ncap + n] = zero ? uint16_t(0) : f2h_bits(nu);
 }
 
-template <int BV, bool BF16>
+// PAGED: row r of the [G][T] append goes to the pool page and slot the page
+// map gives (pages of pm.page_size records; rows without a valid page are
+// not written); else to record pos + r % T of group r / T of a cache of Ncap
+// records per group.
+template <int BV, bool BF16, bool PAGED>
 __global__ __launch_bounds__(256) void append_values128_kernel(
     const void* __restrict__ values, int64_t G, int64_t T, int64_t Ncap, int64_t pos,
-    uint32_t* __restrict__ codes, uint16_t* __restrict__ norms, const DevConsts* __restrict__ cst) {
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ norms, const DevConsts* __restrict__ cst,
+    PageMap pm) {
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // wave-uniform grid-stride loop over the G T values (no barriers)
-  for (int64_t r = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); r < G * T; r += int64_t(gridDim.x) * 4)
-    append_value128<BV, BF16>(values, r, T, Ncap, pos, lane, codes, norms, cst);
+  for (int64_t r = int64_t(blockIdx.x) * 4 + wave; r < G * T; r += int64_t(gridDim.x) * 4) {
+    int64_t dg, dn;
+    if constexpr (PAGED) {
+      if (page_dest(pm, r, dg, dn)) append_value128<BV, BF16>(values, r, dg, dn, pm.page_size, lane, codes, norms, cst);
+    } else {
+      dg = r / T;
+      dn = pos + (r - dg * T);
+      append_value128<BV, BF16>(values, r, dg, dn, Ncap, lane, codes, norms, cst);
+    }
+  }
 }
 
 // ============================================================== measurement helpers
@@ -2563,8 +2610,8 @@ hipError_t launch_append_values(const Codebook& cb, const void* values, int dtyp
   }
   const unsigned grid = unsigned(std::min<int64_t>((G * T + 3) / 4, int64_t(num_cus()) * 8));
 #define TQ_AV(BB, BF)                                                                              \
-  hipLaunchKernelGGL((append_values128_kernel<BB, BF>), dim3(grid), dim3(256), 0, s, values, G, T, Ncap, \
-                     pos, codes, norms, cb.d_consts)
+  hipLaunchKernelGGL((append_values128_kernel<BB, BF, false>), dim3(grid), dim3(256), 0, s, values, G, T, \
+                     Ncap, pos, codes, norms, cb.d_consts, PageMap{})
   switch (cb.bits) {
     case 2: if (dtype == 1) TQ_AV(2, true); else TQ_AV(2, false); break;
     case 3: if (dtype == 1) TQ_AV(3, true); else TQ_AV(3, false); break;
@@ -2863,6 +2910,69 @@ hipError_t launch_score_paged(const Codebook& cb, const void* q, int qdtype, int
     default: if (bf) TQ_SCP(3, true); else TQ_SCP(3, false); break;
   }
 #undef TQ_SCP
+  return hipGetLastError();
+}
+
+// Value append into a paged value pool (num_pages pages of page_size value
+// records, laid out as a value buffer of num_pages groups): the latency
+// kernel, one value per wave, for any number of rows.
+hipError_t launch_append_values_paged(const Codebook& cb, const void* values, int dtype, int64_t G, int64_t T,
+                                      void* pool, int64_t num_pages, int page_size, const int32_t* table,
+                                      int ppg, const int32_t* pos, hipStream_t s) {
+  uint32_t* codes = static_cast<uint32_t*>(pool);
+  uint16_t* norms = reinterpret_cast<uint16_t*>(codes + num_pages * (int64_t(page_size) / 16) * 16 *
+                                                              int64_t(cb.bits) * (cb.d / 32));
+  const PageMap pm{table, pos, nullptr, uint32_t(T), ppg, page_size, int32_t(num_pages), 0};
+  const unsigned grid = unsigned(std::min<int64_t>((G * T + 3) / 4, int64_t(num_cus()) * 8));
+#define TQ_AVP(BB, BF)                                                                             \
+  hipLaunchKernelGGL((append_values128_kernel<BB, BF, true>), dim3(grid), dim3(256), 0, s, values, G, T, \
+                     int64_t(page_size), int64_t(0), codes, norms, cb.d_consts, pm)
+  switch (cb.bits) {
+    case 2: if (dtype == 1) TQ_AVP(2, true); else TQ_AVP(2, false); break;
+    case 3: if (dtype == 1) TQ_AVP(3, true); else TQ_AVP(3, false); break;
+    default: if (dtype == 1) TQ_AVP(4, true); else TQ_AVP(4, false); break;
+  }
+#undef TQ_AVP
+  return hipGetLastError();
+}
+
+// Decode attention over a paged key pool and a paged value pool that share
+// one page table: the scorer in paged form with the value phase (each
+// 64-key tile's key and value records from its page), then the combine.
+// Logits [G][Qg][Lmax] in the workspace, as for tq_attention_decode with
+// N = Lmax.
+hipError_t launch_attention_paged(const Codebook& cb, const void* q, int qdtype, int64_t G, int Qg,
+                                  const void* kpool, const void* vpool, int64_t num_pages, int page_size,
+                                  const int32_t* table, int ppg, const int32_t* lens, int64_t Lmax,
+                                  float scale, float* out, void* ws, hipStream_t s) {
+  int64_t chunk = 0;
+  const dim3 grid = score_grid(G, Qg, Lmax, chunk);
+  float* logits = static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         (size_t(G) * Qg * Lmax * 4 + 255) / 256 * 256);
+  const uint4* planes = static_cast<const uint4*>(kpool);
+  const uint32_t* norms =
+      static_cast<const uint32_t*>(kpool) + num_pages * int64_t(page_size) * int64_t(cb.bits) * (cb.d / 32);
+  const uint4* vpl = static_cast<const uint4*>(vpool);
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(
+      static_cast<const uint32_t*>(vpool) +
+      num_pages * (int64_t(page_size) / 16) * 16 * int64_t(cb.bits) * (cb.d / 32));
+  const AttnArgs aa{vpl, vn, part, scale, int64_t(page_size)};
+  const PageMap pm{table, nullptr, lens, 1u, ppg, page_size, int32_t(num_pages), 0};
+  const bool bf = qdtype == 1;
+#define TQ_ATP(BB, QB, BVV)                                                                      \
+  hipLaunchKernelGGL((score128_kernel<BB, QB, true, BVV>), grid, dim3(kScoreThreads), 0, s, q, planes, \
+                     norms, Lmax, int64_t(page_size), Qg, cb.d_in, chunk, logits, cb.d_consts, cb.d_frag16, pm, aa)
+  switch (cb.bits) {
+    case 2: if (bf) TQ_ATP(1, true, 2); else TQ_ATP(1, false, 2); break;
+    case 3: if (bf) TQ_ATP(2, true, 3); else TQ_ATP(2, false, 3); break;
+    default: if (bf) TQ_ATP(3, true, 4); else TQ_ATP(3, false, 4); break;
+  }
+#undef TQ_ATP
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine128_kernel, dim3(unsigned(G * Qg)), dim3(64), 0, s, part, Qg,
+                     int(grid.y), int(grid.z), cb.d_consts, out);
   return hipGetLastError();
 }
 

@@ -140,6 +140,19 @@ int main() {
   EXPECT(tq_paged_append_keys(cb, p, TQ_F32, 1, 1, p, 4, 64, reinterpret_cast<int32_t*>(buf + 2), 1, i32,
                               nullptr) == TQ_ERR_ARG);
   EXPECT(tq_paged_score(cw, p, TQ_F32, 1, 4, p, 4, 64, i32, 1, i32, 64, f, nullptr) == TQ_ERR_UNSUPPORTED);
+  EXPECT(tq_paged_append_values(cb, p, TQ_F32, 1, 1, p, 4, 48, i32, 1, i32, nullptr) == TQ_ERR_UNSUPPORTED);
+  EXPECT(tq_paged_append_values(cb, p, TQ_F32, 1, 1, p, 4, 64, i32, 1, nullptr, nullptr) == TQ_ERR_ARG);
+  EXPECT(tq_paged_append_values(cb, p, TQ_F32, 1, 1, p, 4, 64, i32, 1, i32, nullptr) == TQ_ERR_HIP);
+  EXPECT(tq_paged_attention(cb, p, TQ_F32, 1, 4, p, p, 4, 64, i32, 1, i32, 0, 0.1f, f, p, 1 << 16, nullptr) ==
+         TQ_ERR_ARG);
+  EXPECT(tq_paged_attention(cb, p, TQ_F32, 1, 4, p, p, 4, 64, i32, 1, i32, 64, -1.f, f, p, 1 << 16, nullptr) ==
+         TQ_ERR_ARG);
+  EXPECT(tq_paged_attention(cb, p, TQ_F32, 1, 4, p, p, 4, 64, i32, 1, i32, 64, 0.1f, f, nullptr, 0, nullptr) ==
+         TQ_ERR_WORKSPACE);
+  EXPECT(tq_paged_attention(cw, p, TQ_F32, 1, 4, p, p, 4, 64, i32, 1, i32, 64, 0.1f, f, p, 1 << 16, nullptr) ==
+         TQ_ERR_UNSUPPORTED);
+  EXPECT(tq_paged_attention(cb, p, TQ_F32, 1, 4, p, p, 4, 64, i32, 1, i32, 64, 0.1f, f, p, 1 << 16, nullptr) ==
+         TQ_ERR_HIP);
   EXPECT(tq_dense_logits_bf16(p, p, 1, 9, 10, 128, f, nullptr) == TQ_ERR_UNSUPPORTED);
   EXPECT(tq_clock_probe(nullptr, 10, nullptr) == TQ_ERR_ARG);
   EXPECT(tq_stream_probe(p, 17, nullptr, 0, 0, nullptr) == TQ_ERR_ARG);

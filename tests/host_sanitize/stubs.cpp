@@ -66,6 +66,11 @@ hipError_t launch_encode_values(const Codebook&, const void*, int, int64_t, int6
 }
 hipError_t launch_attention(const Codebook&, const void*, int, int64_t, int, const void*, const void*,
                             int64_t, int64_t, float, float*, void*, hipStream_t) { return kNo; }
+hipError_t launch_append_values_paged(const Codebook&, const void*, int, int64_t, int64_t, void*, int64_t, int,
+                                      const int32_t*, int, const int32_t*, hipStream_t) { return kNo; }
+hipError_t launch_attention_paged(const Codebook&, const void*, int, int64_t, int, const void*, const void*,
+                                  int64_t, int, const int32_t*, int, const int32_t*, int64_t, float, float*,
+                                  void*, hipStream_t) { return kNo; }
 hipError_t launch_append_keys(const Codebook&, const void*, int, int64_t, int64_t, int64_t, int64_t, void*,
                               hipStream_t) { return kNo; }
 hipError_t launch_append_values(const Codebook&, const void*, int, int64_t, int64_t, void*, int64_t, int64_t,
