@@ -1,14 +1,12 @@
 // TurboQuant key path for d = m = 1024 (the vector-search shape) on gfx950.
 //
-// Encode runs as two kernels over a chunk of keys:
-//   rotate1024_kernel  one key per wave: y = H D k / (nu sqrt(d)) (1024-point
-//                      butterfly: four stages inside the lane, six across
-//                      lanes), Lloyd-Max codes -> code planes, nu and rho, and
-//                      the scaled residual 2^12 (y - c[code]) to a workspace;
-//   qjl1024_kernel     the QJL projection p = (S R^T) r_rot for 64 keys per
-//                      workgroup on the matrix cores (S R^T exact in fp16,
-//                      r_rot split into fp16 hi + lo, fp32 accumulation),
-//                      then sign words [p < 0].
+// Encode is one kernel (encode1024_kernel), tiles of 32 keys per workgroup:
+// each wave rotates keys (y = H D k / (nu sqrt(d)), a 1024-point butterfly:
+// four stages inside the lane, six across lanes), writes their Lloyd-Max
+// code planes, nu and rho, and leaves the residual 2^12 (y - c[code]) in LDS
+// as float16 hi + lo; then the QJL projection p = (S R^T) r_rot of the tile
+// runs on the matrix cores (S R^T exact in fp16, fp32 accumulation) and the
+// sign words [p < 0] are stored.
 // [ICLR 2026 paper digest, "Step 1: PolarQuant" (R = H_d D / sqrt(d)) and the
 //  implementation pseudocode (zero vectors, sign convention); Qiita
 //  explainer, "Stage 2: QJL" (sign sketch of the residual).]
@@ -82,135 +80,169 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------- rotate
-// Lane L holds coordinates 16 L + t, t = 0..15: strides 1..8 inside the lane,
-// 16..512 across lanes.  Each lane fills 16 bits of a plane word (word L / 2,
-// bits 16 (L & 1) + t); even lanes then hold whole words after one DPP swap.
-// The residual is written as 2^12 (y - c[code]) (unit-vector units), zero for
-// zero keys, in natural coordinate order: ws[key][1024] float32.
-template <int B, bool BF16>
-__global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict__ keys, int64_t k0,
-                                                         int64_t nk, int64_t N,
-                                                         uint32_t* __restrict__ planes,
-                                                         uint32_t* __restrict__ norms,
-                                                         float* __restrict__ ws,
-                                                         const DevConsts* __restrict__ cst) {
-  constexpr int K = 1 << (B - 1);   // levels on the positive half
-  constexpr int P = B + 1;
-  const int lane = threadIdx.x & 63;
-  const int64_t wave0 = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int64_t wstride = int64_t(gridDim.x) * 4;
+// One key per wave.  Lane L holds coordinates 16 L + t, t = 0..15: strides
+// 1..8 inside the lane, 16..512 across lanes.  Each lane fills 16 bits of a
+// plane word (word L / 2, bits 16 (L & 1) + t); even lanes then hold whole
+// words after one DPP swap.  The residual comes back as 2^12 (y - c[code])
+// (unit-vector units), zero for zero keys.
+template <int B>
+struct Rot1024 {
+  static constexpr int K = 1 << (B - 1);   // levels on the positive half
   float tpos[K > 1 ? K - 1 : 1], cpos[K];
-#pragma unroll
-  for (int k = 0; k < K - 1; ++k) tpos[k] = cst->tpos[k];
-#pragma unroll
-  for (int k = 0; k < K; ++k) cpos[k] = cst->cpos_s[k];
-  const float sqrt_d = cst->sqrt_d;
-  const uint32_t dn = (cst->dneg[lane >> 1] >> (16 * (lane & 1))) & 0xffffu;
-  // rows of din <= 1024 elements (a multiple of 16): lanes at or past
-  // din / 16 hold zero padding (their loads re-read the row's first chunk)
-  const int din = int(cst->din);
-  const bool lane_in = 16 * lane < din;
-  const int col = lane_in ? 16 * lane : 0;
+  float sqrt_d;
+  uint32_t dn;     // the lane's 16 sign bits of D
+  int din, col;    // row length; the lane's first input column (0 for padding lanes)
+  bool lane_in;    // lanes at or past din / 16 hold zero padding
 
-  for (int64_t w = wave0; w < nk; w += wstride) {
-    const int64_t kk = k0 + w;   // key index over [G][N]
-    float x[16];
-    if constexpr (BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + kk * din + col);
-      uint4 a = src[0], b = src[1];
-      if (!lane_in) a = b = make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  __device__ __forceinline__ void load(const DevConsts* __restrict__ cst, int lane) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[2 * i] = __uint_as_float(u[i] << 16);
-        x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-      }
-    } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + kk * din + col);
+    for (int k = 0; k < K - 1; ++k) tpos[k] = cst->tpos[k];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float4 v = src[i];
-        if (!lane_in) v = make_float4(0.f, 0.f, 0.f, 0.f);
-        x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-      }
-    }
-    float nu2 = 0.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) nu2 = fmaf(x[t], x[t], nu2);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) x[t] = __uint_as_float(__float_as_uint(x[t]) ^ (((dn >> t) & 1u) << 31));
-    // first stage adds +0: sign-flipped zeros would otherwise leave -0, and an
-    // exact zero must count as non-negative
-#pragma unroll
-    for (int t = 0; t < 16; t += 2) {
-      const float a = x[t], b = x[t + 1];
-      x[t] = (a + b) + 0.0f;
-      x[t + 1] = (a - b) + 0.0f;
-    }
-#pragma unroll
-    for (int st = 2; st < 16; st <<= 1)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        if (t & st) continue;
-        const float a = x[t], b = x[t + st];
-        x[t] = a + b;
-        x[t + st] = a - b;
-      }
-    stage_lanes<1>(x, lane);
-    stage_lanes<2>(x, lane);
-    stage_lanes<4>(x, lane);
-    stage_lanes<8>(x, lane);
-    stage_lanes<16>(x, lane);
-    stage_lanes32(x, lane);
+    for (int k = 0; k < K; ++k) cpos[k] = cst->cpos_s[k];
+    sqrt_d = cst->sqrt_d;
+    dn = (cst->dneg[lane >> 1] >> (16 * (lane & 1))) & 0xffffu;
+    // rows of din <= 1024 elements (a multiple of 16): padding lanes re-read
+    // the row's first chunk and zero it
+    din = int(cst->din);
+    lane_in = 16 * lane < din;
+    col = lane_in ? 16 * lane : 0;
+  }
+};
 
-    nu2 = wave_sum(nu2);
-    const float nu = sqrtf(nu2);
-    const bool zero = !(nu >= 1e-10f);
-    const float nsd = nu * sqrt_d;                          // u = y nu sqrt(d)
-    const float gsc = zero ? 0.f : kResidualScale / nsd;    // u -> 2^12 y
-    float tu[K > 1 ? K - 1 : 1];
-#pragma unroll
-    for (int k = 0; k < K - 1; ++k) tu[k] = tpos[k] * nsd;
+// the lane's 16 input coordinates of a key, as loaded (bf16: two 16-byte
+// loads; float32: four)
+template <bool BF16> struct KeyRegs1024;
+template <> struct KeyRegs1024<true> {
+  uint4 v[2];
+  static constexpr int kParts = 2;
+};
+template <> struct KeyRegs1024<false> {
+  float4 v[4];
+  static constexpr int kParts = 4;
+};
 
-    uint32_t wu = 0u, wd[K > 1 ? K - 1 : 1];
-#pragma unroll
-    for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k] = 0u;
-    float rho2 = 0.f;
-    float ep[16];
-#pragma unroll
-    for (int t = 15; t >= 0; --t) {   // pushed last = bit 0: bit t holds coordinate 16 L + t
-      const float u = x[t], a = fabsf(u);
-      wu = push_sign(wu, u);
-      float mag = cpos[0];
-#pragma unroll
-      for (int k = 0; k < K - 1; ++k) {
-        const float dk = a - tu[k];
-        wd[k] = push_sign(wd[k], dk);
-        mag = (dk >= 0.f) ? cpos[k + 1] : mag;
-      }
-      const float e = fmaf(u, gsc, -copysignf(mag, u));     // 2^12 (y - c[code])
-      ep[t] = zero ? 0.f : e;
-      rho2 = fmaf(ep[t], ep[t], rho2);
-    }
-    rho2 = wave_sum(rho2);
-    const float rho = zero ? 0.f : sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+template <bool BF16>
+__device__ __forceinline__ void load_key_part(KeyRegs1024<BF16>& r, int part, const void* __restrict__ keys,
+                                              int64_t kk, int din, int col) {
+  // streamed once: non-temporal, so the keys do not push the L2-resident
+  // sketch fragments out
+  if constexpr (BF16) {
+    const u32x4 v = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(keys) + kk * din + col) + part);
+    r.v[part] = make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    const f32x4 v = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4*>(static_cast<const float*>(keys) + kk * din + col) + part);
+    r.v[part] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
 
-    // the low halves (even lanes) take the odd lane's 16 bits as their high half
-    const uint32_t fu = (wu & 0xffffu) | (lane_xor1_u(wu) << 16);
-    uint32_t fd[K > 1 ? K - 1 : 1];
+template <bool BF16>
+__device__ __forceinline__ void unpack_key(const KeyRegs1024<BF16>& r, bool lane_in, float (&x)[16]) {
+  if constexpr (BF16) {
+    const uint32_t u[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
 #pragma unroll
-    for (int k = 0; k < K - 1; ++k) fd[k] = (wd[k] & 0xffffu) | (lane_xor1_u(wd[k]) << 16);
-    uint32_t pw[P - 1];
-    if constexpr (B == 1) {
-      pw[0] = ~fu;
-    } else if constexpr (B == 2) {
-      pw[1] = ~fu;
-      pw[0] = ~(fu ^ fd[0]);
-    } else {
-      pw[2] = ~fu;
-      pw[1] = ~(fu ^ fd[1]);
-      pw[0] = ~(fu ^ fd[0] ^ fd[1] ^ fd[2]);
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = lane_in ? __uint_as_float(u[i] << 16) : 0.f;
+      x[2 * i + 1] = lane_in ? __uint_as_float(u[i] & 0xffff0000u) : 0.f;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = r.v[i];
+      x[4 * i] = lane_in ? v.x : 0.f;
+      x[4 * i + 1] = lane_in ? v.y : 0.f;
+      x[4 * i + 2] = lane_in ? v.z : 0.f;
+      x[4 * i + 3] = lane_in ? v.w : 0.f;
+    }
+  }
+}
+
+// y = H D k / (nu sqrt(d)), Lloyd-Max codes -> code planes, nu and rho ->
+// norms (both written when `store`), residual 2^12 (y - c[code]) -> ep.
+template <int B>
+__device__ __forceinline__ void rotate_quantize1024(float (&x)[16], const Rot1024<B>& rc, int lane, int64_t kk,
+                                                    int64_t N, bool store, uint32_t* __restrict__ planes,
+                                                    uint32_t* __restrict__ norms, float (&ep)[16]) {
+  constexpr int K = Rot1024<B>::K;
+  constexpr int P = B + 1;
+  float nu2 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) nu2 = fmaf(x[t], x[t], nu2);
+#pragma unroll
+  for (int t = 0; t < 16; ++t) x[t] = __uint_as_float(__float_as_uint(x[t]) ^ (((rc.dn >> t) & 1u) << 31));
+  // first stage adds +0: sign-flipped zeros would otherwise leave -0, and an
+  // exact zero must count as non-negative
+#pragma unroll
+  for (int t = 0; t < 16; t += 2) {
+    const float a = x[t], b = x[t + 1];
+    x[t] = (a + b) + 0.0f;
+    x[t + 1] = (a - b) + 0.0f;
+  }
+#pragma unroll
+  for (int st = 2; st < 16; st <<= 1)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      if (t & st) continue;
+      const float a = x[t], b = x[t + st];
+      x[t] = a + b;
+      x[t + st] = a - b;
+    }
+  stage_lanes<1>(x, lane);
+  stage_lanes<2>(x, lane);
+  stage_lanes<4>(x, lane);
+  stage_lanes<8>(x, lane);
+  stage_lanes<16>(x, lane);
+  stage_lanes32(x, lane);
+
+  nu2 = wave_sum(nu2);
+  const float nu = sqrtf(nu2);
+  const bool zero = !(nu >= 1e-10f);
+  const float nsd = nu * rc.sqrt_d;                       // u = y nu sqrt(d)
+  const float gsc = zero ? 0.f : kResidualScale / nsd;    // u -> 2^12 y
+  float tu[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) tu[k] = rc.tpos[k] * nsd;
+
+  uint32_t wu = 0u, wd[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < (K > 1 ? K - 1 : 1); ++k) wd[k] = 0u;
+  float rho2 = 0.f;
+#pragma unroll
+  for (int t = 15; t >= 0; --t) {   // pushed last = bit 0: bit t holds coordinate 16 L + t
+    const float u = x[t], a = fabsf(u);
+    wu = push_sign(wu, u);
+    float mag = rc.cpos[0];
+#pragma unroll
+    for (int k = 0; k < K - 1; ++k) {
+      const float dk = a - tu[k];
+      wd[k] = push_sign(wd[k], dk);
+      mag = (dk >= 0.f) ? rc.cpos[k + 1] : mag;
+    }
+    const float e = fmaf(u, gsc, -copysignf(mag, u));     // 2^12 (y - c[code])
+    ep[t] = zero ? 0.f : e;
+    rho2 = fmaf(ep[t], ep[t], rho2);
+  }
+  rho2 = wave_sum(rho2);
+  const float rho = zero ? 0.f : sqrtf(rho2) * (nu * (1.0f / kResidualScale));
+
+  // the low halves (even lanes) take the odd lane's 16 bits as their high half
+  const uint32_t fu = (wu & 0xffffu) | (lane_xor1_u(wu) << 16);
+  uint32_t fd[K > 1 ? K - 1 : 1];
+#pragma unroll
+  for (int k = 0; k < K - 1; ++k) fd[k] = (wd[k] & 0xffffu) | (lane_xor1_u(wd[k]) << 16);
+  uint32_t pw[P - 1];
+  if constexpr (B == 1) {
+    pw[0] = ~fu;
+  } else if constexpr (B == 2) {
+    pw[1] = ~fu;
+    pw[0] = ~(fu ^ fd[0]);
+  } else {
+    pw[2] = ~fu;
+    pw[1] = ~(fu ^ fd[1]);
+    pw[0] = ~(fu ^ fd[0] ^ fd[1] ^ fd[2]);
+  }
+  if (store) {
     const int64_t g = kk / N, n = kk - g * N;
     if (!(lane & 1)) {
 #pragma unroll
@@ -218,9 +250,6 @@ __global__ __launch_bounds__(256) void rotate1024_kernel(const void* __restrict_
         planes[((g * P + p) * N + n) * 32 + (lane >> 1)] = zero ? 0u : pw[p];
     }
     if (lane == 0) norms[g * N + n] = zero ? 0u : (uint32_t(f2h_bits(nu)) | (uint32_t(f2h_bits(rho)) << 16));
-    float4* dst = reinterpret_cast<float4*>(ws + w * kD + 16 * lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_float4(ep[4 * i], ep[4 * i + 1], ep[4 * i + 2], ep[4 * i + 3]);
   }
 }
 
@@ -295,23 +324,27 @@ __global__ __launch_bounds__(256) void decode1024_kernel(const uint32_t* __restr
   }
 }
 
-// ---------------------------------------------------------------- QJL projection
-// Workgroup tile: all 1024 sketch rows x 64 keys; wave w owns rows
-// [128 w, 128 w + 128) (four 32-row blocks) and both 32-key blocks.  The
-// residuals stream through LDS in 64-coordinate chunks (converted to fp16
-// hi/lo fragments on the way in, double-buffered); the (S R^T) fragments,
-// exact in float16, come straight from global memory (L2-resident, 2 MB) in
-// matrix-core A order, so each product is two terms: S_rot r_hi + S_rot r_lo.
-// Sixteen waves would cap registers at 128; eight waves with 128 accumulators
-// each keep the fragment reads almost two k-steps ahead.
-constexpr int kQjlThreads = 512;
-constexpr int kQjlKeys = 64;
+// ---------------------------------------------------------------- encoder
+// One kernel per launch, one workgroup per CU walking tiles of 32 keys; the
+// residuals never leave the chip.  Per tile:
+//  * rotation: wave w rotates and quantises keys 4w .. 4w + 3 of the tile
+//    (one key at a time, the whole wave per key), stores their code planes
+//    and norms, and writes the residual into LDS as float16 hi + lo in the
+//    matrix core's B order: rotating lane L holds coordinates 16 L + t, which
+//    is exactly k-step L (its halves 8h .. 8h + 7 for the B lanes of half h);
+//  * sketch: wave w owns sketch rows [128 w, 128 w + 128) (four 32-row
+//    blocks) for all 32 keys and runs the 64 k-steps, each product two terms
+//    S_rot r_hi + S_rot r_lo with (S R^T) exact in float16 (fragments read
+//    from L2, 15 (row block, k-step) steps ahead in a ring of 16, the ring
+//    running on into the next tile's first steps);
+//  * signs: sign words [p < 0] through LDS, one 16-byte store per 4 words.
+// The next tile's keys are loaded into registers as the sketch loop starts.
+// LDS: 128 KB of residual fragments + 4 KB of sign words.
+constexpr int kEncThreads = 512;
+constexpr int kEncKeys = 32;
+constexpr int kRing = 16;
 
-struct QjlLds {
-  uint4 b[2][4][2][2][64];   // [buf][k-step][key block][hi/lo][lane]: 32 KB
-};
-
-__device__ __forceinline__ void split_f16x8(const float (&v)[8], uint4& hi, uint4& lo) {
+__device__ __forceinline__ void split_f16x8(const float* v, uint4& hi, uint4& lo) {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -325,112 +358,133 @@ __device__ __forceinline__ void split_f16x8(const float (&v)[8], uint4& hi, uint
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-__global__ __launch_bounds__(kQjlThreads, 1) void qjl1024_kernel(const float* __restrict__ ws, int64_t k0,
-                                                                 int64_t nk, int64_t N, int P,
-                                                                 uint32_t* __restrict__ planes,
-                                                                 const uint4* __restrict__ fragA) {
-  __shared__ QjlLds sm;
-  __shared__ uint32_t s_sign[kQjlKeys][33];   // [key][word], padded
+template <int B, bool BF16>
+__global__ __launch_bounds__(kEncThreads, 1) void encode1024_kernel(const void* __restrict__ keys, int64_t nk,
+                                                                    int64_t N, uint32_t* __restrict__ planes,
+                                                                    uint32_t* __restrict__ norms,
+                                                                    const uint4* __restrict__ fragA,
+                                                                    const DevConsts* __restrict__ cst) {
+  constexpr int P = B + 1;
+  constexpr int kParts = KeyRegs1024<BF16>::kParts;
+  constexpr int kKeysPerWave = kEncKeys / (kEncThreads / 64);   // 4
+  // [k-step][hi, lo][B lane ^ k-step]: the rotating lane L = k-step writes
+  // the slots (32 h + key) ^ L, so the 8 lanes of one write cycle hit 8
+  // different bank groups; a B read of one k-step is a permutation of one
+  // contiguous 1 KB row
+  __shared__ uint4 sb[64][2][64];
+  __shared__ uint32_t s_sign[kEncKeys][33];   // [key][word], padded
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
-  const int64_t ntiles = (nk + kQjlKeys - 1) / kQjlKeys;
-  // staging: thread -> (key, 8 coordinates) of a 64-coordinate chunk
-  const int skey = tid >> 3, spart = tid & 7;
+  Rot1024<B> rc;
+  rc.load(cst, lane);
+  const int64_t ntiles = (nk + kEncKeys - 1) / kEncKeys;
 
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t kb = tile * kQjlKeys;
-    const int64_t src_key = std::min<int64_t>(kb + skey, nk - 1);
-    const float* srow = ws + src_key * kD + 8 * spart;
-    auto load_chunk = [&](int c, float (&v)[8]) {
-      const float4* p = reinterpret_cast<const float4*>(srow + 64 * c);
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    };
-    auto store_chunk = [&](int buf, const float (&v)[8]) {
+  // A fragments: row block 4 w + rb, k-step ks; step = 4 ks + rb.  Buffer
+  // loads: the wave's 256 KB of fragments as the resource, the lane's 16-byte
+  // slot as the vector offset, the step's 1 KB row as the scalar offset.
+  const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(fragA + size_t(4 * wave) * 64 * 64), short(0), 4 * 64 * 64 * 16, 0x00020000);
+  const int voff = 16 * lane;
+  auto load_a = [&](int step, half8& ah) {
+    const int ks = step >> 2, rb = step & 3;
+    ah = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(frs, voff, (rb * 64 + ks) * 1024, 0));
+  };
+  half8 ah[kRing];
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i) load_a(i, ah[i]);
+
+  KeyRegs1024<BF16> pf[kKeysPerWave];
+  auto key_of = [&](int64_t tile, int i) {   // clamped: tail keys re-read the last key
+    return std::min<int64_t>(tile * kEncKeys + kKeysPerWave * wave + i, nk - 1);
+  };
+  int64_t tile = blockIdx.x;
+  if (tile < ntiles) {
+#pragma unroll
+    for (int i = 0; i < kKeysPerWave; ++i)
+#pragma unroll
+      for (int part = 0; part < kParts; ++part) load_key_part<BF16>(pf[i], part, keys, key_of(tile, i), rc.din, rc.col);
+  }
+
+  for (; tile < ntiles; tile += gridDim.x) {
+#pragma unroll
+    for (int i = 0; i < kKeysPerWave; ++i) {
+      const int n = kKeysPerWave * wave + i;
+      const int64_t kk = tile * kEncKeys + n;
+      float x[16], ep[16];
+      unpack_key<BF16>(pf[i], rc.lane_in, x);
+      rotate_quantize1024<B>(x, rc, lane, kk, N, kk < nk, planes, norms, ep);
       uint4 hi, lo;
-      split_f16x8(v, hi, lo);
-      // coordinates 8 spart..8 spart+7 of the chunk: k-step spart / 2, k half spart & 1
-      const int ks = spart >> 1, slot = (skey & 31) + 32 * (spart & 1), cb = skey >> 5;
-      sm.b[buf][ks][cb][0][slot] = hi;
-      sm.b[buf][ks][cb][1][slot] = lo;
-    };
-    float v[8];
-    load_chunk(0, v);
-    store_chunk(0, v);
+      split_f16x8(ep, hi, lo);
+      sb[lane][0][n ^ lane] = hi;
+      sb[lane][1][n ^ lane] = lo;
+      split_f16x8(ep + 8, hi, lo);
+      sb[lane][0][(32 + n) ^ lane] = hi;
+      sb[lane][1][(32 + n) ^ lane] = lo;
+    }
     __syncthreads();
 
-    f32x16 acc[4][2] = {};
-    // A fragments (row block rb of this wave, global k-step ks; exact in
-    // float16): read seven (row block, k-step) steps ahead into a ring of
-    // eight (an L2 read under full load takes longer than three steps' 12
-    // products; seven steps measured 10% faster than three)
-    const uint4* fa = fragA + (size_t(4 * wave) * 64) * 64 + lane;
-    auto load_a = [&](int step, half8& ah) {   // step = 4 ks + rb
-      const int ks = step >> 2, rb = step & 3;
-      ah = __builtin_bit_cast(half8, fa[(size_t(rb) * 64 + ks) * 64]);
-    };
-    half8 ah[8];
+    // the next tile's keys: in flight while the first ring steps run
+    const int64_t next = tile + gridDim.x;
+    if (next < ntiles) {
 #pragma unroll
-    for (int i = 0; i < 7; ++i) load_a(i, ah[i]);
+      for (int i = 0; i < kKeysPerWave; ++i)
+#pragma unroll
+        for (int part = 0; part < kParts; ++part) load_key_part<BF16>(pf[i], part, keys, key_of(next, i), rc.din, rc.col);
+    }
+    f32x16 acc[4] = {};
+    constexpr int kKsIter = kRing / 4;
+    // B fragments one k-step ahead; the schedule is pinned step by step so
+    // that each fragment load goes out kRing - 1 steps before its products
+    half8 bh = __builtin_bit_cast(half8, sb[0][0][lane]);
+    half8 bl = __builtin_bit_cast(half8, sb[0][1][lane]);
 #pragma unroll 1
-    for (int c = 0; c < 16; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < 16) load_chunk(c + 1, v);
+    for (int c = 0; c < 64 / kKsIter; ++c) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        half8 bh[2], bl[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          bh[cb] = __builtin_bit_cast(half8, sm.b[buf][ks][cb][0][lane]);
-          bl[cb] = __builtin_bit_cast(half8, sm.b[buf][ks][cb][1][lane]);
-        }
+      for (int k4 = 0; k4 < kKsIter; ++k4) {
+        const int ks = kKsIter * c + k4;
+        const int kn = (ks + 1) & 63;
+        const half8 nh = __builtin_bit_cast(half8, sb[kn][0][lane ^ kn]);
+        const half8 nl = __builtin_bit_cast(half8, sb[kn][1][lane ^ kn]);
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const int step = 16 * c + 4 * ks + rb;           // ring slot = step % 8
-          const int slot = (4 * ks + rb) & 7;
-          if (step + 7 < 256) load_a(step + 7, ah[(slot + 7) & 7]);
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[slot], bh[cb], acc[rb][cb], 0, 0, 0);
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[slot], bl[cb], acc[rb][cb], 0, 0, 0);
-          }
+          const int st = 4 * k4 + rb;              // step kRing c + st; ring slot st
+          load_a((kRing * c + st + kRing - 1) & 255, ah[(st + kRing - 1) % kRing]);
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[st], bh, acc[rb], 0, 0, 0);
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[st], bl, acc[rb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        bh = nh;
+        bl = nl;
       }
-      if (c + 1 < 16) store_chunk(buf ^ 1, v);
-      __syncthreads();
     }
 
     // sign words: lane (key kl, half h) holds rows 8 (v / 4) + 4 h + (v % 4) of
     // each 32-row block; spread the 16 bits into nibbles and OR the halves
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 4; ++rb) {
+      uint32_t b16 = 0u;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        uint32_t b16 = 0u;
-#pragma unroll
-        for (int vv = 15; vv >= 0; --vv) b16 = push_sign(b16, acc[rb][cb][vv]);
-        uint32_t t = (b16 | (b16 << 8)) & 0x00FF00FFu;
-        t = (t | (t << 4)) & 0x0F0F0F0Fu;
-        t <<= 4 * h;
-        auto pr = __builtin_amdgcn_permlane32_swap(t, t, false, false);
-        const uint32_t word = pr[0] | pr[1];
-        if (h == 0) s_sign[32 * cb + (lane & 31)][4 * wave + rb] = word;
-      }
+      for (int vv = 15; vv >= 0; --vv) b16 = push_sign(b16, acc[rb][vv]);
+      uint32_t t = (b16 | (b16 << 8)) & 0x00FF00FFu;
+      t = (t | (t << 4)) & 0x0F0F0F0Fu;
+      t <<= 4 * h;
+      auto pr = __builtin_amdgcn_permlane32_swap(t, t, false, false);
+      const uint32_t word = pr[0] | pr[1];
+      if (h == 0) s_sign[lane & 31][4 * wave + rb] = word;
+    }
     __syncthreads();
-    // 64 keys x 32 words: thread -> (key, 4 words)
-    {
+    // 32 keys x 32 words: thread -> (key, 4 words)
+    if (tid < kEncKeys * 8) {
       const int key = tid >> 3, q4 = tid & 7;
-      const int64_t kk = kb + key;
+      const int64_t kk = tile * kEncKeys + key;
       if (kk < nk) {
-        const int64_t gk = k0 + kk;
-        const int64_t g = gk / N, n = gk - g * N;
+        const int64_t g = kk / N, n = kk - g * N;
         uint4* dst = reinterpret_cast<uint4*>(planes + ((g * P + (P - 1)) * N + n) * 32) + q4;
         *dst = make_uint4(s_sign[key][4 * q4], s_sign[key][4 * q4 + 1], s_sign[key][4 * q4 + 2],
                           s_sign[key][4 * q4 + 3]);
       }
     }
-    __syncthreads();
   }
 }
 
@@ -1000,39 +1054,24 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqtopk1024_kernel(
 
 }  // namespace
 
-size_t encode_wide_chunk_keys() { return size_t(1) << 16; }   // 64K keys: 256 MiB of residuals
-
 hipError_t launch_encode_wide(const Codebook& cb, const void* keys, int dtype, int64_t G, int64_t N,
                               void* packed, hipStream_t s) {
   const int64_t total = G * N;
-  const int P = cb.bits;
+  if (total == 0) return hipSuccess;
   uint32_t* planes = static_cast<uint32_t*>(packed);
-  uint32_t* norms = planes + total * int64_t(P) * (kD / 32);
-  const int64_t chunk = std::min<int64_t>(total, int64_t(encode_wide_chunk_keys()));
-  float* ws = nullptr;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), size_t(chunk) * kD * sizeof(float), s);
-  if (e != hipSuccess) return e;
-  const int cus = std::max(1, cb.num_cus);
-  for (int64_t k0 = 0; k0 < total && e == hipSuccess; k0 += chunk) {
-    const int64_t nk = std::min<int64_t>(chunk, total - k0);
-    const int rgrid = int(std::min<int64_t>((nk + 3) / 4, int64_t(cus) * 8));
-#define TQ_ROT(BB, BF)                                                                          \
-    hipLaunchKernelGGL((rotate1024_kernel<BB, BF>), dim3(rgrid), dim3(256), 0, s, keys, k0, nk, N, \
-                       planes, norms, ws, cb.d_consts)
-    const bool bf = dtype == 1;
-    switch (cb.bits - 1) {
-      case 1: if (bf) TQ_ROT(1, true); else TQ_ROT(1, false); break;
-      case 2: if (bf) TQ_ROT(2, true); else TQ_ROT(2, false); break;
-      default: if (bf) TQ_ROT(3, true); else TQ_ROT(3, false); break;
-    }
-#undef TQ_ROT
-    const int qgrid = int(std::min<int64_t>((nk + kQjlKeys - 1) / kQjlKeys, int64_t(cus)));
-    hipLaunchKernelGGL(qjl1024_kernel, dim3(qgrid), dim3(kQjlThreads), 0, s, ws, k0, nk, N, P, planes,
-                       cb.d_fragW);
-    e = hipGetLastError();
+  uint32_t* norms = planes + total * int64_t(cb.bits) * (kD / 32);
+  const int grid = int(std::min<int64_t>((total + kEncKeys - 1) / kEncKeys, int64_t(std::max(1, cb.num_cus))));
+#define TQ_ENC(BB, BF)                                                                               \
+  hipLaunchKernelGGL((encode1024_kernel<BB, BF>), dim3(grid), dim3(kEncThreads), 0, s, keys, total, N, \
+                     planes, norms, cb.d_fragW, cb.d_consts)
+  const bool bf = dtype == 1;
+  switch (cb.bits - 1) {
+    case 1: if (bf) TQ_ENC(1, true); else TQ_ENC(1, false); break;
+    case 2: if (bf) TQ_ENC(2, true); else TQ_ENC(2, false); break;
+    default: if (bf) TQ_ENC(3, true); else TQ_ENC(3, false); break;
   }
-  const hipError_t ef = hipFreeAsync(ws, s);
-  return e != hipSuccess ? e : ef;
+#undef TQ_ENC
+  return hipGetLastError();
 }
 
 size_t score_wide_prep_bytes(int64_t G, int Qg) {
