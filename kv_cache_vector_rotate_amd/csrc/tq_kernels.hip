@@ -2648,14 +2648,16 @@ hipError_t scratch_address(void** ptr) {
   return hipSuccess;
 }
 
-// Grid of the d = 128 scorer: (group, chunk of 4 queries, key range), with
-// enough workgroups for every CU: each (group, query chunk) unit's keys are
-// split into ranges of at least 512 keys, a multiple of 64 each.
+// Grid of the d = 128 scorer: (group, chunk of 4 queries, key range).  One
+// workgroup fills a CU, so each (group, query chunk) unit's keys are split
+// into as many ranges as fit in one round of workgroups over the CUs (at
+// least one; ranges of at least 512 keys, a multiple of 64 each): a second,
+// partial round would cost every range another set-up.
 static dim3 score_grid(int64_t G, int Qg, int64_t N, int64_t& chunk) {
   const int nqc = (Qg + 3) / 4;
   const int64_t units = G * nqc;
   const int64_t cus = num_cus();
-  int64_t want = std::max<int64_t>(1, (cus + units - 1) / units);
+  int64_t want = std::max<int64_t>(1, cus / units);
   want = std::min<int64_t>(want, std::max<int64_t>(1, (N + 511) / 512));
   chunk = ((N + want - 1) / want + 63) / 64 * 64;
   const int64_t splits = (N + chunk - 1) / chunk;
