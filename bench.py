@@ -492,10 +492,18 @@ def run_cache_step(K, cb, keys0, vals, q, G, N, Qg, steps=64):
                     "GPU time back to back"}
 
 
-def _event_times(fn, reps, warm=2):
+def _event_times(fn, reps, warm=2, preroll_s=0.0):
+    """Per-launch HIP-event times (ms) of `reps` calls of fn, after `warm`
+    untimed calls and `preroll_s` seconds of untimed back-to-back calls (the
+    core clock ramps up under load on a fresh box)."""
     import torch
     for _ in range(warm):
         fn(-1)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < preroll_s:
+        for _ in range(10):
+            fn(-1)
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i, (a, b) in enumerate(evs):
@@ -507,14 +515,16 @@ def _event_times(fn, reps, warm=2):
 
 
 def _stats(ms, alg_bytes=None, units=None, unit_name="keys"):
+    """Rates from the median launch time (the mean is reported beside it)."""
     out = {"us_median": round(float(np.median(ms)) * 1e3, 2),
+           "us_mean": round(float(ms.mean()) * 1e3, 2),
            "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
            "us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2)}
-    mean_s = float(ms.mean()) * 1e-3
+    med_s = float(np.median(ms)) * 1e-3
     if units is not None:
-        out[f"{unit_name}_per_s"] = round(units / mean_s, 1)
+        out[f"{unit_name}_per_s"] = round(units / med_s, 1)
     if alg_bytes is not None:
-        gbps = alg_bytes / mean_s / 1e9
+        gbps = alg_bytes / med_s / 1e9
         out.update({"algorithmic_bytes": int(alg_bytes), "hbm_GBps": round(gbps, 1),
                     "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)})
     return out
@@ -541,8 +551,10 @@ def run_long_context(args):
     for p_ in packed:
         K.encode_keys(cb, keys0, out=p_)
     logits = torch.empty((G, Qg, N), dtype=torch.float32, device=dev)
-    enc = _event_times(lambda i: K.encode_keys(cb, keys[i % 2], out=packed[i % npk]), max(3, args.steps // 10))
-    sc = _event_times(lambda i: K.score_logits(cb, q, packed[i % npk], N, out=logits), args.steps)
+    enc = _event_times(lambda i: K.encode_keys(cb, keys[i % 2], out=packed[i % npk]), max(10, args.steps // 2),
+                       preroll_s=args.preroll)
+    sc = _event_times(lambda i: K.score_logits(cb, q, packed[i % npk], N, out=logits), args.steps,
+                      preroll_s=args.preroll)
     dn = _event_times(lambda i: K.dense_logits_bf16(q, keys[i % 2], out=logits), args.steps)
     logit_bytes = G * Qg * N * 4
     q_bytes = q.numel() * 2
@@ -576,9 +588,11 @@ def run_cache_sweep(args):
         cb = K.Codebook(d, bits, d, 42)
         pbytes = K.packed_nbytes(cb, G, N)
         packed = [torch.empty(pbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
-        enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed[i % 2]), max(5, args.steps // 4))
+        enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed[i % 2]), max(10, args.steps // 2),
+                           preroll_s=args.preroll)
         lg = torch.empty((G, Qg, N), dtype=torch.float32, device=dev)
-        sc = _event_times(lambda i: K.score_logits(cb, q, packed[i % 2], N, out=lg), args.steps)
+        sc = _event_times(lambda i: K.score_logits(cb, q, packed[i % 2], N, out=lg), args.steps,
+                          preroll_s=args.preroll)
         est = K.score_logits(cb, q, packed[0], N).double()
         ex = exact.double()
         cos = (est * ex).sum(-1) / (est.norm(dim=-1) * ex.norm(dim=-1))
@@ -620,9 +634,10 @@ def run_search(args):
     cb = K.Codebook(d, bits, d, 42)
     pbytes = K.packed_nbytes(cb, 1, N)
     packed = torch.empty(pbytes, dtype=torch.uint8, device=dev)
-    enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed), max(2, args.steps // 50), warm=1)
+    enc = _event_times(lambda i: K.encode_keys(cb, keys, out=packed), max(10, args.steps // 2), warm=1,
+                       preroll_s=args.preroll)
     ws = torch.empty(K.score_topk_workspace_nbytes(cb, 1, Qn, N, 10), dtype=torch.uint8, device=dev)
-    tk = _event_times(lambda i: K.score_topk(cb, q, packed, N, 10, ws=ws), 3, warm=1)
+    tk = _event_times(lambda i: K.score_topk(cb, q, packed, N, 10, ws=ws), 5, warm=1, preroll_s=args.preroll)
     # recall@10 against the exact top-10 by true inner product (fp32 products
     # in chunks of 64K vectors; a quality report outside the timed launches)
     idx, _ = K.score_topk(cb, q, packed, N, 10, ws=ws)
@@ -638,9 +653,9 @@ def run_search(args):
     ex_i = best_i.cpu().numpy()
     recall = float(np.mean([len(set(est_i[j]) & set(ex_i[j])) / 10.0 for j in range(Qn)]))
     enc_flops = 2.0 * d * d * N * 2        # two fp16 products per output: S R^T (r_hi + r_lo)
-    enc_s = float(enc.mean()) * 1e-3
+    enc_s = float(np.median(enc)) * 1e-3
     tk_flops = 2.0 * d * N * Qn * 5        # 32 query rows per block: Qn = 256 fills them
-    tk_s = float(tk.mean()) * 1e-3
+    tk_s = float(np.median(tk)) * 1e-3
     out = {"metric": "vectors encoded/s; (vector, query) pairs scored/s with top-10",
            "config": {"workload": wl.name, "vectors": N, "d": d, "bits": bits, "queries": Qn, "k": 10},
            "encode": dict(_stats(enc, keys.numel() * 4 + pbytes, N, "vectors"),
