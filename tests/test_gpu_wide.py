@@ -66,6 +66,18 @@ def test_wide_encode(bits, dt):
     _encode_check(bits, keys, dtype, seed=7 + bits)
 
 
+@pytest.mark.parametrize("G,N,dt", [(37, 5, "f32"), (3, 3001, "bf16"), (1, 1, "f32")])
+def test_wide_encode_tiles_across_groups(G, N, dt):
+    """32-key tiles that span several groups (N = 5), workgroups that walk
+    more than one tile with bf16 keys (9003 keys), and a single key."""
+    rng = np.random.default_rng(100 + G + N)
+    keys = _keys(rng, G, N, unit=(dt == "f32"))
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    if dt == "bf16":
+        keys = _round_bf16(keys)
+    _encode_check(4, keys, dtype, seed=11)
+
+
 def test_wide_encode_special_keys():
     rng = np.random.default_rng(3)
     keys = _keys(rng, 1, 70)
@@ -91,8 +103,9 @@ def test_wide_encode_search_workload_sample():
 
 
 def test_wide_encode_chunk_boundary():
-    """More keys than one workspace chunk (65,536): records past the first
-    chunk are encoded exactly like the ones before it."""
+    """65,836 keys: every workgroup walks several 32-key tiles (the fragment
+    ring and the key prefetch run on from tile to tile), and records late in
+    the launch are encoded exactly like the same keys early in it."""
     rng = np.random.default_rng(8)
     n = 65536 + 300
     base = _keys(rng, 1, 300)
