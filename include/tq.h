@@ -181,10 +181,10 @@ size_t tq_packed_bytes(const tq_codebook* cb, int64_t G, int64_t N);
  * zero vectors and "0 counts as positive" [ICLR 2026 paper digest,
  * "実装の擬似コード"].
  * keys and packed are device pointers owned by the caller; G*N == 0 is a
- * no-op.  d = 1024 runs in chunks of 65,536 keys, d = 2048 and 4096 in
- * chunks of 2^26 / d keys, each through a float32 temporary of 256 MiB taken
- * from the device's stream-ordered pool (hipMallocAsync / hipFreeAsync on
- * the given stream); d = 128 allocates nothing.
+ * no-op.  d = 128 and d = 1024 allocate nothing (d = 1024 holds each tile's
+ * residuals on chip); d = 2048 and 4096 run in chunks of 2^26 / d keys, each
+ * through a float32 temporary of 256 MiB taken from the device's
+ * stream-ordered pool (hipMallocAsync / hipFreeAsync on the given stream).
  * Errors: TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_HIP (also when that
  * temporary cannot be allocated).
  */
