@@ -338,7 +338,8 @@ __global__ __launch_bounds__(256) void decode1024_kernel(const uint32_t* __restr
 //    from L2, 15 (row block, k-step) steps ahead in a ring of 16, the ring
 //    running on into the next tile's first steps);
 //  * signs: sign words [p < 0] through LDS, one 16-byte store per 4 words.
-// The next tile's keys are loaded into registers as the sketch loop starts.
+// The next tile's first keys are loaded into registers as the sketch loop
+// starts, the rest as its rotation phase starts.
 // LDS: 128 KB of residual fragments + 4 KB of sign words.
 constexpr int kEncThreads = 512;
 constexpr int kEncKeys = 32;
@@ -394,6 +395,11 @@ __global__ __launch_bounds__(kEncThreads, 1) void encode1024_kernel(const void* 
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) load_a(i, ah[i]);
 
+  // the wave's first two keys of a tile are loaded during the previous
+  // tile's sketch loop, the other two as its rotation starts (they land while
+  // the first two are rotated): registers for all four would not fit beside
+  // the accumulators and the fragment ring
+  constexpr int kEarly = 2;
   KeyRegs1024<BF16> pf[kKeysPerWave];
   auto key_of = [&](int64_t tile, int i) {   // clamped: tail keys re-read the last key
     return std::min<int64_t>(tile * kEncKeys + kKeysPerWave * wave + i, nk - 1);
@@ -401,12 +407,16 @@ __global__ __launch_bounds__(kEncThreads, 1) void encode1024_kernel(const void* 
   int64_t tile = blockIdx.x;
   if (tile < ntiles) {
 #pragma unroll
-    for (int i = 0; i < kKeysPerWave; ++i)
+    for (int i = 0; i < kEarly; ++i)
 #pragma unroll
       for (int part = 0; part < kParts; ++part) load_key_part<BF16>(pf[i], part, keys, key_of(tile, i), rc.din, rc.col);
   }
 
   for (; tile < ntiles; tile += gridDim.x) {
+#pragma unroll
+    for (int i = kEarly; i < kKeysPerWave; ++i)
+#pragma unroll
+      for (int part = 0; part < kParts; ++part) load_key_part<BF16>(pf[i], part, keys, key_of(tile, i), rc.din, rc.col);
 #pragma unroll
     for (int i = 0; i < kKeysPerWave; ++i) {
       const int n = kKeysPerWave * wave + i;
@@ -424,11 +434,11 @@ __global__ __launch_bounds__(kEncThreads, 1) void encode1024_kernel(const void* 
     }
     __syncthreads();
 
-    // the next tile's keys: in flight while the first ring steps run
+    // the next tile's first keys: in flight while the first ring steps run
     const int64_t next = tile + gridDim.x;
     if (next < ntiles) {
 #pragma unroll
-      for (int i = 0; i < kKeysPerWave; ++i)
+      for (int i = 0; i < kEarly; ++i)
 #pragma unroll
         for (int part = 0; part < kParts; ++part) load_key_part<BF16>(pf[i], part, keys, key_of(next, i), rc.din, rc.col);
     }
