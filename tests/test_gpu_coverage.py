@@ -7,7 +7,8 @@
 * value records on the full Llama-3.1-8B-shaped workload, sampled groups
   checked in full against the oracle's value encoder;
 * the vector-search encoder on the whole 16,384-vector subset the oracle
-  checks;
+  checks, and on all 1,048,576 vectors in one launch (the benchmark's
+  configuration): sampled records against the oracle, a rerun bit-identical;
 * the binding refuses buffers smaller than the call reads or writes (the C ABI
   cannot see allocation sizes), before anything is launched.
 """
@@ -135,6 +136,43 @@ def test_search_encode_whole_oracle_subset():
     for s0 in range(0, n, 4096):
         sl = slice(s0, s0 + 4096)
         check_encode(cbo, keys[0, sl], codes[0, sl], signs[0, sl], nu16[0, sl], rho16[0, sl])
+
+
+def test_search_encode_full_size_sampled():
+    """All 1,048,576 vectors of the search workload encoded in one launch, as
+    the benchmark runs it (every workgroup walks ~128 tiles): ~2,000 sampled
+    records (the first and last tiles among them) against the oracle, and a
+    second launch bit-identical to the first."""
+    wl = W.workload(4)
+    N, d, step = wl.N, wl.d, 1 << 16
+    rng = np.random.default_rng(404)
+    sample = np.unique(np.concatenate([rng.choice(N, 2000, replace=False),
+                                       [0, 1, 31, 32, 33, N - 33, N - 32, N - 1]]))
+    keys = torch.empty((1, N, d), dtype=torch.float32, device="cuda")
+    rows = []
+    print("[case] search encode full size: generating", flush=True)
+    for s0 in range(0, N, step):
+        chunk = W.group_keys(wl, 0, s0, min(step, N - s0))
+        keys[0, s0:s0 + chunk.shape[0]] = torch.from_numpy(chunk).to("cuda")
+        sel = sample[(sample >= s0) & (sample < s0 + chunk.shape[0])]
+        rows.append(chunk[sel - s0])
+    host = np.concatenate(rows)
+    cb = K.Codebook(d, wl.bits)
+    cbo = O.make_codebook(d, wl.bits, d, 42)
+    print("[case] search encode full size: encoding", flush=True)
+    packed = K.encode_keys(cb, keys)
+    again = K.encode_keys(cb, keys)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, again)
+    # records of the sampled vectors, gathered into a packed buffer of their own
+    P = wl.bits
+    words = packed.view(torch.int32)
+    planes = words[:P * N * (d // 32)].view(P, N, d // 32)
+    norms = words[P * N * (d // 32):P * N * (d // 32) + N]
+    idx = torch.from_numpy(sample).to("cuda")
+    sub = torch.cat([planes[:, idx, :].reshape(-1), norms[idx]]).cpu().numpy().view(np.uint8)
+    codes, signs, nu16, rho16 = O.unpack(cbo, sub, 1, len(sample))
+    check_encode(cbo, host, codes[0], signs[0], nu16[0], rho16[0])
 
 
 def test_binding_refuses_undersized_buffers():
