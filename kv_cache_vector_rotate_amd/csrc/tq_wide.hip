@@ -382,8 +382,11 @@ __global__ __launch_bounds__(kEncThreads, 1) void encode1024_kernel(const void* 
   const int64_t ntiles = (nk + kEncKeys - 1) / kEncKeys;
 
   // A fragments: row block 4 w + rb, k-step ks; step = 4 ks + rb.  Buffer
-  // loads: the wave's 256 KB of fragments as the resource, the lane's 16-byte
-  // slot as the vector offset, the step's 1 KB row as the scalar offset.
+  // loads: the wave's 256 KB of fragments as the resource (its size as the
+  // range, so a load past it returns zeros; the last word 0x00020000 gives
+  // the 32-bit data format that raw buffer loads need on this family), the
+  // lane's 16-byte slot as the vector offset, the step's 1 KB row as the
+  // scalar offset.
   const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint4*>(fragA + size_t(4 * wave) * 64 * 64), short(0), 4 * 64 * 64 * 16, 0x00020000);
   const int voff = 16 * lane;
