@@ -946,76 +946,125 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqtopk1024_kernel(
   asm volatile("" : "+v"(mone));
 
   const uint4* fa = frag + ((size_t(g) * rbs + (wave < rbs ? wave : 0)) * 4) * 64 * 64 + lane;
+  // B operand of chunk c of tile t (k-steps 4c .. 4c+3), item i = (k-step,
+  // vector block, lane), in two halves: the record loads (into registers, one
+  // chunk ahead of their use, so that their latency is covered by a chunk of
+  // products) and the expansion into LDS
+  struct ChunkRegs {
+    uint32_t by[2][P];
+    uint32_t nr[2];
+  };
+  auto load_chunk = [&](int64_t tile, int c, ChunkRegs& r) {
+    const int64_t nb = tile * 128;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + it * kMqThreads;
+      const int ksl = i >> 8, vb = (i >> 6) & 3, ln = i & 63;
+      const int ks = 4 * c + ksl;
+      const int64_t v = std::min<int64_t>(nb + 32 * vb + (ln & 31), N - 1);
+      const int w = ks >> 1;
+#pragma unroll
+      for (int p = 0; p < P; ++p) r.by[it][p] = planes[((g * P + p) * N + v) * 32 + w];
+      r.nr[it] = norms[g * N + v];
+    }
+  };
+  auto expand = [&](int c, int buf, const ChunkRegs& r) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + it * kMqThreads;
+      const int ksl = i >> 8, vb = (i >> 6) & 3, ln = i & 63;
+      const int ks = 4 * c + ksl;
+      const int bo = 16 * (ks & 1) + 8 * (ln >> 5);
+      uint32_t by[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) by[p] = (r.by[it][p] >> bo) & 0xffu;
+      const uint32_t nr = r.nr[it];
+      const float nu = __builtin_bit_cast(_Float16, uint16_t(nr & 0xffffu));
+      const float rho = __builtin_bit_cast(_Float16, uint16_t(nr >> 16));
+      int e = 0;
+      if (nu > 0.f) (void)frexpf(nu, &e);
+      const float nus = ldexpf(nu, -e), rhos = ldexpf(rho, -e);   // exact
+      const uint32_t rb16 = f2h_bits(rhos);                        // exact: rho~ is a half
+      const uint32_t rr = rb16 | (rb16 << 16);
+      uint32_t ch[4], cl[4], sg[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t idx = 0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) idx |= ((by[p] >> (2 * j)) & 3u) << (2 * p);
+        const uint4 en = s_lut[idx];
+        const float ma = nus * __uint_as_float(en.x), mb = nus * __uint_as_float(en.y);
+        const half2v hv = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ma, mb));
+        const half2v lv = {static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hv[0]), mone, ma)),
+                           static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hv[1]), mone, mb))};
+        ch[j] = __builtin_bit_cast(uint32_t, hv);
+        cl[j] = __builtin_bit_cast(uint32_t, lv);
+        sg[j] = rr ^ en.z;
+      }
+      s_b[buf][ksl][vb][0][ln] = make_uint4(ch[0], ch[1], ch[2], ch[3]);
+      s_b[buf][ksl][vb][1][ln] = make_uint4(cl[0], cl[1], cl[2], cl[3]);
+      s_b[buf][ksl][vb][2][ln] = make_uint4(sg[0], sg[1], sg[2], sg[3]);
+    }
+  };
+  // A fragments of k-step ks (query R q hi, lo; S q hi, lo) in register set
+  // ks % kAr, requested kAr - 1 k-steps before their products
+  constexpr int kAr = 4;   // two ahead: 3.99 ms for workload 4; three ahead: 3.88
+  half8 ar[kAr][4];
+  auto load_a = [&](int ks, half8 (&a)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = __builtin_bit_cast(half8, fa[(t * 64 + ks) * 64]);
+  };
+  auto products = [&](int c, int buf, f32x16 (&acc)[4]) {
+    if (wave < rbs) {
+#pragma unroll
+      for (int ksl = 0; ksl < 4; ++ksl) {
+        const int ks = 4 * c + ksl;
+        load_a((ks + kAr - 1) & 63, ar[(ksl + kAr - 1) % kAr]);   // on into the next tile's first k-steps
+        const half8(&a)[4] = ar[ksl % kAr];
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) {
+          const half8 bh = __builtin_bit_cast(half8, s_b[buf][ksl][vb][0][lane]);
+          const half8 bl = __builtin_bit_cast(half8, s_b[buf][ksl][vb][1][lane]);
+          const half8 bs = __builtin_bit_cast(half8, s_b[buf][ksl][vb][2][lane]);
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], bh, acc[vb], 0, 0, 0);
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[0], bl, acc[vb], 0, 0, 0);
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[1], bh, acc[vb], 0, 0, 0);
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[2], bs, acc[vb], 0, 0, 0);
+          acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[3], bs, acc[vb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (wave < rbs) {
+#pragma unroll
+    for (int i = 0; i < kAr - 1; ++i) load_a(i, ar[i]);
+  }
+  // chunk k of the walk (tile t0 + k / 16, chunk k % 16): its records are
+  // loaded while chunk k - 2 is multiplied, expanded into buffer k % 2 while
+  // chunk k - 1 is; register set k % 2
+  ChunkRegs rg[2];
+  const int64_t nchunks = (t1 - t0) * 16;
+  if (nchunks > 0) load_chunk(t0, 0, rg[0]);
+  if (nchunks > 1) load_chunk(t0, 1, rg[1]);
+  __syncthreads();             // the table
+  if (nchunks > 0) expand(0, 0, rg[0]);
+  __syncthreads();
   for (int64_t tile = t0; tile < t1; ++tile) {
     const int64_t nb = tile * 128;
-    // B operand of chunk c (k-steps 4c .. 4c+3): item i = (k-step, vector block, lane)
-    auto expand = [&](int c, int buf) {
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int i = tid + it * kMqThreads;
-        const int ksl = i >> 8, vb = (i >> 6) & 3, ln = i & 63;
-        const int ks = 4 * c + ksl;
-        const int64_t v = std::min<int64_t>(nb + 32 * vb + (ln & 31), N - 1);
-        const int w = ks >> 1, bo = 16 * (ks & 1) + 8 * (ln >> 5);
-        uint32_t by[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) by[p] = (planes[((g * P + p) * N + v) * 32 + w] >> bo) & 0xffu;
-        const uint32_t nr = norms[g * N + v];
-        const float nu = __builtin_bit_cast(_Float16, uint16_t(nr & 0xffffu));
-        const float rho = __builtin_bit_cast(_Float16, uint16_t(nr >> 16));
-        int e = 0;
-        if (nu > 0.f) (void)frexpf(nu, &e);
-        const float nus = ldexpf(nu, -e), rhos = ldexpf(rho, -e);   // exact
-        const uint32_t rb16 = f2h_bits(rhos);                        // exact: rho~ is a half
-        const uint32_t rr = rb16 | (rb16 << 16);
-        uint32_t ch[4], cl[4], sg[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t idx = 0;
-#pragma unroll
-          for (int p = 0; p < P; ++p) idx |= ((by[p] >> (2 * j)) & 3u) << (2 * p);
-          const uint4 en = s_lut[idx];
-          const float ma = nus * __uint_as_float(en.x), mb = nus * __uint_as_float(en.y);
-          const half2v hv = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(ma, mb));
-          const half2v lv = {static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hv[0]), mone, ma)),
-                             static_cast<_Float16>(__builtin_fmaf(static_cast<float>(hv[1]), mone, mb))};
-          ch[j] = __builtin_bit_cast(uint32_t, hv);
-          cl[j] = __builtin_bit_cast(uint32_t, lv);
-          sg[j] = rr ^ en.z;
-        }
-        s_b[buf][ksl][vb][0][ln] = make_uint4(ch[0], ch[1], ch[2], ch[3]);
-        s_b[buf][ksl][vb][1][ln] = make_uint4(cl[0], cl[1], cl[2], cl[3]);
-        s_b[buf][ksl][vb][2][ln] = make_uint4(sg[0], sg[1], sg[2], sg[3]);
-      }
-    };
+    const int64_t kb = (tile - t0) * 16;
     f32x16 acc[4] = {};
-    __syncthreads();             // the table (first tile) and the previous tile's last reads
-    expand(0, 0);
-    __syncthreads();
-    for (int c = 0; c < 16; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < 16) expand(c + 1, buf ^ 1);
-      if (wave < rbs) {
-#pragma unroll
-        for (int ksl = 0; ksl < 4; ++ksl) {
-          const int ks = 4 * c + ksl;
-          const half8 rh = __builtin_bit_cast(half8, fa[(0 * 64 + ks) * 64]);
-          const half8 rl = __builtin_bit_cast(half8, fa[(1 * 64 + ks) * 64]);
-          const half8 sh = __builtin_bit_cast(half8, fa[(2 * 64 + ks) * 64]);
-          const half8 sl = __builtin_bit_cast(half8, fa[(3 * 64 + ks) * 64]);
-#pragma unroll
-          for (int vb = 0; vb < 4; ++vb) {
-            const half8 bh = __builtin_bit_cast(half8, s_b[buf][ksl][vb][0][lane]);
-            const half8 bl = __builtin_bit_cast(half8, s_b[buf][ksl][vb][1][lane]);
-            const half8 bs = __builtin_bit_cast(half8, s_b[buf][ksl][vb][2][lane]);
-            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, bh, acc[vb], 0, 0, 0);
-            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rh, bl, acc[vb], 0, 0, 0);
-            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rl, bh, acc[vb], 0, 0, 0);
-            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sh, bs, acc[vb], 0, 0, 0);
-            acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sl, bs, acc[vb], 0, 0, 0);
-          }
-        }
-      }
+#pragma unroll 1
+    for (int c = 0; c < 16; c += 2) {
+      // even chunk (buffer 0) multiplied; the odd one (set 1) expanded into
+      // buffer 1; the next even one's records into set 0
+      if (kb + c + 1 < nchunks) expand(c + 1, 1, rg[1]);
+      if (kb + c + 2 < nchunks) load_chunk(t0 + (kb + c + 2) / 16, (c + 2) % 16, rg[0]);
+      products(c, 0, acc);
+      __syncthreads();
+      if (kb + c + 2 < nchunks) expand((c + 2) % 16, 0, rg[0]);
+      if (kb + c + 3 < nchunks) load_chunk(t0 + (kb + c + 3) / 16, (c + 3) % 16, rg[1]);
+      products(c + 1, 1, acc);
       __syncthreads();
     }
     if (wave < rbs) {
