@@ -801,11 +801,36 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict_
   const int64_t gq = blockIdx.x;
   float ms = -__builtin_huge_valf();
   int32_t mi = 0x7fffffff;
-  for (int r = 0; r < ranges; ++r)
-    for (int j = 0; j < K; ++j) {
-      const int64_t at = (gq * ranges + r) * K + j;
-      list_insert(ms, mi, tk_s[at], tk_i[at], lane, K);
+  // the query's ranges x K candidates, 64 per wave step and eight steps'
+  // loads in flight; only candidates better than the current K-th are
+  // inserted (the order of equal scores is by index, so the result does not
+  // depend on the order of insertion)
+  constexpr int U = 8;
+  const int64_t total = int64_t(ranges) * K;
+  const float* cs_q = tk_s + gq * total;
+  const int32_t* ci_q = tk_i + gq * total;
+  for (int64_t base = 0; base < total; base += 64 * U) {
+    float cs[U];
+    int32_t ci[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t at = base + u * 64 + lane;
+      cs[u] = at < total ? cs_q[at] : -__builtin_huge_valf();
+      ci[u] = at < total ? ci_q[at] : 0x7fffffff;
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float t_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ms), K - 1));
+      const int32_t t_i = __builtin_amdgcn_readlane(mi, K - 1);
+      uint64_t m = __builtin_amdgcn_ballot_w64(better(cs[u], ci[u], t_s, t_i));
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        list_insert(ms, mi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs[u]), b)),
+                    __builtin_amdgcn_readlane(ci[u], b), lane, K);
+      }
+    }
+  }
   if (lane < K) {
     const bool some = mi != 0x7fffffff;
     out_i[gq * K + lane] = some ? mi : -1;
