@@ -967,6 +967,13 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqtopk1024_kernel(
   int32_t li[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) { ls[k] = -__builtin_huge_valf(); li[k] = 0x7fffffff; }
+  // each query's current k-th score (wave-uniform), read again only after an
+  // insertion into its list
+  float thr_s[8][4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) thr_s[k][r] = -__builtin_huge_valf();
   float mone = -1.0f;
   asm volatile("" : "+v"(mone));
 
@@ -1109,15 +1116,18 @@ __global__ __launch_bounds__(kMqThreads, 1) void mqtopk1024_kernel(
           for (int hs = 0; hs < 2; ++hs) {
             const int r = 8 * (a >> 2) + 4 * hs + (a & 3);
             const int reg = r >> 2, row = r & 3;
-            const float t_s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[reg]), 16 * row + K - 1));
-            const int32_t t_i = __builtin_amdgcn_readlane(li[reg], 16 * row + K - 1);
-            uint64_t m = __builtin_amdgcn_ballot_w64(valid && h == hs && better(sc, int32_t(v), t_s, t_i));
-            while (m) {
-              const int b = __builtin_ctzll(m);
-              m &= m - 1;
-              const float cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), b));
-              const int32_t ci = __builtin_amdgcn_readlane(int32_t(v), b);
-              row_insert(ls[reg], li[reg], cs, ci, lane, row, K);
+            // (a superset of the candidates that beat the k-th; row_insert
+            // places each exactly and drops the rest)
+            uint64_t m = __builtin_amdgcn_ballot_w64(valid && h == hs && sc >= thr_s[reg][row]);
+            if (m) {
+              while (m) {
+                const int b = __builtin_ctzll(m);
+                m &= m - 1;
+                const float cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), b));
+                const int32_t ci = __builtin_amdgcn_readlane(int32_t(v), b);
+                row_insert(ls[reg], li[reg], cs, ci, lane, row, K);
+              }
+              thr_s[reg][row] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[reg]), 16 * row + K - 1));
             }
           }
         }
