@@ -102,7 +102,7 @@ def test_wide_encode_search_workload_sample():
     _encode_check(wl.bits, keys, torch.float32)
 
 
-def test_wide_encode_chunk_boundary():
+def test_wide_encode_many_tiles_per_workgroup():
     """65,836 keys: every workgroup walks several 32-key tiles (the fragment
     ring and the key prefetch run on from tile to tile), and records late in
     the launch are encoded exactly like the same keys early in it."""
